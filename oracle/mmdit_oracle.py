@@ -1,0 +1,307 @@
+"""Float64 CPU oracle of the dual-stream MMDiT block core.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the bench's CPU-baseline leg
+import this module.  The product path (the HIP library and its binding) never calls it,
+shares no code with it, and is not imported by it.
+
+Each function is the plain definition of one step, evaluated in float64 with numpy.
+Sources (page title, then section):
+- [Vimoo] "Vimoo 1.0: Video Generation for Compact, Lightweight, and High-Speed",
+  section 2.2 "Dual-Stream MMDiT Backbone": per-stream Q/K/V projections, joint attention
+  over the concatenated sequences, split back; per-stream output projections and FFNs;
+  timestep modulation to six C-vectors (shift/scale/gate for attention and FFN) from a
+  shared 1536-d bottleneck; LayerNorm before attention and FFN; per-head RMSNorm on Q and
+  K with distinct learned scales; 3D RoPE split 16/56/56 over (t, h, w) on visual Q/K only.
+  Section 2.4 fixes the modulation Linear's shape through its parameter counts.
+- [Wan-zh] Wan 2.1 report, Chinese translation, section 4: 4.1.1 (VAE 4x8x8, 16 ch),
+  4.2.1 (patchify (1,2,2), L = (1+T/4)*H/16*W/16), 4.3.1 (forward attention cost factor 4).
+- [Wan-guide] reading guide to the Wan report: the DiT's attention is non-causal.
+
+Readings where the pages leave a step open (each one is listed with its reason in the
+design notes of the repository):
+  r1 modulation form LN(x)*(1+scale)+shift; r2 vector order shift_a, scale_a, gate_a,
+  shift_f, scale_f, gate_f; r3 tvec enters the modulation Linear as given; r4 LayerNorm
+  eps 1e-6, no affine; r5 every Linear has a bias; r6 QK-norm scale [D] per stream and q/k
+  (a per-head [H, D] scale is also accepted); r7 RMSNorm before RoPE; r8 RoPE rotates
+  interleaved pairs (2j, 2j+1) inside each band; r9 each band has its own frequency ladder
+  base^(-2j/d_band); r10 bands in t, h, w order; r11 0-based integer positions; r12 tokens
+  flattened (t, h, w) row-major, w fastest; r13 no YaRN; r14 no attention mask;
+  r16 exact erf GELU; r18 parity metric max|err| / rms(oracle) per output tensor.
+
+Tensor conventions: tokens [B, N, ...]; heads split as [B, N, H, D] with head-major
+channels (channel c = head * D + d).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+# ------------------------------------------------------------------ 3D RoPE  [Vimoo 2.2]
+
+
+def token_positions(grid: Tuple[int, int, int]) -> np.ndarray:
+    """(t, h, w) of each visual token, flattened row-major with w fastest (r12).  [N, 3]."""
+    t_n, h_n, w_n = grid
+    n = np.arange(t_n * h_n * w_n)
+    return np.stack([n // (h_n * w_n), (n // w_n) % h_n, n % w_n], axis=1)
+
+
+def rope_angles(grid: Tuple[int, int, int], split: Sequence[int] = (16, 56, 56),
+                base: float = 10000.0) -> np.ndarray:
+    """Rotation angle of every (token, pair): [N, D/2].
+
+    The head dims are cut into three bands, temporal / vertical / horizontal (r10).  Pair j
+    of a band of width d_a turns by pos_a * base^(-2j/d_a) (r9), pos_a the token's integer
+    coordinate on that axis (r11).
+    """
+    pos = token_positions(grid).astype(np.float64)
+    cols = []
+    for axis, d_a in enumerate(split):
+        if d_a % 2:
+            raise ValueError("RoPE band widths must be even")
+        j = np.arange(d_a // 2, dtype=np.float64)
+        freq = base ** (-2.0 * j / d_a)
+        cols.append(pos[:, axis:axis + 1] * freq[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def rope_rotate(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """Rotate interleaved pairs (x[2j], x[2j+1]) by angles[..., j] (r8).
+
+    x: [B, N, H, D]; angles: [N, D/2] (broadcast over batch and heads)."""
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    c = np.cos(angles)[None, :, None, :]
+    s = np.sin(angles)[None, :, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+# ------------------------------------------------------------ QK RMSNorm  [Vimoo 2.2]
+
+
+def rms_norm_heads(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Per-(token, head) RMSNorm over the head dim, times the learned scale g.
+
+    x: [B, N, H, D]; g: [D] shared by all heads, or [H, D] per head (r6)."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    g = np.asarray(g, dtype=np.float64)
+    g = g[None, None, None, :] if g.ndim == 1 else g[None, None, :, :]
+    return x / np.sqrt(ms + eps) * g
+
+
+def qk_norm_rope(q: np.ndarray, k: np.ndarray, gq: np.ndarray, gk: np.ndarray, eps: float,
+                 grid: Optional[Tuple[int, int, int]] = None,
+                 split: Sequence[int] = (16, 56, 56), base: float = 10000.0):
+    """RMSNorm on q and k with their own scales, then 3D RoPE when ``grid`` is given
+    (visual stream); the conditioning stream passes ``grid=None`` and gets no rotation (r7)."""
+    qn = rms_norm_heads(q, gq, eps)
+    kn = rms_norm_heads(k, gk, eps)
+    if grid is not None:
+        ang = rope_angles(grid, split, base)
+        if ang.shape[0] != q.shape[1]:
+            raise ValueError("visual token count differs from T*H*W")
+        qn = rope_rotate(qn, ang)
+        kn = rope_rotate(kn, ang)
+    return qn, kn
+
+
+# ------------------------------------------------------- joint attention  [Vimoo 2.2]
+
+
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(q k^T * scale) v for one batch item and head, no mask (r14).
+    q: [M, D]; k, v: [N, D]."""
+    s = (q @ k.T) * scale
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def joint_attention(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
+                    scale: Optional[float] = None,
+                    vis_rows: Optional[np.ndarray] = None,
+                    cond_rows: Optional[np.ndarray] = None,
+                    chunk: int = 2048):
+    """Joint non-causal attention over the concatenated conditioning and visual tokens,
+    split back into the two streams.
+
+    Inputs [B, N_s, H, D] (already normalised and rotated).  The concatenation order does not
+    change any output, so the keys are taken as [cond | vis].  ``vis_rows`` / ``cond_rows``
+    restrict the output to those query rows (every key is still used); queries are
+    evaluated in chunks of ``chunk`` rows to bound the [chunk, N] score block.
+    Returns (o_vis, o_cond), each [B, rows, H, D].
+    """
+    b, _, h, d = q_vis.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    k_all = np.concatenate([k_cond, k_vis], axis=1)
+    v_all = np.concatenate([v_cond, v_vis], axis=1)
+
+    def run(q, rows):
+        if rows is not None:
+            q = q[:, rows]
+        out = np.empty(q.shape, dtype=np.float64)
+        for bi in range(b):
+            for hi in range(h):
+                kk = k_all[bi, :, hi, :]
+                vv = v_all[bi, :, hi, :]
+                for r0 in range(0, q.shape[1], chunk):
+                    out[bi, r0:r0 + chunk, hi, :] = softmax_attention(
+                        q[bi, r0:r0 + chunk, hi, :], kk, vv, scale)
+        return out
+
+    return run(q_vis, vis_rows), run(q_cond, cond_rows)
+
+
+def attention_block(inp: Dict[str, np.ndarray], grid, eps: float,
+                    split=(16, 56, 56), base: float = 10000.0,
+                    vis_rows=None, cond_rows=None):
+    """QK-RMSNorm (+ RoPE on visual) then joint attention: the attention-only workloads.
+    ``inp`` holds float64 q/k/v_{vis,cond} [B,N,H,D] and gq/gk_{vis,cond}.
+    Returns dict with qh/kh for both streams and o_vis / o_cond."""
+    qv, kv = qk_norm_rope(inp["q_vis"], inp["k_vis"], inp["gq_vis"], inp["gk_vis"], eps,
+                          grid, split, base)
+    qc, kc = qk_norm_rope(inp["q_cond"], inp["k_cond"], inp["gq_cond"], inp["gk_cond"], eps)
+    o_v, o_c = joint_attention(qv, kv, inp["v_vis"], qc, kc, inp["v_cond"],
+                               vis_rows=vis_rows, cond_rows=cond_rows)
+    return {"qh_vis": qv, "kh_vis": kv, "qh_cond": qc, "kh_cond": kc,
+            "o_vis": o_v, "o_cond": o_c}
+
+
+# ------------------------------------------------- modulation, LN, FFN  [Vimoo 2.2]
+
+MOD_ORDER = ("shift_a", "scale_a", "gate_a", "shift_f", "scale_f", "gate_f")   # r2
+
+
+def modulation_param_count(width: int, t_dim: int) -> int:
+    """Parameters of one per-(block, stream) modulation Linear t_dim -> 6*width, with bias."""
+    return 6 * width * t_dim + 6 * width
+
+
+def modulation(w_mod: np.ndarray, b_mod: np.ndarray, tvec: np.ndarray) -> Dict[str, np.ndarray]:
+    """mod = W_mod @ tvec + b_mod (tvec enters as given, r3), cut into six C-vectors.
+    w_mod [6C, Dt]; tvec [B, Dt] -> each vector [B, C]."""
+    m = tvec @ w_mod.T + b_mod[None, :]
+    c = w_mod.shape[0] // 6
+    return {name: m[:, i * c:(i + 1) * c] for i, name in enumerate(MOD_ORDER)}
+
+
+def layer_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """LayerNorm over the last dim, biased variance, no affine (r4)."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def modulate(xn: np.ndarray, shift: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Shift and scale the normalised features (r1).  xn [B, N, C]; shift/scale [B, C]."""
+    return xn * (1.0 + scale[:, None, :]) + shift[:, None, :]
+
+
+def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """nn.Linear: x @ w^T + b, w in [out, in] layout (r5)."""
+    y = x @ w.T
+    return y if b is None else y + b
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU x * Phi(x) (r16)."""
+    from scipy.special import erf
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def block_forward(x_vis: np.ndarray, x_cond: np.ndarray, tvec: np.ndarray,
+                  w_vis: Dict[str, np.ndarray], w_cond: Dict[str, np.ndarray],
+                  grid: Tuple[int, int, int], heads: int,
+                  ln_eps: float = 1e-6, qk_eps: float = 1e-6,
+                  split=(16, 56, 56), base: float = 10000.0,
+                  vis_rows: Optional[np.ndarray] = None,
+                  cond_rows: Optional[np.ndarray] = None,
+                  keep: bool = True) -> Dict[str, np.ndarray]:
+    """One dual-stream block forward [Vimoo 2.2].
+
+    Per stream s: mod_s from the shared tvec; h = LN(x)*(1+scale_a)+shift_a;
+    [q|k|v] = h W_qkv^T + b; QK-RMSNorm, RoPE on visual; joint attention over both streams;
+    a = O W_o^T + b_o; x1 = x + gate_a*a; h2 = LN(x1)*(1+scale_f)+shift_f;
+    out = x1 + gate_f * (GELU(h2 W_1^T + b_1) W_2^T + b_2).
+
+    Every key and value is computed; ``vis_rows`` / ``cond_rows`` restrict the per-query
+    work after the K/V projection to those rows.  Returns the outputs and (``keep``) the
+    intermediates of the same rows, keyed ``<name>_vis`` / ``<name>_cond``.
+    """
+    c = x_vis.shape[-1]
+    d = c // heads
+    res: Dict[str, np.ndarray] = {}
+    qkv = {}
+    mods = {}
+    for s, x, w, rows in (("vis", x_vis, w_vis, vis_rows), ("cond", x_cond, w_cond, cond_rows)):
+        mods[s] = modulation(w[ "w_mod"], w["b_mod"], tvec)
+        m = mods[s]
+        h = modulate(layer_norm(x, ln_eps), m["shift_a"], m["scale_a"])
+        b_, n_ = x.shape[:2]
+        # K and V of every token; Q of the requested rows only.
+        w_q, w_k, w_v = np.split(w["w_qkv"], 3, axis=0)
+        b_q, b_k, b_v = np.split(w["b_qkv"], 3)
+        hq = h if rows is None else h[:, rows]
+        q = linear(hq, w_q, b_q).reshape(b_, hq.shape[1], heads, d)
+        k = linear(h, w_k, b_k).reshape(b_, n_, heads, d)
+        v = linear(h, w_v, b_v).reshape(b_, n_, heads, d)
+        qkv[s] = (q, k, v)
+        if keep:
+            res[f"h_{s}"] = hq
+            res[f"mod_{s}"] = np.concatenate([m[nm] for nm in MOD_ORDER], axis=-1)
+    q_v, k_v, v_v = qkv["vis"]
+    q_c, k_c, v_c = qkv["cond"]
+    # RMSNorm on every k; RoPE needs each row's own position.
+    k_v = rms_norm_heads(k_v, w_vis["k_norm"], qk_eps)
+    k_v = rope_rotate(k_v, rope_angles(grid, split, base))
+    q_v = rms_norm_heads(q_v, w_vis["q_norm"], qk_eps)
+    ang = rope_angles(grid, split, base)
+    q_v = rope_rotate(q_v, ang if vis_rows is None else ang[vis_rows])
+    k_c = rms_norm_heads(k_c, w_cond["k_norm"], qk_eps)
+    q_c = rms_norm_heads(q_c, w_cond["q_norm"], qk_eps)
+    o_v, o_c = joint_attention(q_v, k_v, v_v, q_c, k_c, v_c)
+    if keep:
+        res["qh_vis"], res["qh_cond"] = q_v, q_c
+    for s, x, w, rows, o in (("vis", x_vis, w_vis, vis_rows, o_v),
+                             ("cond", x_cond, w_cond, cond_rows, o_c)):
+        m = mods[s]
+        xs = x if rows is None else x[:, rows]
+        o = o.reshape(o.shape[0], o.shape[1], c)
+        a = linear(o, w["w_o"], w["b_o"])
+        x1 = xs + m["gate_a"][:, None, :] * a
+        h2 = modulate(layer_norm(x1, ln_eps), m["shift_f"], m["scale_f"])
+        g = gelu(linear(h2, w["w_fc1"], w["b_fc1"]))
+        out = x1 + m["gate_f"][:, None, :] * linear(g, w["w_fc2"], w["b_fc2"])
+        res[f"out_{s}"] = out
+        if keep:
+            res[f"o_{s}"] = o
+            res[f"x1_{s}"] = x1
+            res[f"h2_{s}"] = h2
+    return res
+
+
+# ------------------------------------------------------------------ parity metric (r18)
+
+
+def rel_max_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / sqrt(mean(ref^2)), in float64."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref))) / rms if rms > 0 else float(np.max(np.abs(got - ref)))
+
+
+# ------------------------------------------------------------------ FLOP accounting
+
+
+def attention_flops(n_tokens: int, head_dim: int, heads: int, batch: int = 1) -> float:
+    """Forward non-causal attention cost with factor 4 on s^2*h ([Wan-zh] 4.3.1):
+    two N x N x D products per head, 2 FLOP per multiply-add."""
+    return 4.0 * n_tokens * n_tokens * head_dim * heads * batch

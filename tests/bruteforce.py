@@ -1,0 +1,146 @@
+"""Loop-based pure-Python recomputation of the block for tiny inputs.
+
+Independent of ``oracle/``: written from the definitions in the Vimoo 1.0 notes
+(section 2.2) with plain Python floats and the ``math`` module only (no numpy), so a
+mistake in the vectorised oracle (a wrong axis, a transposed weight, a swapped band)
+shows up as a mismatch.  Tensors are nested lists.
+"""
+import math
+
+
+def decode_position(n, grid):
+    """Visual token index -> (t, h, w), w fastest."""
+    _, hh, ww = grid
+    t = n // (hh * ww)
+    rem = n - t * hh * ww
+    return t, rem // ww, rem % ww
+
+
+def pair_angle(pair, pos, split, base):
+    """Angle of rotation pair ``pair`` (0 .. D/2-1) for a token at ``pos`` = (t, h, w)."""
+    start = 0
+    for axis in range(3):
+        width = split[axis]
+        if 2 * pair < start + width:
+            j = pair - start // 2
+            return pos[axis] * base ** (-(2.0 * j) / width)
+        start += width
+    raise ValueError("pair out of range")
+
+
+def rmsnorm_vec(x, g, eps):
+    ms = sum(v * v for v in x) / len(x)
+    r = 1.0 / math.sqrt(ms + eps)
+    return [v * r * gg for v, gg in zip(x, g)]
+
+
+def rope_vec(x, pos, split, base):
+    out = list(x)
+    for p in range(len(x) // 2):
+        a = pair_angle(p, pos, split, base)
+        c, s = math.cos(a), math.sin(a)
+        x0, x1 = x[2 * p], x[2 * p + 1]
+        out[2 * p] = x0 * c - x1 * s
+        out[2 * p + 1] = x0 * s + x1 * c
+    return out
+
+
+def attention_rows(qs, ks, vs, scale):
+    """qs: list of query vectors; ks, vs: lists of key / value vectors (one head)."""
+    outs = []
+    for q in qs:
+        logits = [scale * sum(a * b for a, b in zip(q, k)) for k in ks]
+        m = max(logits)
+        w = [math.exp(l - m) for l in logits]
+        z = sum(w)
+        d = len(vs[0])
+        outs.append([sum(w[j] * vs[j][i] for j in range(len(vs))) / z for i in range(d)])
+    return outs
+
+
+def attention_block(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond, gq_vis, gk_vis, gq_cond, gk_cond,
+                    grid, eps, split=(16, 56, 56), base=10000.0):
+    """Per-head lists: x[n][h] is a D-vector.  Returns (o_vis, o_cond) as nested lists."""
+    n_vis, n_cond = len(q_vis), len(q_cond)
+    heads = len(q_vis[0]) if n_vis else len(q_cond[0])
+    d = len(q_vis[0][0]) if n_vis else len(q_cond[0][0])
+    scale = 1.0 / math.sqrt(d)
+    o_vis = [[None] * heads for _ in range(n_vis)]
+    o_cond = [[None] * heads for _ in range(n_cond)]
+    for h in range(heads):
+        qv, kv, qc, kc = [], [], [], []
+        for n in range(n_vis):
+            pos = decode_position(n, grid)
+            qv.append(rope_vec(rmsnorm_vec(q_vis[n][h], gq_vis, eps), pos, split, base))
+            kv.append(rope_vec(rmsnorm_vec(k_vis[n][h], gk_vis, eps), pos, split, base))
+        for n in range(n_cond):
+            qc.append(rmsnorm_vec(q_cond[n][h], gq_cond, eps))
+            kc.append(rmsnorm_vec(k_cond[n][h], gk_cond, eps))
+        # keys in visual-then-conditioning order (the opposite of the oracle's choice)
+        keys = kv + kc
+        vals = [v_vis[n][h] for n in range(n_vis)] + [v_cond[n][h] for n in range(n_cond)]
+        for n, o in enumerate(attention_rows(qv, keys, vals, scale)):
+            o_vis[n][h] = o
+        for n, o in enumerate(attention_rows(qc, keys, vals, scale)):
+            o_cond[n][h] = o
+    return o_vis, o_cond
+
+
+def matvec(w, x, b):
+    """w: list of rows [out][in]; returns w x + b."""
+    return [sum(wi * xi for wi, xi in zip(row, x)) + bb for row, bb in zip(w, b)]
+
+
+def layernorm_vec(x, eps):
+    mu = sum(x) / len(x)
+    var = sum((v - mu) ** 2 for v in x) / len(x)
+    r = 1.0 / math.sqrt(var + eps)
+    return [(v - mu) * r for v in x]
+
+
+def gelu(x):
+    return 0.5 * x * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+
+def block_forward(x_vis, x_cond, tvec, w_vis, w_cond, grid, heads, ln_eps, qk_eps,
+                  split=(16, 56, 56), base=10000.0):
+    """x_*: [N][C] lists; tvec: [Dt] list; w_*: dict of nested lists (nn.Linear [out][in])."""
+    c = len(x_vis[0]) if x_vis else len(x_cond[0])
+    d = c // heads
+    streams = {"vis": (x_vis, w_vis), "cond": (x_cond, w_cond)}
+    mod, qkv = {}, {}
+    for s, (x, w) in streams.items():
+        m = matvec(w["w_mod"], tvec, w["b_mod"])
+        mod[s] = [m[i * c:(i + 1) * c] for i in range(6)]
+        shift_a, scale_a = mod[s][0], mod[s][1]
+        rows = []
+        for xt in x:
+            hn = layernorm_vec(xt, ln_eps)
+            hm = [v * (1.0 + sc) + sh for v, sc, sh in zip(hn, scale_a, shift_a)]
+            rows.append(matvec(w["w_qkv"], hm, w["b_qkv"]))
+        qkv[s] = rows
+
+    def split_heads(rows, part):
+        return [[r[part * c + h * d: part * c + (h + 1) * d] for h in range(heads)] for r in rows]
+
+    o_vis, o_cond = attention_block(
+        split_heads(qkv["vis"], 0), split_heads(qkv["vis"], 1), split_heads(qkv["vis"], 2),
+        split_heads(qkv["cond"], 0), split_heads(qkv["cond"], 1), split_heads(qkv["cond"], 2),
+        w_vis["q_norm"], w_vis["k_norm"], w_cond["q_norm"], w_cond["k_norm"],
+        grid, qk_eps, split, base)
+    outs = {}
+    for s, o_s in (("vis", o_vis), ("cond", o_cond)):
+        x, w = streams[s]
+        _, _, gate_a, shift_f, scale_f, gate_f = mod[s]
+        res = []
+        for xt, oh in zip(x, o_s):
+            o = [v for head in oh for v in head]
+            a = matvec(w["w_o"], o, w["b_o"])
+            x1 = [xv + g * av for xv, g, av in zip(xt, gate_a, a)]
+            hn = layernorm_vec(x1, ln_eps)
+            h2 = [v * (1.0 + sc) + sh for v, sc, sh in zip(hn, scale_f, shift_f)]
+            f = [gelu(v) for v in matvec(w["w_fc1"], h2, w["b_fc1"])]
+            y = matvec(w["w_fc2"], f, w["b_fc2"])
+            res.append([xv + g * yv for xv, g, yv in zip(x1, gate_f, y)])
+        outs[s] = res
+    return outs["vis"], outs["cond"]

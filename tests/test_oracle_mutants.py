@@ -1,0 +1,153 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each.
+
+Every mutant below is a one-line slip someone could make while writing the oracle: a
+dropped term, a wrong sign, a swapped axis or index, a transposed operand.  The pin suite
+in ``test_oracle_pins.py`` must fail for every one of them.
+"""
+import inspect
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.mmdit_oracle as om
+from tests import test_oracle_pins as pins
+
+ORIG = {name: getattr(om, name) for name in
+        ("rope_angles", "rope_rotate", "token_positions", "rms_norm_heads", "softmax_attention",
+         "modulate", "layer_norm", "linear", "gelu", "modulation", "joint_attention")}
+
+
+def _rope_sign(x, angles):
+    out = ORIG["rope_rotate"](x, -angles)
+    return out
+
+
+def _band_order(grid, split=(16, 56, 56), base=10000.0):
+    a = ORIG["rope_angles"](grid, split, base)
+    return np.concatenate([a[:, 8:36], a[:, :8], a[:, 36:]], axis=1)
+
+
+def _positions_hw_swapped(grid):
+    p = ORIG["token_positions"](grid)
+    return p[:, [0, 2, 1]]
+
+
+def _ladder_full_width(grid, split=(16, 56, 56), base=10000.0):
+    pos = ORIG["token_positions"](grid).astype(np.float64)
+    cols = []
+    for axis, d_a in enumerate(split):
+        j = np.arange(d_a // 2)
+        cols.append(pos[:, axis:axis + 1] * (base ** (-2.0 * j / 128))[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def _rope_half_split(x, angles):
+    d = x.shape[-1]
+    x0, x1 = x[..., :d // 2], x[..., d // 2:]
+    c = np.cos(angles)[None, :, None, :]
+    s = np.sin(angles)[None, :, None, :]
+    return np.concatenate([x0 * c - x1 * s, x0 * s + x1 * c], axis=-1)
+
+
+def _rms_no_eps(x, g, eps):
+    return ORIG["rms_norm_heads"](x, g, 0.0)
+
+
+def _rms_sum(x, g, eps):
+    return ORIG["rms_norm_heads"](x, g, eps) / math.sqrt(x.shape[-1])
+
+
+def _attn_scale_d(q, k, v, scale):
+    return ORIG["softmax_attention"](q, k, v, scale * scale)
+
+
+def _attn_axis(q, k, v, scale):
+    s = (q @ k.T) * scale
+    p = np.exp(s - s.max())
+    p /= p.sum(axis=0, keepdims=True)
+    return p @ v
+
+
+def _mod_no_shift(xn, shift, scale):
+    return ORIG["modulate"](xn, 0.0 * shift, scale)
+
+
+def _mod_plain_scale(xn, shift, scale):
+    return xn * scale[:, None, :] + shift[:, None, :]
+
+
+def _ln_unbiased(x, eps):
+    mu = x.mean(axis=-1, keepdims=True)
+    var = x.var(axis=-1, ddof=1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def _linear_transposed(x, w, b):
+    if w.shape[0] == w.shape[1]:
+        w = w.T
+    return ORIG["linear"](x, w, b)
+
+
+def _linear_no_bias(x, w, b):
+    return ORIG["linear"](x, w, None)
+
+
+def _gelu_tanh(x):
+    return 0.5 * x * (1 + np.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _modulation_swapped(w, b, t):
+    m = ORIG["modulation"](w, b, t)
+    m["gate_a"], m["gate_f"] = m["gate_f"], m["gate_a"]
+    return m
+
+
+def _modulation_order(w, b, t):
+    m = ORIG["modulation"](w, b, t)
+    m["shift_a"], m["scale_a"] = m["scale_a"], m["shift_a"]
+    return m
+
+
+def _joint_drop_cond_keys(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond, **kw):
+    e = k_cond[:, :0]
+    return ORIG["joint_attention"](q_vis, k_vis, v_vis, q_cond, e, v_cond[:, :0], **kw)
+
+
+MUTANTS = {
+    "rope_sign": ("rope_rotate", _rope_sign),
+    "rope_band_order": ("rope_angles", _band_order),
+    "positions_hw_swapped": ("token_positions", _positions_hw_swapped),
+    "rope_ladder_full_width": ("rope_angles", _ladder_full_width),
+    "rope_half_split_pairs": ("rope_rotate", _rope_half_split),
+    "rmsnorm_no_eps": ("rms_norm_heads", _rms_no_eps),
+    "rmsnorm_sum_not_mean": ("rms_norm_heads", _rms_sum),
+    "attn_scale_1_over_d": ("softmax_attention", _attn_scale_d),
+    "attn_softmax_axis": ("softmax_attention", _attn_axis),
+    "modulate_no_shift": ("modulate", _mod_no_shift),
+    "modulate_scale_not_1p": ("modulate", _mod_plain_scale),
+    "layernorm_unbiased": ("layer_norm", _ln_unbiased),
+    "linear_transposed": ("linear", _linear_transposed),
+    "linear_no_bias": ("linear", _linear_no_bias),
+    "gelu_tanh": ("gelu", _gelu_tanh),
+    "gates_swapped": ("modulation", _modulation_swapped),
+    "shift_scale_swapped": ("modulation", _modulation_order),
+    "cond_keys_dropped": ("joint_attention", _joint_drop_cond_keys),
+}
+
+PIN_TESTS = [f for name, f in inspect.getmembers(pins, inspect.isfunction) if name.startswith("test_")]
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(mutant, monkeypatch):
+    name, fn = MUTANTS[mutant]
+    monkeypatch.setattr(om, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+    failed = []
+    for t in PIN_TESTS:
+        try:
+            t()
+        except Exception:
+            failed.append(t.__name__)
+    assert failed, f"no pin caught mutant {mutant}"

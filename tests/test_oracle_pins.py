@@ -1,0 +1,377 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+None of these recomputes the oracle's own formula: each checks a printed figure, a closed
+form, an invariant, a special case that reduces to a library routine (torch float64), or a
+brute-force loop implementation on tiny inputs (``bruteforce.py``).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as wl
+from tests import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng0 = np.random.default_rng(1234)
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([float(t) for t in line.split()])
+    return rows
+
+
+# ------------------------------------------------------------------ printed figures
+
+
+def test_modulation_linear_shape_matches_printed_parameter_counts():
+    """Vimoo 1.0 section 2.4: 80 per-(block, stream) Linears bottleneck -> 6*3072 with bias,
+    plus one shared 3072 -> bottleneck projection, total 2.271 B (0.025 B at width 16)."""
+    for dt, printed in _golden_rows("modulation_params.txt"):
+        dt = int(dt)
+        total = 80 * oracle.modulation_param_count(3072, dt) + (3072 * dt + dt)
+        assert round(total / 1e9, 3) == printed
+        # the shape the oracle consumes is the one counted
+        w = np.zeros((6 * 3072, dt))
+        b = np.zeros(6 * 3072)
+        assert w.size + b.size == oracle.modulation_param_count(3072, dt)
+
+
+def test_token_grid_matches_vae_and_patchify_arithmetic():
+    for frames, hgt, wid, t, h, w, n in _golden_rows("token_grid.txt"):
+        grid = wl.latent_grid(int(frames), int(hgt), int(wid))
+        assert grid == (int(t), int(h), int(w))
+        assert grid[0] * grid[1] * grid[2] == int(n)
+    assert wl.ATTN_480P.grid == (21, 30, 52) and wl.ATTN_720P.grid == (21, 45, 80)
+
+
+def test_attention_flop_factor():
+    """Wan report 4.3.1: forward non-causal attention costs 4*b*s^2*h; with h = H*D."""
+    assert oracle.attention_flops(33272, 128, 24) == 4 * 33272 ** 2 * 3072
+    assert abs(oracle.attention_flops(33272, 128, 24) / 1e12 - 13.603) < 1e-3
+
+
+# ------------------------------------------------------------------ RoPE
+
+
+def test_rope_angles_closed_forms():
+    grid = (3, 5, 7)
+    ang = oracle.rope_angles(grid)
+    assert ang.shape == (105, 64)
+    assert np.all(ang[0] == 0.0)                        # identity at (0, 0, 0)
+    n_t1 = 1 * 5 * 7                                    # (t,h,w) = (1,0,0)
+    assert ang[n_t1, 0] == 1.0                          # e0 at t=1 turns by 1 rad
+    assert np.all(ang[n_t1, 8:] == 0.0)                 # h and w bands untouched
+    assert math.isclose(ang[n_t1, 1], 10000 ** (-2 / 16), rel_tol=1e-15)
+    n_h1 = 7                                            # (0,1,0)
+    assert np.all(ang[n_h1, :8] == 0.0) and np.all(ang[n_h1, 36:] == 0.0)
+    assert ang[n_h1, 8] == 1.0                          # dims 16,17
+    assert math.isclose(ang[n_h1, 9], 10000 ** (-2 / 56), rel_tol=1e-15)   # dims 18,19
+    n_w3 = 3                                            # (0,0,3)
+    assert np.all(ang[n_w3, :36] == 0.0)
+    assert ang[n_w3, 36] == 3.0                         # dims 72,73
+    assert math.isclose(ang[n_w3, 63], 3 * 10000 ** (-54 / 56), rel_tol=1e-14)
+    n_mix = 2 * 35 + 4 * 7 + 6                          # (2,4,6)
+    assert ang[n_mix, 0] == 2.0 and ang[n_mix, 8] == 4.0 and ang[n_mix, 36] == 6.0
+
+
+def test_rope_rotation_of_unit_vectors():
+    grid = (2, 2, 2)
+    x = np.zeros((1, 8, 1, 128))
+    x[0, :, 0, 0] = 1.0       # e0
+    x[0, :, 0, 19] = 1.0      # e19 (second component of the h band's pair 1)
+    y = oracle.rope_rotate(x, oracle.rope_angles(grid))
+    n = 4                     # (1,0,0)
+    assert math.isclose(y[0, n, 0, 0], math.cos(1.0), abs_tol=1e-15)
+    assert math.isclose(y[0, n, 0, 1], math.sin(1.0), abs_tol=1e-15)
+    n = 2                     # (0,1,0): pair 9 (dims 18, 19) turns by 10000^(-2/56)
+    phi = 10000 ** (-2 / 56)
+    assert math.isclose(y[0, n, 0, 18], -math.sin(phi), abs_tol=1e-15)
+    assert math.isclose(y[0, n, 0, 19], math.cos(phi), abs_tol=1e-15)
+    assert y[0, n, 0, 0] == 1.0
+
+
+def test_rope_preserves_norm_per_pair_and_matches_complex_rotation():
+    grid = (2, 3, 4)
+    x = rng0.standard_normal((2, 24, 3, 128))
+    ang = oracle.rope_angles(grid)
+    y = oracle.rope_rotate(x, ang)
+    pn = lambda a: a[..., 0::2] ** 2 + a[..., 1::2] ** 2  # noqa: E731
+    np.testing.assert_allclose(pn(y), pn(x), rtol=1e-12)
+    # complex form z * exp(i*phi), phi from the brute-force band lookup
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    phi = np.array([[bf.pair_angle(p, bf.decode_position(n, grid), (16, 56, 56), 10000.0)
+                     for p in range(64)] for n in range(24)])
+    w = z * np.exp(1j * phi)[None, :, None, :]
+    np.testing.assert_allclose(y[..., 0::2], w.real, atol=1e-12)
+    np.testing.assert_allclose(y[..., 1::2], w.imag, atol=1e-12)
+
+
+def test_rope_logits_depend_only_on_relative_position():
+    grid = (4, 5, 6)
+    ang = oracle.rope_angles(grid)
+    q = rng0.standard_normal((1, 1, 1, 128))
+    k = rng0.standard_normal((1, 1, 1, 128))
+
+    def logit(n1, n2):
+        qa = oracle.rope_rotate(q, ang[n1:n1 + 1])
+        ka = oracle.rope_rotate(k, ang[n2:n2 + 1])
+        return float(np.sum(qa * ka))
+
+    idx = lambda t, h, w: (t * 5 + h) * 6 + w  # noqa: E731
+    a = logit(idx(0, 1, 2), idx(1, 3, 0))
+    b = logit(idx(2, 2, 4), idx(3, 4, 2))     # both shifted by (2, 1, 2)
+    assert math.isclose(a, b, rel_tol=1e-11, abs_tol=1e-11)
+    c = logit(idx(2, 2, 4), idx(3, 4, 3))     # different relative offset
+    assert not math.isclose(a, c, rel_tol=1e-6)
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+
+def test_rmsnorm_matches_library_and_fixes_rms():
+    x = torch.randn(2, 7, 3, 128, dtype=torch.float64, generator=torch.Generator().manual_seed(0))
+    g = 1 + 0.1 * torch.randn(128, dtype=torch.float64, generator=torch.Generator().manual_seed(1))
+    y = oracle.rms_norm_heads(x.numpy(), g.numpy(), 1e-6)
+    ref = F.rms_norm(x, (128,), weight=g, eps=1e-6)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-13, atol=1e-13)
+    # RMS of y / g is sqrt(ms / (ms + eps)) exactly
+    ms = (x.numpy() ** 2).mean(-1)
+    rms = np.sqrt(((y / g.numpy()) ** 2).mean(-1))
+    np.testing.assert_allclose(rms, np.sqrt(ms / (ms + 1e-6)), rtol=1e-13)
+    # constant scale c: the row RMS is c up to the eps term
+    y2 = oracle.rms_norm_heads(x.numpy(), np.full(128, 2.5), 1e-6)
+    np.testing.assert_allclose(np.sqrt((y2 ** 2).mean(-1)), 2.5 * np.sqrt(ms / (ms + 1e-6)), rtol=1e-13)
+    # per-head scales
+    gh = rng0.standard_normal((3, 128))
+    yh = oracle.rms_norm_heads(x.numpy(), gh, 1e-6)
+    for h in range(3):
+        ref_h = F.rms_norm(x[:, :, h], (128,), weight=torch.from_numpy(gh[h]), eps=1e-6)
+        np.testing.assert_allclose(yh[:, :, h], ref_h.numpy(), rtol=1e-13, atol=1e-13)
+    # a zero row stays zero
+    z = oracle.rms_norm_heads(np.zeros((1, 1, 1, 128)), g.numpy(), 1e-6)
+    assert np.all(z == 0.0)
+
+
+def test_qk_norm_rope_keeps_scaled_norm_and_skips_rope_for_cond():
+    x = rng0.standard_normal((1, 12, 2, 128))
+    g = np.full(128, 1.7)
+    qv, kv = oracle.qk_norm_rope(x, x, g, g, 1e-6, grid=(1, 3, 4))
+    ms = (x ** 2).mean(-1)
+    np.testing.assert_allclose(np.sqrt((qv ** 2).mean(-1)), 1.7 * np.sqrt(ms / (ms + 1e-6)), rtol=1e-12)
+    qc, _ = oracle.qk_norm_rope(x, x, g, g, 1e-6, grid=None)
+    np.testing.assert_allclose(qc, F.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(g), 1e-6).numpy(),
+                               rtol=1e-13)
+    # token 0 sits at (0,0,0): RoPE leaves it as the plain RMSNorm output
+    np.testing.assert_array_equal(qv[:, 0], qc[:, 0])
+
+
+# ------------------------------------------------------------------ attention
+
+
+def _rand_attn(n_vis, n_cond, heads=2, d=128, seed=0):
+    r = np.random.default_rng(seed)
+    mk = lambda n: r.standard_normal((1, n, heads, d))  # noqa: E731
+    return [mk(n_vis), mk(n_vis), mk(n_vis), mk(n_cond), mk(n_cond), mk(n_cond)]
+
+
+def test_attention_matches_library_sdpa_in_either_concat_order():
+    qv, kv, vv, qc, kc, vc = _rand_attn(23, 9)
+    o_v, o_c = oracle.joint_attention(qv, kv, vv, qc, kc, vc)
+    t = lambda *a: torch.from_numpy(np.concatenate(a, axis=1)).permute(0, 2, 1, 3)  # noqa: E731
+    ref = F.scaled_dot_product_attention(t(qv, qc), t(kv, kc), t(vv, vc)).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(o_v, ref[:, :23], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(o_c, ref[:, 23:], rtol=1e-12, atol=1e-13)
+    # no conditioning tokens: plain self-attention
+    e = np.zeros((1, 0, 2, 128))
+    o_v2, o_c2 = oracle.joint_attention(qv, kv, vv, e, e, e)
+    ref2 = F.scaled_dot_product_attention(t(qv), t(kv), t(vv)).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(o_v2, ref2, rtol=1e-12, atol=1e-13)
+    assert o_c2.shape == (1, 0, 2, 128)
+
+
+def test_attention_identical_keys_gives_mean_of_values():
+    qv, kv, vv, qc, kc, vc = _rand_attn(17, 5)
+    kv[:] = 0.3
+    kc[:] = 0.3
+    o_v, o_c = oracle.joint_attention(qv, kv, vv, qc, kc, vc)
+    mean = np.concatenate([vv, vc], axis=1).mean(axis=1, keepdims=True)
+    np.testing.assert_allclose(o_v, np.broadcast_to(mean, o_v.shape), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(o_c, np.broadcast_to(mean, o_c.shape), rtol=1e-12, atol=1e-14)
+    # zero keys after QK-norm: RMSNorm maps a zero row to zero
+    inp = {k: v for k, v in zip(("q_vis", "k_vis", "v_vis", "q_cond", "k_cond", "v_cond"),
+                                _rand_attn(12, 4))}
+    inp["k_vis"][:] = 0.0
+    inp["k_cond"][:] = 0.0
+    for s in ("vis", "cond"):
+        inp[f"gq_{s}"] = 1 + 0.1 * rng0.standard_normal(128)
+        inp[f"gk_{s}"] = 1 + 0.1 * rng0.standard_normal(128)
+    out = oracle.attention_block(inp, (1, 3, 4), 1e-6)
+    mean = np.concatenate([inp["v_vis"], inp["v_cond"]], axis=1).mean(axis=1, keepdims=True)
+    np.testing.assert_allclose(out["o_vis"], np.broadcast_to(mean, out["o_vis"].shape), atol=1e-13)
+
+
+def test_attention_single_token_and_convexity_and_linearity():
+    qv, kv, vv, qc, kc, vc = _rand_attn(1, 0)
+    o_v, _ = oracle.joint_attention(qv, kv, vv, qc, kc, vc)
+    np.testing.assert_allclose(o_v, vv, rtol=1e-14)
+    qv, kv, vv, qc, kc, vc = _rand_attn(31, 7, seed=3)
+    o_v, o_c = oracle.joint_attention(qv, kv, vv, qc, kc, vc)
+    v_all = np.concatenate([vv, vc], axis=1)
+    lo, hi = v_all.min(axis=1, keepdims=True), v_all.max(axis=1, keepdims=True)
+    assert np.all(o_v >= lo - 1e-12) and np.all(o_v <= hi + 1e-12)
+    assert np.all(o_c >= lo - 1e-12) and np.all(o_c <= hi + 1e-12)
+    o_v2, o_c2 = oracle.joint_attention(qv, kv, 2.0 * vv - 1.0, qc, kc, 2.0 * vc - 1.0)
+    np.testing.assert_allclose(o_v2, 2.0 * o_v - 1.0, atol=1e-12)
+    np.testing.assert_allclose(o_c2, 2.0 * o_c - 1.0, atol=1e-12)
+
+
+def test_cond_rows_are_permutation_equivariant_and_visual_invariant():
+    inp = {k: v for k, v in zip(("q_vis", "k_vis", "v_vis", "q_cond", "k_cond", "v_cond"),
+                                _rand_attn(24, 9, seed=5))}
+    for s in ("vis", "cond"):
+        inp[f"gq_{s}"] = 1 + 0.1 * rng0.standard_normal(128)
+        inp[f"gk_{s}"] = 1 + 0.1 * rng0.standard_normal(128)
+    out = oracle.attention_block(inp, (2, 3, 4), 1e-6)
+    perm = np.random.default_rng(9).permutation(9)
+    inp2 = dict(inp)
+    for nm in ("q_cond", "k_cond", "v_cond"):
+        inp2[nm] = inp[nm][:, perm]
+    out2 = oracle.attention_block(inp2, (2, 3, 4), 1e-6)
+    np.testing.assert_allclose(out2["o_cond"], out["o_cond"][:, perm], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out2["o_vis"], out["o_vis"], rtol=1e-12, atol=1e-14)
+    # permuting visual tokens does NOT commute (they carry positions)
+    inp3 = dict(inp)
+    pv = np.random.default_rng(2).permutation(24)
+    for nm in ("q_vis", "k_vis", "v_vis"):
+        inp3[nm] = inp[nm][:, pv]
+    out3 = oracle.attention_block(inp3, (2, 3, 4), 1e-6)
+    assert not np.allclose(out3["o_vis"], out["o_vis"][:, pv], atol=1e-6)
+
+
+def test_attention_block_against_bruteforce_config1_shape():
+    cfg = wl.ATTN_TINY
+    inp = wl.attention_inputs(cfg)
+    f64 = {k: wl.to_f64(v, cfg.dtype) for k, v in inp.items()}
+    out = oracle.attention_block(f64, cfg.grid, cfg.qk_eps)
+    lst = lambda a: a[0].tolist()  # noqa: E731
+    bo_v, bo_c = bf.attention_block(lst(f64["q_vis"]), lst(f64["k_vis"]), lst(f64["v_vis"]),
+                                    lst(f64["q_cond"]), lst(f64["k_cond"]), lst(f64["v_cond"]),
+                                    f64["gq_vis"].tolist(), f64["gk_vis"].tolist(),
+                                    f64["gq_cond"].tolist(), f64["gk_cond"].tolist(),
+                                    cfg.grid, cfg.qk_eps)
+    np.testing.assert_allclose(out["o_vis"][0], np.array(bo_v), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["o_cond"][0], np.array(bo_c), rtol=0, atol=1e-12)
+
+
+def test_sampled_rows_equal_full_rows():
+    qv, kv, vv, qc, kc, vc = _rand_attn(50, 11, seed=7)
+    full_v, full_c = oracle.joint_attention(qv, kv, vv, qc, kc, vc, chunk=7)
+    rv, rc = np.array([0, 13, 49]), np.array([2, 10])
+    sv, sc = oracle.joint_attention(qv, kv, vv, qc, kc, vc, vis_rows=rv, cond_rows=rc)
+    np.testing.assert_allclose(sv, full_v[:, rv], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(sc, full_c[:, rc], rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------ LN, modulation, GELU
+
+
+def test_layer_norm_matches_library_and_closed_forms():
+    x = torch.randn(2, 5, 64, dtype=torch.float64, generator=torch.Generator().manual_seed(3)) * 3 + 1
+    y = oracle.layer_norm(x.numpy(), 1e-6)
+    np.testing.assert_allclose(y, F.layer_norm(x, (64,), eps=1e-6).numpy(), rtol=1e-12, atol=1e-13)
+    var = x.numpy().var(-1)
+    np.testing.assert_allclose(y.mean(-1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(y.var(-1), var / (var + 1e-6), rtol=1e-12)
+    # constant row -> exactly the shift
+    shift = rng0.standard_normal((1, 64))
+    scale = rng0.standard_normal((1, 64))
+    c = oracle.modulate(oracle.layer_norm(np.full((1, 3, 64), 4.25), 1e-6), shift, scale)
+    np.testing.assert_array_equal(c, np.broadcast_to(shift[:, None, :], c.shape))
+    # shift = scale = 0 -> plain LayerNorm
+    z = np.zeros((1, 64))
+    np.testing.assert_array_equal(oracle.modulate(y[:1], z, z), y[:1])
+
+
+def test_modulation_against_bruteforce_and_order():
+    w = rng0.standard_normal((6 * 4, 3))
+    b = rng0.standard_normal(6 * 4)
+    t = rng0.standard_normal((1, 3))
+    m = oracle.modulation(w, b, t)
+    ref = bf.matvec(w.tolist(), t[0].tolist(), b.tolist())
+    for i, nm in enumerate(("shift_a", "scale_a", "gate_a", "shift_f", "scale_f", "gate_f")):
+        np.testing.assert_allclose(m[nm][0], ref[4 * i:4 * i + 4], rtol=1e-13)
+
+
+def test_gelu_matches_library_and_identities():
+    x = np.linspace(-8, 8, 1001)
+    np.testing.assert_allclose(oracle.gelu(x), F.gelu(torch.from_numpy(x), approximate="none").numpy(),
+                               rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.gelu(x) - oracle.gelu(-x), x, atol=1e-13)
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+
+
+# ------------------------------------------------------------------ whole block
+
+
+def _tiny_block(seed=0, c=256, heads=2, f=48, dt=8, grid=(1, 2, 3), n_cond=3):
+    r = np.random.default_rng(seed)
+    n_vis = grid[0] * grid[1] * grid[2]
+    ws = {}
+    for s in ("vis", "cond"):
+        ws[s] = {"w_mod": 0.2 * r.standard_normal((6 * c, dt)), "b_mod": 0.2 * r.standard_normal(6 * c),
+                 "w_qkv": 0.1 * r.standard_normal((3 * c, c)), "b_qkv": 0.1 * r.standard_normal(3 * c),
+                 "q_norm": 1 + 0.1 * r.standard_normal(128), "k_norm": 1 + 0.1 * r.standard_normal(128),
+                 "w_o": 0.1 * r.standard_normal((c, c)), "b_o": 0.1 * r.standard_normal(c),
+                 "w_fc1": 0.1 * r.standard_normal((f, c)), "b_fc1": 0.1 * r.standard_normal(f),
+                 "w_fc2": 0.1 * r.standard_normal((c, f)), "b_fc2": 0.1 * r.standard_normal(c)}
+    x_vis = r.standard_normal((1, n_vis, c))
+    x_cond = r.standard_normal((1, n_cond, c))
+    tvec = r.standard_normal((1, dt))
+    return x_vis, x_cond, tvec, ws, grid, heads
+
+
+def test_block_against_bruteforce_loops():
+    x_vis, x_cond, tvec, ws, grid, heads = _tiny_block()
+    res = oracle.block_forward(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads)
+    lw = {s: {k: v.tolist() for k, v in ws[s].items()} for s in ws}
+    bv, bc = bf.block_forward(x_vis[0].tolist(), x_cond[0].tolist(), tvec[0].tolist(),
+                              lw["vis"], lw["cond"], grid, heads, 1e-6, 1e-6)
+    np.testing.assert_allclose(res["out_vis"][0], np.array(bv), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(res["out_cond"][0], np.array(bc), rtol=0, atol=1e-10)
+
+
+def test_block_with_zero_modulation_is_identity():
+    x_vis, x_cond, tvec, ws, grid, heads = _tiny_block(seed=4)
+    for s in ws:
+        ws[s]["w_mod"][:] = 0.0
+        ws[s]["b_mod"][:] = 0.0
+    res = oracle.block_forward(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads)
+    np.testing.assert_array_equal(res["out_vis"], x_vis)
+    np.testing.assert_array_equal(res["out_cond"], x_cond)
+
+
+def test_block_sampled_rows_equal_full_rows():
+    x_vis, x_cond, tvec, ws, grid, heads = _tiny_block(seed=6, grid=(2, 2, 3), n_cond=4)
+    full = oracle.block_forward(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads)
+    rv, rc = np.array([1, 5, 11]), np.array([0, 3])
+    part = oracle.block_forward(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads,
+                                vis_rows=rv, cond_rows=rc)
+    for nm in ("out", "x1", "h2", "o", "qh"):
+        np.testing.assert_allclose(part[f"{nm}_vis"], full[f"{nm}_vis"][:, rv], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(part[f"{nm}_cond"], full[f"{nm}_cond"][:, rc], rtol=1e-12, atol=1e-13)
+
+
+def test_parity_metric():
+    ref = np.array([3.0, -4.0])          # rms = sqrt(12.5)
+    got = np.array([3.5, -4.0])
+    assert math.isclose(oracle.rel_max_err(got, ref), 0.5 / math.sqrt(12.5))
