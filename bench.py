@@ -1,0 +1,199 @@
+"""Throughput of the dual-stream MMDiT block core on one MI355X.
+
+A step is one mmdit_block_fwd over the 480p workload: 32760 visual tokens (81 frames at
+480x832 -> 21x30x52 latent grid) + 512 conditioning tokens, width 3072, 24 heads x 128,
+FFN 12288 (GELU), 1536-d timestep bottleneck, bf16 weights and activations (seeded
+synthetic inputs, resident in HBM before the timed region).
+
+Prints one JSON line: block tokens/s (value), the joint-attention TFLOP/s and its fraction
+of the bf16 MFMA peak (roofline; the attention kernel's duration is read from hipEvents the
+library records around it on the stream it runs on), the per-stage breakdown, and the
+float64 oracle timed on this host on a bounded sample (cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "joint-attn TFLOP/s + % bf16 MFMA peak; block tokens/s at 32760+512 tokens"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0
+
+
+class Hip:
+    """hipEvent plumbing through ctypes (the library records the events on its stream)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        if self.L.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e: int):
+        self.L.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, raw):
+    """The float64 oracle on this host, on a bounded sample of the same workload.
+
+    The oracle computes K and V of every token (fixed cost) and then the per-query work of
+    the sampled rows.  Two sample sizes give the fixed and the per-row cost; the full-job
+    time is extrapolated linearly (rows are independent given K and V)."""
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    x_vis = wl.to_f64(raw["x_vis"], wl.BF16)
+    x_cond = wl.to_f64(raw["x_cond"], wl.BF16)
+    tvec = wl.to_f64(raw["tvec"], wl.BF16)
+    w = {s: {k: wl.to_f64(raw[f"{s}.{k}"], wl.BF16) for k in wl.STREAM_WEIGHTS} for s in ("vis", "cond")}
+    times = []
+    sizes = [(24, 8), (48, 16)]
+    for nv, nc in sizes:
+        rv = wl.sample_rows(cfg.n_vis, nv, seed=900 + nv)
+        rc = wl.sample_rows(cfg.n_cond, nc, seed=901 + nc)
+        t0 = time.perf_counter()
+        oracle.block_forward(x_vis, x_cond, tvec, w["vis"], w["cond"], cfg.grid, cfg.heads, cfg.ln_eps,
+                             cfg.qk_eps, vis_rows=rv, cond_rows=rc, keep=False)
+        times.append(time.perf_counter() - t0)
+        log(f"oracle sample {nv}+{nc} rows: {times[-1]:.2f} s")
+    (n1, t1), (n2, t2) = (sum(sizes[0]), times[0]), (sum(sizes[1]), times[1])
+    per_row = max((t2 - t1) / (n2 - n1), 1e-9)
+    fixed = max(t1 - n1 * per_row, 0.0)
+    t_full = fixed + cfg.n_tokens * per_row
+    return {"value": cfg.n_tokens / t_full, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"float64 numpy oracle block forward, K/V of all {cfg.n_tokens} tokens plus "
+                       f"{sizes[0][0]}+{sizes[0][1]} and {sizes[1][0]}+{sizes[1][1]} sampled query rows "
+                       f"({t1:.1f} s, {t2:.1f} s); full job extrapolated as fixed {fixed:.1f} s + "
+                       f"{per_row * 1e3:.1f} ms/row x {cfg.n_tokens} rows = {t_full:.0f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--ffn-dtype", choices=("f16", "bf16"), default="f16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the block core runs on a single MI355X (no sharding, no "
+              "collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    import workloads as wl
+
+    cfg = wl.BLOCK_480P
+    dev = torch.device("cuda:0")
+    log(f"generating inputs {cfg.name}")
+    raw = wl.block_inputs(cfg)
+    t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in raw.items()}
+    wv = {k: t[f"vis.{k}"] for k in wl.STREAM_WEIGHTS}
+    wc = {k: t[f"cond.{k}"] for k in wl.STREAM_WEIGHTS}
+    ffn_dt = torch.float16 if args.ffn_dtype == "f16" else torch.bfloat16
+    dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, cfg.ln_eps, cfg.qk_eps, ffn_dtype=ffn_dt)
+    rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
+    ws = torch.empty(mm.block_workspace_bytes(dims, 1, cfg.n_vis, cfg.n_cond), dtype=torch.uint8, device=dev)
+    out_v = torch.empty((1, cfg.n_vis, cfg.width), dtype=torch.float32, device=dev)
+    out_c = torch.empty((1, cfg.n_cond, cfg.width), dtype=torch.float32, device=dev)
+
+    hip = Hip()
+    nst = mm.STAGE_COUNT
+    events = [[hip.event() for _ in range(2 * nst)] for _ in range(args.steps)]
+
+    def step(evs=None):
+        mm.block_fwd(dims, wv, wc, t["x_vis"], t["x_cond"], t["tvec"], rope, workspace=ws,
+                     out_vis=out_v, out_cond=out_c, stage_events=evs)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {name: [] for name in mm.STAGES}
+    for evs in events:
+        for si, name in enumerate(mm.STAGES):
+            stage_ms[name].append(hip.elapsed_ms(evs[2 * si], evs[2 * si + 1]))
+    step_gpu_ms = [hip.elapsed_ms(evs[0], evs[-1]) for evs in events]
+    for evs in events:
+        for e in evs:
+            hip.destroy(e)
+    ms_per_step = wall * 1e3 / args.steps
+    stage_avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+    attn_ms = stage_avg["attention"]
+    attn_tflops = cfg.attn_flops / (attn_ms * 1e-3) / 1e12
+    tokens_s = cfg.n_tokens / (ms_per_step * 1e-3)
+    log(f"{ms_per_step:.3f} ms/step, attention {attn_ms:.3f} ms = {attn_tflops:.1f} TFLOP/s")
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no checkpoint)",
+        "config": {"workload": "480p MMDiT block forward: 32760 visual (21x30x52) + 512 conditioning tokens, "
+                               "C=3072, 24x128 heads, FFN 12288 GELU, Dt=1536",
+                   "global_batch": 1, "seq_len": cfg.n_tokens, "parallelism": "none (1 GPU)",
+                   "ffn_operand_dtype": args.ffn_dtype, "output_dtype": "f32"},
+        "roofline": {"bound": "mfma", "kernel": "joint_attn_bf16_kernel",
+                     "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": cfg.attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+        "joint_attention": {"tflops": round(attn_tflops, 1), "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                            "ms": round(attn_ms, 4), "tokens": cfg.n_tokens},
+        "block_tflops": round(cfg.total_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
+        "step_gpu_ms": round(float(np.mean(step_gpu_ms)), 4),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on this host)")
+        res["cpu_baseline"] = cpu_baseline(cfg, raw)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,276 @@
+/*
+ * mmdit.h -- C ABI of the MI355X (gfx950) dual-stream MMDiT block core.
+ *
+ * The block is the one described in "Vimoo 1.0: Video Generation for Compact,
+ * Lightweight, and High-Speed", section 2.2 (Dual-Stream MMDiT Backbone): visual and
+ * conditioning tokens keep separate projections and FFNs, are concatenated for one joint
+ * non-causal attention, and are modulated by shift / scale / gate vectors produced from a
+ * shared timestep bottleneck.  The fusion of QK-Norm with RoPE and of the other
+ * memory-bound steps follows "Seaweed-7B: Cost-Effective Training of Video Generation
+ * Foundation Model", section 3.4 (kernel fusion).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers.  Every tensor argument is a DEVICE pointer owned by the caller.  The library
+ *   never allocates, frees or synchronizes; scratch memory of mmdit_block_fwd comes from
+ *   the caller's workspace.  Host-side structs (mmdit_rope3d, mmdit_block_dims,
+ *   mmdit_stream_weights) are read during the call only.
+ * - Streams.  Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *   null stream) and runs in stream order.  Calls return after enqueueing.
+ * - Errors.  Every call returns an mmdit_status.  Arguments are validated before anything
+ *   is enqueued; on a validation error nothing runs.  A failed launch returns
+ *   MMDIT_ERR_HIP.  mmdit_last_error() returns a thread-local text for the last failure of
+ *   the calling thread.  Device faults surface at the caller's next synchronization.
+ * - Layouts.  Row-major; tokens are [B, N, ...] with a token row stride given in elements
+ *   (batch items are N rows apart).  Heads split channels head-major: channel c of a row
+ *   is head c / D, dim c % D.  Weights use the nn.Linear layout [out, in], rows contiguous.
+ * - Dtypes.  MMDIT_F32, MMDIT_BF16, MMDIT_F16.  Conversions to 16-bit round to nearest
+ *   even.  Accumulation is fp32 everywhere.
+ * - Alignment.  Every pointer must be 16-byte aligned and every row stride a multiple of
+ *   8 elements (16 bytes for 16-bit types).
+ * - Thread safety.  No global mutable state besides the thread-local error text.
+ */
+#ifndef MMDIT_H_
+#define MMDIT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mmdit_dtype { MMDIT_F32 = 0, MMDIT_BF16 = 1, MMDIT_F16 = 2 };
+
+enum mmdit_status {
+  MMDIT_OK = 0,
+  MMDIT_ERR_NULL = 1,        /* a required pointer is NULL                               */
+  MMDIT_ERR_ALIGN = 2,       /* a pointer or a row stride is not 16-byte aligned         */
+  MMDIT_ERR_SHAPE = 3,       /* sizes are inconsistent or out of the supported range     */
+  MMDIT_ERR_DTYPE = 4,       /* unsupported dtype or dtype combination                   */
+  MMDIT_ERR_WORKSPACE = 5,   /* workspace smaller than mmdit_block_workspace_bytes()     */
+  MMDIT_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed               */
+  MMDIT_ERR_ALIAS = 7        /* an output overlaps an input where that is not allowed    */
+};
+
+/* 3D rotary embedding of visual tokens (Vimoo 1.0 notes, section 2.2): the D head dims
+ * are cut into bands of d_t, d_h, d_w dims (16/56/56 for D = 128) rotated by the token's
+ * temporal, vertical and horizontal position.  Visual token n of a batch item sits at
+ * t = n / (H*W), h = (n / W) % H, w = n % W (w fastest).  Pair j of a band of width d
+ * (dims 2j, 2j+1 counted from the band's start) turns by pos * base^(-2j/d).
+ * Requirements: T, H, W >= 1; d_t, d_h, d_w even, >= 0, summing to D; base > 0. */
+typedef struct {
+  int64_t T, H, W;
+  int32_t d_t, d_h, d_w;
+  float base;
+} mmdit_rope3d;
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_modulate_ln -- LayerNorm with timestep shift/scale, optionally after a gated
+ * residual (Vimoo 1.0 notes, section 2.2: LayerNorm precedes attention and FFN, shift and
+ * scale come from the timestep path, gates weight each branch's residual update).
+ *
+ *   x'  = x + gate * branch          (branch given)   or   x' = x   (branch NULL)
+ *   y   = LN(x') * (1 + scale) + shift
+ *   LN(v) = (v - mean(v)) / sqrt(var(v) + eps), biased variance over C, no affine.
+ *
+ * x       [B, N, C]  x_dtype F32 | BF16, rows contiguous (row stride C).
+ * branch  [B, N, C]  branch_dtype F32 | BF16, or NULL.
+ * gate, shift, scale: f32, [B, C] each; item b's vector starts at ptr + b * mod_stride
+ *         (mod_stride in elements, >= C; pass 6*C to read straight from an mmdit
+ *         modulation buffer).  gate is required iff branch is given.
+ * x_out   [B, N, C] f32 receives x' (may be NULL).
+ * y       [B, N, C] y_dtype F32 | BF16 | F16.
+ * C must be a multiple of 8 and at most 16384.  N may be 0.  Outputs must not overlap
+ * inputs.
+ * ------------------------------------------------------------------------------- */
+int mmdit_modulate_ln(const void* x, int x_dtype,
+                      const void* branch, int branch_dtype, const float* gate,
+                      float* x_out,
+                      const float* shift, const float* scale, int64_t mod_stride,
+                      void* y, int y_dtype,
+                      int64_t B, int64_t N, int64_t C, float eps, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_qk_norm_rope -- per-head RMSNorm of Q and K with their own learned scales, then
+ * (visual stream, rope != NULL) 3D RoPE; the conditioning stream passes rope = NULL and
+ * gets no rotation (Vimoo 1.0 notes, section 2.2).  Norm first, rotation second, fused in
+ * one pass over HBM (Seaweed-7B, section 3.4).
+ *
+ *   q^ = RoPE(q / sqrt(mean_d(q^2) + eps) * g_q),  likewise k with g_k.
+ *
+ * q, k       [B, N, H, D] in_dtype F32 | BF16; token row stride in_row_stride (>= H*D).
+ * q_scale, k_scale  scale_dtype F32 | BF16: [D] shared by all heads (scale_head_stride 0)
+ *            or [H, D] (scale_head_stride = D).
+ * q_out, k_out  [B, N, H, D] out_dtype F32 | BF16 | F16, row stride out_row_stride.
+ *            In place is allowed (q_out == q and k_out == k with equal strides and dtypes);
+ *            partial overlap is not.
+ * D must be 128.  N may be 0.  With rope, N must equal rope->T * rope->H * rope->W.
+ * ------------------------------------------------------------------------------- */
+int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_row_stride,
+                       const void* q_scale, const void* k_scale, int scale_dtype,
+                       int64_t scale_head_stride,
+                       void* q_out, void* k_out, int out_dtype, int64_t out_row_stride,
+                       int64_t B, int64_t N, int64_t H, int64_t D, float eps,
+                       const mmdit_rope3d* rope, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_joint_attention -- one non-causal softmax attention over the concatenation of
+ * the conditioning and visual tokens, split back into the two streams (Vimoo 1.0 notes,
+ * section 2.2; non-causal per the Wan report).  For every batch item and head:
+ *
+ *   O = softmax(Q_all K_all^T * softmax_scale) V_all,  Q/K/V_all = [cond rows | vis rows]
+ *
+ * (The order of the concatenation does not change any output.)  No mask.
+ *
+ * q/k/v_vis   [B, n_vis, H, D], q/k/v_cond [B, n_cond, H, D]; in_dtype BF16 (MFMA path)
+ *             or F32 (fp32 VALU path); one token row stride in_row_stride for all six.
+ *             Q and K are used as given: normalise / rotate them first.
+ * o_vis, o_cond  [B, n_s, H, D] out_dtype F32 | BF16 | F16, row stride out_row_stride.
+ * lse         optional f32 [B, H, n_cond + n_vis], cond rows first: the natural-log
+ *             sum of exp(scaled logits) of each query row, or NULL.
+ * D must be 128; n_vis + n_cond >= 1; a stream with n_s = 0 may pass NULL pointers.
+ * ------------------------------------------------------------------------------- */
+int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
+                          const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
+                          int in_dtype, int64_t in_row_stride,
+                          int64_t B, int64_t H, int64_t D, float softmax_scale,
+                          void* o_vis, void* o_cond, int out_dtype, int64_t out_row_stride,
+                          float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_linear -- y = epilogue(x W^T + bias) on bf16 / f16 MFMA, fp32 accumulate.  The
+ * per-stream projections of the block (QKV, output, FFN) all run through this GEMM.
+ *
+ * x  [M, K] x_dtype BF16 | F16 (row stride K);  w [N, K] same dtype as x;  bias [N] f32 |
+ *    bf16 (bias_dtype) or NULL.
+ * epilogue:
+ *   MMDIT_EPI_NONE      y = acc + bias
+ *   MMDIT_EPI_GELU      y = GELU(acc + bias), exact erf form
+ *   MMDIT_EPI_GATED_RES y = res + gate[b] * (acc + bias), b = row / rows_per_batch;
+ *                       res [M, N] res_dtype F32 | BF16; gate f32, item b at
+ *                       gate + b * gate_stride.
+ * y  [M, N] y_dtype F32 | BF16 | F16.  K must be a multiple of 64.  M, N >= 0.
+ * ------------------------------------------------------------------------------- */
+enum mmdit_epilogue { MMDIT_EPI_NONE = 0, MMDIT_EPI_GELU = 1, MMDIT_EPI_GATED_RES = 2 };
+
+int mmdit_linear(const void* x, const void* w, int x_dtype,
+                 const void* bias, int bias_dtype,
+                 void* y, int y_dtype,
+                 int64_t M, int64_t N, int64_t K,
+                 int epilogue, const void* res, int res_dtype,
+                 const float* gate, int64_t gate_stride, int64_t rows_per_batch,
+                 void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_modulation -- the per-(block, stream) modulation Linear: the shared timestep
+ * bottleneck tvec is mapped directly to six C-vectors (Vimoo 1.0 notes, sections 2.2 and
+ * 2.4), in the order shift_attn, scale_attn, gate_attn, shift_ffn, scale_ffn, gate_ffn.
+ *
+ *   mod[b] = W_mod tvec[b] + b_mod
+ *
+ * w_mod [6C, Dt] BF16;  b_mod [6C] BF16 or NULL;  tvec [B, Dt] t_dtype F32 | BF16;
+ * mod   [B, 6C] f32.  Dt must be a multiple of 8.
+ * ------------------------------------------------------------------------------- */
+int mmdit_modulation(const void* w_mod, const void* b_mod, const void* tvec, int t_dtype,
+                     float* mod, int64_t B, int64_t C6, int64_t Dt, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_block_fwd -- one dual-stream MMDiT block forward (Vimoo 1.0 notes, section 2.2).
+ * Per stream s (vis, cond):
+ *   mod_s = W_mod,s tvec + b_mod,s  -> shift_a, scale_a, gate_a, shift_f, scale_f, gate_f
+ *   h     = LN(x_s) (1 + scale_a) + shift_a
+ *   q,k,v = split(h W_qkv^T + b_qkv);  q,k <- RMSNorm (scales q_norm, k_norm), RoPE on vis
+ *   O_vis, O_cond = joint attention over [cond | vis]
+ *   x1    = x_s + gate_a (O_s W_o^T + b_o)                       (fp32)
+ *   h2    = LN(x1) (1 + scale_f) + shift_f
+ *   out_s = x1 + gate_f (GELU(h2 W_fc1^T + b_fc1) W_fc2^T + b_fc2)   (out_dtype)
+ *
+ * dims: C = H*D, D = 128, F and C multiples of 256, Dt a multiple of 8, w_dtype BF16.
+ * Weights (per stream, nn.Linear layout, all w_dtype): w_mod [6C, Dt], b_mod [6C],
+ * w_qkv [3C, C], b_qkv [3C] (rows: q, then k, then v), q_norm, k_norm [D] (or [H, D] with
+ * qk_scale_head_stride = D), w_o [C, C], b_o [C], w_fc1 [F, C], b_fc1 [F], w_fc2 [C, F],
+ * b_fc2 [C].  Bias pointers may be NULL (no bias).
+ * x_vis [B, n_vis, C], x_cond [B, n_cond, C] x_dtype BF16 | F32; tvec [B, Dt] t_dtype
+ * BF16 | F32; rope describes the visual grid (n_vis = T*H*W); out_vis, out_cond
+ * [B, n_s, C] out_dtype F32 | BF16.
+ * ffn_dtype selects the operand type of the two FFN GEMMs: MMDIT_BF16 (h2 and the GELU
+ * output stored bf16) or MMDIT_F16 (both stored f16; the FFN weights are converted to f16
+ * in the workspace on every call).
+ * workspace: >= mmdit_block_workspace_bytes(dims, B, n_vis, n_cond), 256-byte aligned;
+ * its contents after the call are the intermediates listed by mmdit_block_workspace_offsets.
+ * ------------------------------------------------------------------------------- */
+typedef struct {
+  const void *w_mod, *b_mod, *w_qkv, *b_qkv, *q_norm, *k_norm,
+             *w_o, *b_o, *w_fc1, *b_fc1, *w_fc2, *b_fc2;
+} mmdit_stream_weights;
+
+typedef struct {
+  int64_t C, H, D, F, Dt;
+  float ln_eps, qk_eps;
+  int64_t qk_scale_head_stride;
+  int w_dtype;
+  int ffn_dtype;
+} mmdit_block_dims;
+
+/* Workspace regions (byte offsets from the workspace start), per stream s = 0 (vis), 1 (cond):
+ *   MMDIT_WS_MOD    f32  [B, 6C]   modulation vectors
+ *   MMDIT_WS_H      16b  [B*n, C]  LN-modulated input of the QKV GEMM; reused for O (bf16)
+ *   MMDIT_WS_QKV    bf16 [B*n, 3C] q^ | k^ | v after QK-norm and RoPE; reused for h2
+ *   MMDIT_WS_X1     f32  [B*n, C]  residual after the attention branch
+ *   MMDIT_WS_G      16b  [B*n, F]  GELU(h2 W_fc1^T + b_fc1)
+ * and, for ffn_dtype F16, MMDIT_WS_W1H / MMDIT_WS_W2H, f16 copies of w_fc1 / w_fc2. */
+enum { MMDIT_WS_MOD = 0, MMDIT_WS_H = 1, MMDIT_WS_QKV = 2, MMDIT_WS_X1 = 3, MMDIT_WS_G = 4,
+       MMDIT_WS_W1H = 5, MMDIT_WS_W2H = 6, MMDIT_WS_COUNT = 7 };
+
+size_t mmdit_block_workspace_bytes(const mmdit_block_dims* dims, int64_t B, int64_t n_vis,
+                                   int64_t n_cond);
+
+/* Fills offsets[2][MMDIT_WS_COUNT] (stream-major); unused regions get SIZE_MAX.  Returns a
+ * status (dims validated as for mmdit_block_fwd). */
+int mmdit_block_workspace_offsets(const mmdit_block_dims* dims, int64_t B, int64_t n_vis,
+                                  int64_t n_cond, size_t* offsets);
+
+int mmdit_block_fwd(const mmdit_block_dims* dims,
+                    const mmdit_stream_weights* w_vis, const mmdit_stream_weights* w_cond,
+                    const void* x_vis, const void* x_cond, int x_dtype,
+                    const void* tvec, int t_dtype,
+                    const mmdit_rope3d* rope, int64_t n_cond,
+                    void* out_vis, void* out_cond, int out_dtype,
+                    void* workspace, size_t workspace_bytes, int64_t B, void* stream);
+
+/* mmdit_block_fwd_events -- mmdit_block_fwd that also records caller-owned hipEvents on
+ * `stream` around each stage, for per-kernel timing of the same launch sequence.
+ * events: array of 2 * MMDIT_STAGE_COUNT hipEvent_t handles (passed as void*), entry
+ * 2*i before stage i and 2*i+1 after it; the array or any entry may be NULL (not
+ * recorded).  Everything else is exactly mmdit_block_fwd. */
+enum { MMDIT_STAGE_MOD_LN1 = 0,       /* modulation GEMV, LN-modulate (+ f16 FFN weight copy) */
+       MMDIT_STAGE_QKV = 1,           /* QKV GEMM                                            */
+       MMDIT_STAGE_QK_NORM_ROPE = 2,  /* QK RMSNorm + 3D RoPE                                */
+       MMDIT_STAGE_ATTENTION = 3,     /* joint attention                                     */
+       MMDIT_STAGE_OUT_PROJ = 4,      /* output projection + gated residual                  */
+       MMDIT_STAGE_LN2 = 5,           /* LN-modulate of the FFN branch                       */
+       MMDIT_STAGE_FFN_UP = 6,        /* FFN up + GELU                                       */
+       MMDIT_STAGE_FFN_DOWN = 7,      /* FFN down + gated residual                           */
+       MMDIT_STAGE_COUNT = 8 };
+
+int mmdit_block_fwd_events(const mmdit_block_dims* dims,
+                           const mmdit_stream_weights* w_vis, const mmdit_stream_weights* w_cond,
+                           const void* x_vis, const void* x_cond, int x_dtype,
+                           const void* tvec, int t_dtype,
+                           const mmdit_rope3d* rope, int64_t n_cond,
+                           void* out_vis, void* out_cond, int out_dtype,
+                           void* workspace, size_t workspace_bytes, int64_t B, void* stream,
+                           void* const* events);
+
+/* Text of a status code (static storage). */
+const char* mmdit_status_str(int status);
+/* Thread-local detail of the calling thread's last failed call ("" if none). */
+const char* mmdit_last_error(void);
+/* ABI version: bumped whenever a signature or a layout above changes. */
+int mmdit_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMDIT_H_ */

@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every function include/mmdit.h declares, and rejects
+invalid arguments with the documented status before any HIP call (no GPU needed: these
+calls return from host-side validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_diffusion_transformer_mmdit_amd as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mmdit.h")
+
+ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS = 1, 2, 3, 4, 5, 6, 7
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(mmdit_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mm.library_path()):
+        pytest.skip("libmmdit.so not built")
+    return mm.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in mmdit.h but not exported"
+    for n in ("mmdit_modulate_ln", "mmdit_qk_norm_rope", "mmdit_joint_attention", "mmdit_block_fwd"):
+        assert n in names
+
+
+def test_status_strings_and_version(L):
+    assert mm.abi_version() == 1
+    assert L.mmdit_status_str(0) == b"MMDIT_OK"
+    assert L.mmdit_status_str(ERR_ALIAS) == b"MMDIT_ERR_ALIAS"
+    assert L.mmdit_status_str(99) == b"MMDIT_ERR_UNKNOWN"
+
+
+def _fake(addr):
+    """A non-null, 16-byte aligned address that is never dereferenced (validation fails first)."""
+    return ctypes.c_void_p(addr)
+
+
+def test_qk_norm_rope_validation(L):
+    p = _fake(0x10000)
+    rope = mm.Rope3D.make((2, 2, 2))
+    f = L.mmdit_qk_norm_rope
+    args = [p, _fake(0x20000), mm.BF16, 3 * 128, p, p, mm.BF16, 0, p, _fake(0x20000), mm.BF16, 3 * 128,
+            1, 8, 1, 128, 1e-6, ctypes.byref(rope), None]
+    a = list(args); a[15] = 64
+    assert f(*a) == ERR_SHAPE                                       # D != 128
+    a = list(args); a[13] = 9
+    assert f(*a) == ERR_SHAPE and b"T * H * W" in L.mmdit_last_error()
+    bad = mm.Rope3D.make((2, 2, 2), (16, 55, 57))
+    a = list(args); a[17] = ctypes.byref(bad)
+    assert f(*a) == ERR_SHAPE                                       # odd band
+    a = list(args); a[0] = None
+    assert f(*a) == ERR_NULL
+    a = list(args); a[0] = _fake(0x10008)
+    assert f(*a) == ERR_ALIGN
+    a = list(args); a[2] = mm.F16
+    assert f(*a) == ERR_DTYPE
+    a = list(args); a[8] = _fake(0x10000 + 64 * 2)                  # q_out half-overlapping q
+    assert f(*a) == ERR_ALIAS
+    a = list(args); a[13] = 0                                       # N = 0 with a grid of 8 -> shape
+    assert f(*a) == ERR_SHAPE
+
+
+def test_joint_attention_validation(L):
+    p, o = _fake(0x10000), _fake(0x900000)
+    f = L.mmdit_joint_attention
+    args = [p, p, p, 10, p, p, p, 3, mm.BF16, 256, 1, 2, 128, 0.088, o, _fake(0xA00000), mm.F32, 256, None, None]
+    a = list(args); a[12] = 96
+    assert f(*a) == ERR_SHAPE
+    a = list(args); a[3] = 0; a[7] = 0
+    assert f(*a) == ERR_SHAPE                                       # no tokens at all
+    a = list(args); a[14] = None
+    assert f(*a) == ERR_NULL
+    a = list(args); a[8] = mm.F16
+    assert f(*a) == ERR_DTYPE
+    a = list(args); a[14] = p
+    assert f(*a) == ERR_ALIAS                                       # output on top of the inputs
+    a = list(args); a[13] = 0.0
+    assert f(*a) == ERR_SHAPE
+    a = list(args); a[9] = 100
+    assert f(*a) == ERR_SHAPE                                       # row stride < H*D
+
+
+def test_linear_modulate_modulation_validation(L):
+    p = _fake(0x10000)
+    assert L.mmdit_linear(p, p, mm.BF16, None, mm.BF16, _fake(0x900000), mm.BF16, 10, 256, 100,
+                          mm.EPI_NONE, None, mm.F32, None, 0, 10, None) == ERR_SHAPE      # K % 64
+    assert L.mmdit_linear(p, p, mm.F32, None, mm.BF16, _fake(0x900000), mm.BF16, 10, 256, 128,
+                          mm.EPI_NONE, None, mm.F32, None, 0, 10, None) == ERR_DTYPE
+    assert L.mmdit_linear(p, p, mm.BF16, None, mm.BF16, _fake(0x900000), mm.F32, 10, 256, 128,
+                          mm.EPI_GATED_RES, None, mm.F32, None, 256, 10, None) == ERR_NULL
+    assert L.mmdit_modulate_ln(p, mm.BF16, None, mm.BF16, None, None, p, p, 3072, _fake(0x900000), mm.BF16,
+                               1, 4, 3004, 1e-6, None) == ERR_SHAPE                      # C % 8
+    assert L.mmdit_modulate_ln(p, mm.BF16, p, mm.BF16, None, None, p, p, 3072, _fake(0x900000), mm.BF16,
+                               1, 4, 3072, 1e-6, None) == ERR_NULL                       # branch w/o gate
+    assert L.mmdit_modulate_ln(p, mm.BF16, None, mm.BF16, None, None, p, p, 3072, p, mm.BF16,
+                               1, 4, 3072, 1e-6, None) == ERR_ALIAS
+    assert L.mmdit_modulation(p, None, p, mm.BF16, _fake(0x900000), 1, 18432, 1500, None) == ERR_SHAPE
+
+
+def test_block_workspace_and_validation(L):
+    dims = mm.BlockDims.make(3072, 24, 12288, 1536)
+    n = mm.block_workspace_bytes(dims, 1, 32760, 512)
+    # mod + h + qkv + x1 + g per stream, f32 residual, bf16 FFN: no f16 weight copies
+    expect = 0
+    for rows in (32760, 512):
+        for sz in (6 * 3072 * 4, rows * 3072 * 2, rows * 9216 * 2, rows * 3072 * 4, rows * 12288 * 2):
+            expect += (sz + 255) // 256 * 256
+    assert n == expect
+    offs = mm.block_workspace_offsets(dims, 1, 32760, 512)
+    assert offs[0][mm.WS_MOD] == 0 and offs[0][mm.WS_W1H] == 2 ** 64 - 1
+    d16 = mm.BlockDims.make(3072, 24, 12288, 1536, ffn_dtype=__import__("torch").float16)
+    assert mm.block_workspace_bytes(d16, 1, 32760, 512) == n + 4 * 12288 * 3072 * 2
+    bad = mm.BlockDims.make(3000, 24, 12288, 1536)
+    assert mm.block_workspace_bytes(bad, 1, 100, 5) == 0
+    rope = mm.Rope3D.make((21, 30, 52))
+    sw = mm._abi.StreamWeights()
+    p = _fake(0x10000)
+    st = L.mmdit_block_fwd(ctypes.byref(dims), ctypes.byref(sw), ctypes.byref(sw), p, p, mm.BF16, p, mm.BF16,
+                           ctypes.byref(rope), 512, p, p, mm.F32, _fake(0x100000), 1024, 1, None)
+    assert st == ERR_NULL                                            # weights missing
+    for k in mm._abi.STREAM_KEYS:
+        setattr(sw, k, 0x20000)
+    st = L.mmdit_block_fwd(ctypes.byref(dims), ctypes.byref(sw), ctypes.byref(sw), p, p, mm.BF16, p, mm.BF16,
+                           ctypes.byref(rope), 512, p, p, mm.F32, _fake(0x100000), 1024, 1, None)
+    assert st == ERR_WS

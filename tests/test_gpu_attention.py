@@ -1,0 +1,206 @@
+"""GPU parity of QK-RMSNorm + 3D RoPE and joint attention against the float64 oracle.
+
+Workloads 1 (fp32) and 2 (bf16) are compared element by element; the 480p and 720p
+workloads are compared on sampled query rows (every key is used), in the same launch
+configuration the bench times.  Tolerance: max|err| / rms(oracle) <= 1e-4 (fp32) and
+<= 2e-2 (bf16) per output tensor.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import video_diffusion_transformer_mmdit_amd as mm
+import workloads as wl
+from tests.util import TOL, assert_close, log, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg):
+    raw = wl.attention_inputs(cfg)
+    dev = {k: to_dev(v, cfg.dtype) for k, v in raw.items()}
+    return raw, dev
+
+
+def _gpu_attention(cfg, dev, out_dtype=torch.float32, qk_dtype=None, return_lse=False):
+    rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
+    qv, kv = mm.qk_norm_rope(dev["q_vis"], dev["k_vis"], dev["gq_vis"], dev["gk_vis"], rope=rope,
+                             eps=cfg.qk_eps, out_dtype=qk_dtype)
+    qc, kc = mm.qk_norm_rope(dev["q_cond"], dev["k_cond"], dev["gq_cond"], dev["gk_cond"],
+                             eps=cfg.qk_eps, out_dtype=qk_dtype)
+    res = mm.joint_attention(qv, kv, dev["v_vis"], qc, kc, dev["v_cond"], out_dtype=out_dtype,
+                             return_lse=return_lse)
+    torch.cuda.synchronize()
+    return (qv, kv, qc, kc) + tuple(res)
+
+
+@pytest.mark.parametrize("cfg", [wl.ATTN_TINY, wl.ATTN_LAYER], ids=lambda c: c.name)
+def test_attention_full_parity(cfg):
+    log(f"attention full parity {cfg.name}")
+    raw, dev = _inputs(cfg)
+    f64 = {k: wl.to_f64(v, cfg.dtype) for k, v in raw.items()}
+    ref = oracle.attention_block(f64, cfg.grid, cfg.qk_eps, cfg.rope_split, cfg.rope_base)
+    qv, kv, qc, kc, o_v, o_c, lse = _gpu_attention(cfg, dev, return_lse=True)
+    tol = TOL[cfg.dtype]
+    for nm, got in (("qh_vis", qv), ("kh_vis", kv), ("qh_cond", qc), ("kh_cond", kc)):
+        assert_close(nm, to_host64(got), ref[nm], tol)
+    assert_close("o_vis", to_host64(o_v), ref["o_vis"], tol)
+    assert_close("o_cond", to_host64(o_c), ref["o_cond"], tol)
+    # log-sum-exp of every query row, [cond | vis] order, against the oracle's normalised
+    # inputs: lse = log sum_j exp(q.k_j / sqrt(D))
+    kall = np.concatenate([ref["kh_cond"], ref["kh_vis"]], axis=1)[0]
+    qall = np.concatenate([ref["qh_cond"], ref["qh_vis"]], axis=1)[0]
+    lse_ref = np.empty((cfg.heads, qall.shape[0]))
+    for h in range(cfg.heads):
+        s = qall[:, h] @ kall[:, h].T / math.sqrt(cfg.head_dim)
+        m = s.max(axis=1, keepdims=True)
+        lse_ref[h] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+    got = to_host64(lse)[0]
+    err = np.max(np.abs(got - lse_ref))
+    log(f"  lse: max abs err {err:.3e}")
+    assert err < (1e-4 if cfg.dtype == wl.F32 else 3e-2)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [wl.ATTN_480P, wl.ATTN_720P], ids=lambda c: c.name)
+def test_attention_sampled_parity_full_size(cfg):
+    log(f"attention sampled parity {cfg.name}: generating inputs")
+    raw, dev = _inputs(cfg)
+    log("  GPU qk_norm_rope + joint_attention")
+    qv, kv, qc, kc, o_v, o_c = _gpu_attention(cfg, dev)
+    rv = wl.sample_rows(cfg.n_vis, 192, seed=cfg.seed + 100)
+    rc = wl.sample_rows(cfg.n_cond, 48, seed=cfg.seed + 200)
+    o_v_s = to_host64(o_v[:, torch.from_numpy(rv).cuda()])
+    o_c_s = to_host64(o_c[:, torch.from_numpy(rc).cuda()])
+    kv_h, qv_s = to_host64(kv), to_host64(qv[:, torch.from_numpy(rv).cuda()])
+    del dev, qv, kv, qc, kc, o_v, o_c
+    torch.cuda.empty_cache()
+    log("  oracle (float64) on sampled rows")
+    f64 = {k: wl.to_f64(v, cfg.dtype) for k, v in raw.items()}
+    del raw
+    ref = oracle.attention_block(f64, cfg.grid, cfg.qk_eps, cfg.rope_split, cfg.rope_base,
+                                 vis_rows=rv, cond_rows=rc)
+    tol = TOL[cfg.dtype]
+    assert_close("kh_vis(all rows)", kv_h, ref["kh_vis"], tol)
+    assert_close("qh_vis(sampled)", qv_s, ref["qh_vis"][:, rv], tol)
+    assert_close("o_vis(sampled)", o_v_s, ref["o_vis"], tol)
+    assert_close("o_cond(sampled)", o_c_s, ref["o_cond"], tol)
+
+
+def _rand(shape, seed, dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype).cuda()
+
+
+def _oracle_attn(qv, kv, vv, qc, kc, vc):
+    f = lambda t: to_host64(t) if t is not None else np.zeros((qv.shape[0], 0) + tuple(qv.shape[2:]))  # noqa: E731
+    return oracle.joint_attention(f(qv), f(kv), f(vv), f(qc), f(kc), f(vc))
+
+
+@pytest.mark.parametrize("n_vis,n_cond", [(1, 0), (0, 5), (63, 1), (64, 64), (129, 77), (200, 0), (300, 130)])
+def test_attention_ragged_edges(n_vis, n_cond):
+    """Tails of the 64-key and 128-query tiles, empty streams, a single token."""
+    H, D = 3, 128
+    qv, kv, vv = (_rand((1, n_vis, H, D), s) for s in (1, 2, 3))
+    qc, kc, vc = (_rand((1, n_cond, H, D), s) for s in (4, 5, 6))
+    o_v, o_c = mm.joint_attention(qv, kv, vv, qc if n_cond else None, kc if n_cond else None,
+                                  vc if n_cond else None)
+    torch.cuda.synchronize()
+    r_v, r_c = _oracle_attn(qv, kv, vv, qc, kc, vc)
+    if n_vis:
+        assert_close("o_vis", to_host64(o_v), r_v, 2e-2)
+    if n_cond:
+        assert_close("o_cond", to_host64(o_c), r_c, 2e-2)
+
+
+def test_attention_batch_and_strided_packed_rows():
+    """B = 2 and Q/K/V read as views of one packed [B, N, 3, H, D] buffer."""
+    B, nv, nc, H, D = 2, 150, 20, 2, 128
+    pv = _rand((B, nv, 3, H, D), 7)
+    pc = _rand((B, nc, 3, H, D), 8)
+    o_v, o_c = mm.joint_attention(pv[:, :, 0], pv[:, :, 1], pv[:, :, 2], pc[:, :, 0], pc[:, :, 1], pc[:, :, 2])
+    torch.cuda.synchronize()
+    for b in range(B):
+        r_v, r_c = _oracle_attn(*(t[b:b + 1].contiguous() for t in (pv[:, :, 0], pv[:, :, 1], pv[:, :, 2],
+                                                                     pc[:, :, 0], pc[:, :, 1], pc[:, :, 2])))
+        assert_close(f"o_vis[b={b}]", to_host64(o_v[b:b + 1]), r_v, 2e-2)
+        assert_close(f"o_cond[b={b}]", to_host64(o_c[b:b + 1]), r_c, 2e-2)
+
+
+def test_attention_identical_keys_give_mean_of_values_and_is_deterministic():
+    nv, nc, H, D = 333, 21, 2, 128
+    qv, vv = _rand((1, nv, H, D), 11), _rand((1, nv, H, D), 12)
+    qc, vc = _rand((1, nc, H, D), 13), _rand((1, nc, H, D), 14)
+    kv = torch.full((1, nv, H, D), 0.25, dtype=torch.bfloat16, device="cuda")
+    kc = torch.full((1, nc, H, D), 0.25, dtype=torch.bfloat16, device="cuda")
+    o_v, o_c = mm.joint_attention(qv, kv, vv, qc, kc, vc)
+    o_v2, o_c2 = mm.joint_attention(qv, kv, vv, qc, kc, vc)
+    torch.cuda.synchronize()
+    mean = torch.cat([vv, vc], dim=1).double().mean(dim=1, keepdim=True).cpu().numpy()
+    assert_close("o_vis vs mean(V)", to_host64(o_v), np.broadcast_to(mean, o_v.shape), 2e-2)
+    assert_close("o_cond vs mean(V)", to_host64(o_c), np.broadcast_to(mean, o_c.shape), 2e-2)
+    assert torch.equal(o_v, o_v2) and torch.equal(o_c, o_c2), "attention is not bitwise deterministic"
+
+
+def test_attention_bf16_output_and_cond_permutation():
+    nv, nc, H, D = 260, 40, 2, 128
+    qv, kv, vv = (_rand((1, nv, H, D), s) for s in (21, 22, 23))
+    qc, kc, vc = (_rand((1, nc, H, D), s) for s in (24, 25, 26))
+    o_v, o_c = mm.joint_attention(qv, kv, vv, qc, kc, vc, out_dtype=torch.bfloat16)
+    perm = torch.randperm(nc, generator=torch.Generator().manual_seed(3)).cuda()
+    o_v2, o_c2 = mm.joint_attention(qv, kv, vv, qc[:, perm].contiguous(), kc[:, perm].contiguous(),
+                                    vc[:, perm].contiguous(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    r_v, r_c = _oracle_attn(qv, kv, vv, qc, kc, vc)
+    assert_close("o_vis bf16", to_host64(o_v), r_v, 2e-2)
+    assert_close("o_cond bf16", to_host64(o_c), r_c, 2e-2)
+    assert_close("o_vis permuted cond", to_host64(o_v2), r_v, 2e-2)
+    assert_close("o_cond permuted", to_host64(o_c2), r_c[:, perm.cpu().numpy()], 2e-2)
+
+
+def test_qk_norm_rope_in_place_matches_out_of_place_and_per_head_scales():
+    cfg = wl.ATTN_LAYER
+    raw, dev = _inputs(cfg)
+    H = cfg.heads
+    rope = mm.Rope3D.make(cfg.grid)
+    qkv = torch.stack([dev["q_vis"], dev["k_vis"], dev["v_vis"]], dim=2)   # [1, N, 3, H, D]
+    gq = _rand((H, 128), 31, torch.float32) * 0.1 + 1
+    gk = _rand((H, 128), 32, torch.float32) * 0.1 + 1
+    qo, ko = mm.qk_norm_rope(qkv[:, :, 0], qkv[:, :, 1], gq, gk, rope=rope)
+    mm.qk_norm_rope(qkv[:, :, 0], qkv[:, :, 1], gq, gk, rope=rope, q_out=qkv[:, :, 0], k_out=qkv[:, :, 1])
+    torch.cuda.synchronize()
+    assert torch.equal(qo, qkv[:, :, 0]) and torch.equal(ko, qkv[:, :, 1])
+    assert torch.equal(qkv[:, :, 2], dev["v_vis"]), "V must be untouched"
+    f64 = lambda k: wl.to_f64(raw[k], cfg.dtype)  # noqa: E731
+    rq, rk = oracle.qk_norm_rope(f64("q_vis"), f64("k_vis"), to_host64(gq), to_host64(gk), cfg.qk_eps, cfg.grid)
+    assert_close("q^ per-head scales", to_host64(qo), rq, 2e-2)
+    assert_close("k^ per-head scales", to_host64(ko), rk, 2e-2)
+
+
+def test_qk_norm_rope_f32_out_tight():
+    """bf16 in, f32 out: only the fp32 arithmetic separates it from the oracle."""
+    cfg = wl.ATTN_LAYER
+    raw, dev = _inputs(cfg)
+    rope = mm.Rope3D.make(cfg.grid)
+    qo, ko = mm.qk_norm_rope(dev["q_vis"], dev["k_vis"], dev["gq_vis"], dev["gk_vis"], rope=rope,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    f64 = lambda k: wl.to_f64(raw[k], cfg.dtype)  # noqa: E731
+    rq, rk = oracle.qk_norm_rope(f64("q_vis"), f64("k_vis"), f64("gq_vis"), f64("gk_vis"), cfg.qk_eps, cfg.grid)
+    assert_close("q^ f32", to_host64(qo), rq, 1e-5)
+    assert_close("k^ f32", to_host64(ko), rk, 1e-5)
+
+
+def test_invalid_arguments_raise_before_launch():
+    q = _rand((1, 8, 2, 128), 1)
+    g = torch.ones(128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mm.MmditError, match="N != T"):
+        mm.qk_norm_rope(q, q.clone(), g, g, rope=mm.Rope3D.make((2, 2, 3)))
+    with pytest.raises(mm.MmditError, match="d_t"):
+        mm.qk_norm_rope(q, q.clone(), g, g, rope=mm.Rope3D.make((2, 2, 2), (16, 56, 54)))
+    with pytest.raises(mm.MmditError, match="overlap"):
+        mm.joint_attention(q, q, q, out_dtype=torch.bfloat16, o_vis=q)

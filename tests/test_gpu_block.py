@@ -1,0 +1,139 @@
+"""GPU parity of the whole dual-stream block (mmdit_block_fwd) against the float64 oracle.
+
+Outputs and the per-stage intermediates kept in the workspace (modulation vectors, Q^ after
+norm/RoPE, attention output O, residual x1, FFN input h2) are compared so that the large
+FFN branch cannot hide an error in the attention branch.  Small blocks are compared
+element by element; the 480p block on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import video_diffusion_transformer_mmdit_amd as mm
+import workloads as wl
+from tests.util import TOL, assert_close, log, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_block(cfg, raw):
+    dev = {k: to_dev(v, wl.BF16) for k, v in raw.items()}
+    wv = {k: dev[f"vis.{k}"] for k in wl.STREAM_WEIGHTS}
+    wc = {k: dev[f"cond.{k}"] for k in wl.STREAM_WEIGHTS}
+    return dev, wv, wc
+
+
+def _host_weights(raw, s):
+    return {k: wl.to_f64(raw[f"{s}.{k}"], wl.BF16) for k in wl.STREAM_WEIGHTS}
+
+
+def _run_block(cfg, dev, wv, wc, ffn_dtype, out_dtype=torch.float32):
+    dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, cfg.ln_eps, cfg.qk_eps,
+                             ffn_dtype=ffn_dtype)
+    rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
+    out_v, out_c, ws = mm.block_fwd(dims, wv, wc, dev["x_vis"], dev["x_cond"] if cfg.n_cond else None,
+                                    dev["tvec"], rope, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return dims, out_v, out_c, ws
+
+
+def _ws_views(dims, cfg, ws, s, n, rows=None):
+    """Intermediates of stream s from the workspace: mod [B,6C], qkv-region h2, x1, O."""
+    off = mm.block_workspace_offsets(dims, cfg.batch, cfg.n_vis, cfg.n_cond)[s]
+    B, C = cfg.batch, cfg.width
+    ffn_t = torch.float16 if dims.ffn_dtype == mm.F16 else torch.bfloat16
+
+    def view(region, dtype, shape):
+        nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        return ws[off[region]:off[region] + nbytes].view(dtype).view(shape)
+
+    out = {"mod": view(mm.WS_MOD, torch.float32, (B, 6 * C)),
+           "o": view(mm.WS_H, torch.bfloat16, (B, n, C)),
+           "h2": view(mm.WS_QKV, ffn_t, (B, n, C)),
+           "x1": view(mm.WS_X1, torch.float32, (B, n, C))}
+    if rows is not None:
+        idx = torch.from_numpy(rows).cuda()
+        for k in ("o", "h2", "x1"):
+            out[k] = out[k][:, idx]
+    return {k: to_host64(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("cfg,ffn", [(wl.BLOCK_TINY, torch.bfloat16), (wl.BLOCK_TINY, torch.float16),
+                                     (wl.BLOCK_SMALL, torch.float16), (wl.BLOCK_SMALL, torch.bfloat16)],
+                         ids=["tiny-bf16ffn", "tiny-f16ffn", "small-f16ffn", "small-bf16ffn"])
+def test_block_full_parity(cfg, ffn):
+    log(f"block parity {cfg.name} ffn={ffn}")
+    raw = wl.block_inputs(cfg)
+    dev, wv, wc = _dev_block(cfg, raw)
+    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, ffn)
+    ref = oracle.block_forward(wl.to_f64(raw["x_vis"], wl.BF16), wl.to_f64(raw["x_cond"], wl.BF16),
+                               wl.to_f64(raw["tvec"], wl.BF16), _host_weights(raw, "vis"),
+                               _host_weights(raw, "cond"), cfg.grid, cfg.heads, cfg.ln_eps, cfg.qk_eps)
+    tol = TOL[wl.BF16]
+    for s, n in (("vis", cfg.n_vis), ("cond", cfg.n_cond)):
+        iv = _ws_views(dims, cfg, ws, 0 if s == "vis" else 1, n)
+        assert_close(f"mod_{s}", iv["mod"], ref[f"mod_{s}"], 1e-5)
+        assert_close(f"o_{s}", iv["o"], ref[f"o_{s}"], tol)
+        assert_close(f"x1_{s}", iv["x1"], ref[f"x1_{s}"], tol)
+        assert_close(f"h2_{s}", iv["h2"], ref[f"h2_{s}"], tol)
+    assert_close("out_vis", to_host64(out_v), ref["out_vis"], tol)
+    assert_close("out_cond", to_host64(out_c), ref["out_cond"], tol)
+
+
+def test_block_zero_modulation_is_exact_identity():
+    cfg = wl.BLOCK_TINY
+    raw = wl.block_inputs(cfg)
+    for s in ("vis", "cond"):
+        raw[f"{s}.w_mod"][:] = 0
+        raw[f"{s}.b_mod"][:] = 0
+    dev, wv, wc = _dev_block(cfg, raw)
+    _, out_v, out_c, _ = _run_block(cfg, dev, wv, wc, torch.float16)
+    assert torch.equal(out_v, dev["x_vis"].float())
+    assert torch.equal(out_c, dev["x_cond"].float())
+
+
+def test_block_without_cond_tokens_and_determinism():
+    cfg = wl.BlockConfig("block_nocond", 256, 2, 128, 512, 64, (2, 3, 5), 0, seed=21)
+    raw = wl.block_inputs(cfg)
+    dev, wv, wc = _dev_block(cfg, raw)
+    _, out_v, _, _ = _run_block(cfg, dev, wv, wc, torch.float16)
+    _, out_v2, _, _ = _run_block(cfg, dev, wv, wc, torch.float16)
+    assert torch.equal(out_v, out_v2), "block forward is not bitwise deterministic"
+    ref = oracle.block_forward(wl.to_f64(raw["x_vis"], wl.BF16), wl.to_f64(raw["x_cond"], wl.BF16),
+                               wl.to_f64(raw["tvec"], wl.BF16), _host_weights(raw, "vis"),
+                               _host_weights(raw, "cond"), cfg.grid, cfg.heads)
+    assert_close("out_vis (no cond)", to_host64(out_v), ref["out_vis"], TOL[wl.BF16])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ffn", [torch.float16], ids=["f16ffn"])
+def test_block_480p_sampled_parity(ffn):
+    cfg = wl.BLOCK_480P
+    log("block 480p: generating inputs")
+    raw = wl.block_inputs(cfg)
+    dev, wv, wc = _dev_block(cfg, raw)
+    log("  GPU block forward")
+    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, ffn)
+    rv = wl.sample_rows(cfg.n_vis, 128, seed=501)
+    rc = wl.sample_rows(cfg.n_cond, 32, seed=502)
+    got = {"out_vis": to_host64(out_v[:, torch.from_numpy(rv).cuda()]),
+           "out_cond": to_host64(out_c[:, torch.from_numpy(rc).cuda()])}
+    iv = _ws_views(dims, cfg, ws, 0, cfg.n_vis, rv)
+    ic = _ws_views(dims, cfg, ws, 1, cfg.n_cond, rc)
+    del dev, wv, wc, out_v, out_c, ws
+    torch.cuda.empty_cache()
+    log("  oracle (float64) on sampled rows; K/V of every token")
+    ref = oracle.block_forward(wl.to_f64(raw["x_vis"], wl.BF16), wl.to_f64(raw["x_cond"], wl.BF16),
+                               wl.to_f64(raw["tvec"], wl.BF16), _host_weights(raw, "vis"),
+                               _host_weights(raw, "cond"), cfg.grid, cfg.heads, cfg.ln_eps, cfg.qk_eps,
+                               vis_rows=rv, cond_rows=rc)
+    tol = TOL[wl.BF16]
+    for s, i in (("vis", iv), ("cond", ic)):
+        assert_close(f"mod_{s}", i["mod"], ref[f"mod_{s}"], 1e-5)
+        assert_close(f"o_{s}", i["o"], ref[f"o_{s}"], tol)
+        assert_close(f"x1_{s}", i["x1"], ref[f"x1_{s}"], tol)
+        assert_close(f"h2_{s}", i["h2"], ref[f"h2_{s}"], tol)
+    assert_close("out_vis", got["out_vis"], ref["out_vis"], tol)
+    assert_close("out_cond", got["out_cond"], ref["out_cond"], tol)

@@ -1,0 +1,43 @@
+"""Shared helpers of the tests: moving seeded workload tensors to the GPU and the float64
+comparison metric.  No step of the block's arithmetic lives here."""
+import math
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads as wl
+
+TOL = {wl.F32: 1e-4, wl.BF16: 2e-2}
+
+
+def log(*a):
+    print(f"[{time.strftime('%H:%M:%S')}]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Stored workload tensor -> torch tensor on the GPU with the same bytes."""
+    if dtype == wl.BF16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def to_host64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref))) / rms
+
+
+def assert_close(name, got, ref, tol):
+    e = rel_err(got, ref)
+    log(f"  {name}: max|err|/rms = {e:.3e} (tol {tol:.0e})")
+    assert np.all(np.isfinite(np.asarray(got))), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: max|err|/rms {e:.3e} > {tol:.0e}"
+    return e

@@ -1,0 +1,13 @@
+"""MI355X-native dual-stream MMDiT block core.
+
+Thin Python binding over the C ABI of ``libmmdit.so`` (header ``include/mmdit.h``): each
+function marshals torch tensors (device memory, current stream) into the C call of the
+same name.  Every step of the computation runs in the library's HIP kernels; there is no
+Python or PyTorch compute fallback, and importing a missing library raises.
+"""
+from ._abi import (  # noqa: F401
+    BF16, F16, F32, STAGES, STAGE_COUNT, EPI_GATED_RES, EPI_GELU, EPI_NONE, MmditError, Rope3D, BlockDims,
+    WS_G, WS_H, WS_MOD, WS_QKV, WS_W1H, WS_W2H, WS_X1,
+    abi_version, block_fwd, block_workspace_bytes, block_workspace_offsets, joint_attention,
+    lib, library_path, linear, modulate_ln, modulation, qk_norm_rope,
+)

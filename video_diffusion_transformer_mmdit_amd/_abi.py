@@ -1,0 +1,350 @@
+"""ctypes binding of libmmdit.so: argument marshalling only.
+
+Torch supplies device memory and the current HIP stream; every function below checks
+shapes, takes ``data_ptr()`` and strides, and calls the C entry point of the same name
+declared in include/mmdit.h.  A non-zero status raises MmditError with the library's text.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+F32, BF16, F16 = 0, 1, 2
+EPI_NONE, EPI_GELU, EPI_GATED_RES = 0, 1, 2
+WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_W1H, WS_W2H = range(7)
+WS_COUNT = 7
+STAGES = ("mod_ln1", "qkv", "qk_norm_rope", "attention", "out_proj", "ln2", "ffn_up", "ffn_down")
+STAGE_COUNT = len(STAGES)
+
+_TORCH_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_DT_TORCH = {v: k for k, v in _TORCH_DT.items()}
+
+
+class MmditError(RuntimeError):
+    pass
+
+
+class Rope3D(ctypes.Structure):
+    """3D RoPE of the visual grid: T x H x W tokens, head dims split d_t/d_h/d_w."""
+    _fields_ = [("T", c_int64), ("H", c_int64), ("W", c_int64),
+                ("d_t", c_int32), ("d_h", c_int32), ("d_w", c_int32), ("base", c_float)]
+
+    @classmethod
+    def make(cls, grid: Sequence[int], split: Sequence[int] = (16, 56, 56), base: float = 10000.0):
+        return cls(int(grid[0]), int(grid[1]), int(grid[2]), int(split[0]), int(split[1]),
+                   int(split[2]), float(base))
+
+
+class StreamWeights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm",
+                                         "w_o", "b_o", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+
+
+class BlockDims(ctypes.Structure):
+    _fields_ = [("C", c_int64), ("H", c_int64), ("D", c_int64), ("F", c_int64), ("Dt", c_int64),
+                ("ln_eps", c_float), ("qk_eps", c_float), ("qk_scale_head_stride", c_int64),
+                ("w_dtype", c_int), ("ffn_dtype", c_int)]
+
+    @classmethod
+    def make(cls, C, H, F, Dt, ln_eps=1e-6, qk_eps=1e-6, qk_scale_head_stride=0,
+             ffn_dtype=torch.bfloat16):
+        return cls(C, H, C // H, F, Dt, ln_eps, qk_eps, qk_scale_head_stride, BF16,
+                   _TORCH_DT[ffn_dtype])
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmmdit.so once.  Raises if it has not been built: there is no fallback."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise MmditError(f"{path} is missing; build it with "
+                         "`python -m video_diffusion_transformer_mmdit_amd.build`")
+    L = ctypes.CDLL(path)
+    i64, vp, f, i = c_int64, c_void_p, c_float, c_int
+    sig = {
+        "mmdit_modulate_ln": [vp, i, vp, i, vp, vp, vp, vp, i64, vp, i, i64, i64, i64, f, vp],
+        "mmdit_qk_norm_rope": [vp, vp, i, i64, vp, vp, i, i64, vp, vp, i, i64, i64, i64, i64, i64, f,
+                               ctypes.POINTER(Rope3D), vp],
+        "mmdit_joint_attention": [vp, vp, vp, i64, vp, vp, vp, i64, i, i64, i64, i64, i64, f, vp, vp, i,
+                                  i64, vp, vp],
+        "mmdit_linear": [vp, vp, i, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
+        "mmdit_modulation": [vp, vp, vp, i, vp, i64, i64, i64, vp],
+        "mmdit_block_workspace_offsets": [ctypes.POINTER(BlockDims), i64, i64, i64, ctypes.POINTER(c_size_t)],
+        "mmdit_block_fwd": [ctypes.POINTER(BlockDims), ctypes.POINTER(StreamWeights),
+                            ctypes.POINTER(StreamWeights), vp, vp, i, vp, i, ctypes.POINTER(Rope3D), i64,
+                            vp, vp, i, vp, c_size_t, i64, vp],
+        "mmdit_block_fwd_events": [ctypes.POINTER(BlockDims), ctypes.POINTER(StreamWeights),
+                                   ctypes.POINTER(StreamWeights), vp, vp, i, vp, i, ctypes.POINTER(Rope3D),
+                                   i64, vp, vp, i, vp, c_size_t, i64, vp, ctypes.POINTER(c_void_p)],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = c_int
+    L.mmdit_block_workspace_bytes.argtypes = [ctypes.POINTER(BlockDims), i64, i64, i64]
+    L.mmdit_block_workspace_bytes.restype = c_size_t
+    L.mmdit_status_str.argtypes = [c_int]
+    L.mmdit_status_str.restype = ctypes.c_char_p
+    L.mmdit_last_error.argtypes = []
+    L.mmdit_last_error.restype = ctypes.c_char_p
+    L.mmdit_abi_version.argtypes = []
+    L.mmdit_abi_version.restype = c_int
+    _LIB = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().mmdit_abi_version()
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        msg = lib().mmdit_last_error().decode()
+        raise MmditError(f"{name} failed ({lib().mmdit_status_str(status).decode()}): {msg}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _TORCH_DT[t.dtype]
+    except KeyError:
+        raise MmditError(f"unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise MmditError("tensors must live on the GPU")
+
+
+def _rows(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
+    """[B, N, H, D] view with contiguous (H, D) and batch items N rows apart ->
+    (B, N, row_stride)."""
+    if t.dim() != 4:
+        raise MmditError(f"{name} must be [B, N, H, D]")
+    B, N, H, D = t.shape
+    if t.stride(3) != 1 or (H > 1 and t.stride(2) != D):
+        raise MmditError(f"{name}: heads and dims must be contiguous")
+    rs = t.stride(1)
+    if B > 1 and N > 0 and t.stride(0) != N * rs:
+        raise MmditError(f"{name}: batch items must be N rows apart")
+    return B, N, rs
+
+
+# --------------------------------------------------------------------------- calls
+def modulate_ln(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, *,
+                branch: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                x_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                y_dtype=torch.bfloat16, eps: float = 1e-6) -> torch.Tensor:
+    """y = LN(x + gate*branch) * (1 + scale) + shift.  x [B, N, C]; shift/scale/gate f32
+    [B, C] (rows may be strided, e.g. slices of a [B, 6C] modulation buffer)."""
+    _need_gpu(x, shift, scale, branch, gate, x_out, y)
+    B, N, C = x.shape
+    if not x.is_contiguous():
+        raise MmditError("x must be contiguous")
+    mods = [m for m in (shift, scale, gate) if m is not None]
+    for m in mods:
+        if m.dtype != torch.float32 or m.dim() != 2 or m.stride(1) != 1 or m.shape != (B, C):
+            raise MmditError("shift / scale / gate must be f32 [B, C] with unit inner stride")
+    strides = {m.stride(0) for m in mods} if B > 1 else {max(m.stride(0) for m in mods) if B else C}
+    if len(strides) != 1:
+        raise MmditError("shift / scale / gate must share one batch stride")
+    ms = max(strides.pop(), C)
+    if y is None:
+        y = torch.empty((B, N, C), dtype=y_dtype, device=x.device)
+    st = lib().mmdit_modulate_ln(x.data_ptr(), _dt(x), _ptr(branch), _dt(branch) if branch is not None else BF16,
+                                 _ptr(gate), _ptr(x_out), shift.data_ptr(), scale.data_ptr(), ms,
+                                 y.data_ptr(), _dt(y), B, N, C, eps, _stream(x))
+    _check(st, "mmdit_modulate_ln")
+    return y
+
+
+def qk_norm_rope(q: torch.Tensor, k: torch.Tensor, q_scale: torch.Tensor, k_scale: torch.Tensor, *,
+                 rope: Optional[Rope3D] = None, eps: float = 1e-6,
+                 q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                 out_dtype=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-head RMSNorm of q and k (+ 3D RoPE when ``rope`` is given).  q, k: [B, N, H, D]
+    views sharing one row stride; pass q_out=q, k_out=k for in place."""
+    _need_gpu(q, k, q_scale, k_scale, q_out, k_out)
+    B, N, rs = _rows(q, "q")
+    _, _, rsk = _rows(k, "k")
+    if k.shape != q.shape or rsk != rs or k.dtype != q.dtype:
+        raise MmditError("q and k must share shape, dtype and row stride")
+    H, D = q.shape[2], q.shape[3]
+    od = out_dtype or q.dtype
+    if q_out is None:
+        q_out = torch.empty(q.shape, dtype=od, device=q.device)
+    if k_out is None:
+        k_out = torch.empty(q.shape, dtype=od, device=q.device)
+    _, _, ors = _rows(q_out, "q_out")
+    _, _, orsk = _rows(k_out, "k_out")
+    if orsk != ors or k_out.dtype != q_out.dtype:
+        raise MmditError("q_out and k_out must share dtype and row stride")
+    if q_scale.dtype != k_scale.dtype or q_scale.shape != k_scale.shape:
+        raise MmditError("q_scale and k_scale must match")
+    shs = 0 if q_scale.dim() == 1 else D
+    st = lib().mmdit_qk_norm_rope(q.data_ptr(), k.data_ptr(), _dt(q), rs, q_scale.data_ptr(),
+                                  k_scale.data_ptr(), _dt(q_scale), shs, q_out.data_ptr(),
+                                  k_out.data_ptr(), _dt(q_out), ors, B, N, H, D, eps,
+                                  ctypes.byref(rope) if rope is not None else None, _stream(q))
+    _check(st, "mmdit_qk_norm_rope")
+    return q_out, k_out
+
+
+def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, *,
+                    softmax_scale: Optional[float] = None, out_dtype=torch.float32,
+                    o_vis: Optional[torch.Tensor] = None, o_cond: Optional[torch.Tensor] = None,
+                    return_lse: bool = False):
+    """softmax(Q K^T * scale) V over [cond | vis] per head, outputs split per stream.
+    Inputs [B, N_s, H, D] views with one common row stride."""
+    ts = [t for t in (q_vis, k_vis, v_vis, q_cond, k_cond, v_cond) if t is not None]
+    _need_gpu(*ts)
+    B, n_vis, rs = _rows(q_vis, "q_vis")
+    H, D = q_vis.shape[2], q_vis.shape[3]
+    n_cond = 0 if q_cond is None else q_cond.shape[1]
+    for nm, t in zip(("k_vis", "v_vis", "q_cond", "k_cond", "v_cond"), (k_vis, v_vis, q_cond, k_cond, v_cond)):
+        if t is None:
+            continue
+        b, n, r = _rows(t, nm)
+        if t.dtype != q_vis.dtype or t.shape[0] != B or t.shape[2:] != q_vis.shape[2:]:
+            raise MmditError(f"{nm}: dtype / shape mismatch")
+        if n > 0 and r != rs and not (n == 1 or rs == 0):
+            raise MmditError(f"{nm}: all inputs must share one row stride")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    dev = q_vis.device
+    if o_vis is None:
+        o_vis = torch.empty((B, n_vis, H, D), dtype=out_dtype, device=dev)
+    if o_cond is None and n_cond > 0:
+        o_cond = torch.empty((B, n_cond, H, D), dtype=out_dtype, device=dev)
+    _, _, ors = _rows(o_vis, "o_vis")
+    lse = torch.empty((B, H, n_vis + n_cond), dtype=torch.float32, device=dev) if return_lse else None
+    st = lib().mmdit_joint_attention(q_vis.data_ptr(), k_vis.data_ptr(), v_vis.data_ptr(), n_vis,
+                                     _ptr(q_cond) if n_cond else None, _ptr(k_cond) if n_cond else None,
+                                     _ptr(v_cond) if n_cond else None, n_cond, _dt(q_vis), rs, B, H, D,
+                                     softmax_scale, o_vis.data_ptr(), _ptr(o_cond) if n_cond else None,
+                                     _dt(o_vis), ors, _ptr(lse), _stream(q_vis))
+    _check(st, "mmdit_joint_attention")
+    if return_lse:
+        return o_vis, o_cond, lse
+    return o_vis, o_cond
+
+
+def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+           epilogue: int = EPI_NONE, res: Optional[torch.Tensor] = None,
+           gate: Optional[torch.Tensor] = None, rows_per_batch: Optional[int] = None,
+           y: Optional[torch.Tensor] = None, y_dtype=torch.bfloat16) -> torch.Tensor:
+    """y = epilogue(x W^T + bias).  x [M, K], w [N, K] (bf16 or f16, contiguous)."""
+    _need_gpu(x, w, bias, res, gate, y)
+    M, K = x.shape
+    N = w.shape[0]
+    if not (x.is_contiguous() and w.is_contiguous()) or w.shape[1] != K:
+        raise MmditError("x [M, K] and w [N, K] must be contiguous")
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=x.device)
+    gs = 0
+    if gate is not None:
+        if gate.dtype != torch.float32 or gate.stride(-1) != 1:
+            raise MmditError("gate must be f32 with unit inner stride")
+        gs = gate.stride(0) if gate.dim() == 2 else N
+    st = lib().mmdit_linear(x.data_ptr(), w.data_ptr(), _dt(x), _ptr(bias),
+                            _dt(bias) if bias is not None else BF16, y.data_ptr(), _dt(y), M, N, K,
+                            epilogue, _ptr(res), _dt(res) if res is not None else F32, _ptr(gate), gs,
+                            rows_per_batch or M, _stream(x))
+    _check(st, "mmdit_linear")
+    return y
+
+
+def modulation(w_mod: torch.Tensor, b_mod: Optional[torch.Tensor], tvec: torch.Tensor,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mod [B, 6C] f32 = W_mod tvec + b_mod."""
+    _need_gpu(w_mod, b_mod, tvec, out)
+    C6, Dt = w_mod.shape
+    B = tvec.shape[0]
+    if out is None:
+        out = torch.empty((B, C6), dtype=torch.float32, device=w_mod.device)
+    st = lib().mmdit_modulation(w_mod.data_ptr(), _ptr(b_mod), tvec.data_ptr(), _dt(tvec), out.data_ptr(),
+                                B, C6, Dt, _stream(w_mod))
+    _check(st, "mmdit_modulation")
+    return out
+
+
+STREAM_KEYS = ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm", "w_o", "b_o", "w_fc1", "b_fc1",
+               "w_fc2", "b_fc2")
+
+
+def _stream_weights(w: Dict[str, torch.Tensor]) -> StreamWeights:
+    sw = StreamWeights()
+    for k in STREAM_KEYS:
+        t = w.get(k)
+        if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
+            raise MmditError(f"weight {k} must be contiguous bf16")
+        setattr(sw, k, None if t is None else t.data_ptr())
+    return sw
+
+
+def block_workspace_bytes(dims: BlockDims, B: int, n_vis: int, n_cond: int) -> int:
+    return lib().mmdit_block_workspace_bytes(ctypes.byref(dims), B, n_vis, n_cond)
+
+
+def block_workspace_offsets(dims: BlockDims, B: int, n_vis: int, n_cond: int):
+    arr = (c_size_t * (2 * WS_COUNT))()
+    _check(lib().mmdit_block_workspace_offsets(ctypes.byref(dims), B, n_vis, n_cond, arr),
+           "mmdit_block_workspace_offsets")
+    return [list(arr[:WS_COUNT]), list(arr[WS_COUNT:])]
+
+
+def block_fwd(dims: BlockDims, w_vis: Dict[str, torch.Tensor], w_cond: Dict[str, torch.Tensor],
+              x_vis: torch.Tensor, x_cond: Optional[torch.Tensor], tvec: torch.Tensor, rope: Rope3D, *,
+              out_dtype=torch.float32, workspace: Optional[torch.Tensor] = None,
+              out_vis: Optional[torch.Tensor] = None, out_cond: Optional[torch.Tensor] = None,
+              stage_events: Optional[Sequence[int]] = None):
+    """One dual-stream block forward.  Returns (out_vis, out_cond, workspace).
+    ``stage_events``: optional 2 * STAGE_COUNT raw hipEvent_t handles (ints or None)
+    recorded around each stage on the current stream."""
+    _need_gpu(x_vis, x_cond, tvec, workspace)
+    B, n_vis, C = x_vis.shape
+    n_cond = 0 if x_cond is None else x_cond.shape[1]
+    need = block_workspace_bytes(dims, B, n_vis, n_cond)
+    if need == 0:
+        raise MmditError("invalid block dims")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_vis.device)
+    if out_vis is None:
+        out_vis = torch.empty((B, n_vis, C), dtype=out_dtype, device=x_vis.device)
+    if out_cond is None and n_cond > 0:
+        out_cond = torch.empty((B, n_cond, C), dtype=out_dtype, device=x_vis.device)
+    swv, swc = _stream_weights(w_vis), _stream_weights(w_cond)
+    args = (ctypes.byref(dims), ctypes.byref(swv), ctypes.byref(swc), x_vis.data_ptr(),
+            _ptr(x_cond) if n_cond else None, _dt(x_vis), tvec.data_ptr(), _dt(tvec),
+            ctypes.byref(rope), n_cond, out_vis.data_ptr(), _ptr(out_cond) if n_cond else None,
+            _dt(out_vis), workspace.data_ptr(), workspace.numel(), B, _stream(x_vis))
+    if stage_events is None:
+        _check(lib().mmdit_block_fwd(*args), "mmdit_block_fwd")
+    else:
+        if len(stage_events) != 2 * STAGE_COUNT:
+            raise MmditError(f"stage_events needs {2 * STAGE_COUNT} entries")
+        arr = (c_void_p * (2 * STAGE_COUNT))(*stage_events)
+        _check(lib().mmdit_block_fwd_events(*args, arr), "mmdit_block_fwd_events")
+    return out_vis, out_cond, workspace

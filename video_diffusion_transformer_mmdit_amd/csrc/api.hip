@@ -1,0 +1,240 @@
+// extern "C" entry points of libmmdit: argument validation, then dispatch to the kernels.
+// Every check runs before anything is enqueued, so a rejected call touches no HIP state.
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+
+namespace mmdit {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+int fail(int status, const std::string& msg) {
+  g_last_error = std::string(mmdit_status_str(status)) + ": " + msg;
+  return status;
+}
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MMDIT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return MMDIT_OK;
+}
+
+static bool valid_dtype(int dt) { return dt == MMDIT_F32 || dt == MMDIT_BF16 || dt == MMDIT_F16; }
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// bytes spanned by `rows` rows of `row_elems` elements at `stride` elements
+static size_t span(int64_t rows, int64_t row_elems, int64_t stride, int dt) {
+  if (rows <= 0) return 0;
+  return (size_t)((rows - 1) * stride + row_elems) * (size_t)dtype_size(dt);
+}
+
+int validate_rope(const mmdit_rope3d* r, int64_t N, int64_t D) {
+  if (r->T < 1 || r->H < 1 || r->W < 1) return fail(MMDIT_ERR_SHAPE, "rope: T, H, W must be >= 1");
+  if (r->d_t < 0 || r->d_h < 0 || r->d_w < 0 || (r->d_t & 1) || (r->d_h & 1) || (r->d_w & 1))
+    return fail(MMDIT_ERR_SHAPE, "rope: band widths must be even and >= 0");
+  if ((int64_t)r->d_t + r->d_h + r->d_w != D) return fail(MMDIT_ERR_SHAPE, "rope: d_t + d_h + d_w != D");
+  if (!(r->base > 0.f)) return fail(MMDIT_ERR_SHAPE, "rope: base must be > 0");
+  if (r->T * r->H * r->W != N) return fail(MMDIT_ERR_SHAPE, "rope: N != T * H * W");
+  return MMDIT_OK;
+}
+
+}  // namespace mmdit
+
+using namespace mmdit;
+
+extern "C" {
+
+const char* mmdit_status_str(int s) {
+  switch (s) {
+    case MMDIT_OK: return "MMDIT_OK";
+    case MMDIT_ERR_NULL: return "MMDIT_ERR_NULL";
+    case MMDIT_ERR_ALIGN: return "MMDIT_ERR_ALIGN";
+    case MMDIT_ERR_SHAPE: return "MMDIT_ERR_SHAPE";
+    case MMDIT_ERR_DTYPE: return "MMDIT_ERR_DTYPE";
+    case MMDIT_ERR_WORKSPACE: return "MMDIT_ERR_WORKSPACE";
+    case MMDIT_ERR_HIP: return "MMDIT_ERR_HIP";
+    case MMDIT_ERR_ALIAS: return "MMDIT_ERR_ALIAS";
+    default: return "MMDIT_ERR_UNKNOWN";
+  }
+}
+
+const char* mmdit_last_error(void) { return g_last_error.c_str(); }
+
+int mmdit_abi_version(void) { return 1; }
+
+int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
+                      const float* gate, float* x_out, const float* shift, const float* scale,
+                      int64_t mod_stride, void* y, int y_dtype, int64_t B, int64_t N, int64_t C,
+                      float eps, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || N < 0 || C < 8 || C % 8 || C > 8192)
+    return fail(MMDIT_ERR_SHAPE, "modulate_ln: need B, N >= 0 and C a multiple of 8 in [8, 8192]");
+  if (mod_stride < C) return fail(MMDIT_ERR_SHAPE, "modulate_ln: mod_stride < C");
+  if (!(eps >= 0.f)) return fail(MMDIT_ERR_SHAPE, "modulate_ln: eps must be >= 0");
+  if (x_dtype != MMDIT_F32 && x_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "modulate_ln: x must be f32 or bf16");
+  if (branch && branch_dtype != MMDIT_F32 && branch_dtype != MMDIT_BF16)
+    return fail(MMDIT_ERR_DTYPE, "modulate_ln: branch must be f32 or bf16");
+  if (!valid_dtype(y_dtype)) return fail(MMDIT_ERR_DTYPE, "modulate_ln: bad y dtype");
+  if (B * N == 0) return MMDIT_OK;
+  if (!x || !shift || !scale || !y) return fail(MMDIT_ERR_NULL, "modulate_ln: x, shift, scale and y are required");
+  if (branch && !gate) return fail(MMDIT_ERR_NULL, "modulate_ln: gate is required with branch");
+  if (!aligned16(x) || !aligned16(y) || (branch && !aligned16(branch)) || (x_out && !aligned16(x_out)) ||
+      !aligned16(shift) || !aligned16(scale) || (gate && !aligned16(gate)) || (mod_stride % 4))
+    return fail(MMDIT_ERR_ALIGN, "modulate_ln: pointers must be 16-byte aligned, mod_stride a multiple of 4");
+  const int64_t rows = B * N;
+  const size_t ny = span(rows, C, C, y_dtype), nx = span(rows, C, C, x_dtype);
+  const size_t nxo = x_out ? span(rows, C, C, MMDIT_F32) : 0;
+  const size_t nb = branch ? span(rows, C, C, branch_dtype) : 0;
+  if (overlaps(y, ny, x, nx) || overlaps(y, ny, branch, nb) || overlaps(x_out, nxo, x, nx) ||
+      overlaps(x_out, nxo, branch, nb) || overlaps(x_out, nxo, y, ny))
+    return fail(MMDIT_ERR_ALIAS, "modulate_ln: outputs overlap inputs");
+  return launch_modulate_ln(x, x_dtype, branch, branch_dtype, gate, x_out, shift, scale, mod_stride, y,
+                            y_dtype, B, N, C, eps, static_cast<hipStream_t>(stream));
+}
+
+int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_row_stride,
+                       const void* q_scale, const void* k_scale, int scale_dtype,
+                       int64_t scale_head_stride, void* q_out, void* k_out, int out_dtype,
+                       int64_t out_row_stride, int64_t B, int64_t N, int64_t H, int64_t D,
+                       float eps, const mmdit_rope3d* rope, void* stream) {
+  g_last_error.clear();
+  if (D != 128) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: D must be 128");
+  if (B < 0 || N < 0 || H < 1 || H > 4096) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: need B, N >= 0, 1 <= H <= 4096");
+  if (in_row_stride < H * D || out_row_stride < H * D) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: row stride < H*D");
+  if (scale_head_stride != 0 && scale_head_stride != D)
+    return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: scale_head_stride must be 0 or D");
+  if (!(eps >= 0.f)) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: eps must be >= 0");
+  if (in_dtype != MMDIT_F32 && in_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: in dtype must be f32 or bf16");
+  if (scale_dtype != MMDIT_F32 && scale_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: scale dtype must be f32 or bf16");
+  if (!valid_dtype(out_dtype)) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: bad out dtype");
+  if (in_dtype == MMDIT_F32 && out_dtype == MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: f32 -> f16 not supported");
+  if (rope) { const int r = validate_rope(rope, N, D); if (r) return r; }
+  if (B * N == 0) return MMDIT_OK;
+  if (!q || !k || !q_scale || !k_scale || !q_out || !k_out) return fail(MMDIT_ERR_NULL, "qk_norm_rope: null pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(q_scale) ||
+      !aligned16(k_scale) || (in_row_stride % 8) || (out_row_stride % 8))
+    return fail(MMDIT_ERR_ALIGN, "qk_norm_rope: pointers 16-byte aligned, strides multiples of 8 elements");
+  const int64_t rows = B * N, hd = H * D;
+  const size_t nq = span(rows, hd, in_row_stride, in_dtype), nqo = span(rows, hd, out_row_stride, out_dtype);
+  const bool q_inplace = q_out == q, k_inplace = k_out == k;
+  if ((q_inplace || k_inplace) && (in_dtype != out_dtype || in_row_stride != out_row_stride))
+    return fail(MMDIT_ERR_ALIAS, "qk_norm_rope: in place needs equal dtypes and strides");
+  // Outputs may only coincide exactly with their own input.  With a shared packed row
+  // (q, k, v of one token in one row) the spans interleave, so check per-row extents.
+  auto rows_clash = [&](const void* o, const void* i, int odt, int idt) {
+    const uintptr_t po = reinterpret_cast<uintptr_t>(o), pi = reinterpret_cast<uintptr_t>(i);
+    const int64_t so = out_row_stride * dtype_size(odt), si = in_row_stride * dtype_size(idt);
+    const int64_t lo = hd * dtype_size(odt), li = hd * dtype_size(idt);
+    if (so == si) {  // same row pitch: compare the in-row windows
+      const int64_t delta = (int64_t)po - (int64_t)pi;
+      int64_t r = delta % so;
+      if (r < 0) r += so;
+      const bool hit = (r < li) || (so - r < lo);
+      return hit && overlaps(o, nqo, i, nq);
+    }
+    return overlaps(o, nqo, i, nq);
+  };
+  if ((!q_inplace && rows_clash(q_out, q, out_dtype, in_dtype)) || rows_clash(q_out, k, out_dtype, in_dtype) ||
+      (!k_inplace && rows_clash(k_out, k, out_dtype, in_dtype)) || rows_clash(k_out, q, out_dtype, in_dtype) ||
+      rows_clash(q_out, k_out, out_dtype, out_dtype))
+    return fail(MMDIT_ERR_ALIAS, "qk_norm_rope: outputs partially overlap inputs");
+  return launch_qk_norm_rope(q, k, in_dtype, in_row_stride, q_scale, k_scale, scale_dtype,
+                             scale_head_stride, q_out, k_out, out_dtype, out_row_stride, B, N, H,
+                             eps, rope, static_cast<hipStream_t>(stream));
+}
+
+int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
+                          const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
+                          int in_dtype, int64_t in_row_stride, int64_t B, int64_t H, int64_t D,
+                          float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
+                          int64_t out_row_stride, float* lse, void* stream) {
+  g_last_error.clear();
+  if (D != 128) return fail(MMDIT_ERR_SHAPE, "joint_attention: D must be 128");
+  if (B < 0 || H < 1 || n_vis < 0 || n_cond < 0 || n_vis + n_cond < 1)
+    return fail(MMDIT_ERR_SHAPE, "joint_attention: need B >= 0, H >= 1, n_vis + n_cond >= 1");
+  if (in_row_stride < H * D || out_row_stride < H * D) return fail(MMDIT_ERR_SHAPE, "joint_attention: row stride < H*D");
+  if (!(softmax_scale > 0.f)) return fail(MMDIT_ERR_SHAPE, "joint_attention: softmax_scale must be > 0");
+  if (in_dtype != MMDIT_BF16 && in_dtype != MMDIT_F32) return fail(MMDIT_ERR_DTYPE, "joint_attention: in dtype must be bf16 or f32");
+  if (!valid_dtype(out_dtype)) return fail(MMDIT_ERR_DTYPE, "joint_attention: bad out dtype");
+  if (B == 0) return MMDIT_OK;
+  if (n_vis > 0 && (!q_vis || !k_vis || !v_vis || !o_vis)) return fail(MMDIT_ERR_NULL, "joint_attention: visual pointers required");
+  if (n_cond > 0 && (!q_cond || !k_cond || !v_cond || !o_cond)) return fail(MMDIT_ERR_NULL, "joint_attention: conditioning pointers required");
+  const void* ins[6] = {q_vis, k_vis, v_vis, q_cond, k_cond, v_cond};
+  const int64_t nin[6] = {n_vis, n_vis, n_vis, n_cond, n_cond, n_cond};
+  for (int i = 0; i < 6; ++i)
+    if (nin[i] > 0 && !aligned16(ins[i])) return fail(MMDIT_ERR_ALIGN, "joint_attention: inputs must be 16-byte aligned");
+  if ((n_vis > 0 && !aligned16(o_vis)) || (n_cond > 0 && !aligned16(o_cond)) || (lse && !aligned16(lse)) ||
+      (in_row_stride % 8) || (out_row_stride % 8))
+    return fail(MMDIT_ERR_ALIGN, "joint_attention: outputs 16-byte aligned, strides multiples of 8 elements");
+  const int64_t hd = H * D;
+  const void* outs[2] = {o_vis, o_cond};
+  const int64_t nout[2] = {n_vis, n_cond};
+  for (int o = 0; o < 2; ++o) {
+    if (nout[o] == 0) continue;
+    const size_t no = span(B * nout[o], hd, out_row_stride, out_dtype);
+    for (int i = 0; i < 6; ++i)
+      if (nin[i] > 0 && overlaps(outs[o], no, ins[i], span(B * nin[i], hd, in_row_stride, in_dtype)))
+        return fail(MMDIT_ERR_ALIAS, "joint_attention: outputs overlap inputs");
+    if (lse && overlaps(outs[o], no, lse, (size_t)(B * H * (n_vis + n_cond)) * 4))
+      return fail(MMDIT_ERR_ALIAS, "joint_attention: lse overlaps an output");
+  }
+  if (n_vis > 0 && n_cond > 0 &&
+      overlaps(o_vis, span(B * n_vis, hd, out_row_stride, out_dtype), o_cond, span(B * n_cond, hd, out_row_stride, out_dtype)))
+    return fail(MMDIT_ERR_ALIAS, "joint_attention: o_vis and o_cond overlap");
+  return launch_joint_attention(q_vis, k_vis, v_vis, n_vis, q_cond, k_cond, v_cond, n_cond, in_dtype,
+                                in_row_stride, B, H, softmax_scale, o_vis, o_cond, out_dtype,
+                                out_row_stride, lse, static_cast<hipStream_t>(stream));
+}
+
+int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, int bias_dtype,
+                 void* y, int y_dtype, int64_t M, int64_t N, int64_t K, int epilogue,
+                 const void* res, int res_dtype, const float* gate, int64_t gate_stride,
+                 int64_t rows_per_batch, void* stream) {
+  g_last_error.clear();
+  if (M < 0 || N < 0 || K < 64 || K % 64) return fail(MMDIT_ERR_SHAPE, "linear: need M, N >= 0 and K a positive multiple of 64");
+  if (x_dtype != MMDIT_BF16 && x_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "linear: x/w must be bf16 or f16");
+  if (bias && bias_dtype != MMDIT_F32 && bias_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear: bias must be f32 or bf16");
+  if (!valid_dtype(y_dtype)) return fail(MMDIT_ERR_DTYPE, "linear: bad y dtype");
+  if (epilogue < MMDIT_EPI_NONE || epilogue > MMDIT_EPI_GATED_RES) return fail(MMDIT_ERR_SHAPE, "linear: bad epilogue");
+  if (epilogue == MMDIT_EPI_GATED_RES) {
+    if (res_dtype != MMDIT_F32 && res_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear: res must be f32 or bf16");
+    if (y_dtype == MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "linear: gated residual output must be f32 or bf16");
+    if (rows_per_batch < 1 || gate_stride < N) return fail(MMDIT_ERR_SHAPE, "linear: rows_per_batch >= 1 and gate_stride >= N");
+  }
+  if (M == 0 || N == 0) return MMDIT_OK;
+  if (!x || !w || !y) return fail(MMDIT_ERR_NULL, "linear: x, w, y required");
+  if (epilogue == MMDIT_EPI_GATED_RES && (!res || !gate)) return fail(MMDIT_ERR_NULL, "linear: res and gate required");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)) || (res && !aligned16(res)) ||
+      (gate && !aligned16(gate)))
+    return fail(MMDIT_ERR_ALIGN, "linear: pointers must be 16-byte aligned");
+  const size_t ny = (size_t)(M * N) * dtype_size(y_dtype);
+  if (overlaps(y, ny, x, (size_t)(M * K) * dtype_size(x_dtype)) || overlaps(y, ny, w, (size_t)(N * K) * dtype_size(x_dtype)) ||
+      (res && res != y && overlaps(y, ny, res, (size_t)(M * N) * dtype_size(res_dtype))))
+    return fail(MMDIT_ERR_ALIAS, "linear: y overlaps an input");
+  GemmProblem p{};
+  p.x = x; p.w = w; p.bias = bias; p.y = y; p.res = res; p.gate = gate; p.M = M;
+  p.gate_stride = gate_stride; p.rows_per_batch = rows_per_batch > 0 ? rows_per_batch : M;
+  return launch_linear(&p, 1, x_dtype, bias_dtype, y_dtype, N, K, epilogue, res_dtype,
+                       static_cast<hipStream_t>(stream));
+}
+
+int mmdit_modulation(const void* w_mod, const void* b_mod, const void* tvec, int t_dtype, float* mod,
+                     int64_t B, int64_t C6, int64_t Dt, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || C6 < 0 || Dt < 8 || Dt % 8) return fail(MMDIT_ERR_SHAPE, "modulation: Dt must be a positive multiple of 8");
+  if (B * Dt > 16384) return fail(MMDIT_ERR_SHAPE, "modulation: B * Dt must be <= 16384");
+  if (t_dtype != MMDIT_F32 && t_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "modulation: tvec must be f32 or bf16");
+  if (B == 0 || C6 == 0) return MMDIT_OK;
+  if (!w_mod || !tvec || !mod) return fail(MMDIT_ERR_NULL, "modulation: w_mod, tvec, mod required");
+  if (!aligned16(w_mod) || !aligned16(tvec) || !aligned16(mod)) return fail(MMDIT_ERR_ALIGN, "modulation: pointers must be 16-byte aligned");
+  return launch_modulation(w_mod, b_mod, tvec, t_dtype, mod, B, C6, Dt, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
