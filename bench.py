@@ -103,7 +103,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--ffn-dtype", choices=("f16", "bf16"), default="f16")
+    ap.add_argument("--act-dtype", choices=("f16", "bf16"), default="f16",
+                    help="type of the 16-bit intermediates and MFMA operands")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,8 +123,8 @@ def main():
     t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in raw.items()}
     wv = {k: t[f"vis.{k}"] for k in wl.STREAM_WEIGHTS}
     wc = {k: t[f"cond.{k}"] for k in wl.STREAM_WEIGHTS}
-    ffn_dt = torch.float16 if args.ffn_dtype == "f16" else torch.bfloat16
-    dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, cfg.ln_eps, cfg.qk_eps, ffn_dtype=ffn_dt)
+    act_dt = torch.float16 if args.act_dtype == "f16" else torch.bfloat16
+    dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, cfg.ln_eps, cfg.qk_eps, act_dtype=act_dt)
     rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
     ws = torch.empty(mm.block_workspace_bytes(dims, 1, cfg.n_vis, cfg.n_cond), dtype=torch.uint8, device=dev)
     out_v = torch.empty((1, cfg.n_vis, cfg.width), dtype=torch.float32, device=dev)
@@ -173,13 +174,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.act_dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no checkpoint)",
         "config": {"workload": "480p MMDiT block forward: 32760 visual (21x30x52) + 512 conditioning tokens, "
                                "C=3072, 24x128 heads, FFN 12288 GELU, Dt=1536",
                    "global_batch": 1, "seq_len": cfg.n_tokens, "parallelism": "none (1 GPU)",
-                   "ffn_operand_dtype": args.ffn_dtype, "output_dtype": "f32"},
-        "roofline": {"bound": "mfma", "kernel": "joint_attn_bf16_kernel",
+                   "inputs_and_weights": "bf16", "mfma_operands": args.act_dtype,
+                   "accumulate": "f32", "output_dtype": "f32"},
+        "roofline": {"bound": "mfma", "kernel": "joint_attn_mfma_kernel",
                      "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": cfg.attn_flops, "avg_launch_ms": round(attn_ms, 4)},

@@ -81,7 +81,7 @@ typedef struct {
  *         modulation buffer).  gate is required iff branch is given.
  * x_out   [B, N, C] f32 receives x' (may be NULL).
  * y       [B, N, C] y_dtype F32 | BF16 | F16.
- * C must be a multiple of 8 and at most 16384.  N may be 0.  Outputs must not overlap
+ * C must be a multiple of 8 and at most 8192.  N may be 0.  Outputs must not overlap
  * inputs.
  * ------------------------------------------------------------------------------- */
 int mmdit_modulate_ln(const void* x, int x_dtype,
@@ -99,7 +99,7 @@ int mmdit_modulate_ln(const void* x, int x_dtype,
  *
  *   q^ = RoPE(q / sqrt(mean_d(q^2) + eps) * g_q),  likewise k with g_k.
  *
- * q, k       [B, N, H, D] in_dtype F32 | BF16; token row stride in_row_stride (>= H*D).
+ * q, k       [B, N, H, D] in_dtype F32 | BF16 | F16; token row stride in_row_stride (>= H*D).
  * q_scale, k_scale  scale_dtype F32 | BF16: [D] shared by all heads (scale_head_stride 0)
  *            or [H, D] (scale_head_stride = D).
  * q_out, k_out  [B, N, H, D] out_dtype F32 | BF16 | F16, row stride out_row_stride.
@@ -123,9 +123,13 @@ int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_ro
  *
  * (The order of the concatenation does not change any output.)  No mask.
  *
- * q/k/v_vis   [B, n_vis, H, D], q/k/v_cond [B, n_cond, H, D]; in_dtype BF16 (MFMA path)
- *             or F32 (fp32 VALU path); one token row stride in_row_stride for all six.
- *             Q and K are used as given: normalise / rotate them first.
+ * q/k/v_vis   [B, n_vis, H, D], q/k/v_cond [B, n_cond, H, D]; one token row stride
+ *             in_row_stride for all six.  Q and K are used as given: normalise / rotate
+ *             them first.
+ * qk_dtype, v_dtype  F16 or BF16 each (MFMA path), or both F32 (fp32 VALU path).  On the
+ *             MFMA path Q K^T runs on qk_dtype operands; the probabilities P are rounded to
+ *             f16 and P V runs on f16 operands, a bf16 V being converted to f16 on the way
+ *             into LDS (V values must lie within the f16 range).
  * o_vis, o_cond  [B, n_s, H, D] out_dtype F32 | BF16 | F16, row stride out_row_stride.
  * lse         optional f32 [B, H, n_cond + n_vis], cond rows first: the natural-log
  *             sum of exp(scaled logits) of each query row, or NULL.
@@ -133,7 +137,7 @@ int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_ro
  * ------------------------------------------------------------------------------- */
 int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
                           const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
-                          int in_dtype, int64_t in_row_stride,
+                          int qk_dtype, int v_dtype, int64_t in_row_stride,
                           int64_t B, int64_t H, int64_t D, float softmax_scale,
                           void* o_vis, void* o_cond, int out_dtype, int64_t out_row_stride,
                           float* lse, void* stream);
@@ -194,9 +198,12 @@ int mmdit_modulation(const void* w_mod, const void* b_mod, const void* tvec, int
  * x_vis [B, n_vis, C], x_cond [B, n_cond, C] x_dtype BF16 | F32; tvec [B, Dt] t_dtype
  * BF16 | F32; rope describes the visual grid (n_vis = T*H*W); out_vis, out_cond
  * [B, n_s, C] out_dtype F32 | BF16.
- * ffn_dtype selects the operand type of the two FFN GEMMs: MMDIT_BF16 (h2 and the GELU
- * output stored bf16) or MMDIT_F16 (both stored f16; the FFN weights are converted to f16
- * in the workspace on every call).
+ * act_dtype selects the type of every 16-bit intermediate (h, q|k|v, O, h2, GELU output)
+ * and hence of every MFMA operand: MMDIT_BF16 (weights used as given) or MMDIT_F16 (the
+ * four weight matrices of each stream are converted to f16 in the workspace on every call;
+ * f16 keeps 3 more mantissa bits, which the block's range-bounded intermediates can use).
+ * The modulation vectors, LayerNorm statistics, softmax state and the residual stream x1
+ * are f32 in both cases.
  * workspace: >= mmdit_block_workspace_bytes(dims, B, n_vis, n_cond), 256-byte aligned;
  * its contents after the call are the intermediates listed by mmdit_block_workspace_offsets.
  * ------------------------------------------------------------------------------- */
@@ -210,18 +217,20 @@ typedef struct {
   float ln_eps, qk_eps;
   int64_t qk_scale_head_stride;
   int w_dtype;
-  int ffn_dtype;
+  int act_dtype;
 } mmdit_block_dims;
 
-/* Workspace regions (byte offsets from the workspace start), per stream s = 0 (vis), 1 (cond):
- *   MMDIT_WS_MOD    f32  [B, 6C]   modulation vectors
- *   MMDIT_WS_H      16b  [B*n, C]  LN-modulated input of the QKV GEMM; reused for O (bf16)
- *   MMDIT_WS_QKV    bf16 [B*n, 3C] q^ | k^ | v after QK-norm and RoPE; reused for h2
- *   MMDIT_WS_X1     f32  [B*n, C]  residual after the attention branch
- *   MMDIT_WS_G      16b  [B*n, F]  GELU(h2 W_fc1^T + b_fc1)
- * and, for ffn_dtype F16, MMDIT_WS_W1H / MMDIT_WS_W2H, f16 copies of w_fc1 / w_fc2. */
+/* Workspace regions (byte offsets from the workspace start), per stream s = 0 (vis), 1 (cond);
+ * "act" is act_dtype:
+ *   MMDIT_WS_MOD    f32 [B, 6C]   modulation vectors
+ *   MMDIT_WS_H      act [B*n, C]  LN-modulated input of the QKV GEMM; then the attention output O
+ *   MMDIT_WS_QKV    act [B*n, 3C] q^ | k^ | v after QK-norm and RoPE; then h2 (first B*n*C)
+ *   MMDIT_WS_X1     f32 [B*n, C]  residual after the attention branch
+ *   MMDIT_WS_G      act [B*n, F]  GELU(h2 W_fc1^T + b_fc1)
+ *   MMDIT_WS_WQKV, MMDIT_WS_WO, MMDIT_WS_W1, MMDIT_WS_W2: f16 copies of w_qkv, w_o, w_fc1,
+ *                   w_fc2 (act_dtype F16 only). */
 enum { MMDIT_WS_MOD = 0, MMDIT_WS_H = 1, MMDIT_WS_QKV = 2, MMDIT_WS_X1 = 3, MMDIT_WS_G = 4,
-       MMDIT_WS_W1H = 5, MMDIT_WS_W2H = 6, MMDIT_WS_COUNT = 7 };
+       MMDIT_WS_WQKV = 5, MMDIT_WS_WO = 6, MMDIT_WS_W1 = 7, MMDIT_WS_W2 = 8, MMDIT_WS_COUNT = 9 };
 
 size_t mmdit_block_workspace_bytes(const mmdit_block_dims* dims, int64_t B, int64_t n_vis,
                                    int64_t n_cond);

@@ -66,7 +66,7 @@ def test_qk_norm_rope_validation(L):
     assert f(*a) == ERR_NULL
     a = list(args); a[0] = _fake(0x10008)
     assert f(*a) == ERR_ALIGN
-    a = list(args); a[2] = mm.F16
+    a = list(args); a[2] = 5
     assert f(*a) == ERR_DTYPE
     a = list(args); a[8] = _fake(0x10000 + 64 * 2)                  # q_out half-overlapping q
     assert f(*a) == ERR_ALIAS
@@ -77,20 +77,22 @@ def test_qk_norm_rope_validation(L):
 def test_joint_attention_validation(L):
     p, o = _fake(0x10000), _fake(0x900000)
     f = L.mmdit_joint_attention
-    args = [p, p, p, 10, p, p, p, 3, mm.BF16, 256, 1, 2, 128, 0.088, o, _fake(0xA00000), mm.F32, 256, None, None]
-    a = list(args); a[12] = 96
+    args = [p, p, p, 10, p, p, p, 3, mm.BF16, mm.BF16, 256, 1, 2, 128, 0.088, o, _fake(0xA00000), mm.F32, 256, None, None]
+    a = list(args); a[13] = 96
     assert f(*a) == ERR_SHAPE
     a = list(args); a[3] = 0; a[7] = 0
     assert f(*a) == ERR_SHAPE                                       # no tokens at all
-    a = list(args); a[14] = None
+    a = list(args); a[15] = None
     assert f(*a) == ERR_NULL
-    a = list(args); a[8] = mm.F16
+    a = list(args); a[8] = mm.F32
+    assert f(*a) == ERR_DTYPE                                       # f32 Q/K with a 16-bit V
+    a = list(args); a[9] = 7
     assert f(*a) == ERR_DTYPE
-    a = list(args); a[14] = p
+    a = list(args); a[15] = p
     assert f(*a) == ERR_ALIAS                                       # output on top of the inputs
-    a = list(args); a[13] = 0.0
+    a = list(args); a[14] = 0.0
     assert f(*a) == ERR_SHAPE
-    a = list(args); a[9] = 100
+    a = list(args); a[10] = 100
     assert f(*a) == ERR_SHAPE                                       # row stride < H*D
 
 
@@ -112,18 +114,20 @@ def test_linear_modulate_modulation_validation(L):
 
 
 def test_block_workspace_and_validation(L):
-    dims = mm.BlockDims.make(3072, 24, 12288, 1536)
+    import torch
+    dims = mm.BlockDims.make(3072, 24, 12288, 1536, act_dtype=torch.bfloat16)
     n = mm.block_workspace_bytes(dims, 1, 32760, 512)
-    # mod + h + qkv + x1 + g per stream, f32 residual, bf16 FFN: no f16 weight copies
+    # mod + h + qkv + x1 + g per stream, f32 residual, bf16 intermediates: no weight copies
     expect = 0
     for rows in (32760, 512):
         for sz in (6 * 3072 * 4, rows * 3072 * 2, rows * 9216 * 2, rows * 3072 * 4, rows * 12288 * 2):
             expect += (sz + 255) // 256 * 256
     assert n == expect
     offs = mm.block_workspace_offsets(dims, 1, 32760, 512)
-    assert offs[0][mm.WS_MOD] == 0 and offs[0][mm.WS_W1H] == 2 ** 64 - 1
-    d16 = mm.BlockDims.make(3072, 24, 12288, 1536, ffn_dtype=__import__("torch").float16)
-    assert mm.block_workspace_bytes(d16, 1, 32760, 512) == n + 4 * 12288 * 3072 * 2
+    assert offs[0][mm.WS_MOD] == 0 and offs[0][mm.WS_W1] == 2 ** 64 - 1
+    d16 = mm.BlockDims.make(3072, 24, 12288, 1536, act_dtype=torch.float16)
+    per_stream = (3 * 3072 * 3072 + 3072 * 3072 + 2 * 12288 * 3072) * 2
+    assert mm.block_workspace_bytes(d16, 1, 32760, 512) == n + 2 * per_stream
     bad = mm.BlockDims.make(3000, 24, 12288, 1536)
     assert mm.block_workspace_bytes(bad, 1, 100, 5) == 0
     rope = mm.Rope3D.make((21, 30, 52))

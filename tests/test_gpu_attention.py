@@ -14,7 +14,7 @@ import torch
 import oracle
 import video_diffusion_transformer_mmdit_amd as mm
 import workloads as wl
-from tests.util import TOL, assert_close, log, to_dev, to_host64
+from tests.util import TOL, assert_close, assert_close_stored, log, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +26,10 @@ def _inputs(cfg):
 
 
 def _gpu_attention(cfg, dev, out_dtype=torch.float32, qk_dtype=None, return_lse=False):
+    """QK-norm/RoPE then attention.  bf16 workloads keep Q^/K^ in f16 (their range is
+    bounded by the RMSNorm), fp32 workloads in f32."""
+    if qk_dtype is None:
+        qk_dtype = torch.float32 if cfg.dtype == wl.F32 else torch.float16
     rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
     qv, kv = mm.qk_norm_rope(dev["q_vis"], dev["k_vis"], dev["gq_vis"], dev["gk_vis"], rope=rope,
                              eps=cfg.qk_eps, out_dtype=qk_dtype)
@@ -46,7 +50,7 @@ def test_attention_full_parity(cfg):
     qv, kv, qc, kc, o_v, o_c, lse = _gpu_attention(cfg, dev, return_lse=True)
     tol = TOL[cfg.dtype]
     for nm, got in (("qh_vis", qv), ("kh_vis", kv), ("qh_cond", qc), ("kh_cond", kc)):
-        assert_close(nm, to_host64(got), ref[nm], tol)
+        assert_close(nm, to_host64(got), ref[nm], tol if cfg.dtype == wl.F32 else 4e-3)
     assert_close("o_vis", to_host64(o_v), ref["o_vis"], tol)
     assert_close("o_cond", to_host64(o_c), ref["o_cond"], tol)
     # log-sum-exp of every query row, [cond | vis] order, against the oracle's normalised
@@ -85,8 +89,8 @@ def test_attention_sampled_parity_full_size(cfg):
     ref = oracle.attention_block(f64, cfg.grid, cfg.qk_eps, cfg.rope_split, cfg.rope_base,
                                  vis_rows=rv, cond_rows=rc)
     tol = TOL[cfg.dtype]
-    assert_close("kh_vis(all rows)", kv_h, ref["kh_vis"], tol)
-    assert_close("qh_vis(sampled)", qv_s, ref["qh_vis"][:, rv], tol)
+    assert_close("kh_vis(all rows)", kv_h, ref["kh_vis"], 4e-3)
+    assert_close("qh_vis(sampled)", qv_s, ref["qh_vis"][:, rv], 4e-3)
     assert_close("o_vis(sampled)", o_v_s, ref["o_vis"], tol)
     assert_close("o_cond(sampled)", o_c_s, ref["o_cond"], tol)
 
@@ -170,15 +174,15 @@ def test_qk_norm_rope_in_place_matches_out_of_place_and_per_head_scales():
     qkv = torch.stack([dev["q_vis"], dev["k_vis"], dev["v_vis"]], dim=2)   # [1, N, 3, H, D]
     gq = _rand((H, 128), 31, torch.float32) * 0.1 + 1
     gk = _rand((H, 128), 32, torch.float32) * 0.1 + 1
-    qo, ko = mm.qk_norm_rope(qkv[:, :, 0], qkv[:, :, 1], gq, gk, rope=rope)
+    qo, ko = mm.qk_norm_rope(qkv[:, :, 0], qkv[:, :, 1], gq, gk, rope=rope)   # bf16 out
     mm.qk_norm_rope(qkv[:, :, 0], qkv[:, :, 1], gq, gk, rope=rope, q_out=qkv[:, :, 0], k_out=qkv[:, :, 1])
     torch.cuda.synchronize()
     assert torch.equal(qo, qkv[:, :, 0]) and torch.equal(ko, qkv[:, :, 1])
     assert torch.equal(qkv[:, :, 2], dev["v_vis"]), "V must be untouched"
     f64 = lambda k: wl.to_f64(raw[k], cfg.dtype)  # noqa: E731
     rq, rk = oracle.qk_norm_rope(f64("q_vis"), f64("k_vis"), to_host64(gq), to_host64(gk), cfg.qk_eps, cfg.grid)
-    assert_close("q^ per-head scales", to_host64(qo), rq, 2e-2)
-    assert_close("k^ per-head scales", to_host64(ko), rk, 2e-2)
+    assert_close_stored("q^ per-head scales", to_host64(qo), rq, torch.bfloat16, 1e-4)
+    assert_close_stored("k^ per-head scales", to_host64(ko), rk, torch.bfloat16, 1e-4)
 
 
 def test_qk_norm_rope_f32_out_tight():
@@ -204,3 +208,21 @@ def test_invalid_arguments_raise_before_launch():
         mm.qk_norm_rope(q, q.clone(), g, g, rope=mm.Rope3D.make((2, 2, 2), (16, 56, 54)))
     with pytest.raises(mm.MmditError, match="overlap"):
         mm.joint_attention(q, q, q, out_dtype=torch.bfloat16, o_vis=q)
+    with pytest.raises(mm.MmditError, match="f16 / bf16"):
+        mm.joint_attention(q, q, q.float())
+
+
+@pytest.mark.parametrize("qk,v", [(torch.float16, torch.float16), (torch.bfloat16, torch.bfloat16),
+                                  (torch.bfloat16, torch.float16), (torch.float16, torch.bfloat16)])
+def test_attention_operand_dtype_combinations(qk, v):
+    """Every Q/K x V operand type pair on ragged sizes (V in bf16 is converted to f16 on its
+    way into LDS; P V always runs on f16)."""
+    nv, nc, H, D = 190, 33, 2, 128
+    qv, kv = _rand((1, nv, H, D), 41, qk), _rand((1, nv, H, D), 42, qk)
+    qc, kc = _rand((1, nc, H, D), 43, qk), _rand((1, nc, H, D), 44, qk)
+    vv, vc = _rand((1, nv, H, D), 45, v), _rand((1, nc, H, D), 46, v)
+    o_v, o_c = mm.joint_attention(qv, kv, vv, qc, kc, vc)
+    torch.cuda.synchronize()
+    r_v, r_c = _oracle_attn(qv, kv, vv, qc, kc, vc)
+    assert_close("o_vis", to_host64(o_v), r_v, 1e-2)
+    assert_close("o_cond", to_host64(o_c), r_c, 1e-2)

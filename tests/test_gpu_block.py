@@ -12,7 +12,7 @@ import torch
 import oracle
 import video_diffusion_transformer_mmdit_amd as mm
 import workloads as wl
-from tests.util import TOL, assert_close, log, to_dev, to_host64
+from tests.util import TOL, assert_close, assert_close_stored, log, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -28,9 +28,9 @@ def _host_weights(raw, s):
     return {k: wl.to_f64(raw[f"{s}.{k}"], wl.BF16) for k in wl.STREAM_WEIGHTS}
 
 
-def _run_block(cfg, dev, wv, wc, ffn_dtype, out_dtype=torch.float32):
+def _run_block(cfg, dev, wv, wc, act_dtype, out_dtype=torch.float32):
     dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, cfg.ln_eps, cfg.qk_eps,
-                             ffn_dtype=ffn_dtype)
+                             act_dtype=act_dtype)
     rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
     out_v, out_c, ws = mm.block_fwd(dims, wv, wc, dev["x_vis"], dev["x_cond"] if cfg.n_cond else None,
                                     dev["tvec"], rope, out_dtype=out_dtype)
@@ -42,15 +42,15 @@ def _ws_views(dims, cfg, ws, s, n, rows=None):
     """Intermediates of stream s from the workspace: mod [B,6C], qkv-region h2, x1, O."""
     off = mm.block_workspace_offsets(dims, cfg.batch, cfg.n_vis, cfg.n_cond)[s]
     B, C = cfg.batch, cfg.width
-    ffn_t = torch.float16 if dims.ffn_dtype == mm.F16 else torch.bfloat16
+    act_t = torch.float16 if dims.act_dtype == mm.F16 else torch.bfloat16
 
     def view(region, dtype, shape):
         nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
         return ws[off[region]:off[region] + nbytes].view(dtype).view(shape)
 
     out = {"mod": view(mm.WS_MOD, torch.float32, (B, 6 * C)),
-           "o": view(mm.WS_H, torch.bfloat16, (B, n, C)),
-           "h2": view(mm.WS_QKV, ffn_t, (B, n, C)),
+           "o": view(mm.WS_H, act_t, (B, n, C)),
+           "h2": view(mm.WS_QKV, act_t, (B, n, C)),
            "x1": view(mm.WS_X1, torch.float32, (B, n, C))}
     if rows is not None:
         idx = torch.from_numpy(rows).cuda()
@@ -59,26 +59,44 @@ def _ws_views(dims, cfg, ws, s, n, rows=None):
     return {k: to_host64(v) for k, v in out.items()}
 
 
-@pytest.mark.parametrize("cfg,ffn", [(wl.BLOCK_TINY, torch.bfloat16), (wl.BLOCK_TINY, torch.float16),
-                                     (wl.BLOCK_SMALL, torch.float16), (wl.BLOCK_SMALL, torch.bfloat16)],
-                         ids=["tiny-bf16ffn", "tiny-f16ffn", "small-f16ffn", "small-bf16ffn"])
-def test_block_full_parity(cfg, ffn):
-    log(f"block parity {cfg.name} ffn={ffn}")
+def _check_intermediates(s, iv, ref, act):
+    """mod (f32), O and h2 (stored in act), x1 (f32)."""
+    assert_close(f"mod_{s}", iv["mod"], ref[f"mod_{s}"], 1e-5)
+    assert_close_stored(f"o_{s}", iv["o"], ref[f"o_{s}"], act, TOL[wl.BF16])
+    assert_close(f"x1_{s}", iv["x1"], ref[f"x1_{s}"], TOL[wl.BF16])
+    assert_close_stored(f"h2_{s}", iv["h2"], ref[f"h2_{s}"], act, TOL[wl.BF16])
+
+
+@pytest.mark.parametrize("cfg,act", [(wl.BLOCK_TINY, torch.float16), (wl.BLOCK_SMALL, torch.float16)],
+                         ids=["tiny", "small"])
+def test_block_full_parity(cfg, act):
+    log(f"block parity {cfg.name} act={act}")
     raw = wl.block_inputs(cfg)
     dev, wv, wc = _dev_block(cfg, raw)
-    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, ffn)
+    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, act)
     ref = oracle.block_forward(wl.to_f64(raw["x_vis"], wl.BF16), wl.to_f64(raw["x_cond"], wl.BF16),
                                wl.to_f64(raw["tvec"], wl.BF16), _host_weights(raw, "vis"),
                                _host_weights(raw, "cond"), cfg.grid, cfg.heads, cfg.ln_eps, cfg.qk_eps)
     tol = TOL[wl.BF16]
     for s, n in (("vis", cfg.n_vis), ("cond", cfg.n_cond)):
-        iv = _ws_views(dims, cfg, ws, 0 if s == "vis" else 1, n)
-        assert_close(f"mod_{s}", iv["mod"], ref[f"mod_{s}"], 1e-5)
-        assert_close(f"o_{s}", iv["o"], ref[f"o_{s}"], tol)
-        assert_close(f"x1_{s}", iv["x1"], ref[f"x1_{s}"], tol)
-        assert_close(f"h2_{s}", iv["h2"], ref[f"h2_{s}"], tol)
+        _check_intermediates(s, _ws_views(dims, cfg, ws, 0 if s == "vis" else 1, n), ref, act)
     assert_close("out_vis", to_host64(out_v), ref["out_vis"], tol)
     assert_close("out_cond", to_host64(out_c), ref["out_cond"], tol)
+
+
+def test_block_all_bf16_intermediates_runs_and_stays_near_oracle():
+    """act_dtype bf16: every intermediate and MFMA operand bf16 (no weight conversion).
+    Its output error is reported against a looser 5e-2 bar: bf16 storage of h2 and of the
+    GELU output alone is expected to reach about 2e-2 at this crest factor."""
+    cfg = wl.BLOCK_SMALL
+    raw = wl.block_inputs(cfg)
+    dev, wv, wc = _dev_block(cfg, raw)
+    _, out_v, out_c, _ = _run_block(cfg, dev, wv, wc, torch.bfloat16)
+    ref = oracle.block_forward(wl.to_f64(raw["x_vis"], wl.BF16), wl.to_f64(raw["x_cond"], wl.BF16),
+                               wl.to_f64(raw["tvec"], wl.BF16), _host_weights(raw, "vis"),
+                               _host_weights(raw, "cond"), cfg.grid, cfg.heads, cfg.ln_eps, cfg.qk_eps)
+    assert_close("out_vis (bf16 act)", to_host64(out_v), ref["out_vis"], 5e-2)
+    assert_close("out_cond (bf16 act)", to_host64(out_c), ref["out_cond"], 5e-2)
 
 
 def test_block_zero_modulation_is_exact_identity():
@@ -108,14 +126,14 @@ def test_block_without_cond_tokens_and_determinism():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("ffn", [torch.float16], ids=["f16ffn"])
-def test_block_480p_sampled_parity(ffn):
+def test_block_480p_sampled_parity():
     cfg = wl.BLOCK_480P
     log("block 480p: generating inputs")
     raw = wl.block_inputs(cfg)
     dev, wv, wc = _dev_block(cfg, raw)
     log("  GPU block forward")
-    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, ffn)
+    act = torch.float16
+    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, act)
     rv = wl.sample_rows(cfg.n_vis, 128, seed=501)
     rc = wl.sample_rows(cfg.n_cond, 32, seed=502)
     got = {"out_vis": to_host64(out_v[:, torch.from_numpy(rv).cuda()]),
@@ -131,9 +149,6 @@ def test_block_480p_sampled_parity(ffn):
                                vis_rows=rv, cond_rows=rc)
     tol = TOL[wl.BF16]
     for s, i in (("vis", iv), ("cond", ic)):
-        assert_close(f"mod_{s}", i["mod"], ref[f"mod_{s}"], 1e-5)
-        assert_close(f"o_{s}", i["o"], ref[f"o_{s}"], tol)
-        assert_close(f"x1_{s}", i["x1"], ref[f"x1_{s}"], tol)
-        assert_close(f"h2_{s}", i["h2"], ref[f"h2_{s}"], tol)
+        _check_intermediates(s, i, ref, act)
     assert_close("out_vis", got["out_vis"], ref["out_vis"], tol)
     assert_close("out_cond", got["out_cond"], ref["out_cond"], tol)

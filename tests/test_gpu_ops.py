@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import video_diffusion_transformer_mmdit_amd as mm
-from tests.util import assert_close, log, to_host64
+from tests.util import assert_close, assert_close_stored, log, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -49,8 +49,10 @@ def test_modulate_ln(xdt, ydt, branch, C, N):
         x64 = x64 + to_host64(gate)[:, None, :] * to_host64(br)
         assert_close("x_out", to_host64(xo), x64, 1e-6)
     ref = oracle.modulate(oracle.layer_norm(x64, 1e-6), to_host64(shift), to_host64(scale))
-    tol = {torch.float32: 1e-5, torch.float16: 4e-3, torch.bfloat16: 2e-2}[ydt]
-    assert_close("y", to_host64(y), ref, tol)
+    if ydt == torch.float32:
+        assert_close("y", to_host64(y), ref, 1e-5)
+    else:
+        assert_close_stored("y", to_host64(y), ref, ydt, 1e-4)
 
 
 @pytest.mark.parametrize("M,N,K,dt,epi,ydt", [
@@ -70,8 +72,10 @@ def test_linear(M, N, K, dt, epi, ydt):
     ref = oracle.linear(to_host64(x), to_host64(w), to_host64(b))
     if epi == mm.EPI_GELU:
         ref = oracle.gelu(ref)
-    tol = {torch.float32: 1e-5, torch.float16: 4e-3, torch.bfloat16: 2e-2}[ydt]
-    assert_close("y", to_host64(y), ref, tol)
+    if ydt == torch.float32:
+        assert_close("y", to_host64(y), ref, 1e-4)
+    else:
+        assert_close_stored("y", to_host64(y), ref, ydt, 1e-4)
 
 
 @pytest.mark.parametrize("resdt,ydt", [(torch.bfloat16, torch.float32), (torch.float32, torch.float32),
@@ -88,16 +92,18 @@ def test_linear_gated_residual(resdt, ydt):
     torch.cuda.synchronize()
     a = oracle.linear(to_host64(x), to_host64(w), to_host64(b)).reshape(B, n, C)
     ref = to_host64(res).reshape(B, n, C) + to_host64(gate)[:, None, :] * a
-    tol = {torch.float32: 1e-5, torch.bfloat16: 2e-2}[ydt]
-    assert_close("y", to_host64(y).reshape(B, n, C), ref, tol)
+    if ydt == torch.float32:
+        assert_close("y", to_host64(y).reshape(B, n, C), ref, 1e-4)
+    else:
+        assert_close_stored("y", to_host64(y).reshape(B, n, C), ref, ydt, 1e-4)
 
 
 def test_linear_full_width_shapes():
     """The block's GEMM shapes at full width on a few hundred rows (ragged M)."""
     for N, K in ((9216, 3072), (3072, 3072), (12288, 3072), (3072, 12288)):
         log(f"  N={N} K={K}")
-        x = _rand((333, K), N, 1.0)
-        w = _rand((N, K), K, 0.02)
+        x = _rand((333, K), 1000 + N, 1.0)
+        w = _rand((N, K), 2000 + K, 0.02)
         y = mm.linear(x, w, None, y_dtype=torch.float32)
         torch.cuda.synchronize()
-        assert_close(f"y[{N}x{K}]", to_host64(y), to_host64(x) @ to_host64(w).T, 1e-5)
+        assert_close(f"y[{N}x{K}]", to_host64(y), to_host64(x) @ to_host64(w).T, 1e-4)

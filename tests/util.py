@@ -10,6 +10,7 @@ import torch
 import workloads as wl
 
 TOL = {wl.F32: 1e-4, wl.BF16: 2e-2}
+SIG_BITS = {torch.bfloat16: 8, torch.float16: 11, torch.float32: 24}
 
 
 def log(*a):
@@ -40,4 +41,30 @@ def assert_close(name, got, ref, tol):
     log(f"  {name}: max|err|/rms = {e:.3e} (tol {tol:.0e})")
     assert np.all(np.isfinite(np.asarray(got))), f"{name}: non-finite values"
     assert e <= tol, f"{name}: max|err|/rms {e:.3e} > {tol:.0e}"
+    return e
+
+
+def half_ulp(ref: np.ndarray, dtype) -> np.ndarray:
+    """Half the spacing of `dtype` around |ref| (round-to-nearest bound of storing ref)."""
+    p = SIG_BITS[dtype]
+    e = np.frexp(np.abs(ref))[1]
+    h = np.ldexp(0.5, e - p)
+    if dtype == torch.float16:
+        h = np.maximum(h, 2.0 ** -25)
+    return h
+
+
+def assert_close_stored(name, got, ref, dtype, tol):
+    """Parity of a result that is stored in `dtype`: the error beyond the unavoidable
+    rounding to `dtype` (half an ulp at |ref|), relative to rms(ref), must be <= tol.  The
+    plain max|err|/rms is logged beside it."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    excess = np.maximum(np.abs(got - ref) - half_ulp(ref, dtype), 0.0)
+    e = float(excess.max()) / rms
+    log(f"  {name} [{str(dtype).replace('torch.', '')}]: error beyond storage rounding / rms = {e:.3e} "
+        f"(tol {tol:.0e}); plain max|err|/rms = {rel_err(got, ref):.3e}")
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: {e:.3e} > {tol:.0e}"
     return e

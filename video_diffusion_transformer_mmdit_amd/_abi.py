@@ -16,8 +16,8 @@ import torch
 
 F32, BF16, F16 = 0, 1, 2
 EPI_NONE, EPI_GELU, EPI_GATED_RES = 0, 1, 2
-WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_W1H, WS_W2H = range(7)
-WS_COUNT = 7
+WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_WQKV, WS_WO, WS_W1, WS_W2 = range(9)
+WS_COUNT = 9
 STAGES = ("mod_ln1", "qkv", "qk_norm_rope", "attention", "out_proj", "ln2", "ffn_up", "ffn_down")
 STAGE_COUNT = len(STAGES)
 
@@ -48,13 +48,13 @@ class StreamWeights(ctypes.Structure):
 class BlockDims(ctypes.Structure):
     _fields_ = [("C", c_int64), ("H", c_int64), ("D", c_int64), ("F", c_int64), ("Dt", c_int64),
                 ("ln_eps", c_float), ("qk_eps", c_float), ("qk_scale_head_stride", c_int64),
-                ("w_dtype", c_int), ("ffn_dtype", c_int)]
+                ("w_dtype", c_int), ("act_dtype", c_int)]
 
     @classmethod
     def make(cls, C, H, F, Dt, ln_eps=1e-6, qk_eps=1e-6, qk_scale_head_stride=0,
-             ffn_dtype=torch.bfloat16):
+             act_dtype=torch.float16):
         return cls(C, H, C // H, F, Dt, ln_eps, qk_eps, qk_scale_head_stride, BF16,
-                   _TORCH_DT[ffn_dtype])
+                   _TORCH_DT[act_dtype])
 
 
 def library_path() -> str:
@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         "mmdit_modulate_ln": [vp, i, vp, i, vp, vp, vp, vp, i64, vp, i, i64, i64, i64, f, vp],
         "mmdit_qk_norm_rope": [vp, vp, i, i64, vp, vp, i, i64, vp, vp, i, i64, i64, i64, i64, i64, f,
                                ctypes.POINTER(Rope3D), vp],
-        "mmdit_joint_attention": [vp, vp, vp, i64, vp, vp, vp, i64, i, i64, i64, i64, i64, f, vp, vp, i,
+        "mmdit_joint_attention": [vp, vp, vp, i64, vp, vp, vp, i64, i, i, i64, i64, i64, i64, f, vp, vp, i,
                                   i64, vp, vp],
         "mmdit_linear": [vp, vp, i, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
         "mmdit_modulation": [vp, vp, vp, i, vp, i64, i64, i64, vp],
@@ -227,7 +227,8 @@ def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, 
         if t is None:
             continue
         b, n, r = _rows(t, nm)
-        if t.dtype != q_vis.dtype or t.shape[0] != B or t.shape[2:] != q_vis.shape[2:]:
+        ref_dt = v_vis.dtype if nm.startswith("v") else q_vis.dtype
+        if t.dtype != ref_dt or t.shape[0] != B or t.shape[2:] != q_vis.shape[2:]:
             raise MmditError(f"{nm}: dtype / shape mismatch")
         if n > 0 and r != rs and not (n == 1 or rs == 0):
             raise MmditError(f"{nm}: all inputs must share one row stride")
@@ -242,7 +243,7 @@ def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, 
     lse = torch.empty((B, H, n_vis + n_cond), dtype=torch.float32, device=dev) if return_lse else None
     st = lib().mmdit_joint_attention(q_vis.data_ptr(), k_vis.data_ptr(), v_vis.data_ptr(), n_vis,
                                      _ptr(q_cond) if n_cond else None, _ptr(k_cond) if n_cond else None,
-                                     _ptr(v_cond) if n_cond else None, n_cond, _dt(q_vis), rs, B, H, D,
+                                     _ptr(v_cond) if n_cond else None, n_cond, _dt(q_vis), _dt(v_vis), rs, B, H, D,
                                      softmax_scale, o_vis.data_ptr(), _ptr(o_cond) if n_cond else None,
                                      _dt(o_vis), ors, _ptr(lse), _stream(q_vis))
     _check(st, "mmdit_joint_attention")

@@ -111,7 +111,7 @@ int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_ro
   if (scale_head_stride != 0 && scale_head_stride != D)
     return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: scale_head_stride must be 0 or D");
   if (!(eps >= 0.f)) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: eps must be >= 0");
-  if (in_dtype != MMDIT_F32 && in_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: in dtype must be f32 or bf16");
+  if (!valid_dtype(in_dtype)) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: bad in dtype");
   if (scale_dtype != MMDIT_F32 && scale_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: scale dtype must be f32 or bf16");
   if (!valid_dtype(out_dtype)) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: bad out dtype");
   if (in_dtype == MMDIT_F32 && out_dtype == MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: f32 -> f16 not supported");
@@ -152,7 +152,7 @@ int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_ro
 
 int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
                           const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
-                          int in_dtype, int64_t in_row_stride, int64_t B, int64_t H, int64_t D,
+                          int qk_dtype, int v_dtype, int64_t in_row_stride, int64_t B, int64_t H, int64_t D,
                           float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
                           int64_t out_row_stride, float* lse, void* stream) {
   g_last_error.clear();
@@ -161,7 +161,8 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
     return fail(MMDIT_ERR_SHAPE, "joint_attention: need B >= 0, H >= 1, n_vis + n_cond >= 1");
   if (in_row_stride < H * D || out_row_stride < H * D) return fail(MMDIT_ERR_SHAPE, "joint_attention: row stride < H*D");
   if (!(softmax_scale > 0.f)) return fail(MMDIT_ERR_SHAPE, "joint_attention: softmax_scale must be > 0");
-  if (in_dtype != MMDIT_BF16 && in_dtype != MMDIT_F32) return fail(MMDIT_ERR_DTYPE, "joint_attention: in dtype must be bf16 or f32");
+  if (!valid_dtype(qk_dtype) || !valid_dtype(v_dtype) || ((qk_dtype == MMDIT_F32) != (v_dtype == MMDIT_F32)))
+    return fail(MMDIT_ERR_DTYPE, "joint_attention: Q/K and V must be 16-bit (f16 / bf16) or all f32");
   if (!valid_dtype(out_dtype)) return fail(MMDIT_ERR_DTYPE, "joint_attention: bad out dtype");
   if (B == 0) return MMDIT_OK;
   if (n_vis > 0 && (!q_vis || !k_vis || !v_vis || !o_vis)) return fail(MMDIT_ERR_NULL, "joint_attention: visual pointers required");
@@ -180,7 +181,7 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
     if (nout[o] == 0) continue;
     const size_t no = span(B * nout[o], hd, out_row_stride, out_dtype);
     for (int i = 0; i < 6; ++i)
-      if (nin[i] > 0 && overlaps(outs[o], no, ins[i], span(B * nin[i], hd, in_row_stride, in_dtype)))
+      if (nin[i] > 0 && overlaps(outs[o], no, ins[i], span(B * nin[i], hd, in_row_stride, i % 3 == 2 ? v_dtype : qk_dtype)))
         return fail(MMDIT_ERR_ALIAS, "joint_attention: outputs overlap inputs");
     if (lse && overlaps(outs[o], no, lse, (size_t)(B * H * (n_vis + n_cond)) * 4))
       return fail(MMDIT_ERR_ALIAS, "joint_attention: lse overlaps an output");
@@ -188,7 +189,7 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
   if (n_vis > 0 && n_cond > 0 &&
       overlaps(o_vis, span(B * n_vis, hd, out_row_stride, out_dtype), o_cond, span(B * n_cond, hd, out_row_stride, out_dtype)))
     return fail(MMDIT_ERR_ALIAS, "joint_attention: o_vis and o_cond overlap");
-  return launch_joint_attention(q_vis, k_vis, v_vis, n_vis, q_cond, k_cond, v_cond, n_cond, in_dtype,
+  return launch_joint_attention(q_vis, k_vis, v_vis, n_vis, q_cond, k_cond, v_cond, n_cond, qk_dtype, v_dtype,
                                 in_row_stride, B, H, softmax_scale, o_vis, o_cond, out_dtype,
                                 out_row_stride, lse, static_cast<hipStream_t>(stream));
 }

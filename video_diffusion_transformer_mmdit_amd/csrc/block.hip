@@ -28,7 +28,7 @@ static int validate_dims(const mmdit_block_dims* d, int64_t B, int64_t n_vis, in
     return fail(MMDIT_ERR_SHAPE, "block: qk_scale_head_stride must be 0 or D");
   if (!(d->ln_eps >= 0.f) || !(d->qk_eps >= 0.f)) return fail(MMDIT_ERR_SHAPE, "block: eps must be >= 0");
   if (d->w_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "block: weights must be bf16");
-  if (d->ffn_dtype != MMDIT_BF16 && d->ffn_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "block: ffn_dtype must be bf16 or f16");
+  if (d->act_dtype != MMDIT_BF16 && d->act_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "block: act_dtype must be bf16 or f16");
   return MMDIT_OK;
 }
 
@@ -38,11 +38,12 @@ static void layout(const mmdit_block_dims* d, int64_t B, int64_t n_vis, int64_t 
   const int64_t ns[2] = {n_vis, n_cond};
   for (int s = 0; s < 2; ++s) {
     const size_t n = (size_t)(B * ns[s]);
+    const bool cvt = d->act_dtype != d->w_dtype;   // bf16 weights, f16 operands
     const size_t sz[MMDIT_WS_COUNT] = {(size_t)B * 6 * C * 4, n * C * 2, n * 3 * C * 2, n * C * 4, n * F * 2,
-                                       d->ffn_dtype == MMDIT_F16 ? F * C * 2 : 0,
-                                       d->ffn_dtype == MMDIT_F16 ? C * F * 2 : 0};
+                                       cvt ? 3 * C * C * 2 : 0, cvt ? C * C * 2 : 0,
+                                       cvt ? F * C * 2 : 0, cvt ? C * F * 2 : 0};
     for (int r = 0; r < MMDIT_WS_COUNT; ++r) {
-      if (sz[r] == 0 && r >= MMDIT_WS_W1H) { L->off[s][r] = SIZE_MAX; continue; }
+      if (sz[r] == 0 && r >= MMDIT_WS_WQKV) { L->off[s][r] = SIZE_MAX; continue; }
       L->off[s][r] = cur;
       cur = align256(cur + sz[r]);
     }
@@ -123,32 +124,37 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
   float* mod[2];
   void *hbuf[2], *qkv[2], *g[2];
   float* x1[2];
-  const void *w1[2], *w2[2];
+  const void *wqkv[2], *wo[2], *w1[2], *w2[2];
   for (int s = 0; s < 2; ++s) {
     mod[s] = reinterpret_cast<float*>(wsb + L.off[s][MMDIT_WS_MOD]);
     hbuf[s] = wsb + L.off[s][MMDIT_WS_H];
     qkv[s] = wsb + L.off[s][MMDIT_WS_QKV];
     x1[s] = reinterpret_cast<float*>(wsb + L.off[s][MMDIT_WS_X1]);
     g[s] = wsb + L.off[s][MMDIT_WS_G];
+    wqkv[s] = ws[s]->w_qkv;
+    wo[s] = ws[s]->w_o;
     w1[s] = ws[s]->w_fc1;
     w2[s] = ws[s]->w_fc2;
   }
   const int nstreams = n_cond > 0 ? 2 : 1;
-  const int fdt = d.ffn_dtype;
+  const int act = d.act_dtype;
 
   // S1 modulation vectors; S2 LN-modulate for the attention branch
   if ((st = mark(MMDIT_STAGE_MOD_LN1, 0))) return st;
   for (int s = 0; s < nstreams; ++s) {
     if ((st = launch_modulation(ws[s]->w_mod, ws[s]->b_mod, tvec, t_dtype, mod[s], B, 6 * C, d.Dt, sm))) return st;
     if ((st = launch_modulate_ln(xs[s], x_dtype, nullptr, MMDIT_BF16, nullptr, nullptr, mod[s] + 0, mod[s] + C,
-                                 6 * C, hbuf[s], MMDIT_BF16, B, ns[s], C, d.ln_eps, sm))) return st;
-    if (fdt == MMDIT_F16) {
-      void* w1h = wsb + L.off[s][MMDIT_WS_W1H];
-      void* w2h = wsb + L.off[s][MMDIT_WS_W2H];
-      if ((st = launch_convert_bf16_to_f16(ws[s]->w_fc1, w1h, F * C, sm))) return st;
-      if ((st = launch_convert_bf16_to_f16(ws[s]->w_fc2, w2h, C * F, sm))) return st;
-      w1[s] = w1h;
-      w2[s] = w2h;
+                                 6 * C, hbuf[s], act, B, ns[s], C, d.ln_eps, sm))) return st;
+    if (act != d.w_dtype) {
+      const void* src[4] = {ws[s]->w_qkv, ws[s]->w_o, ws[s]->w_fc1, ws[s]->w_fc2};
+      const void** dst[4] = {&wqkv[s], &wo[s], &w1[s], &w2[s]};
+      const int region[4] = {MMDIT_WS_WQKV, MMDIT_WS_WO, MMDIT_WS_W1, MMDIT_WS_W2};
+      const int64_t count[4] = {3 * C * C, C * C, F * C, C * F};
+      for (int i = 0; i < 4; ++i) {
+        void* copy = wsb + L.off[s][region[i]];
+        if ((st = launch_convert_bf16_to_f16(src[i], copy, count[i], sm))) return st;
+        *dst[i] = copy;
+      }
     }
   }
   if ((st = mark(MMDIT_STAGE_MOD_LN1, 1))) return st;
@@ -157,16 +163,16 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
     for (int s = 0; s < nstreams; ++s) { p[s] = GemmProblem{}; p[s].M = B * ns[s]; p[s].rows_per_batch = ns[s]; fill(s, p[s]); }
   };
   // S3 QKV projection
-  problems([&](int s, GemmProblem& q) { q.x = hbuf[s]; q.w = ws[s]->w_qkv; q.bias = ws[s]->b_qkv; q.y = qkv[s]; });
+  problems([&](int s, GemmProblem& q) { q.x = hbuf[s]; q.w = wqkv[s]; q.bias = ws[s]->b_qkv; q.y = qkv[s]; });
   if ((st = mark(MMDIT_STAGE_QKV, 0))) return st;
-  if ((st = launch_linear(p, nstreams, MMDIT_BF16, MMDIT_BF16, MMDIT_BF16, 3 * C, C, MMDIT_EPI_NONE, MMDIT_F32, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, act, 3 * C, C, MMDIT_EPI_NONE, MMDIT_F32, sm))) return st;
   if ((st = mark(MMDIT_STAGE_QKV, 1))) return st;
   // S4 QK RMSNorm (+ RoPE on the visual stream), in place in the packed qkv rows
   if ((st = mark(MMDIT_STAGE_QK_NORM_ROPE, 0))) return st;
   for (int s = 0; s < nstreams; ++s) {
     uint16_t* base = static_cast<uint16_t*>(qkv[s]);
-    if ((st = launch_qk_norm_rope(base, base + C, MMDIT_BF16, 3 * C, ws[s]->q_norm, ws[s]->k_norm, MMDIT_BF16,
-                                  d.qk_scale_head_stride, base, base + C, MMDIT_BF16, 3 * C, B, ns[s], H, d.qk_eps,
+    if ((st = launch_qk_norm_rope(base, base + C, act, 3 * C, ws[s]->q_norm, ws[s]->k_norm, MMDIT_BF16,
+                                  d.qk_scale_head_stride, base, base + C, act, 3 * C, B, ns[s], H, d.qk_eps,
                                   s == 0 ? rope : nullptr, sm))) return st;
   }
   if ((st = mark(MMDIT_STAGE_QK_NORM_ROPE, 1))) return st;
@@ -176,28 +182,28 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
     const uint16_t* qv = static_cast<const uint16_t*>(qkv[0]);
     const uint16_t* qc = n_cond > 0 ? static_cast<const uint16_t*>(qkv[1]) : nullptr;
     if ((st = launch_joint_attention(qv, qv + C, qv + 2 * C, n_vis, qc, qc ? qc + C : nullptr, qc ? qc + 2 * C : nullptr,
-                                     n_cond, MMDIT_BF16, 3 * C, B, H, 1.0f / sqrtf((float)d.D), hbuf[0],
-                                     n_cond > 0 ? hbuf[1] : nullptr, MMDIT_BF16, C, nullptr, sm))) return st;
+                                     n_cond, act, act, 3 * C, B, H, 1.0f / sqrtf((float)d.D), hbuf[0],
+                                     n_cond > 0 ? hbuf[1] : nullptr, act, C, nullptr, sm))) return st;
   }
   if ((st = mark(MMDIT_STAGE_ATTENTION, 1))) return st;
   // S6 output projection with the attention gate: x1 = x + gate_a (O W_o^T + b_o), f32
   problems([&](int s, GemmProblem& q) {
-    q.x = hbuf[s]; q.w = ws[s]->w_o; q.bias = ws[s]->b_o; q.y = x1[s]; q.res = xs[s];
+    q.x = hbuf[s]; q.w = wo[s]; q.bias = ws[s]->b_o; q.y = x1[s]; q.res = xs[s];
     q.gate = mod[s] + 2 * C; q.gate_stride = 6 * C;
   });
   if ((st = mark(MMDIT_STAGE_OUT_PROJ, 0))) return st;
-  if ((st = launch_linear(p, nstreams, MMDIT_BF16, MMDIT_BF16, MMDIT_F32, C, C, MMDIT_EPI_GATED_RES, x_dtype, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, MMDIT_F32, C, C, MMDIT_EPI_GATED_RES, x_dtype, sm))) return st;
   if ((st = mark(MMDIT_STAGE_OUT_PROJ, 1))) return st;
   if ((st = mark(MMDIT_STAGE_LN2, 0))) return st;
   // S7 LN-modulate for the FFN branch -> h2 in the qkv region
   for (int s = 0; s < nstreams; ++s)
     if ((st = launch_modulate_ln(x1[s], MMDIT_F32, nullptr, MMDIT_F32, nullptr, nullptr, mod[s] + 3 * C, mod[s] + 4 * C,
-                                 6 * C, qkv[s], fdt, B, ns[s], C, d.ln_eps, sm))) return st;
+                                 6 * C, qkv[s], act, B, ns[s], C, d.ln_eps, sm))) return st;
   if ((st = mark(MMDIT_STAGE_LN2, 1))) return st;
   // S8 FFN up + GELU
   problems([&](int s, GemmProblem& q) { q.x = qkv[s]; q.w = w1[s]; q.bias = ws[s]->b_fc1; q.y = g[s]; });
   if ((st = mark(MMDIT_STAGE_FFN_UP, 0))) return st;
-  if ((st = launch_linear(p, nstreams, fdt, MMDIT_BF16, fdt, F, C, MMDIT_EPI_GELU, MMDIT_F32, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, act, F, C, MMDIT_EPI_GELU, MMDIT_F32, sm))) return st;
   if ((st = mark(MMDIT_STAGE_FFN_UP, 1))) return st;
   // S9 FFN down with the FFN gate: out = x1 + gate_f (g W_2^T + b_2)
   problems([&](int s, GemmProblem& q) {
@@ -205,7 +211,7 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
     q.gate = mod[s] + 5 * C; q.gate_stride = 6 * C;
   });
   if ((st = mark(MMDIT_STAGE_FFN_DOWN, 0))) return st;
-  if ((st = launch_linear(p, nstreams, fdt, MMDIT_BF16, out_dtype, C, F, MMDIT_EPI_GATED_RES, MMDIT_F32, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, out_dtype, C, F, MMDIT_EPI_GATED_RES, MMDIT_F32, sm))) return st;
   if ((st = mark(MMDIT_STAGE_FFN_DOWN, 1))) return st;
   return MMDIT_OK;
 }

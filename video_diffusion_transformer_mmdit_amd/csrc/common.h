@@ -122,7 +122,7 @@ int launch_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_s
                         const mmdit_rope3d* rope, hipStream_t stream);
 int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
                            const void* q_cond, const void* k_cond, const void* v_cond,
-                           int64_t n_cond, int in_dtype, int64_t in_stride, int64_t B, int64_t H,
+                           int64_t n_cond, int qk_dtype, int v_dtype, int64_t in_stride, int64_t B, int64_t H,
                            float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
                            int64_t out_stride, float* lse, hipStream_t stream);
 

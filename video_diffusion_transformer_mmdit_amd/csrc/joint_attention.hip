@@ -6,20 +6,23 @@
 // term of the block.  The concatenation is never materialised: key / query index j < n_cond
 // reads the conditioning tensors, j >= n_cond the visual ones.
 //
-// bf16 MFMA flash kernel (gfx950):
+// 16-bit MFMA flash kernel (gfx950):
 //   - workgroup = 4 wave64s = 128 queries of one (batch, head); each wave owns 32 queries.
-//   - The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims
+//   - The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16} (A = 32 keys x 16 dims
 //     from LDS, B = the wave's Q held in registers for the whole kernel).  In the S^T
 //     accumulator layout every lane holds one query (lane % 32) and 16 keys, so the online
 //     softmax statistics are per-lane scalars and only the row max needs one exchange
 //     between the two half-waves per tile; the row sum is combined once at the end.
-//   - P^T comes straight from those accumulators (converted to bf16) as the B operand of
+//   - P^T comes straight from those accumulators (converted to f16) as the B operand of
 //     O^T = V^T P^T; O^T accumulates 128 dims x 32 queries per wave in registers.
 //   - K and V tiles of 64 keys are staged in LDS (2 stages x 32 KiB).  K rows are stored
 //     as is with an XOR swizzle; V is transposed on the way in (register 4x2 byte shuffles,
 //     8-byte LDS stores) so each lane reads its 8 keys of one dim as a single 16-byte LDS
 //     read, with keys permuted inside each 16-key group to match the accumulator layout.
 //   - exp2 with log2(e) * softmax_scale folded into one FMA per score.
+//   - Precision: S = Q K^T runs on the operand type of Q and K (f16 or bf16); P is rounded
+//     to f16 (P lies in [0, 1], where f16 keeps 3 more mantissa bits than bf16) and PV runs
+//     on f16 MFMA, so a bf16 V is converted to f16 while it is staged into LDS.
 //
 // fp32 path: a plain wave-per-query VALU kernel with the same online softmax, used for the
 // fp32 workload (small sizes).
@@ -55,9 +58,19 @@ __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* const* base, 
                     : base[1] + (b * n_vis + (j - n_cond)) * stride + h * ATT_D;
 }
 
-__device__ __forceinline__ f32x16 mfma_bf16(const uint4& a, const uint4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+template <int DT>
+__device__ __forceinline__ f32x16 mfma16(const uint4& a, const uint4& b, const f32x16& c) {
+  if constexpr (DT == MMDIT_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two bf16 in one word -> the same two values as f16 in one word.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(lo_bf16(w), hi_bf16(w));
 }
 
 // Physical 8-byte slot (0..15) of the V^T row for key quad `qd` (keys 4qd .. 4qd+3) of a
@@ -71,8 +84,8 @@ __device__ __forceinline__ int vt_slot8(int qd, int d) {
   return logical ^ (((d >> 1) & 7) << 1);
 }
 
-template <int OUT_DT, bool LSE>
-__global__ __launch_bounds__(ATT_THREADS) void joint_attn_bf16_kernel(AttnArgs a) {
+template <int QK_DT, int V_DT, int OUT_DT, bool LSE>
+__global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ATT_STAGE];
 
   const int tid = threadIdx.x;
@@ -124,10 +137,17 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_bf16_kernel(AttnArgs a
       *reinterpret_cast<uint4*>(sk + key * 256 + ((cc ^ (key & 15)) << 4)) = rk[i];
     }
     // transpose 4 keys x 8 dims: word for dim 2m+e holds the 4 keys' values of that dim
-    const uint32_t w0[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
-    const uint32_t w1[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
-    const uint32_t w2[4] = {rv[2].x, rv[2].y, rv[2].z, rv[2].w};
-    const uint32_t w3[4] = {rv[3].x, rv[3].y, rv[3].z, rv[3].w};
+    uint32_t w0[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
+    uint32_t w1[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
+    uint32_t w2[4] = {rv[2].x, rv[2].y, rv[2].z, rv[2].w};
+    uint32_t w3[4] = {rv[3].x, rv[3].y, rv[3].z, rv[3].w};
+    if constexpr (V_DT == MMDIT_BF16) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        w0[m] = bf16x2_to_f16x2(w0[m]); w1[m] = bf16x2_to_f16x2(w1[m]);
+        w2[m] = bf16x2_to_f16x2(w2[m]); w3[m] = bf16x2_to_f16x2(w3[m]);
+      }
+    }
     uint2 col[8];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -176,7 +196,7 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_bf16_kernel(AttnArgs a
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const uint4 kf = *reinterpret_cast<const uint4*>(sk + key * 256 + (((2 * ks + g) ^ (key & 15)) << 4));
-        s[st] = mfma_bf16(kf, qf[ks], s[st]);
+        s[st] = mfma16<QK_DT>(kf, qf[ks], s[st]);
       }
     }
     // mask keys past the end (last tile only)
@@ -210,10 +230,10 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_bf16_kernel(AttnArgs a
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        pf[st * 2 + hh] = make_uint4(pack_bf16x2(p[8 * hh + 0], p[8 * hh + 1]),
-                                     pack_bf16x2(p[8 * hh + 2], p[8 * hh + 3]),
-                                     pack_bf16x2(p[8 * hh + 4], p[8 * hh + 5]),
-                                     pack_bf16x2(p[8 * hh + 6], p[8 * hh + 7]));
+        pf[st * 2 + hh] = make_uint4(pack_f16x2(p[8 * hh + 0], p[8 * hh + 1]),
+                                     pack_f16x2(p[8 * hh + 2], p[8 * hh + 3]),
+                                     pack_f16x2(p[8 * hh + 4], p[8 * hh + 5]),
+                                     pack_f16x2(p[8 * hh + 6], p[8 * hh + 7]));
     }
     l_run = l_run * alpha + psum;
 #pragma unroll
@@ -228,7 +248,7 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_bf16_kernel(AttnArgs a
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 vf = *reinterpret_cast<const uint4*>(sv + d * 128 + (((2 * ks + g) ^ ((d >> 1) & 7)) << 4));
-        o[dt] = mfma_bf16(vf, pf[ks], o[dt]);
+        o[dt] = mfma16<MMDIT_F16>(vf, pf[ks], o[dt]);
       }
     }
     if (jt + 1 < ntiles) sstore(buf ^ 1);
@@ -337,15 +357,26 @@ __global__ __launch_bounds__(64) void joint_attn_f32_kernel(AttnArgsF32 a) {
   }
 }
 
+template <int QK, int V>
+static int attn_go(const AttnArgs& a, dim3 grid, int out_dtype, bool has_lse, hipStream_t stream) {
+#define ATT_GO(O, L) joint_attn_mfma_kernel<QK, V, O, L><<<grid, ATT_THREADS, 0, stream>>>(a)
+  if (out_dtype == MMDIT_F32) { if (has_lse) ATT_GO(MMDIT_F32, true); else ATT_GO(MMDIT_F32, false); }
+  else if (out_dtype == MMDIT_BF16) { if (has_lse) ATT_GO(MMDIT_BF16, true); else ATT_GO(MMDIT_BF16, false); }
+  else if (out_dtype == MMDIT_F16) { if (has_lse) ATT_GO(MMDIT_F16, true); else ATT_GO(MMDIT_F16, false); }
+  else return fail(MMDIT_ERR_DTYPE, "joint_attention: bad out dtype");
+#undef ATT_GO
+  return check_launch("joint_attention");
+}
+
 int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
                            const void* q_cond, const void* k_cond, const void* v_cond,
-                           int64_t n_cond, int in_dtype, int64_t in_stride, int64_t B, int64_t H,
+                           int64_t n_cond, int qk_dtype, int v_dtype, int64_t in_stride, int64_t B, int64_t H,
                            float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
                            int64_t out_stride, float* lse, hipStream_t stream) {
   const int64_t N = n_vis + n_cond;
   if (B == 0 || H == 0 || N == 0) return MMDIT_OK;
   const bool has_lse = lse != nullptr;
-  if (in_dtype == MMDIT_BF16) {
+  if (qk_dtype != MMDIT_F32) {
     AttnArgs a{};
     a.q[0] = static_cast<const uint16_t*>(q_cond); a.q[1] = static_cast<const uint16_t*>(q_vis);
     a.k[0] = static_cast<const uint16_t*>(k_cond); a.k[1] = static_cast<const uint16_t*>(k_vis);
@@ -360,15 +391,13 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
     const int64_t blocks = (int64_t)a.nqt * H * B;
     if (blocks > 0x7fffffff) return fail(MMDIT_ERR_SHAPE, "joint_attention: grid too large");
     const dim3 grid((unsigned)blocks);
-#define ATT_GO(O, L) joint_attn_bf16_kernel<O, L><<<grid, ATT_THREADS, 0, stream>>>(a)
-    if (out_dtype == MMDIT_F32) { if (has_lse) ATT_GO(MMDIT_F32, true); else ATT_GO(MMDIT_F32, false); }
-    else if (out_dtype == MMDIT_BF16) { if (has_lse) ATT_GO(MMDIT_BF16, true); else ATT_GO(MMDIT_BF16, false); }
-    else if (out_dtype == MMDIT_F16) { if (has_lse) ATT_GO(MMDIT_F16, true); else ATT_GO(MMDIT_F16, false); }
-    else return fail(MMDIT_ERR_DTYPE, "joint_attention: bad out dtype");
-#undef ATT_GO
-    return check_launch("joint_attention_bf16");
+    if (qk_dtype == MMDIT_F16 && v_dtype == MMDIT_F16) return attn_go<MMDIT_F16, MMDIT_F16>(a, grid, out_dtype, has_lse, stream);
+    if (qk_dtype == MMDIT_F16 && v_dtype == MMDIT_BF16) return attn_go<MMDIT_F16, MMDIT_BF16>(a, grid, out_dtype, has_lse, stream);
+    if (qk_dtype == MMDIT_BF16 && v_dtype == MMDIT_BF16) return attn_go<MMDIT_BF16, MMDIT_BF16>(a, grid, out_dtype, has_lse, stream);
+    if (qk_dtype == MMDIT_BF16 && v_dtype == MMDIT_F16) return attn_go<MMDIT_BF16, MMDIT_F16>(a, grid, out_dtype, has_lse, stream);
+    return fail(MMDIT_ERR_DTYPE, "joint_attention: unsupported dtype combination");
   }
-  if (in_dtype == MMDIT_F32) {
+  if (qk_dtype == MMDIT_F32 && v_dtype == MMDIT_F32) {
     AttnArgsF32 a{};
     a.q[0] = static_cast<const float*>(q_cond); a.q[1] = static_cast<const float*>(q_vis);
     a.k[0] = static_cast<const float*>(k_cond); a.k[1] = static_cast<const float*>(k_vis);
@@ -390,7 +419,7 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
 #undef ATT_GO
     return check_launch("joint_attention_f32");
   }
-  return fail(MMDIT_ERR_DTYPE, "joint_attention: in_dtype must be bf16 or f32");
+  return fail(MMDIT_ERR_DTYPE, "joint_attention: f32 Q/K need an f32 V");
 }
 
 }  // namespace mmdit

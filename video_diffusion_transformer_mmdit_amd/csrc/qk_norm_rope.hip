@@ -147,6 +147,10 @@ int launch_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_s
   QKN_CASE(MMDIT_F32, MMDIT_F32, MMDIT_BF16)
   QKN_CASE(MMDIT_F32, MMDIT_BF16, MMDIT_F32)
   QKN_CASE(MMDIT_F32, MMDIT_BF16, MMDIT_BF16)
+  QKN_CASE(MMDIT_F16, MMDIT_F16, MMDIT_BF16)
+  QKN_CASE(MMDIT_F16, MMDIT_F16, MMDIT_F32)
+  QKN_CASE(MMDIT_F16, MMDIT_F32, MMDIT_BF16)
+  QKN_CASE(MMDIT_F16, MMDIT_F32, MMDIT_F32)
 #undef QKN_CASE
   return fail(MMDIT_ERR_DTYPE, "qk_norm_rope: unsupported dtype combination");
 }
