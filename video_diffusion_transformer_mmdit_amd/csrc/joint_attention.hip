@@ -31,32 +31,30 @@
 namespace mmdit {
 
 constexpr int ATT_D = 128;
-constexpr int ATT_BM = 128;
-constexpr int ATT_BN = 64;
+constexpr int ATT_BM = 128;                       // queries per workgroup (4 waves x 32)
+constexpr int ATT_BN = 64;                        // keys per tile
 constexpr int ATT_THREADS = 256;
 constexpr int ATT_K_BYTES = ATT_BN * ATT_D * 2;   // 16 KiB
 constexpr int ATT_V_BYTES = ATT_D * ATT_BN * 2;   // 16 KiB
 constexpr int ATT_STAGE = ATT_K_BYTES + ATT_V_BYTES;
+constexpr float ATT_RESCALE_LOG2 = 8.0f;          // lazy rescale threshold: P <= 2^8
 
 struct AttnArgs {
-  const uint16_t* q[2];   // [0] cond, [1] vis
+  const uint16_t* q[2];   // [0] visual, [1] conditioning (segment order of the key loop)
   const uint16_t* k[2];
   const uint16_t* v[2];
   void* o[2];
   float* lse;
-  int64_t n_cond, n_vis, N;
+  int64_t n_seg[2];       // n_vis, n_cond
+  int64_t N;
   int64_t in_stride, out_stride;
   int H;
   int nqt;
   float scale_log2;       // softmax_scale * log2(e)
 };
 
-__device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* const* base, int64_t j,
-                                                   int64_t n_cond, int64_t n_vis, int64_t b,
-                                                   int64_t stride, int h) {
-  return j < n_cond ? base[0] + (b * n_cond + j) * stride + h * ATT_D
-                    : base[1] + (b * n_vis + (j - n_cond)) * stride + h * ATT_D;
-}
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma16(const uint4& a, const uint4& b, const f32x16& c) {
@@ -68,10 +66,14 @@ __device__ __forceinline__ f32x16 mfma16(const uint4& a, const uint4& b, const f
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Two bf16 in one word -> the same two values as f16 in one word.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  return pack_f16x2(lo_bf16(w), hi_bf16(w));
+// Round two floats to f16 (nearest even); a single v_cvt_pk_f16_f32 on gfx950.
+__device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
+  const float2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
 }
+
+// Two bf16 in one word -> the same two values as f16 in one word.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return cvt_pk_f16(lo_bf16(w), hi_bf16(w)); }
 
 // Physical 8-byte slot (0..15) of the V^T row for key quad `qd` (keys 4qd .. 4qd+3) of a
 // 64-key tile.  Inside each group of 16 keys the quads are stored in order 0, 2, 1, 3 so
@@ -84,8 +86,17 @@ __device__ __forceinline__ int vt_slot8(int qd, int d) {
   return logical ^ (((d >> 1) & 7) << 1);
 }
 
+// Buffer descriptor over one (segment, batch item, head): rows of `stride` elements, 128
+// valid elements in the last row.  Every read stays inside it: the partial last tile of a
+// segment clamps its rows to the segment's last row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const uint16_t* base, int64_t rows, int64_t stride) {
+  const int64_t bytes = rows > 0 ? ((rows - 1) * stride + ATT_D) * 2 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int QK_DT, int V_DT, int OUT_DT, bool LSE>
-__global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void joint_attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ATT_STAGE];
 
   const int tid = threadIdx.x;
@@ -96,12 +107,15 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
   const int h = bh % a.H;
   const int64_t b = bh / a.H;
   const int64_t N = a.N;
+  const int64_t n_vis = a.n_seg[0], n_cond = a.n_seg[1];
+  const int stride = (int)a.in_stride;
 
-  // ---- this lane's query row, held as the B operand (8 k-steps of 16 dims)
+  // ---- this lane's query row (queries in [cond | vis] order), the B operand of S^T
   const int64_t qi = (int64_t)qt * ATT_BM + wave * 32 + l32;
   uint4 qf[8];
   if (qi < N) {
-    const uint16_t* qp = row_ptr(a.q, qi, a.n_cond, a.n_vis, b, a.in_stride, h);
+    const uint16_t* qp = qi < n_cond ? a.q[1] + (b * n_cond + qi) * a.in_stride + h * ATT_D
+                                     : a.q[0] + (b * n_vis + (qi - n_cond)) * a.in_stride + h * ATT_D;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qp + ks * 16 + g * 8);
   } else {
@@ -109,33 +123,78 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
     for (int ks = 0; ks < 8; ++ks) qf[ks] = make_uint4(0, 0, 0, 0);
   }
 
-  // ---- K / V tile staging.  K: thread owns chunks tid + 256 i (key = chunk / 16, 16-byte
-  // column chunk % 16).  V: thread owns key quad tid % 16 and dim chunk tid / 16.
-  uint4 rk[4], rv[4];
+  // ---- key segments: visual tiles first, then conditioning tiles; each segment has its own
+  // buffer descriptors so the partial last tile of a segment reads zeros.
+  __amdgpu_buffer_rsrc_t rk[2], rvv[2];
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int64_t off = (b * a.n_seg[sg]) * a.in_stride + h * ATT_D;
+    rk[sg] = seg_rsrc(a.k[sg] ? a.k[sg] + off : a.k[0], a.n_seg[sg], a.in_stride);
+    rvv[sg] = seg_rsrc(a.v[sg] ? a.v[sg] + off : a.v[0], a.n_seg[sg], a.in_stride);
+  }
+  const int t_vis = (int)((n_vis + ATT_BN - 1) / ATT_BN);
+  const int ntiles = t_vis + (int)((n_cond + ATT_BN - 1) / ATT_BN);
+
+  // K: DMA straight into LDS.  Instruction i of this wave fills LDS rows 4*(4*wave+i) ..
+  // +3 (1 KiB, lane order); lane l writes physical chunk l % 16 of row 4*(4*wave+i) + l/16,
+  // so it loads logical chunk (l % 16) ^ (row % 16).
+  int k_voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (4 * wave + i) + (lane >> 4);
+    const int cc = (lane & 15) ^ (row & 15);
+    k_voff[i] = (row * stride + cc * 8) * 2;
+  }
+  // V: thread owns key quad tid % 16 (keys 4qd .. 4qd+3) and dim chunk tid / 16.
   const int v_qd = tid & 15, v_dc = tid >> 4;
-  auto gload = [&](int64_t j0) {
+  int v_voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v_voff[i] = ((4 * v_qd + i) * stride + v_dc * 8) * 2;
+
+  auto tile_seg = [&](int jt, int& sg, int& t) { sg = jt < t_vis ? 0 : 1; t = sg ? jt - t_vis : jt; };
+  // rows of tile t of segment sg that exist (ATT_BN except for a segment's last tile)
+  auto tile_rows = [&](int sg, int t) {
+    const int64_t r = a.n_seg[sg] - (int64_t)t * ATT_BN;
+    return r < ATT_BN ? (int)r : ATT_BN;
+  };
+  auto issue_k = [&](int jt, int buf) {
+    int sg, t;
+    tile_seg(jt, sg, t);
+    const int rows = tile_rows(sg, t);
+    const int soff = t * ATT_BN * stride * 2;
+    uint8_t* dst = lds + buf * ATT_STAGE + wave * 4096;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = tid + ATT_THREADS * i;
-      const int64_t j = j0 + (ch >> 4);
-      rk[i] = j < N ? *reinterpret_cast<const uint4*>(
-                          row_ptr(a.k, j, a.n_cond, a.n_vis, b, a.in_stride, h) + (ch & 15) * 8)
-                    : make_uint4(0, 0, 0, 0);
-      const int64_t jv = j0 + v_qd * 4 + i;
-      rv[i] = jv < N ? *reinterpret_cast<const uint4*>(
-                           row_ptr(a.v, jv, a.n_cond, a.n_vis, b, a.in_stride, h) + v_dc * 8)
-                     : make_uint4(0, 0, 0, 0);
+      int voff = k_voff[i];
+      if (rows < ATT_BN) {   // partial tile: rows past the end re-read the last row
+        const int row = 4 * (4 * wave + i) + (lane >> 4);
+        const int cc = (lane & 15) ^ (row & 15);
+        voff = ((row < rows ? row : rows - 1) * stride + cc * 8) * 2;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sg ? rk[1] : rk[0],
+                                               (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                               voff, soff, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-    uint8_t* sk = lds + buf * ATT_STAGE;
-    uint8_t* sv = sk + ATT_K_BYTES;
+  uint4 rv[4];
+  auto load_v = [&](int jt) {
+    int sg, t;
+    tile_seg(jt, sg, t);
+    const int rows = tile_rows(sg, t);
+    const int soff = t * ATT_BN * stride * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = tid + ATT_THREADS * i;
-      const int key = ch >> 4, cc = ch & 15;
-      *reinterpret_cast<uint4*>(sk + key * 256 + ((cc ^ (key & 15)) << 4)) = rk[i];
+      int voff = v_voff[i];
+      if (rows < ATT_BN) {
+        const int row = 4 * v_qd + i;
+        voff = ((row < rows ? row : rows - 1) * stride + v_dc * 8) * 2;
+      }
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(sg ? rvv[1] : rvv[0], voff, soff, 0);
+      rv[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+  };
+  auto store_v = [&](int buf) {
+    uint8_t* sv = lds + buf * ATT_STAGE + ATT_K_BYTES;
     // transpose 4 keys x 8 dims: word for dim 2m+e holds the 4 keys' values of that dim
     uint32_t w0[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
     uint32_t w1[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
@@ -148,22 +207,19 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
         w2[m] = bf16x2_to_f16x2(w2[m]); w3[m] = bf16x2_to_f16x2(w3[m]);
       }
     }
-    uint2 col[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      col[2 * m] = make_uint2((w0[m] & 0xffffu) | (w1[m] << 16), (w2[m] & 0xffffu) | (w3[m] << 16));
-      col[2 * m + 1] = make_uint2((w0[m] >> 16) | (w1[m] & 0xffff0000u),
-                                  (w2[m] >> 16) | (w3[m] & 0xffff0000u));
-    }
-    // odd dim chunks store their 8 dims in swapped pair order so that one store
+    // odd dim chunks store their dims in swapped pair order so that one store
     // instruction covers both parities of d (both halves of the LDS banks)
     const bool swp = v_dc & 1;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int rr = r ^ (swp ? 1 : 0);
-      const int d = v_dc * 8 + rr;
-      const uint2 val = swp ? col[r ^ 1] : col[r];
-      *reinterpret_cast<uint2*>(sv + d * 128 + (vt_slot8(v_qd, d) << 3)) = val;
+    for (int m = 0; m < 4; ++m) {
+      const uint2 c_even = make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u),
+                                      __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u));
+      const uint2 c_odd = make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u),
+                                     __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u));
+      const int d_first = v_dc * 8 + 2 * m + (swp ? 1 : 0);
+      const int d_second = v_dc * 8 + 2 * m + (swp ? 0 : 1);
+      *reinterpret_cast<uint2*>(sv + d_first * 128 + (vt_slot8(v_qd, d_first) << 3)) = swp ? c_odd : c_even;
+      *reinterpret_cast<uint2*>(sv + d_second * 128 + (vt_slot8(v_qd, d_second) << 3)) = swp ? c_even : c_odd;
     }
   };
 
@@ -172,17 +228,24 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float m_run = -INFINITY;   // running max of scaled logits (log2 domain)
-  float l_run = 0.f;         // this lane's partial row sum
+  float m_run = -INFINITY;   // running max of scaled logits (log2 domain), possibly stale by < 2^8
+  float l_run = 0.f;         // this lane's partial sum of the f16-rounded probabilities
+  const float c = a.scale_log2;
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  const int ntiles = (int)((N + ATT_BN - 1) / ATT_BN);
-  gload(0);
-  sstore(0);
+  if (ntiles > 0) {
+    issue_k(0, 0);
+    load_v(0);
+    store_v(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's LDS DMA has landed
   __syncthreads();
   for (int jt = 0; jt < ntiles; ++jt) {
     const int buf = jt & 1;
-    const int64_t j0 = (int64_t)jt * ATT_BN;
-    if (jt + 1 < ntiles) gload(j0 + ATT_BN);
+    if (jt + 1 < ntiles) {
+      issue_k(jt + 1, buf ^ 1);
+      load_v(jt + 1);
+    }
     const uint8_t* sk = lds + buf * ATT_STAGE;
     const uint8_t* sv = sk + ATT_K_BYTES;
 
@@ -199,47 +262,53 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
         s[st] = mfma16<QK_DT>(kf, qf[ks], s[st]);
       }
     }
-    // mask keys past the end (last tile only)
-    if (j0 + ATT_BN > N) {
+    // keys past the end of their segment (partial last tile of a segment)
+    {
+      int sg, t;
+      tile_seg(jt, sg, t);
+      const int valid = tile_rows(sg, t);
+      if (valid < ATT_BN) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t j = j0 + st * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (j >= N) s[st][e] = -INFINITY;
-        }
+          for (int e = 0; e < 16; ++e)
+            if (st * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= valid) s[st][e] = -INFINITY;
+      }
     }
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    // lazy rescale: keep a stale max while it stays within 2^8 of the true one
+    if (__any(mx > m_run + ATT_RESCALE_LOG2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    }
     uint4 pf[4];
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      float p[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = exp2f(fmaf(s[st][e], a.scale_log2, -m_new));
-        psum += p[e];
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i], c, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i + 1], c, -m_run));
+          w[i] = cvt_pk_f16(p0, p1);
+          if (i & 1) ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls1, false);
+          else ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls0, false);
+        }
+        pf[st * 2 + hh] = make_uint4(w[0], w[1], w[2], w[3]);
       }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        pf[st * 2 + hh] = make_uint4(pack_f16x2(p[8 * hh + 0], p[8 * hh + 1]),
-                                     pack_f16x2(p[8 * hh + 2], p[8 * hh + 3]),
-                                     pack_f16x2(p[8 * hh + 4], p[8 * hh + 5]),
-                                     pack_f16x2(p[8 * hh + 6], p[8 * hh + 7]));
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    l_run += ls0 + ls1;
 
     // O^T (128 dims x 32 queries) += V^T P^T
 #pragma unroll
@@ -251,7 +320,8 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
         o[dt] = mfma16<MMDIT_F16>(vf, pf[ks], o[dt]);
       }
     }
-    if (jt + 1 < ntiles) sstore(buf ^ 1);
+    if (jt + 1 < ntiles) store_v(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();
   }
 
@@ -259,9 +329,9 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qi >= N) return;
   const float inv = 1.0f / l_tot;
-  const int s_idx = qi < a.n_cond ? 0 : 1;
-  const int64_t row = qi < a.n_cond ? b * a.n_cond + qi : b * a.n_vis + (qi - a.n_cond);
-  void* obase = a.o[s_idx];
+  const bool is_cond = qi < n_cond;
+  const int64_t row = is_cond ? b * n_cond + qi : b * n_vis + (qi - n_cond);
+  void* obase = is_cond ? a.o[1] : a.o[0];
   const int64_t ooff = row * a.out_stride + (int64_t)h * ATT_D;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -277,7 +347,7 @@ __global__ __launch_bounds__(ATT_THREADS) void joint_attn_mfma_kernel(AttnArgs a
             make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
       } else {
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + ooff + d0) =
-            make_uint2(pack_f16x2(v0, v1), pack_f16x2(v2, v3));
+            make_uint2(cvt_pk_f16(v0, v1), cvt_pk_f16(v2, v3));
       }
     }
   if constexpr (LSE) {
@@ -377,13 +447,17 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
   if (B == 0 || H == 0 || N == 0) return MMDIT_OK;
   const bool has_lse = lse != nullptr;
   if (qk_dtype != MMDIT_F32) {
+    // the kernel addresses each (segment, batch item, head) through a 32-bit buffer range
+    if (((n_vis > 0 ? n_vis - 1 : 0) * in_stride + 128) * 2 >= (int64_t)1 << 31 ||
+        ((n_cond > 0 ? n_cond - 1 : 0) * in_stride + 128) * 2 >= (int64_t)1 << 31)
+      return fail(MMDIT_ERR_SHAPE, "joint_attention: one stream spans 2 GiB or more per batch item");
     AttnArgs a{};
-    a.q[0] = static_cast<const uint16_t*>(q_cond); a.q[1] = static_cast<const uint16_t*>(q_vis);
-    a.k[0] = static_cast<const uint16_t*>(k_cond); a.k[1] = static_cast<const uint16_t*>(k_vis);
-    a.v[0] = static_cast<const uint16_t*>(v_cond); a.v[1] = static_cast<const uint16_t*>(v_vis);
-    a.o[0] = o_cond; a.o[1] = o_vis;
+    a.q[0] = static_cast<const uint16_t*>(q_vis); a.q[1] = static_cast<const uint16_t*>(q_cond);
+    a.k[0] = static_cast<const uint16_t*>(k_vis); a.k[1] = static_cast<const uint16_t*>(k_cond);
+    a.v[0] = static_cast<const uint16_t*>(v_vis); a.v[1] = static_cast<const uint16_t*>(v_cond);
+    a.o[0] = o_vis; a.o[1] = o_cond;
     a.lse = lse;
-    a.n_cond = n_cond; a.n_vis = n_vis; a.N = N;
+    a.n_seg[0] = n_vis; a.n_seg[1] = n_cond; a.N = N;
     a.in_stride = in_stride; a.out_stride = out_stride;
     a.H = (int)H;
     a.nqt = (int)((N + ATT_BM - 1) / ATT_BM);
