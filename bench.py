@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--act-dtype", choices=("f16", "bf16"), default="f16",
                     help="type of the 16-bit intermediates and MFMA operands")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times): the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the block core runs on a single MI355X (no sharding, no "
@@ -115,6 +118,16 @@ def main():
     import torch
     import video_diffusion_transformer_mmdit_amd as mm
     import workloads as wl
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 5}), flush=True)
+        return
 
     cfg = wl.BLOCK_480P
     dev = torch.device("cuda:0")

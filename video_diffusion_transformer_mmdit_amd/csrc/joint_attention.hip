@@ -26,6 +26,8 @@
 //
 // fp32 path: a plain wave-per-query VALU kernel with the same online softmax, used for the
 // fp32 workload (small sizes).
+#include <type_traits>
+
 #include "common.h"
 
 namespace mmdit {
@@ -35,8 +37,6 @@ constexpr int ATT_BM = 128;                       // queries per workgroup (4 wa
 constexpr int ATT_BN = 64;                        // keys per tile
 constexpr int ATT_THREADS = 256;
 constexpr int ATT_K_BYTES = ATT_BN * ATT_D * 2;   // 16 KiB
-constexpr int ATT_V_BYTES = ATT_D * ATT_BN * 2;   // 16 KiB
-constexpr int ATT_STAGE = ATT_K_BYTES + ATT_V_BYTES;
 constexpr float ATT_RESCALE_LOG2 = 8.0f;          // lazy rescale threshold: P <= 2^8
 
 struct AttnArgs {
@@ -72,32 +72,53 @@ __device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
 }
 
-// Two bf16 in one word -> the same two values as f16 in one word.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return cvt_pk_f16(lo_bf16(w), hi_bf16(w)); }
-
-// Physical 8-byte slot (0..15) of the V^T row for key quad `qd` (keys 4qd .. 4qd+3) of a
-// 64-key tile.  Inside each group of 16 keys the quads are stored in order 0, 2, 1, 3 so
-// that lane half g reads keys {16s+4g .. +3, 16s+8+4g .. +3} as one 16-byte slot 2s+g,
-// which is the key order of the S^T accumulator; the 16-byte slot is XOR-swizzled by
-// (d / 2) % 8.
-__device__ __forceinline__ int vt_slot8(int qd, int d) {
-  const int r = qd & 3;
-  const int logical = (qd & ~3) | (((r & 1) << 1) | (r >> 1));
-  return logical ^ (((d >> 1) & 7) << 1);
-}
 
 // Buffer descriptor over one (segment, batch item, head): rows of `stride` elements, 128
 // valid elements in the last row.  Every read stays inside it: the partial last tile of a
-// segment clamps its rows to the segment's last row.
+// segment clamps its rows to the segment's last row.  The descriptor is built from
+// readfirstlane'd words so it provably lives in SGPRs (a descriptor the compiler believes
+// divergent costs a waterfall loop per load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const uint16_t* base, int64_t rows, int64_t stride) {
   const int64_t bytes = rows > 0 ? ((rows - 1) * stride + ATT_D) * 2 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t addr = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  const int num = __builtin_amdgcn_readfirstlane((int)bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, num, 0x00020000);
+}
+
+__device__ __forceinline__ float xhalf_max(float x) {   // max with the lane 32 apart
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint4 lds_read16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element (i % 4) of the
+// 8-byte reads of lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr(const uint8_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<uint8_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
 }
 
 template <int QK_DT, int V_DT, int OUT_DT, bool LSE>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void joint_attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ATT_STAGE];
+  // LDS: two K stages and two V stages, 16 KiB each, rows of 256 bytes (one key, 128 dims).
+  // Four distinct objects, always addressed with a compile-time stage index, so the wait-count
+  // pass can tell an LDS-DMA into one stage from reads of another and does not stall the
+  // reads on the prefetch in flight.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[ATT_K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[ATT_K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[ATT_K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[ATT_K_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -109,8 +130,9 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   const int64_t N = a.N;
   const int64_t n_vis = a.n_seg[0], n_cond = a.n_seg[1];
   const int stride = (int)a.in_stride;
+  const float c = a.scale_log2;
 
-  // ---- this lane's query row (queries in [cond | vis] order), the B operand of S^T
+  // ---- this lane's query row (queries in [cond | vis] order): the B operand of S^T
   const int64_t qi = (int64_t)qt * ATT_BM + wave * 32 + l32;
   uint4 qf[8];
   if (qi < N) {
@@ -123,104 +145,94 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     for (int ks = 0; ks < 8; ++ks) qf[ks] = make_uint4(0, 0, 0, 0);
   }
 
-  // ---- key segments: visual tiles first, then conditioning tiles; each segment has its own
-  // buffer descriptors so the partial last tile of a segment reads zeros.
-  __amdgpu_buffer_rsrc_t rk[2], rvv[2];
+  // ---- key segments: visual tiles first, then conditioning tiles, one descriptor pair each
+  __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
     const int64_t off = (b * a.n_seg[sg]) * a.in_stride + h * ATT_D;
     rk[sg] = seg_rsrc(a.k[sg] ? a.k[sg] + off : a.k[0], a.n_seg[sg], a.in_stride);
-    rvv[sg] = seg_rsrc(a.v[sg] ? a.v[sg] + off : a.v[0], a.n_seg[sg], a.in_stride);
+    rv[sg] = seg_rsrc(a.v[sg] ? a.v[sg] + off : a.v[0], a.n_seg[sg], a.in_stride);
   }
   const int t_vis = (int)((n_vis + ATT_BN - 1) / ATT_BN);
   const int ntiles = t_vis + (int)((n_cond + ATT_BN - 1) / ATT_BN);
 
-  // K: DMA straight into LDS.  Instruction i of this wave fills LDS rows 4*(4*wave+i) ..
-  // +3 (1 KiB, lane order); lane l writes physical chunk l % 16 of row 4*(4*wave+i) + l/16,
-  // so it loads logical chunk (l % 16) ^ (row % 16).
-  int k_voff[4];
+  // ---- LDS-DMA of one 64-key tile: DMA i of this wave fills rows 4*(4*wave+i) .. +3 in lane
+  // order (lane l -> row + l/16, physical 16-byte chunk l % 16).  K chunks are XOR-swizzled
+  // by (row % 16) for the column reads of S^T; V chunks by 4*(row % 4) for the transposed
+  // reads of O^T.  Each lane loads the logical chunk that belongs at its physical slot.
+  int k_col[4], v_col[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * (4 * wave + i) + (lane >> 4);
-    const int cc = (lane & 15) ^ (row & 15);
-    k_voff[i] = (row * stride + cc * 8) * 2;
+    k_col[i] = (((lane & 15) ^ (row & 15)) * 8) * 2;
+    v_col[i] = (((lane & 15) ^ ((row & 3) << 2)) * 8) * 2;
   }
-  // V: thread owns key quad tid % 16 (keys 4qd .. 4qd+3) and dim chunk tid / 16.
-  const int v_qd = tid & 15, v_dc = tid >> 4;
-  int v_voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v_voff[i] = ((4 * v_qd + i) * stride + v_dc * 8) * 2;
-
   auto tile_seg = [&](int jt, int& sg, int& t) { sg = jt < t_vis ? 0 : 1; t = sg ? jt - t_vis : jt; };
-  // rows of tile t of segment sg that exist (ATT_BN except for a segment's last tile)
   auto tile_rows = [&](int sg, int t) {
     const int64_t r = a.n_seg[sg] - (int64_t)t * ATT_BN;
     return r < ATT_BN ? (int)r : ATT_BN;
   };
-  auto issue_k = [&](int jt, int buf) {
+  auto dma_tile = [&](int jt, uint8_t* dst, const __amdgpu_buffer_rsrc_t* rs, const int* col) {
     int sg, t;
     tile_seg(jt, sg, t);
     const int rows = tile_rows(sg, t);
     const int soff = t * ATT_BN * stride * 2;
-    uint8_t* dst = lds + buf * ATT_STAGE + wave * 4096;
+    dst += wave * 4096;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int voff = k_voff[i];
-      if (rows < ATT_BN) {   // partial tile: rows past the end re-read the last row
-        const int row = 4 * (4 * wave + i) + (lane >> 4);
-        const int cc = (lane & 15) ^ (row & 15);
-        voff = ((row < rows ? row : rows - 1) * stride + cc * 8) * 2;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sg ? rk[1] : rk[0],
+      int row = 4 * (4 * wave + i) + (lane >> 4);
+      if (rows < ATT_BN) row = row < rows ? row : rows - 1;   // partial tile: re-read the last row
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sg ? rs[1] : rs[0],
                                                (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
-                                               voff, soff, 0, 0);
+                                               row * stride * 2 + col[i], soff, 0, 0);
     }
   };
-  uint4 rv[4];
-  auto load_v = [&](int jt) {
-    int sg, t;
-    tile_seg(jt, sg, t);
-    const int rows = tile_rows(sg, t);
-    const int soff = t * ATT_BN * stride * 2;
+  auto kbuf = [&](auto stage) -> uint8_t* { if constexpr (decltype(stage)::value == 0) return lds_k0; else return lds_k1; };
+  auto vbuf = [&](auto stage) -> uint8_t* { if constexpr (decltype(stage)::value == 0) return lds_v0; else return lds_v1; };
+  constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
+
+  // ---- per-lane LDS read offsets
+  // S^T A operand: key = 32*st + l32, logical chunk 2*ks + g, physical chunk ^ (key % 16)
+  int k_rd[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int voff = v_voff[i];
-      if (rows < ATT_BN) {
-        const int row = 4 * v_qd + i;
-        voff = ((row < rows ? row : rows - 1) * stride + v_dc * 8) * 2;
-      }
-      const auto w = __builtin_amdgcn_raw_buffer_load_b128(sg ? rvv[1] : rvv[0], voff, soff, 0);
-      rv[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int ks = 0; ks < 8; ++ks) k_rd[ks] = l32 * 256 + (((2 * ks + g) ^ (l32 & 15)) << 4);
+  // O^T A operand (dims x keys) through transposed reads: 16-lane group G = lane / 16 with
+  // k-group g = G / 2 and dim half = G % 2; lane j of the group reads key 4*g + j/4 (+16 s
+  // + 8 r) at dims 32*dt + 16*half + 4*(j % 4), and receives 4 consecutive keys of dim
+  // 32*dt + 16*half + j.  Physical chunk = logical chunk ^ 4*(key % 4), key % 4 = j / 4.
+  int v_rd[4];
+  {
+    const int G = lane >> 4, j = lane & 15;
+    const int gg = G >> 1, half = G & 1;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int chunk = (4 * dt + 2 * half + ((j & 3) >> 1)) ^ ((j >> 2) << 2);
+      v_rd[dt] = (4 * gg + (j >> 2)) * 256 + chunk * 16 + (j & 1) * 8;
     }
+  }
+
+  auto compute_s = [&](const uint8_t* kb, f32x16 (&s)[2]) {
+    // the two 32-key halves are independent accumulator chains: interleave them so that
+    // consecutive MFMAs never wait on each other's result
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) s[st] = mfma16<QK_DT>(lds_read16(kb + st * 8192 + k_rd[ks]), qf[ks], s[st]);
   };
-  auto store_v = [&](int buf) {
-    uint8_t* sv = lds + buf * ATT_STAGE + ATT_K_BYTES;
-    // transpose 4 keys x 8 dims: word for dim 2m+e holds the 4 keys' values of that dim
-    uint32_t w0[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
-    uint32_t w1[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
-    uint32_t w2[4] = {rv[2].x, rv[2].y, rv[2].z, rv[2].w};
-    uint32_t w3[4] = {rv[3].x, rv[3].y, rv[3].z, rv[3].w};
+  auto v_frag = [&](const uint8_t* vb, int dt, int ks) {
+    const uint8_t* p = vb + v_rd[dt] + ks * 4096;
+    const uint2 lo = lds_read_tr(p), hi = lds_read_tr(p + 2048);
+    uint4 f = make_uint4(lo.x, lo.y, hi.x, hi.y);
     if constexpr (V_DT == MMDIT_BF16) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        w0[m] = bf16x2_to_f16x2(w0[m]); w1[m] = bf16x2_to_f16x2(w1[m]);
-        w2[m] = bf16x2_to_f16x2(w2[m]); w3[m] = bf16x2_to_f16x2(w3[m]);
-      }
+      f.x = cvt_pk_f16(lo_bf16(f.x), hi_bf16(f.x)); f.y = cvt_pk_f16(lo_bf16(f.y), hi_bf16(f.y));
+      f.z = cvt_pk_f16(lo_bf16(f.z), hi_bf16(f.z)); f.w = cvt_pk_f16(lo_bf16(f.w), hi_bf16(f.w));
     }
-    // odd dim chunks store their dims in swapped pair order so that one store
-    // instruction covers both parities of d (both halves of the LDS banks)
-    const bool swp = v_dc & 1;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint2 c_even = make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u),
-                                      __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u));
-      const uint2 c_odd = make_uint2(__builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u),
-                                     __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u));
-      const int d_first = v_dc * 8 + 2 * m + (swp ? 1 : 0);
-      const int d_second = v_dc * 8 + 2 * m + (swp ? 0 : 1);
-      *reinterpret_cast<uint2*>(sv + d_first * 128 + (vt_slot8(v_qd, d_first) << 3)) = swp ? c_odd : c_even;
-      *reinterpret_cast<uint2*>(sv + d_second * 128 + (vt_slot8(v_qd, d_second) << 3)) = swp ? c_even : c_odd;
-    }
+    return f;
   };
 
   f32x16 o[4];
@@ -230,40 +242,18 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   float m_run = -INFINITY;   // running max of scaled logits (log2 domain), possibly stale by < 2^8
   float l_run = 0.f;         // this lane's partial sum of the f16-rounded probabilities
-  const float c = a.scale_log2;
   const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  uint4 pf[4];               // P of the previous tile (B operand of O^T)
 
-  if (ntiles > 0) {
-    issue_k(0, 0);
-    load_v(0);
-    store_v(0);
-  }
-  __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's LDS DMA has landed
-  __syncthreads();
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int buf = jt & 1;
-    if (jt + 1 < ntiles) {
-      issue_k(jt + 1, buf ^ 1);
-      load_v(jt + 1);
-    }
-    const uint8_t* sk = lds + buf * ATT_STAGE;
-    const uint8_t* sv = sk + ATT_K_BYTES;
-
-    // S^T (64 keys x 32 queries) = K Q^T
-    f32x16 s[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
-      const int key = st * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(sk + key * 256 + (((2 * ks + g) ^ (key & 15)) << 4));
-        s[st] = mfma16<QK_DT>(kf, qf[ks], s[st]);
-      }
-    }
-    // keys past the end of their segment (partial last tile of a segment)
-    {
+  // One pipeline step: P V of tile jt-1 overlapped with the row max of tile jt, then the
+  // probabilities of tile jt overlapped with S of tile jt+1.
+  auto step = [&](auto cur_c, int jt, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+    constexpr int CUR = decltype(cur_c)::value;   // jt % 2
+    constexpr std::integral_constant<int, CUR> cur{};
+    constexpr std::integral_constant<int, CUR ^ 1> oth{};
+    if (jt + 2 < ntiles) dma_tile(jt + 2, kbuf(cur), rk, k_col);
+    dma_tile(jt, vbuf(cur), rv, v_col);
+    {  // keys past the end of their segment (a segment's partial last tile)
       int sg, t;
       tile_seg(jt, sg, t);
       const int valid = tile_rows(sg, t);
@@ -275,10 +265,24 @@ void joint_attn_mfma_kernel(AttnArgs a) {
             if (st * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= valid) s[st][e] = -INFINITY;
       }
     }
+    // region A: O^T += V^T P^T (tile jt-1; zero P and zero V at jt = 0) | row max of tile jt
+    {
+      const uint8_t* vb = vbuf(oth);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] = mfma16<MMDIT_F16>(v_frag(vb, dt, ks), pf[ks], o[dt]);
+    }
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    mx = xhalf_max(mx) * c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);   // 2 VALU
+    }
     // lazy rescale: keep a stale max while it stays within 2^8 of the true one
     if (__any(mx > m_run + ATT_RESCALE_LOG2)) {
       const float m_new = fmaxf(m_run, mx);
@@ -290,7 +294,7 @@ void joint_attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
     }
-    uint4 pf[4];
+    // region C: P of tile jt | S of tile jt+1
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -309,24 +313,49 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       }
     }
     l_run += ls0 + ls1;
-
-    // O^T (128 dims x 32 queries) += V^T P^T
+    // S of tile jt+1 (after the last tile this reads a stale buffer; the result is unused)
+    compute_s(kbuf(oth), sn);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = dt * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(sv + d * 128 + (((2 * ks + g) ^ ((d >> 1) & 7)) << 4));
-        o[dt] = mfma16<MMDIT_F16>(vf, pf[ks], o[dt]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);   // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);   // 6 VALU
     }
-    if (jt + 1 < ntiles) store_v(buf ^ 1);
-    __builtin_amdgcn_s_waitcnt(0xF70);
+    __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
+  };
+
+  // prologue: K of tiles 0 and 1, S of tile 0; V stage 1 and P start at zero so that the
+  // first step's P V (of a tile -1) adds exactly nothing
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pf[i] = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(lds_v1 + (tid + ATT_THREADS * i) * 16) = make_uint4(0, 0, 0, 0);
+  }
+  dma_tile(0, lds_k0, rk, k_col);
+  if (ntiles > 1) dma_tile(1, lds_k1, rk, k_col);
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  compute_s(lds_k0, sa);
+  __syncthreads();   // K stage 0 is refilled by the first step
+  int jt = 0;
+  for (; jt + 1 < ntiles; jt += 2) {
+    step(S0, jt, sa, sb);
+    step(S1, jt + 1, sb, sa);
+  }
+  if (jt < ntiles) step(S0, jt, sa, sb);
+  // epilogue: P V of the last tile
+  {
+    const uint8_t* vb = ((ntiles - 1) & 1) ? lds_v1 : lds_v0;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) o[dt] = mfma16<MMDIT_F16>(v_frag(vb, dt, ks), pf[ks], o[dt]);
   }
 
   // ---- finish: combine the two half-wave partial sums, normalise, store
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   if (qi >= N) return;
   const float inv = 1.0f / l_tot;
   const bool is_cond = qi < n_cond;
