@@ -277,11 +277,19 @@ void joint_attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
     mx = xhalf_max(mx) * c;
+    // the V^T fragment of an MFMA is read two MFMAs ahead so that LDS latency hides
+    // behind the MFMA pipe
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);     // 4 LDS reads (2 fragments)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // 2 LDS reads
+    for (int i = 0; i < 14; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);   // 2 VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // 2 LDS reads
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
     }
     // lazy rescale: keep a stale max while it stays within 2^8 of the true one
     if (__any(mx > m_run + ATT_RESCALE_LOG2)) {
@@ -315,11 +323,17 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     l_run += ls0 + ls1;
     // S of tile jt+1 (after the last tile this reads a stale buffer; the result is unused)
     compute_s(kbuf(oth), sn);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);     // K fragments two MFMAs ahead
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);   // 1 LDS read
+    for (int i = 0; i < 14; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);   // 6 VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);   // 1 LDS read
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);
     }
     __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
