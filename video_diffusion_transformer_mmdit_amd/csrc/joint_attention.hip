@@ -7,22 +7,26 @@
 // reads the conditioning tensors, j >= n_cond the visual ones.
 //
 // 16-bit MFMA flash kernel (gfx950):
-//   - workgroup = 4 wave64s = 128 queries of one (batch, head); each wave owns 32 queries.
+//   - workgroup = 8 wave64s = 256 queries of one (batch, head); each wave owns 32 queries and
+//     the workgroup fills one CU (two waves per SIMD).
 //   - The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16} (A = 32 keys x 16 dims
 //     from LDS, B = the wave's Q held in registers for the whole kernel).  In the S^T
 //     accumulator layout every lane holds one query (lane % 32) and 16 keys, so the online
 //     softmax statistics are per-lane scalars and only the row max needs one exchange
 //     between the two half-waves per tile; the row sum is combined once at the end.
-//   - P^T comes straight from those accumulators (converted to f16) as the B operand of
-//     O^T = V^T P^T; O^T accumulates 128 dims x 32 queries per wave in registers.
-//   - K and V tiles of 64 keys are staged in LDS (2 stages x 32 KiB).  K rows are stored
-//     as is with an XOR swizzle; V is transposed on the way in (register 4x2 byte shuffles,
-//     8-byte LDS stores) so each lane reads its 8 keys of one dim as a single 16-byte LDS
-//     read, with keys permuted inside each 16-key group to match the accumulator layout.
-//   - exp2 with log2(e) * softmax_scale folded into one FMA per score.
+//   - P^T comes straight from those accumulators (rounded to f16) as the B operand of
+//     O^T = V^T P^T; O^T accumulates 128 dims x 32 queries per wave in registers.  The V^T
+//     operand is read from row-major V tiles with ds_read_b64_tr_b16.
+//   - K and V tiles of 64 keys reach LDS by LDS-DMA (buffer loads straight into LDS, two
+//     stages each, XOR-swizzled chunks for conflict-free reads).
+//   - Two wave groups ping-pong: a wave alternates an MFMA-only phase (S of the next tile,
+//     P V of this one) and a VALU-only phase (max, lazy rescale, exp2), one group a phase
+//     behind the other, so on every SIMD the matrix pipe and the VALU work concurrently.
+//   - exp2 with log2(e) * softmax_scale folded into one FMA per score; the running max is
+//     only raised when a score exceeds it by more than 2^8 (lazy rescale).
 //   - Precision: S = Q K^T runs on the operand type of Q and K (f16 or bf16); P is rounded
-//     to f16 (P lies in [0, 1], where f16 keeps 3 more mantissa bits than bf16) and PV runs
-//     on f16 MFMA, so a bf16 V is converted to f16 while it is staged into LDS.
+//     to f16 (P lies in [0, 2^8], where f16 keeps 3 more mantissa bits than bf16) and PV runs
+//     on f16 MFMA, so a bf16 V is converted to f16 after it is read from LDS.
 //
 // fp32 path: a plain wave-per-query VALU kernel with the same online softmax, used for the
 // fp32 workload (small sizes).
@@ -33,9 +37,9 @@
 namespace mmdit {
 
 constexpr int ATT_D = 128;
-constexpr int ATT_BM = 128;                       // queries per workgroup (4 waves x 32)
+constexpr int ATT_BM = 256;                       // queries per workgroup (8 waves x 32)
 constexpr int ATT_BN = 64;                        // keys per tile
-constexpr int ATT_THREADS = 256;
+constexpr int ATT_THREADS = 512;
 constexpr int ATT_K_BYTES = ATT_BN * ATT_D * 2;   // 16 KiB
 constexpr float ATT_RESCALE_LOG2 = 8.0f;          // lazy rescale threshold: P <= 2^8
 
@@ -121,7 +125,7 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_v1[ATT_K_BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave index in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
   const int qt = blockIdx.x % a.nqt;
   const int bh = blockIdx.x / a.nqt;
@@ -144,48 +148,12 @@ void joint_attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = make_uint4(0, 0, 0, 0);
   }
-
-  // ---- key segments: visual tiles first, then conditioning tiles, one descriptor pair each
-  __amdgpu_buffer_rsrc_t rk[2], rv[2];
-#pragma unroll
-  for (int sg = 0; sg < 2; ++sg) {
-    const int64_t off = (b * a.n_seg[sg]) * a.in_stride + h * ATT_D;
-    rk[sg] = seg_rsrc(a.k[sg] ? a.k[sg] + off : a.k[0], a.n_seg[sg], a.in_stride);
-    rv[sg] = seg_rsrc(a.v[sg] ? a.v[sg] + off : a.v[0], a.n_seg[sg], a.in_stride);
-  }
   const int t_vis = (int)((n_vis + ATT_BN - 1) / ATT_BN);
   const int ntiles = t_vis + (int)((n_cond + ATT_BN - 1) / ATT_BN);
-
-  // ---- LDS-DMA of one 64-key tile: DMA i of this wave fills rows 4*(4*wave+i) .. +3 in lane
-  // order (lane l -> row + l/16, physical 16-byte chunk l % 16).  K chunks are XOR-swizzled
-  // by (row % 16) for the column reads of S^T; V chunks by 4*(row % 4) for the transposed
-  // reads of O^T.  Each lane loads the logical chunk that belongs at its physical slot.
-  int k_col[4], v_col[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (4 * wave + i) + (lane >> 4);
-    k_col[i] = (((lane & 15) ^ (row & 15)) * 8) * 2;
-    v_col[i] = (((lane & 15) ^ ((row & 3) << 2)) * 8) * 2;
-  }
   auto tile_seg = [&](int jt, int& sg, int& t) { sg = jt < t_vis ? 0 : 1; t = sg ? jt - t_vis : jt; };
   auto tile_rows = [&](int sg, int t) {
     const int64_t r = a.n_seg[sg] - (int64_t)t * ATT_BN;
     return r < ATT_BN ? (int)r : ATT_BN;
-  };
-  auto dma_tile = [&](int jt, uint8_t* dst, const __amdgpu_buffer_rsrc_t* rs, const int* col) {
-    int sg, t;
-    tile_seg(jt, sg, t);
-    const int rows = tile_rows(sg, t);
-    const int soff = t * ATT_BN * stride * 2;
-    dst += wave * 4096;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = 4 * (4 * wave + i) + (lane >> 4);
-      if (rows < ATT_BN) row = row < rows ? row : rows - 1;   // partial tile: re-read the last row
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sg ? rs[1] : rs[0],
-                                               (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
-                                               row * stride * 2 + col[i], soff, 0, 0);
-    }
   };
   auto kbuf = [&](auto stage) -> uint8_t* { if constexpr (decltype(stage)::value == 0) return lds_k0; else return lds_k1; };
   auto vbuf = [&](auto stage) -> uint8_t* { if constexpr (decltype(stage)::value == 0) return lds_v0; else return lds_v1; };
@@ -234,168 +202,215 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     }
     return f;
   };
+  // Phase barrier: only orders LDS use between the waves; no memory-fence waits.  Every LDS
+  // read before it has been consumed (waited for) by an MFMA of the same phase.
+  auto phase_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
-  f32x16 o[4];
+  // ---- Ping-pong of two wave groups.  Waves 0-3 (group 0) and 4-7 (group 1) each hold one
+  // wave on every SIMD.  Each wave alternates two phases per 64-key tile:
+  //   M(j): S_{j+1} = K_{j+1} Q^T and O^T += V_j^T P_j^T -- MFMA and LDS reads only;
+  //   V(j): mask, row max, lazy rescale and P_j = exp2(S_j - m) -- VALU only.
+  // Group 1 runs one phase behind group 0 and every phase ends with a workgroup barrier, so
+  // on each SIMD one wave keeps the matrix pipe busy while the other runs the softmax.
+  // Tiles move by LDS-DMA: group 0 loads V_{j+1} during its M(j), group 1 loads K_{j+2}
+  // during its V(j); each waits for its own loads at the end of its next phase.
+  auto run = [&](auto grp_c) {
+    constexpr int GRP = decltype(grp_c)::value;
+    const int wg = wave & 3;   // this wave's index inside its group
+    __amdgpu_buffer_rsrc_t rs[2];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int sg = 0; sg < 2; ++sg) {
+      const int64_t off = (b * a.n_seg[sg]) * a.in_stride + h * ATT_D;
+      const uint16_t* base = GRP ? a.k[sg] : a.v[sg];
+      rs[sg] = seg_rsrc(base ? base + off : (GRP ? a.k[0] : a.v[0]), a.n_seg[sg], a.in_stride);
+    }
+    // DMA i of this wave fills tile rows 4*(4*wg+i) .. +3 in lane order (lane l -> row +
+    // l/16, physical 16-byte chunk l % 16).  K chunks are XOR-swizzled by (row % 16) for the
+    // column reads of S^T, V chunks by 4*(row % 4) for the transposed reads of O^T; each lane
+    // loads the logical chunk that belongs at its physical slot.  The tile's offset is added
+    // to the per-lane offset (not passed as the unchecked scalar offset), so the descriptor's
+    // range check turns rows past the end of a segment into zeros and the DMA needs no branch.
+    int off[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float m_run = -INFINITY;   // running max of scaled logits (log2 domain), possibly stale by < 2^8
-  float l_run = 0.f;         // this lane's partial sum of the f16-rounded probabilities
-  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-  uint4 pf[4];               // P of the previous tile (B operand of O^T)
-
-  // One pipeline step: P V of tile jt-1 overlapped with the row max of tile jt, then the
-  // probabilities of tile jt overlapped with S of tile jt+1.
-  auto step = [&](auto cur_c, int jt, f32x16 (&s)[2], f32x16 (&sn)[2]) {
-    constexpr int CUR = decltype(cur_c)::value;   // jt % 2
-    constexpr std::integral_constant<int, CUR> cur{};
-    constexpr std::integral_constant<int, CUR ^ 1> oth{};
-    if (jt + 2 < ntiles) dma_tile(jt + 2, kbuf(cur), rk, k_col);
-    dma_tile(jt, vbuf(cur), rv, v_col);
-    {  // keys past the end of their segment (a segment's partial last tile)
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (4 * wg + i) + (lane >> 4);
+      const int chunk = GRP ? ((lane & 15) ^ (row & 15)) : ((lane & 15) ^ ((row & 3) << 2));
+      off[i] = row * stride * 2 + chunk * 16;
+    }
+    auto dma_tile = [&](int jt, uint8_t* dst) {
       int sg, t;
       tile_seg(jt, sg, t);
-      const int valid = tile_rows(sg, t);
-      if (valid < ATT_BN) {
+      const int tile_off = t * ATT_BN * stride * 2;
+      const __amdgpu_buffer_rsrc_t r = sg ? rs[1] : rs[0];
+      dst += wg * 4096;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                                 off[i] + tile_off, 0, 0, 0);
+    };
+
+    f32x16 o[4];
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (st * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= valid) s[st][e] = -INFINITY;
-      }
-    }
-    // region A: O^T += V^T P^T (tile jt-1; zero P and zero V at jt = 0) | row max of tile jt
-    {
-      const uint8_t* vb = vbuf(oth);
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+    float m_run = -INFINITY;   // running max of scaled logits (log2 domain), possibly stale by < 2^8
+    float l_run = 0.f;         // this lane's partial sum of the f16-rounded probabilities
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    uint4 pf[4];               // P_j, the B operand of O^T
+
+    // M(j): S_{j+1} (past the last tile from a stale stage; never used) and O^T += V_j^T P_j^T
+    auto phase_m = [&](auto cur_c, int jt, f32x16 (&sn)[2]) {
+      constexpr int CUR = decltype(cur_c)::value;   // jt % 2
+      constexpr std::integral_constant<int, CUR> cur{};
+      constexpr std::integral_constant<int, CUR ^ 1> oth{};
+      // group 0: V_{j+1} into the other V stage (past the last tile: a reload nobody reads)
+      if constexpr (GRP == 0) dma_tile(jt + 1 < ntiles ? jt + 1 : ntiles - 1, vbuf(oth));
+      compute_s(kbuf(oth), sn);
+      const uint8_t* vb = vbuf(cur);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt] = mfma16<MMDIT_F16>(v_frag(vb, dt, ks), pf[ks], o[dt]);
-    }
-    float mx = fmaxf(s[0][0], s[1][0]);
+      // LDS operands are read four MFMAs ahead (K fragments: one read, V^T fragments: two)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
-    mx = xhalf_max(mx) * c;
-    // the V^T fragment of an MFMA is read two MFMAs ahead so that LDS latency hides
-    // behind the MFMA pipe
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);     // 4 LDS reads (2 fragments)
-#pragma unroll
-    for (int i = 0; i < 14; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);   // 2 VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // 2 LDS reads
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
-    }
-    // lazy rescale: keep a stale max while it stays within 2^8 of the true one
-    if (__any(mx > m_run + ATT_RESCALE_LOG2)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-    }
-    // region C: P of tile jt | S of tile jt+1
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i], c, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i + 1], c, -m_run));
-          w[i] = cvt_pk_f16(p0, p1);
-          if (i & 1) ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls1, false);
-          else ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls0, false);
-        }
-        pf[st * 2 + hh] = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        else if (i + 4 < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        if (GRP == 0 && i < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
       }
-    }
-    l_run += ls0 + ls1;
-    // S of tile jt+1 (after the last tile this reads a stale buffer; the result is unused)
-    compute_s(kbuf(oth), sn);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);     // K fragments two MFMAs ahead
+      // the products must issue in this phase: pin their results ahead of the barrier (the
+      // compiler would otherwise sink MFMAs into the softmax phase that first reads them)
+      asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
+      asm volatile("" ::"v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]));
+      if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's K loads have landed
+      phase_barrier();
+    };
+    // V(j): softmax of S_j into P_j
+    auto phase_v = [&](auto cur_c, int jt, f32x16 (&s)[2]) {
+      constexpr int CUR = decltype(cur_c)::value;
+      constexpr std::integral_constant<int, CUR> cur{};
+      // group 1: K_{j+2} into this K stage (its last reader, M(j-1), is behind the barrier)
+      if constexpr (GRP == 1) dma_tile(jt + 2 < ntiles ? jt + 2 : ntiles - 1, kbuf(cur));
+      {  // keys past the end of their segment (a segment's partial last tile)
+        int sg, t;
+        tile_seg(jt, sg, t);
+        const int valid = tile_rows(sg, t);
+        if (valid < ATT_BN) {
 #pragma unroll
-    for (int i = 0; i < 14; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);   // 6 VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);   // 1 LDS read
-    }
+          for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);
-    }
-    __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's DMA has landed
-    __syncthreads();
-  };
+            for (int e = 0; e < 16; ++e)
+              if (st * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= valid) s[st][e] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
+      mx = xhalf_max(mx) * c;
+      // lazy rescale: keep a stale max while it stays within 2^8 of the true one
+      if (__any(mx > m_run + ATT_RESCALE_LOG2)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      }
+      float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i], c, -m_run));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i + 1], c, -m_run));
+            w[i] = cvt_pk_f16(p0, p1);
+            if (i & 1) ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls1, false);
+            else ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls0, false);
+          }
+          pf[st * 2 + hh] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+      l_run += ls0 + ls1;
+      // likewise pin P, l and m: the exponentials belong to this phase, not the next M phase
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w));
+      asm volatile("" ::"v"(l_run), "v"(m_run));
+      if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's V loads have landed
+      phase_barrier();
+    };
 
-  // prologue: K of tiles 0 and 1, S of tile 0; V stage 1 and P start at zero so that the
-  // first step's P V (of a tile -1) adds exactly nothing
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pf[i] = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(lds_v1 + (tid + ATT_THREADS * i) * 16) = make_uint4(0, 0, 0, 0);
-  }
-  dma_tile(0, lds_k0, rk, k_col);
-  if (ntiles > 1) dma_tile(1, lds_k1, rk, k_col);
-  __builtin_amdgcn_s_waitcnt(0xF70);
-  __syncthreads();
-  f32x16 sa[2], sb[2];
-  compute_s(lds_k0, sa);
-  __syncthreads();   // K stage 0 is refilled by the first step
-  int jt = 0;
-  for (; jt + 1 < ntiles; jt += 2) {
-    step(S0, jt, sa, sb);
-    step(S1, jt + 1, sb, sa);
-  }
-  if (jt < ntiles) step(S0, jt, sa, sb);
-  // epilogue: P V of the last tile
-  {
-    const uint8_t* vb = ((ntiles - 1) & 1) ? lds_v1 : lds_v0;
+    // prologue: group 1 loads K_0 and K_1; S_0 is an M phase of its own in which group 0
+    // starts loading V_0
+    if constexpr (GRP == 1) {
+      dma_tile(0, lds_k0);
+      if (ntiles > 1) dma_tile(1, lds_k1);
+      __builtin_amdgcn_s_waitcnt(0xF70);
+    }
+    __syncthreads();
+    if constexpr (GRP == 1) phase_barrier();   // group 1 runs one phase behind
+    if constexpr (GRP == 0) dma_tile(0, lds_v0);
+    f32x16 sa[2], sb[2];
+    compute_s(lds_k0, sa);
+    phase_barrier();
+    int jt = 0;
+    for (; jt + 1 < ntiles; jt += 2) {
+      phase_v(S0, jt, sa);
+      phase_m(S0, jt, sb);
+      phase_v(S1, jt + 1, sb);
+      phase_m(S1, jt + 1, sa);
+    }
+    if (jt < ntiles) {
+      phase_v(S0, jt, sa);
+      phase_m(S0, jt, sb);
+    }
+    if constexpr (GRP == 0) {   // drain the last (unused) V reload, then match group 1's extra barrier
+      __builtin_amdgcn_s_waitcnt(0xF70);
+      phase_barrier();
+    }
+
+    // ---- finish: combine the two half-wave partial sums, normalise, store
+    const float l_tot = xhalf_sum(l_run);
+    if (qi >= N) return;
+    const float inv = 1.0f / l_tot;
+    const bool is_cond = qi < n_cond;
+    const int64_t row = is_cond ? b * n_cond + qi : b * n_vis + (qi - n_cond);
+    void* obase = is_cond ? a.o[1] : a.o[0];
+    const int64_t ooff = row * a.out_stride + (int64_t)h * ATT_D;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) o[dt] = mfma16<MMDIT_F16>(v_frag(vb, dt, ks), pf[ks], o[dt]);
-  }
-
-  // ---- finish: combine the two half-wave partial sums, normalise, store
-  const float l_tot = xhalf_sum(l_run);
-  if (qi >= N) return;
-  const float inv = 1.0f / l_tot;
-  const bool is_cond = qi < n_cond;
-  const int64_t row = is_cond ? b * n_cond + qi : b * n_vis + (qi - n_cond);
-  void* obase = is_cond ? a.o[1] : a.o[0];
-  const int64_t ooff = row * a.out_stride + (int64_t)h * ATT_D;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int d0 = dt * 32 + 8 * e4 + 4 * g;
-      const float v0 = o[dt][4 * e4 + 0] * inv, v1 = o[dt][4 * e4 + 1] * inv;
-      const float v2 = o[dt][4 * e4 + 2] * inv, v3 = o[dt][4 * e4 + 3] * inv;
-      if constexpr (OUT_DT == MMDIT_F32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(obase) + ooff + d0) = make_float4(v0, v1, v2, v3);
-      } else if constexpr (OUT_DT == MMDIT_BF16) {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + ooff + d0) =
-            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-      } else {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + ooff + d0) =
-            make_uint2(cvt_pk_f16(v0, v1), cvt_pk_f16(v2, v3));
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d0 = dt * 32 + 8 * e4 + 4 * g;
+        const float v0 = o[dt][4 * e4 + 0] * inv, v1 = o[dt][4 * e4 + 1] * inv;
+        const float v2 = o[dt][4 * e4 + 2] * inv, v3 = o[dt][4 * e4 + 3] * inv;
+        if constexpr (OUT_DT == MMDIT_F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(obase) + ooff + d0) = make_float4(v0, v1, v2, v3);
+        } else if constexpr (OUT_DT == MMDIT_BF16) {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + ooff + d0) =
+              make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        } else {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + ooff + d0) =
+              make_uint2(cvt_pk_f16(v0, v1), cvt_pk_f16(v2, v3));
+        }
       }
+    if constexpr (LSE) {
+      if (g == 0) a.lse[(b * a.H + h) * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
     }
-  if constexpr (LSE) {
-    if (g == 0) a.lse[(b * a.H + h) * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
-  }
+  };
+  if (wave >= 4) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
 }
 
 // ------------------------------------------------------------------ fp32 VALU path
