@@ -42,6 +42,9 @@ constexpr int ATT_BN = 64;                        // keys per tile
 constexpr int ATT_THREADS = 512;
 constexpr int ATT_K_BYTES = ATT_BN * ATT_D * 2;   // 16 KiB
 constexpr float ATT_RESCALE_LOG2 = 8.0f;          // lazy rescale threshold: P <= 2^8
+#ifndef ATT_LDS_AHEAD
+#define ATT_LDS_AHEAD 4                           // MFMAs between an LDS operand read and its use
+#endif
 
 struct AttnArgs {
   const uint16_t* q[2];   // [0] visual, [1] conditioning (segment order of the key loop)
@@ -127,8 +130,21 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave index in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
-  const int qt = blockIdx.x % a.nqt;
-  const int bh = blockIdx.x / a.nqt;
+  // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8), each with its own L2.
+  // When the (batch, head) count allows, XCD x takes whole heads x, x + 8, ... so that the 32
+  // workgroups it runs at a time stream the same K and V through one L2.
+  int qt, bh;
+  {
+    const int bid = blockIdx.x, nbh = gridDim.x / a.nqt;
+    if ((nbh & 7) == 0) {
+      const int i = bid >> 3;
+      bh = (bid & 7) + 8 * (i / a.nqt);
+      qt = i % a.nqt;
+    } else {
+      bh = bid / a.nqt;
+      qt = bid % a.nqt;
+    }
+  }
   const int h = bh % a.H;
   const int64_t b = bh / a.H;
   const int64_t N = a.N;
@@ -147,6 +163,23 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   } else {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = make_uint4(0, 0, 0, 0);
+  }
+  // f16 Q is scaled once by softmax_scale * log2(e) (rounded to f16 again), so S comes out of
+  // the MFMA in log2 units and the exponential needs no multiply; a bf16 Q would lose 3 more
+  // bits in that rounding, so there the accumulator is scaled at the exponential instead.
+  constexpr bool PRESCALE = QK_DT == MMDIT_F16;
+  const float ce = PRESCALE ? 1.0f : c;          // log2 units per accumulator unit
+  const float inv_ce = PRESCALE ? 1.0f : 1.0f / c;
+  if constexpr (PRESCALE) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint32_t* w = reinterpret_cast<uint32_t*>(&qf[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t hq = __builtin_bit_cast(half2_t, w[i]);
+        w[i] = cvt_pk_f16((float)hq[0] * c, (float)hq[1] * c);
+      }
+    }
   }
   const int t_vis = (int)((n_vis + ATT_BN - 1) / ATT_BN);
   const int ntiles = t_vis + (int)((n_cond + ATT_BN - 1) / ATT_BN);
@@ -180,17 +213,30 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  auto compute_s = [&](const uint8_t* kb, f32x16 (&s)[2]) {
-    // the two 32-key halves are independent accumulator chains: interleave them so that
-    // consecutive MFMAs never wait on each other's result
+  // S^T of one tile, accumulated onto s (set beforehand to minus the running max, so the
+  // product comes out relative to it); the two 32-key halves are independent accumulator
+  // chains, interleaved so that consecutive MFMAs never wait on each other's result
+  auto init_s = [&](f32x16 (&s)[2], float v) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s[st][e] = v;
+  };
+  auto compute_s = [&](const uint8_t* kb, f32x16 (&s)[2]) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int st = 0; st < 2; ++st) s[st] = mfma16<QK_DT>(lds_read16(kb + st * 8192 + k_rd[ks]), qf[ks], s[st]);
+  };
+  auto row_max = [&](const f32x16 (&s)[2]) {   // max over this query's 64 keys (both half-waves)
+    float m4[4];                                 // four independent chains, then a short tree
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m4[k] = fmaxf(s[0][k], s[1][k]);
+#pragma unroll
+    for (int e = 4; e < 16; e += 4)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m4[k] = fmaxf(m4[k], fmaxf(s[0][e + k], s[1][e + k]));
+    return xhalf_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   };
   auto v_frag = [&](const uint8_t* vb, int dt, int ks) {
     const uint8_t* p = vb + v_rd[dt] + ks * 4096;
@@ -216,41 +262,47 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   //   V(j): mask, row max, lazy rescale and P_j = exp2(S_j - m) -- VALU only.
   // Group 1 runs one phase behind group 0 and every phase ends with a workgroup barrier, so
   // on each SIMD one wave keeps the matrix pipe busy while the other runs the softmax.
-  // Tiles move by LDS-DMA: group 0 loads V_{j+1} during its M(j), group 1 loads K_{j+2}
-  // during its V(j); each waits for its own loads at the end of its next phase.
+  // Tiles move by LDS-DMA, issued between the MFMAs of M(j): group 0 loads V_{j+1} and waits
+  // for it at the end of its V(j+1); group 1 loads K_{j+2} and waits at the end of its M(j).
   auto run = [&](auto grp_c) {
     constexpr int GRP = decltype(grp_c)::value;
     const int wg = wave & 3;   // this wave's index inside its group
-    __amdgpu_buffer_rsrc_t rs[2];
+    // this group's tensor, one (batch item, head) slice per segment: base and byte extent
+    const uint16_t* seg_base[2];
+    int64_t seg_bytes[2];
 #pragma unroll
     for (int sg = 0; sg < 2; ++sg) {
-      const int64_t off = (b * a.n_seg[sg]) * a.in_stride + h * ATT_D;
       const uint16_t* base = GRP ? a.k[sg] : a.v[sg];
-      rs[sg] = seg_rsrc(base ? base + off : (GRP ? a.k[0] : a.v[0]), a.n_seg[sg], a.in_stride);
+      seg_base[sg] = base ? base + (b * a.n_seg[sg]) * a.in_stride + h * ATT_D : (GRP ? a.k[0] : a.v[0]);
+      seg_bytes[sg] = a.n_seg[sg] > 0 ? ((a.n_seg[sg] - 1) * a.in_stride + ATT_D) * 2 : 0;
     }
     // DMA i of this wave fills tile rows 4*(4*wg+i) .. +3 in lane order (lane l -> row +
     // l/16, physical 16-byte chunk l % 16).  K chunks are XOR-swizzled by (row % 16) for the
     // column reads of S^T, V chunks by 4*(row % 4) for the transposed reads of O^T; each lane
-    // loads the logical chunk that belongs at its physical slot.  The tile's offset is added
-    // to the per-lane offset (not passed as the unchecked scalar offset), so the descriptor's
-    // range check turns rows past the end of a segment into zeros and the DMA needs no branch.
+    // loads the logical chunk that belongs at its physical slot.  The descriptor starts at
+    // the tile and ends with the segment, so rows past the segment's end fail its range check
+    // and arrive as zeros.  All four loads share one LDS base (M0): the immediate offset
+    // i * 1024 moves both the LDS destination and the source, and is taken back out of the
+    // per-lane offset, which is therefore fixed for the whole loop.
     int off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * (4 * wg + i) + (lane >> 4);
       const int chunk = GRP ? ((lane & 15) ^ (row & 15)) : ((lane & 15) ^ ((row & 3) << 2));
-      off[i] = row * stride * 2 + chunk * 16;
+      off[i] = row * stride * 2 + chunk * 16 - i * 1024;
     }
     auto dma_tile = [&](int jt, uint8_t* dst) {
       int sg, t;
       tile_seg(jt, sg, t);
-      const int tile_off = t * ATT_BN * stride * 2;
-      const __amdgpu_buffer_rsrc_t r = sg ? rs[1] : rs[0];
-      dst += wg * 4096;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
-                                                 off[i] + tile_off, 0, 0, 0);
+      const int64_t tile_elems = (int64_t)t * ATT_BN * stride;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>((sg ? seg_base[1] : seg_base[0]) + tile_elems), (short)0,
+          (int)((sg ? seg_bytes[1] : seg_bytes[0]) - tile_elems * 2), 0x00020000);
+      auto* l = (__attribute__((address_space(3))) void*)(dst + wg * 4096);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[0], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[1], 0, 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[2], 0, 2048, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[3], 0, 3072, 0);
     };
 
     f32x16 o[4];
@@ -258,32 +310,35 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-    float m_run = -INFINITY;   // running max of scaled logits (log2 domain), possibly stale by < 2^8
-    float l_run = 0.f;         // this lane's partial sum of the f16-rounded probabilities
-    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    uint4 pf[4];               // P_j, the B operand of O^T
+    float m_run = 0.f;         // running max of the logits (log2 units), possibly stale by < 2^8;
+                               // S accumulators hold logit - m_run in accumulator units
+    float l_run = 0.f;         // this lane's partial sum of the probabilities
+    uint4 pf[4];               // P_j rounded to f16, the B operand of O^T
 
     // M(j): S_{j+1} (past the last tile from a stale stage; never used) and O^T += V_j^T P_j^T
     auto phase_m = [&](auto cur_c, int jt, f32x16 (&sn)[2]) {
       constexpr int CUR = decltype(cur_c)::value;   // jt % 2
       constexpr std::integral_constant<int, CUR> cur{};
       constexpr std::integral_constant<int, CUR ^ 1> oth{};
-      // group 0: V_{j+1} into the other V stage (past the last tile: a reload nobody reads)
+      // group 0: V_{j+1} into the other V stage; group 1: K_{j+2} into this K stage (its last
+      // reader, group 1's M(j-1), is behind the barrier).  Past the last tile: a reload of the
+      // last one into a stage nobody reads again.
       if constexpr (GRP == 0) dma_tile(jt + 1 < ntiles ? jt + 1 : ntiles - 1, vbuf(oth));
+      else dma_tile(jt + 2 < ntiles ? jt + 2 : ntiles - 1, kbuf(cur));
       compute_s(kbuf(oth), sn);
       const uint8_t* vb = vbuf(cur);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt] = mfma16<MMDIT_F16>(v_frag(vb, dt, ks), pf[ks], o[dt]);
-      // LDS operands are read four MFMAs ahead (K fragments: one read, V^T fragments: two)
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      // LDS operands are read ATT_LDS_AHEAD MFMAs ahead (K fragments: one read, V^T fragments: two)
+      __builtin_amdgcn_sched_group_barrier(0x100, ATT_LDS_AHEAD, 1);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        else if (i + 4 < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        if (GRP == 0 && i < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
+        if (i + ATT_LDS_AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        else if (i + ATT_LDS_AHEAD < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        if (i < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
       }
       // the products must issue in this phase: pin their results ahead of the barrier (the
       // compiler would otherwise sink MFMAs into the softmax phase that first reads them)
@@ -293,11 +348,7 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       phase_barrier();
     };
     // V(j): softmax of S_j into P_j
-    auto phase_v = [&](auto cur_c, int jt, f32x16 (&s)[2]) {
-      constexpr int CUR = decltype(cur_c)::value;
-      constexpr std::integral_constant<int, CUR> cur{};
-      // group 1: K_{j+2} into this K stage (its last reader, M(j-1), is behind the barrier)
-      if constexpr (GRP == 1) dma_tile(jt + 2 < ntiles ? jt + 2 : ntiles - 1, kbuf(cur));
+    auto phase_v = [&](auto cur_c, int jt, f32x16 (&s)[2], f32x16 (&sn)[2]) {
       {  // keys past the end of their segment (a segment's partial last tile)
         int sg, t;
         tile_seg(jt, sg, t);
@@ -310,22 +361,28 @@ void joint_attn_mfma_kernel(AttnArgs a) {
               if (st * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= valid) s[st][e] = -INFINITY;
         }
       }
-      float mx = fmaxf(s[0][0], s[1][0]);
+      const float mx = row_max(s);
+      // S and mx hold logit - m_run.  The first tile sets the running max exactly; later the
+      // max is only raised when a logit exceeds it by more than 2^8 (lazy rescale)
+      const float dl = mx * ce;
+      if (jt == 0 || __any(dl > ATT_RESCALE_LOG2)) {
+        const float delta = jt == 0 ? dl : fmaxf(dl, 0.f);
+        if (jt != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          l_run *= alpha;
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
-      mx = xhalf_max(mx) * c;
-      // lazy rescale: keep a stale max while it stays within 2^8 of the true one
-      if (__any(mx > m_run + ATT_RESCALE_LOG2)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+          for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        }
+        m_run += delta;
+        const float d = delta * inv_ce;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[st][e] -= d;
       }
-      float ls0 = 0.f, ls1 = 0.f;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -333,20 +390,25 @@ void joint_attn_mfma_kernel(AttnArgs a) {
           uint32_t w[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i], c, -m_run));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][8 * hh + 2 * i + 1], c, -m_run));
+            const float p0 = __builtin_amdgcn_exp2f(PRESCALE ? s[st][8 * hh + 2 * i] : s[st][8 * hh + 2 * i] * ce);
+            const float p1 = __builtin_amdgcn_exp2f(PRESCALE ? s[st][8 * hh + 2 * i + 1] : s[st][8 * hh + 2 * i + 1] * ce);
             w[i] = cvt_pk_f16(p0, p1);
-            if (i & 1) ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls1, false);
-            else ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[i]), ones, ls0, false);
+            // plain f32 adds in four chains: the dot-product path (v_dot2) shares the matrix
+            // pipe and stalls behind the other wave's MFMAs
+            ls[(i & 1) * 2] += p0;
+            ls[(i & 1) * 2 + 1] += p1;
           }
           pf[st * 2 + hh] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
-      l_run += ls0 + ls1;
-      // likewise pin P, l and m: the exponentials belong to this phase, not the next M phase
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      // the next M phase accumulates S_{j+1} onto minus the running max
+      init_s(sn, -m_run * inv_ce);
+      // likewise pin P, l, m and the initialised accumulators: this VALU work belongs to this
+      // phase, not the next M phase
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w));
-      asm volatile("" ::"v"(l_run), "v"(m_run));
+      asm volatile("" ::"v"(l_run), "v"(m_run), "v"(sn[0]), "v"(sn[1]));
       if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's V loads have landed
       phase_barrier();
     };
@@ -362,17 +424,19 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     if constexpr (GRP == 1) phase_barrier();   // group 1 runs one phase behind
     if constexpr (GRP == 0) dma_tile(0, lds_v0);
     f32x16 sa[2], sb[2];
+    init_s(sa, 0.f);
     compute_s(lds_k0, sa);
+    asm volatile("" ::"v"(sa[0]), "v"(sa[1]));
     phase_barrier();
     int jt = 0;
     for (; jt + 1 < ntiles; jt += 2) {
-      phase_v(S0, jt, sa);
+      phase_v(S0, jt, sa, sb);
       phase_m(S0, jt, sb);
-      phase_v(S1, jt + 1, sb);
+      phase_v(S1, jt + 1, sb, sa);
       phase_m(S1, jt + 1, sa);
     }
     if (jt < ntiles) {
-      phase_v(S0, jt, sa);
+      phase_v(S0, jt, sa, sb);
       phase_m(S0, jt, sb);
     }
     if constexpr (GRP == 0) {   // drain the last (unused) V reload, then match group 1's extra barrier
