@@ -30,6 +30,24 @@ METRIC = "joint-attn TFLOP/s + % bf16 MFMA peak; block tokens/s at 32760+512 tok
 PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the attention kernel at this workload, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+# for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel
+# source they were taken on: a different joint_attention.hip reports traffic as null.
+ATTN_COUNTERS = {"source_sha256": "2c9deed0ab938ea4",
+                 "fetch_kib": 1113838.0, "write_kib": 199696.6, "fetch_scale": 2.0, "write_scale": 1.0}
+
+
+def attention_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "video_diffusion_transformer_mmdit_amd", "csrc", "joint_attention.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    c = ATTN_COUNTERS
+    if not digest.startswith(c["source_sha256"]):
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
+
 
 class Hip:
     """hipEvent plumbing through ctypes (the library records the events on its stream)."""
@@ -200,7 +218,7 @@ def main():
                    "accumulate": "f32", "output_dtype": "f32"},
         "roofline": {"bound": "mfma", "kernel": "joint_attn_mfma_kernel",
                      "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attention_traffic_bytes(),
                      "flops_per_launch": cfg.attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "joint_attention": {"tflops": round(attn_tflops, 1), "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                             "ms": round(attn_ms, 4), "tokens": cfg.n_tokens},
