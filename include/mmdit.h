@@ -150,11 +150,14 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
  *    bf16 (bias_dtype) or NULL.
  * epilogue:
  *   MMDIT_EPI_NONE      y = acc + bias
- *   MMDIT_EPI_GELU      y = GELU(acc + bias), exact erf form
+ *   MMDIT_EPI_GELU      y = GELU(acc + bias), erf form (erf to 1.5e-7 absolute,
+ *                       Abramowitz & Stegun 7.1.26)
  *   MMDIT_EPI_GATED_RES y = res + gate[b] * (acc + bias), b = row / rows_per_batch;
  *                       res [M, N] res_dtype F32 | BF16; gate f32, item b at
- *                       gate + b * gate_stride.
- * y  [M, N] y_dtype F32 | BF16 | F16.  K must be a multiple of 64.  M, N >= 0.
+ *                       gate + b * gate_stride (gate_stride a multiple of 4).
+ * y  [M, N] y_dtype F32 | BF16 | F16.  K must be a multiple of 64, N a multiple of 4,
+ * M, N >= 0; x and w are addressed with 32-bit offsets: (M + 256) * K and (N + 256) * K
+ * elements must stay below 2^30.  Pointers 16-byte aligned.
  * ------------------------------------------------------------------------------- */
 enum mmdit_epilogue { MMDIT_EPI_NONE = 0, MMDIT_EPI_GELU = 1, MMDIT_EPI_GATED_RES = 2 };
 

@@ -100,6 +100,12 @@ def test_linear_modulate_modulation_validation(L):
     p = _fake(0x10000)
     assert L.mmdit_linear(p, p, mm.BF16, None, mm.BF16, _fake(0x900000), mm.BF16, 10, 256, 100,
                           mm.EPI_NONE, None, mm.F32, None, 0, 10, None) == ERR_SHAPE      # K % 64
+    assert L.mmdit_linear(p, p, mm.BF16, None, mm.BF16, _fake(0x900000), mm.BF16, 10, 258, 128,
+                          mm.EPI_NONE, None, mm.F32, None, 0, 10, None) == ERR_SHAPE      # N % 4
+    assert L.mmdit_linear(p, p, mm.BF16, None, mm.BF16, _fake(0x900000), mm.BF16, 1 << 20, 256, 1024,
+                          mm.EPI_NONE, None, mm.F32, None, 0, 10, None) == ERR_SHAPE      # 32-bit offsets
+    assert L.mmdit_linear(p, p, mm.BF16, None, mm.BF16, _fake(0x900000), mm.F32, 10, 256, 128,
+                          mm.EPI_GATED_RES, p, mm.F32, p, 258, 10, None) == ERR_SHAPE     # gate_stride % 4
     assert L.mmdit_linear(p, p, mm.F32, None, mm.BF16, _fake(0x900000), mm.BF16, 10, 256, 128,
                           mm.EPI_NONE, None, mm.F32, None, 0, 10, None) == ERR_DTYPE
     assert L.mmdit_linear(p, p, mm.BF16, None, mm.BF16, _fake(0x900000), mm.F32, 10, 256, 128,

@@ -60,6 +60,13 @@ def build(verbose: bool = True, extra=()) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # a kernel whose host stub the compiler dropped (a deferred host-side diagnostic) links
+    # fine and only fails when loaded: load it here so the build fails instead
+    import ctypes
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -199,7 +199,10 @@ int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, in
                  const void* res, int res_dtype, const float* gate, int64_t gate_stride,
                  int64_t rows_per_batch, void* stream) {
   g_last_error.clear();
-  if (M < 0 || N < 0 || K < 64 || K % 64) return fail(MMDIT_ERR_SHAPE, "linear: need M, N >= 0 and K a positive multiple of 64");
+  if (M < 0 || N < 0 || K < 64 || K % 64 || N % 4)
+    return fail(MMDIT_ERR_SHAPE, "linear: need M, N >= 0, N a multiple of 4 and K a positive multiple of 64");
+  if ((M + 256) * K * 2 >= ((int64_t)1 << 31) || (N + 256) * K * 2 >= ((int64_t)1 << 31))
+    return fail(MMDIT_ERR_SHAPE, "linear: x or w too large for 32-bit buffer offsets");
   if (x_dtype != MMDIT_BF16 && x_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "linear: x/w must be bf16 or f16");
   if (bias && bias_dtype != MMDIT_F32 && bias_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear: bias must be f32 or bf16");
   if (!valid_dtype(y_dtype)) return fail(MMDIT_ERR_DTYPE, "linear: bad y dtype");
@@ -207,7 +210,8 @@ int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, in
   if (epilogue == MMDIT_EPI_GATED_RES) {
     if (res_dtype != MMDIT_F32 && res_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear: res must be f32 or bf16");
     if (y_dtype == MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "linear: gated residual output must be f32 or bf16");
-    if (rows_per_batch < 1 || gate_stride < N) return fail(MMDIT_ERR_SHAPE, "linear: rows_per_batch >= 1 and gate_stride >= N");
+    if (rows_per_batch < 1 || gate_stride < N || gate_stride % 4)
+      return fail(MMDIT_ERR_SHAPE, "linear: rows_per_batch >= 1 and gate_stride >= N, a multiple of 4");
   }
   if (M == 0 || N == 0) return MMDIT_OK;
   if (!x || !w || !y) return fail(MMDIT_ERR_NULL, "linear: x, w, y required");

@@ -4,25 +4,39 @@
 //
 // gfx950 design:
 //   - 256 x 256 output tile per workgroup of 8 wave64s arranged 2 (M) x 4 (N); each wave
-//     owns 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_{bf16,f16} (128 fp32 accumulators).
-//   - K advances 64 at a time through two LDS stages of 2 x 32 KiB (A rows and W rows,
-//     both K-contiguous, so both MFMA operands are plain 16-byte LDS reads).  The next
-//     stage's global loads are issued before the current stage's MFMAs and written to the
-//     other LDS buffer afterwards: one barrier per K step.
-//   - LDS rows are 128 B; the 16-byte chunk index is XOR-swizzled with (row / 2) % 8 so the
-//     32-row fragment reads and the row-wise stores both spread over all 64 banks.
+//     owns 128 x 64 outputs = 4 x 2 tiles of v_mfma_f32_32x32x16_{bf16,f16}.  The MFMA
+//     computes C^T (A operand = W rows, B operand = x rows), so every lane ends up holding
+//     four consecutive output columns of one row and the epilogue stores 8 or 16 bytes at
+//     a time.
+//   - K advances 32 at a time through four LDS stages (x tile and W tile, 16 KiB each, rows
+//     of 64 bytes, both K-contiguous so both MFMA operands are plain 16-byte LDS reads).
+//     Tiles move by LDS-DMA (buffer loads straight into LDS) three stages ahead, issued
+//     between the MFMAs; before the barrier that ends stage k each wave waits only for its
+//     loads of stage k+2, so stage k+1 is visible one stage early and the first fragments
+//     of the next stage are read while the current stage's last MFMAs run.  The eight stage
+//     buffers are distinct LDS objects addressed with compile-time stage indices, so the
+//     wait-count pass never stalls reads of one stage on the DMA into another (one object
+//     per stage: with one per operand tile it loses track and waits for every load).
+//   - LDS chunks are XOR-swizzled with (row / 4) % 4, which puts the 16 rows a 16-lane group
+//     of a fragment read touches on distinct bank groups; a DMA writes 16 bytes per lane in
+//     lane order, so each lane loads the logical chunk that belongs at its physical slot.
+//     Rows past the end of x or W fail the buffer descriptor's range check and arrive as
+//     zeros.
 //   - Tiles are renumbered so that each XCD (workgroups go round-robin over the 8 XCDs) owns
 //     a contiguous run of tiles, and runs are rastered in groups of 8 M-tiles, keeping the
-//     A and W panels that concurrent workgroups of one XCD share inside its L2.
-//   - Epilogues are applied on the accumulators before the only store of y.
+//     x and W panels that concurrent workgroups of one XCD share inside its L2.
+//   - Epilogues (bias, GELU, gated residual) are applied on the accumulators before the only
+//     store of y.
+#include <type_traits>
+
 #include "common.h"
 
 namespace mmdit {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int GTHREADS = 512;
+constexpr int GBM = 256, GBN = 256, GBK = 32;
+constexpr int GTHREADS = 256;
 constexpr int GROUP_M = 8;
-constexpr int G_LDS_STAGE = (GBM + GBN) * GBK * 2;  // bytes per stage (64 KiB)
+constexpr int G_TILE_BYTES = 256 * GBK * 2;   // one operand tile of one stage: 16 KiB
 
 struct GemmArgs {
   GemmProblem p[2];
@@ -31,7 +45,7 @@ struct GemmArgs {
   int64_t N, K;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 template <int IN_DT>
 __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
@@ -43,13 +57,81 @@ __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// erf by the rational approximation of Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (absolute error at most 1.5e-7):
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),  t = 1 / (1 + p x),
+// for x >= 0, extended to x < 0 by symmetry.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.44269504088896340736f);
+  return copysignf(fmaf(-(q * t), e, 1.0f), x);
+}
+
 __device__ __forceinline__ float gelu_erf(float v) {
-  return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+  return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752440f));
+}
+
+// Four consecutive elements of dtype DT (0 f32, 1 bf16, 2 f16) as floats, and back.
+template <int DT>
+__device__ __forceinline__ void load4(const void* base, int64_t idx, float (&v)[4]) {
+  if constexpr (DT == MMDIT_F32) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    if constexpr (DT == MMDIT_BF16) {
+      v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x); v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
+    } else {
+      v[0] = lo_f16(w.x); v[1] = hi_f16(w.x); v[2] = lo_f16(w.y); v[3] = hi_f16(w.y);
+    }
+  }
+}
+template <int DT>
+__device__ __forceinline__ void store4(void* base, int64_t idx, const float (&v)[4]) {
+  if constexpr (DT == MMDIT_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (DT == MMDIT_BF16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
+        make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
+  }
+}
+
+// Buffer descriptor over `bytes` bytes at `p`, built from readfirstlane'd words so that it
+// provably lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* p, int64_t bytes) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  const int num = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, num,
+                                           0x00020000);
+}
+
+// An LDS-DMA destination passed through an opaque SGPR copy: the compiler then cannot tell
+// which LDS object the load writes and leaves every wait for it to the explicit per-stage
+// waits of the kernel (otherwise it drains all stages in flight at each loop iteration).
+__device__ __forceinline__ __attribute__((address_space(3))) void* opaque_lds(__attribute__((address_space(3))) void* p) {
+  uint32_t a = (uint32_t)(uintptr_t)p;
+  asm volatile("" : "+s"(a));
+  return (__attribute__((address_space(3))) void*)(uintptr_t)a;
 }
 
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT>
-__global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * G_LDS_STAGE];
+__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(GemmArgs args) {
+  // one LDS object per stage: x tile, then W tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s0[2 * G_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s1[2 * G_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s2[2 * G_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s3[2 * G_TILE_BYTES];
 
   // ---- tile selection: XCD-contiguous runs, grouped raster inside a problem
   int64_t t = blockIdx.x;
@@ -66,100 +148,172 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(GemmArgs args) {
   const int64_t in_grp = t - grp * per_group;
   const int64_t tm = first_m + in_grp % gm;
   const int64_t tn = in_grp / gm;
-  const int64_t m0 = tm * GBM, n0 = tn * GBN;
+  const int m0 = (int)(tm * GBM), n0 = (int)(tn * GBN);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
 
-  const uint16_t* X = static_cast<const uint16_t*>(P.x);
-  const uint16_t* W = static_cast<const uint16_t*>(P.w);
-
-  // ---- global -> register staging: 4 A chunks + 4 W chunks of 16 B per thread
-  uint4 ra[4], rb[4];
-  auto gload = [&](int64_t k0) {
+  // ---- LDS-DMA: wave w fills rows 64w .. 64w+63 of the x tile and of the W tile with four
+  // 1 KiB loads each (lane l -> row 64w + 16i + l/4, physical chunk l % 4).  The immediate
+  // offset i * 1024 moves the LDS destination and the source alike and is taken back out of
+  // the per-lane offset, so all loads of a tile share one LDS base; the K position goes in
+  // the scalar offset.
+  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * 2);
+  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * 2);
+  int xo[4], wo[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + GTHREADS * i;
-      const int r = ch >> 3, cc = ch & 7;
-      const int64_t am = m0 + r, bn = n0 + r;
-      ra[i] = am < M ? *reinterpret_cast<const uint4*>(X + am * K + k0 + cc * 8) : make_uint4(0, 0, 0, 0);
-      rb[i] = bn < N ? *reinterpret_cast<const uint4*>(W + bn * K + k0 + cc * 8) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int row = 64 * wave + 16 * i + (lane >> 2);
+    const int lc = (lane & 3) ^ swz(row);
+    xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - i * 1024;
+    wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - i * 1024;
+  }
+  auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
+    const int so = k0 * 2;
+    auto* lx = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 4096));
+    auto* lw = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 4096));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], so, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[3], so, 3072, 0);
   };
-  auto sstore = [&](int buf) {
-    uint8_t* sa = lds + buf * G_LDS_STAGE;
-    uint8_t* sb = sa + GBM * GBK * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + GTHREADS * i;
-      const int r = ch >> 3, cc = ch & 7;
-      const int off = r * 128 + ((cc ^ swz(r)) << 4);
-      *reinterpret_cast<uint4*>(sa + off) = ra[i];
-      *reinterpret_cast<uint4*>(sb + off) = rb[i];
-    }
+  auto xbuf = [&](auto s) -> uint8_t* {
+    constexpr int v = decltype(s)::value;
+    if constexpr (v == 0) return lds_s0; else if constexpr (v == 1) return lds_s1;
+    else if constexpr (v == 2) return lds_s2; else return lds_s3;
   };
+  auto wbuf = [&](auto s) -> uint8_t* { return xbuf(s) + G_TILE_BYTES; };
+  constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
+  constexpr std::integral_constant<int, 2> S2{};
+  constexpr std::integral_constant<int, 3> S3{};
 
-  f32x16 acc[4][2];
+  // ---- fragment reads: row base + l32 of a tile, logical chunk 2 ks + g; the swizzle of
+  // row base + l32 (base a multiple of 32) depends on l32 only
+  int cofs[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int ks = 0; ks < 2; ++ks) cofs[ks] = l32 * 64 + (((2 * ks + g) ^ swz(l32)) << 4);
+
+  f32x16 acc[4][4];   // [n tile][m tile] of C^T
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
 
   const int nk = (int)(K / GBK);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * GBK);
-    const uint8_t* sa = lds + buf * G_LDS_STAGE;
-    const uint8_t* sb = sa + GBM * GBK * 2;
+  auto gbarrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Fragments of k16 slice 0 of the current stage, read during the previous stage.
+  uint4 wf0[4], xf0[4];
+  auto read_slice = [&](const uint8_t* xs, const uint8_t* ws, int ks, uint4 (&wf)[4], uint4 (&xf)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
-      uint4 af[4], bfr[2];
-      const int chunk = 2 * ks + g;
+    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const uint4*>(ws + (wn * 128 + j * 32) * 64 + cofs[ks]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const uint4*>(xs + (wm * 128 + i * 32) * 64 + cofs[ks]);
+  };
+  auto mma = [&](const uint4 (&wf)[4], const uint4 (&xf)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wf[j], xf[i], acc[j][i]);
+  };
+  // One K stage.  At its start stages kt and kt+1 are in LDS for every wave.  MAIN: stage
+  // kt+3 exists (load it; at the end wait with its loads in flight); otherwise the tail
+  // decides at run time.
+  auto step = [&](auto cur_c, auto main_c, int kt) {
+    constexpr int CUR = decltype(cur_c)::value;
+    constexpr bool MAIN = decltype(main_c)::value;
+    constexpr std::integral_constant<int, CUR> cur{};
+    constexpr std::integral_constant<int, (CUR + 1) & 3> next{};
+    constexpr std::integral_constant<int, (CUR + 3) & 3> ahead{};
+    // stage kt+3 goes into the buffers stage kt-1 used (every wave has passed the barrier
+    // that ended stage kt-1)
+    if (MAIN || kt + 3 < nk) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * GBK);
+    uint4 wf1[4], xf1[4];
+    read_slice(xbuf(cur), wbuf(cur), 1, wf1, xf1);
+    mma(wf0, xf0);
+    // slice 0 of the next stage is read while this stage's second slice runs
+    if (MAIN || kt + 1 < nk) read_slice(xbuf(next), wbuf(next), 0, wf0, xf0);
+    mma(wf1, xf1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if ((i < 4) || (i >= 16 && i < 24)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      if (MAIN && i >= 4 && i < 12) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
+    }
+    // this wave's loads of stage kt+2 have landed once at most the eight loads of stage kt+3
+    // are outstanding; after the barrier stage kt+2 is in LDS for everyone
+    if (MAIN || kt + 3 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
+    gbarrier();
+  };
+  constexpr std::true_type MAIN{};
+  constexpr std::false_type TAIL{};
+
+  dma(xbuf(S0), wbuf(S0), 0);
+  if (1 < nk) dma(xbuf(S1), wbuf(S1), GBK);
+  if (2 < nk) dma(xbuf(S2), wbuf(S2), 2 * GBK);
+  // stages 0 and 1 must be in LDS; stage 2 may still be in flight
+  if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  gbarrier();
+  read_slice(xbuf(S0), wbuf(S0), 0, wf0, xf0);
+  int kt = 0;
+  for (; kt + 6 < nk; kt += 4) {   // every step of the group has its stage kt+3
+    step(S0, MAIN, kt);
+    step(S1, MAIN, kt + 1);
+    step(S2, MAIN, kt + 2);
+    step(S3, MAIN, kt + 3);
+  }
+  // at most six stages remain (kt % 4 == 0)
+  if (kt < nk) step(S0, TAIL, kt);
+  if (kt + 1 < nk) step(S1, TAIL, kt + 1);
+  if (kt + 2 < nk) step(S2, TAIL, kt + 2);
+  if (kt + 3 < nk) step(S3, TAIL, kt + 3);
+  if (kt + 4 < nk) step(S0, TAIL, kt + 4);
+  if (kt + 5 < nk) step(S1, TAIL, kt + 5);
+
+  // ---- epilogue: lane holds C^T rows (output columns) 8 (e/4) + 4 g + e%4 of each 32 x 32
+  // tile at output row l32: four consecutive columns per e/4
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int64_t n = n0 + wn * 128 + j * 32 + 8 * e4 + 4 * g;
+      if (n >= N) continue;
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if (P.bias) load4<BIAS_DT>(P.bias, n, bias);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + i * 32 + l32;
-        af[i] = *reinterpret_cast<const uint4*>(sa + r * 128 + ((chunk ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + l32;
-        bfr[j] = *reinterpret_cast<const uint4*>(sb + r * 128 + ((chunk ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<IN_DT>(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane holds rows 8*(e/4) + 4*g + e%4 of each 32 x 32 tile, column l32
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + wn * 64 + j * 32 + l32;
-    if (n >= N) continue;
-    const float bias = P.bias ? load1<BIAS_DT>(P.bias, n) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+        const int64_t m = m0 + wm * 128 + i * 32 + l32;
         if (m >= M) continue;
-        float v = acc[i][j][e] + bias;
-        if constexpr (EPI == MMDIT_EPI_GELU) v = gelu_erf(v);
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = acc[j][i][4 * e4 + q] + bias[q];
+          if constexpr (EPI == MMDIT_EPI_GELU) v[q] = gelu_erf(v[q]);
+        }
         if constexpr (EPI == MMDIT_EPI_GATED_RES) {
           const int64_t b = m / P.rows_per_batch;
-          v = load1<RES_DT>(P.res, m * N + n) + P.gate[b * P.gate_stride + n] * v;
+          float r[4], gt[4];
+          load4<RES_DT>(P.res, m * N + n, r);
+          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(gt[q], v[q], r[q]);
         }
-        store1<Y_DT>(P.y, m * N + n, v);
+        store4<Y_DT>(P.y, m * N + n, v);
       }
     }
   }
@@ -175,7 +329,12 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   GemmArgs a{};
   const int64_t nTn = (N + GBN - 1) / GBN;
   int64_t tiles[2] = {0, 0};
+  // x and W are addressed through 32-bit buffer offsets, a tile's rows may run 256 past M
+  if (N % 4 || (N + GBN) * K * 2 >= ((int64_t)1 << 31))
+    return fail(MMDIT_ERR_SHAPE, "linear: need N a multiple of 4 and (N + 256) * K * 2 < 2^31");
   for (int i = 0; i < nprobs; ++i) {
+    if ((probs[i].M + GBM) * K * 2 >= ((int64_t)1 << 31))
+      return fail(MMDIT_ERR_SHAPE, "linear: need (M + 256) * K * 2 < 2^31");
     a.p[i] = probs[i];
     tiles[i] = ((probs[i].M + GBM - 1) / GBM) * nTn;
   }
