@@ -26,7 +26,17 @@ design notes of the repository):
   interleaved pairs (2j, 2j+1) inside each band; r9 each band has its own frequency ladder
   base^(-2j/d_band); r10 bands in t, h, w order; r11 0-based integer positions; r12 tokens
   flattened (t, h, w) row-major, w fastest; r13 no YaRN; r14 no attention mask;
-  r16 exact erf GELU; r18 parity metric max|err| / rms(oracle) per output tensor.
+  r16 exact erf GELU; r18 parity metric max|err| / rms(oracle) per output tensor;
+  r20 timestep sinusoid: cosines of the first half of the frequencies, then sines,
+  frequency j = max_period^(-j/half), max_period 10000, the timestep value taken as given;
+  r21 the timestep MLP and the bottleneck Linear carry biases, SiLU is x*sigmoid(x);
+  r22 Lite merge concatenates the 2x2 neighbours in (dh, dw) row-major order, each
+  neighbour's C channels contiguous; the unpatchify output splits the same way;
+  r23 Lite merge/unpatchify is defined for even H and W only (odd grids are rejected).
+
+Further sources for the Lite parts: [Vimoo] section 2.4 "Vimoo 1.0-Lite" (2x2 hidden-space
+merge 4C -> C after the input projection, unpatchify C -> 4C after the backbone, time axis
+untouched; the shared timestep bottleneck narrowed from 1536 to 16).
 
 Tensor conventions: tokens [B, N, ...]; heads split as [B, N, H, D] with head-major
 channels (channel c = head * D + d).
@@ -285,6 +295,87 @@ def block_forward(x_vis: np.ndarray, x_cond: np.ndarray, tvec: np.ndarray,
             res[f"x1_{s}"] = x1
             res[f"h2_{s}"] = h2
     return res
+
+
+# ------------------------------------------------------- timestep path  [Vimoo 2.2, 2.4]
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU x * sigmoid(x) (r21)."""
+    from scipy.special import expit
+    return x * expit(x)
+
+
+def timestep_sinusoid(t: np.ndarray, dim: int = 256, max_period: float = 10000.0) -> np.ndarray:
+    """Sinusoidal embedding of each timestep: [B] -> [B, dim] (r20).
+
+    With half = dim/2 frequencies w_j = max_period^(-j/half), j = 0..half-1, the first half of
+    the vector holds cos(t*w_j) and the second half sin(t*w_j)."""
+    half = dim // 2
+    j = np.arange(half, dtype=np.float64)
+    freqs = max_period ** (-j / half)
+    ang = np.asarray(t, dtype=np.float64)[:, None] * freqs[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
+
+
+def timestep_path(t: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: np.ndarray,
+                  w3: np.ndarray, b3: np.ndarray, dim: int = 256,
+                  max_period: float = 10000.0) -> Dict[str, np.ndarray]:
+    """Timestep conditioning [Vimoo 2.2]: the 256-d sinusoid goes through a two-layer MLP with
+    a SiLU between the layers to the 3072-d representation ``temb``; SiLU and one Linear then
+    give the shared bottleneck ``tvec`` (1536-d, 16-d in Lite [Vimoo 2.4]).
+
+    w1 [Dh, dim], w2 [Dh, Dh], w3 [Dt, Dh] in nn.Linear layout.  Returns ``hidden`` (the first
+    layer's output before its SiLU), ``temb`` and ``tvec``."""
+    e = timestep_sinusoid(t, dim, max_period)
+    hidden = linear(e, w1, b1)
+    temb = linear(silu(hidden), w2, b2)
+    tvec = linear(silu(temb), w3, b3)
+    return {"hidden": hidden, "temb": temb, "tvec": tvec}
+
+
+# ------------------------------------------------- Lite 2x2 hidden-space merge  [Vimoo 2.4]
+
+NEIGHBOURS = ((0, 0), (0, 1), (1, 0), (1, 1))   # r22: (dh, dw) row-major
+
+
+def _check_even(grid: Tuple[int, int, int]):
+    if grid[1] % 2 or grid[2] % 2:
+        raise ValueError(f"Lite 2x2 merge needs an even H and W grid, got {grid} (r23)")
+
+
+def lite_merge_gather(x: np.ndarray, grid: Tuple[int, int, int]) -> np.ndarray:
+    """[B, T*H*W, C] visual tokens -> [B, T*(H/2)*(W/2), 4C]: for each 2x2 spatial region of
+    each frame, the four neighbours' vectors side by side (r22).  Time is not merged."""
+    _check_even(grid)
+    t_n, h_n, w_n = grid
+    b, n, c = x.shape
+    x5 = x.reshape(b, t_n, h_n, w_n, c)
+    parts = [x5[:, :, dh::2, dw::2, :] for dh, dw in NEIGHBOURS]     # each [B, T, H/2, W/2, C]
+    return np.concatenate(parts, axis=-1).reshape(b, t_n * (h_n // 2) * (w_n // 2), 4 * c)
+
+
+def lite_merge(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray],
+               grid: Tuple[int, int, int]) -> np.ndarray:
+    """Lite merge: concatenate each 2x2 neighbourhood, then Linear 4C -> C.  w [C, 4C]."""
+    return linear(lite_merge_gather(x, grid), w, b)
+
+
+def lite_unpatchify(y: np.ndarray, w: np.ndarray, b: Optional[np.ndarray],
+                    grid: Tuple[int, int, int]) -> np.ndarray:
+    """Lite unpatchify: Linear C -> 4C expands each merged token into four position-specific
+    vectors, placed back at the 2x2 positions in the merge's order.  y [B, T*(H/2)*(W/2), C],
+    w [4C, C]; ``grid`` is the full (T, H, W) grid.  Returns [B, T*H*W, C]."""
+    _check_even(grid)
+    t_n, h_n, w_n = grid
+    z = linear(y, w, b)
+    bsz, _, c4 = z.shape
+    c = c4 // 4
+    z5 = z.reshape(bsz, t_n, h_n // 2, w_n // 2, c4)
+    out = np.zeros((bsz, t_n, h_n, w_n, c), dtype=z.dtype)
+    for s, (dh, dw) in enumerate(NEIGHBOURS):
+        out[:, :, dh::2, dw::2, :] = z5[..., s * c:(s + 1) * c]
+    return out.reshape(bsz, t_n * h_n * w_n, c)
 
 
 # ------------------------------------------------------------------ parity metric (r18)

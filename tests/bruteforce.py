@@ -144,3 +144,60 @@ def block_forward(x_vis, x_cond, tvec, w_vis, w_cond, grid, heads, ln_eps, qk_ep
             res.append([xv + g * yv for xv, g, yv in zip(x1, gate_f, y)])
         outs[s] = res
     return outs["vis"], outs["cond"]
+
+
+# ------------------------------------------------------------------ timestep path, Lite merge
+def sinusoid_vec(t, dim, max_period=10000.0):
+    """One timestep's embedding: entry i < dim/2 is cos(t * f_i), entry dim/2 + i is
+    sin(t * f_i), with f_i = max_period ** (-i / (dim/2))."""
+    half = dim // 2
+    out = [0.0] * dim
+    for i in range(half):
+        f = max_period ** (-i / half)
+        out[i] = math.cos(t * f)
+        out[half + i] = math.sin(t * f)
+    return out
+
+
+def silu_scalar(x):
+    return x / (1.0 + math.exp(-x)) if x > -700 else 0.0
+
+
+def timestep_path(t, w1, b1, w2, b2, w3, b3, dim, max_period=10000.0):
+    """Returns (hidden, temb, tvec) lists for one timestep value."""
+    hidden = matvec(w1, sinusoid_vec(t, dim, max_period), b1)
+    temb = matvec(w2, [silu_scalar(v) for v in hidden], b2)
+    tvec = matvec(w3, [silu_scalar(v) for v in temb], b3)
+    return hidden, temb, tvec
+
+
+def lite_merge(x, w, b, grid):
+    """x: [T*H*W][C] lists (w fastest).  Merged token (t, i, j) reads the four tokens
+    (t, 2i+dh, 2j+dw), (dh, dw) in row-major order, side by side, then w [C][4C] + b."""
+    tt, hh, ww = grid
+    out = []
+    for t in range(tt):
+        for i in range(hh // 2):
+            for j in range(ww // 2):
+                cat = []
+                for dh in range(2):
+                    for dw in range(2):
+                        cat += x[(t * hh + 2 * i + dh) * ww + 2 * j + dw]
+                out.append(matvec(w, cat, b))
+    return out
+
+
+def lite_unpatchify(y, w, b, grid):
+    """y: [T*(H/2)*(W/2)][C]; w [4C][C].  Token (t, h, w) of the output takes part
+    (h % 2) * 2 + (w % 2) of merged token (t, h // 2, w // 2)'s expansion."""
+    tt, hh, ww = grid
+    c = len(y[0])
+    out = []
+    for t in range(tt):
+        for h in range(hh):
+            for x_ in range(ww):
+                m = (t * (hh // 2) + h // 2) * (ww // 2) + x_ // 2
+                z = matvec(w, y[m], b)
+                part = (h % 2) * 2 + (x_ % 2)
+                out.append(z[part * c:(part + 1) * c])
+    return out

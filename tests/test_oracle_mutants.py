@@ -16,7 +16,8 @@ from tests import test_oracle_pins as pins
 
 ORIG = {name: getattr(om, name) for name in
         ("rope_angles", "rope_rotate", "token_positions", "rms_norm_heads", "softmax_attention",
-         "modulate", "layer_norm", "linear", "gelu", "modulation", "joint_attention")}
+         "modulate", "layer_norm", "linear", "gelu", "modulation", "joint_attention",
+         "timestep_sinusoid", "silu", "timestep_path", "lite_merge_gather", "lite_unpatchify")}
 
 
 def _rope_sign(x, angles):
@@ -115,6 +116,56 @@ def _joint_drop_cond_keys(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond, **kw):
     return ORIG["joint_attention"](q_vis, k_vis, v_vis, q_cond, e, v_cond[:, :0], **kw)
 
 
+def _sinusoid_sin_first(t, dim=256, max_period=10000.0):
+    e = ORIG["timestep_sinusoid"](t, dim, max_period)
+    return np.concatenate([e[:, dim // 2:], e[:, :dim // 2]], axis=1)
+
+
+def _sinusoid_half_minus_one(t, dim=256, max_period=10000.0):
+    half = dim // 2
+    ang = np.asarray(t, dtype=np.float64)[:, None] * max_period ** (-np.arange(half) / (half - 1))[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
+
+
+def _silu_sigmoid_only(x):
+    return ORIG["silu"](x) / np.where(x == 0, 1.0, x) * (x != 0)
+
+
+def _timestep_no_inner_silu(t, w1, b1, w2, b2, w3, b3, dim=256, max_period=10000.0):
+    e = om.timestep_sinusoid(t, dim, max_period)
+    hidden = om.linear(e, w1, b1)
+    temb = om.linear(hidden, w2, b2)
+    return {"hidden": hidden, "temb": temb, "tvec": om.linear(om.silu(temb), w3, b3)}
+
+
+def _timestep_no_outer_silu(t, w1, b1, w2, b2, w3, b3, dim=256, max_period=10000.0):
+    r = ORIG["timestep_path"](t, w1, b1, w2, b2, w3, b3, dim, max_period)
+    r["tvec"] = om.linear(r["temb"], w3, b3)
+    return r
+
+
+def _merge_column_major(x, grid):
+    t_n, h_n, w_n = grid
+    b, n, c = x.shape
+    x5 = x.reshape(b, t_n, h_n, w_n, c)
+    parts = [x5[:, :, dh::2, dw::2, :] for dw in (0, 1) for dh in (0, 1)]
+    return np.concatenate(parts, axis=-1).reshape(b, -1, 4 * c)
+
+
+def _merge_channel_interleaved(x, grid):
+    g = ORIG["lite_merge_gather"](x, grid)
+    b, m, c4 = g.shape
+    return g.reshape(b, m, 4, c4 // 4).transpose(0, 1, 3, 2).reshape(b, m, c4)
+
+
+def _unpatchify_swapped_w(y, w, b, grid):
+    out = ORIG["lite_unpatchify"](y, w, b, grid)
+    t_n, h_n, w_n = grid
+    o5 = out.reshape(out.shape[0], t_n, h_n, w_n, -1)
+    o5 = o5.reshape(out.shape[0], t_n, h_n, w_n // 2, 2, -1)[:, :, :, :, ::-1, :]
+    return o5.reshape(out.shape)
+
+
 MUTANTS = {
     "rope_sign": ("rope_rotate", _rope_sign),
     "rope_band_order": ("rope_angles", _band_order),
@@ -134,6 +185,14 @@ MUTANTS = {
     "gates_swapped": ("modulation", _modulation_swapped),
     "shift_scale_swapped": ("modulation", _modulation_order),
     "cond_keys_dropped": ("joint_attention", _joint_drop_cond_keys),
+    "sinusoid_sin_first": ("timestep_sinusoid", _sinusoid_sin_first),
+    "sinusoid_half_minus_one": ("timestep_sinusoid", _sinusoid_half_minus_one),
+    "silu_sigmoid_only": ("silu", _silu_sigmoid_only),
+    "timestep_no_inner_silu": ("timestep_path", _timestep_no_inner_silu),
+    "timestep_no_outer_silu": ("timestep_path", _timestep_no_outer_silu),
+    "merge_column_major": ("lite_merge_gather", _merge_column_major),
+    "merge_channel_interleaved": ("lite_merge_gather", _merge_channel_interleaved),
+    "unpatchify_swapped_w": ("lite_unpatchify", _unpatchify_swapped_w),
 }
 
 PIN_TESTS = [f for name, f in inspect.getmembers(pins, inspect.isfunction) if name.startswith("test_")]

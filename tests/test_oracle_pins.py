@@ -375,3 +375,170 @@ def test_parity_metric():
     ref = np.array([3.0, -4.0])          # rms = sqrt(12.5)
     got = np.array([3.5, -4.0])
     assert math.isclose(oracle.rel_max_err(got, ref), 0.5 / math.sqrt(12.5))
+
+
+# ------------------------------------------------------------------ timestep path
+
+
+def test_timestep_sinusoid_closed_forms():
+    """At t = 0 every cosine is 1 and every sine 0; each (cos, sin) pair lies on the unit
+    circle; frequency 0 is 1 rad per unit of t, frequency half/2 is max_period^(-1/2)."""
+    e0 = oracle.timestep_sinusoid(np.array([0.0]), 256)
+    assert e0.shape == (1, 256)
+    assert np.all(e0[0, :128] == 1.0) and np.all(e0[0, 128:] == 0.0)
+    t = np.array([1.0, 37.5, 999.0])
+    e = oracle.timestep_sinusoid(t, 256)
+    np.testing.assert_allclose(e[:, :128] ** 2 + e[:, 128:] ** 2, 1.0, atol=1e-14)
+    assert math.isclose(e[0, 0], math.cos(1.0), abs_tol=1e-15)           # 0.5403023...
+    assert math.isclose(e[0, 128], math.sin(1.0), abs_tol=1e-15)         # 0.8414709...
+    assert math.isclose(e[2, 64], math.cos(999.0 * 0.01), abs_tol=1e-14)  # 10000^(-64/128)
+    assert math.isclose(e[1, 128 + 127], math.sin(37.5 * 10000 ** (-127 / 128)), abs_tol=1e-15)
+    # the same embedding, entry by entry, from the brute-force loops
+    for i, tv in enumerate(t):
+        np.testing.assert_allclose(e[i], bf.sinusoid_vec(float(tv), 256), atol=1e-13)
+
+
+def test_silu_identities():
+    x = np.array([-30.0, -2.0, -0.5, 0.0, 0.5, 1.0, 2.0, 30.0])
+    s = oracle.silu(x)
+    assert s[3] == 0.0
+    assert math.isclose(s[5], 1.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)   # 0.7310585...
+    np.testing.assert_allclose(s - oracle.silu(-x), x, atol=1e-14)           # silu(x) - silu(-x) = x
+    assert abs(s[-1] - 30.0) < 1e-11 and abs(s[0]) < 1e-11
+    np.testing.assert_allclose(s, F.silu(torch.from_numpy(x)).numpy(), rtol=1e-15, atol=1e-300)
+
+
+def _timestep_weights(rng, dim, dh, dt, std=0.3):
+    return (rng.standard_normal((dh, dim)) * std, rng.standard_normal(dh) * std,
+            rng.standard_normal((dh, dh)) * std, rng.standard_normal(dh) * std,
+            rng.standard_normal((dt, dh)) * std, rng.standard_normal(dt) * std)
+
+
+def test_timestep_path_against_bruteforce_loops():
+    rng = np.random.default_rng(77)
+    dim, dh, dt = 16, 12, 5
+    ws = _timestep_weights(rng, dim, dh, dt)
+    t = np.array([0.0, 3.0, 250.0, 999.0])
+    got = oracle.timestep_path(t, *ws, dim=dim)
+    assert got["temb"].shape == (4, dh) and got["tvec"].shape == (4, dt)
+    lists = [w.tolist() for w in ws]
+    for i, tv in enumerate(t):
+        hid, temb, tvec = bf.timestep_path(float(tv), *lists, dim=dim)
+        np.testing.assert_allclose(got["hidden"][i], hid, atol=1e-12)
+        np.testing.assert_allclose(got["temb"][i], temb, atol=1e-12)
+        np.testing.assert_allclose(got["tvec"][i], tvec, atol=1e-12)
+
+
+def test_timestep_path_special_cases():
+    """Zero weights give the biases through; a first layer that makes every pre-activation
+    very negative switches the MLP's SiLU off, so temb = b2 exactly up to exp underflow."""
+    rng = np.random.default_rng(78)
+    dim, dh, dt = 8, 6, 3
+    w1, b1, w2, b2, w3, b3 = _timestep_weights(rng, dim, dh, dt)
+    z = oracle.timestep_path(np.array([5.0]), 0 * w1, b1, 0 * w2, b2, 0 * w3, b3, dim=dim)
+    np.testing.assert_allclose(z["hidden"][0], b1, atol=0)
+    np.testing.assert_allclose(z["temb"][0], b2, atol=0)
+    np.testing.assert_allclose(z["tvec"][0], b3, atol=0)
+    off = oracle.timestep_path(np.array([5.0]), 0 * w1, np.full(dh, -800.0), w2, b2, w3, b3, dim=dim)
+    np.testing.assert_allclose(off["temb"][0], b2, atol=1e-300)
+    sil = b2 / (1.0 + np.exp(-b2))
+    np.testing.assert_allclose(off["tvec"][0], w3 @ sil + b3, rtol=1e-14)
+
+
+def test_lite_timestep_bottleneck_is_sixteen_wide():
+    """Vimoo 1.0 section 2.4: Lite keeps the structure and narrows the shared bottleneck to
+    16; the shared projection then has 3072*16 + 16 parameters, the per-(block, stream)
+    Linears 80 * (6*3072*16 + 6*3072), 25,116,688 in total (printed as 0.025 billion)."""
+    rng = np.random.default_rng(79)
+    ws = _timestep_weights(rng, 256, 3072, 16, std=0.02)
+    out = oracle.timestep_path(np.array([500.0]), *ws)
+    assert out["temb"].shape == (1, 3072) and out["tvec"].shape == (1, 16)
+    total = ws[4].size + ws[5].size + 80 * oracle.modulation_param_count(3072, 16)
+    assert total == 25_116_688
+
+
+# ------------------------------------------------------------------ Lite 2x2 merge
+
+
+def _coord_tokens(grid, c):
+    """Tokens whose channels spell out their own (t, h, w) coordinates."""
+    pos = oracle.token_positions(grid).astype(np.float64)
+    x = np.zeros((1, pos.shape[0], c))
+    x[0, :, 0], x[0, :, 1], x[0, :, 2] = pos[:, 0], pos[:, 1], pos[:, 2]
+    return x
+
+
+def test_lite_merge_places_each_neighbour_in_its_slot():
+    """A selector weight that copies slot s of the 4C concatenation back to C channels must
+    return, for merged token (t, i, j), the token at (t, 2i + dh, 2j + dw), with slot
+    s = 2*dh + dw (row-major neighbours)."""
+    grid, c = (2, 4, 6), 4
+    x = _coord_tokens(grid, c)
+    eye = np.eye(c)
+    for s, (dh, dw) in enumerate(((0, 0), (0, 1), (1, 0), (1, 1))):
+        sel = np.zeros((c, 4 * c))
+        sel[:, s * c:(s + 1) * c] = eye
+        y = oracle.lite_merge(x, sel, None, grid)
+        assert y.shape == (1, 2 * 2 * 3, c)
+        m = 0
+        for t in range(2):
+            for i in range(2):
+                for j in range(3):
+                    assert tuple(y[0, m, :3]) == (t, 2 * i + dh, 2 * j + dw)
+                    m += 1
+
+
+def test_lite_merge_mean_weights_give_2x2_average_pool():
+    grid, c = (3, 4, 6), 5
+    x = np.random.default_rng(80).standard_normal((2, 3 * 4 * 6, c))
+    w = np.concatenate([np.eye(c)] * 4, axis=1) / 4.0
+    y = oracle.lite_merge(x, w, None, grid)
+    pool = F.avg_pool2d(torch.from_numpy(x).reshape(2, 3, 4, 6, c).permute(0, 1, 4, 2, 3)
+                        .reshape(6, c, 4, 6), 2)                        # [B*T, C, 2, 3]
+    ref = pool.reshape(2, 3, c, 2, 3).permute(0, 1, 3, 4, 2).reshape(2, 18, c).numpy()
+    np.testing.assert_allclose(y, ref, atol=1e-14)
+
+
+def test_lite_unpatchify_stacked_identity_is_nearest_upsample():
+    grid, c = (2, 4, 6), 3
+    y = np.random.default_rng(81).standard_normal((1, 2 * 2 * 3, c))
+    w = np.concatenate([np.eye(c)] * 4, axis=0)
+    out = oracle.lite_unpatchify(y, w, None, grid)
+    up = F.interpolate(torch.from_numpy(y).reshape(1, 2, 2, 3, c).permute(0, 1, 4, 2, 3)
+                       .reshape(2, c, 2, 3), scale_factor=2, mode="nearest")
+    ref = up.reshape(1, 2, c, 4, 6).permute(0, 1, 3, 4, 2).reshape(1, 48, c).numpy()
+    np.testing.assert_array_equal(out, ref)
+
+
+def test_lite_merge_and_unpatchify_against_bruteforce_loops():
+    rng = np.random.default_rng(82)
+    grid, c = (2, 2, 4), 3
+    n = 16
+    x = rng.standard_normal((1, n, c))
+    wm, bm = rng.standard_normal((c, 4 * c)), rng.standard_normal(c)
+    wu, bu = rng.standard_normal((4 * c, c)), rng.standard_normal(4 * c)
+    y = oracle.lite_merge(x, wm, bm, grid)
+    np.testing.assert_allclose(y[0], bf.lite_merge(x[0].tolist(), wm.tolist(), bm.tolist(), grid), atol=1e-12)
+    out = oracle.lite_unpatchify(y, wu, bu, grid)
+    np.testing.assert_allclose(out[0], bf.lite_unpatchify(y[0].tolist(), wu.tolist(), bu.tolist(), grid),
+                               atol=1e-12)
+
+
+def test_lite_selector_round_trip_and_odd_grid():
+    """Merge that keeps all four slots (an identity on 4C) followed by an unpatchify that
+    copies slot s into output position s gives every token back its own vector, in the slot
+    of its position inside the 2x2 region.  The pages define the merge only for even grids,
+    so H = 45 (the 720p grid) is refused."""
+    grid, c = (2, 4, 6), 4
+    x = np.random.default_rng(83).standard_normal((1, 48, c))
+    y = oracle.lite_merge(x, np.eye(4 * c), None, grid)          # [1, 12, 4C]
+    wu = np.zeros((4 * 4 * c, 4 * c))
+    for s in range(4):
+        wu[s * 4 * c + s * c: s * 4 * c + (s + 1) * c, s * c:(s + 1) * c] = np.eye(c)
+    back = oracle.lite_unpatchify(y, wu, None, grid)              # [1, 48, 4C]
+    pos = oracle.token_positions(grid)
+    slot = (pos[:, 1] % 2) * 2 + pos[:, 2] % 2
+    picked = np.stack([back[0, n, s * c:(s + 1) * c] for n, s in enumerate(slot)])
+    np.testing.assert_array_equal(picked, x[0])
+    with pytest.raises(ValueError):
+        oracle.lite_merge_gather(np.zeros((1, 21 * 45 * 80, 2)), (21, 45, 80))
