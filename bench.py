@@ -120,6 +120,53 @@ def cpu_baseline(cfg, raw):
                        f"{per_row * 1e3:.1f} ms/row x {cfg.n_tokens} rows = {t_full:.0f} s")}
 
 
+def time_calls(fn, reps: int = 20, warm: int = 3) -> float:
+    """Average ms of fn() over reps calls on torch's current stream (the library launches on
+    it), from one pair of events around the loop."""
+    import torch
+    for _ in range(warm):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def next_rows(dev):
+    """The conditioning path that produces tvec (full 1536-d and Lite 16-d bottleneck) and the
+    Lite 2x2 merge / unpatchify at 480p, timed on their own (not part of the block step)."""
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    import workloads as wl
+    out = {}
+    for cfg in (wl.TIMESTEP_FULL, wl.TIMESTEP_LITE):
+        raw = wl.timestep_inputs(cfg)
+        t = torch.from_numpy(raw["t"]).to(dev)
+        ws = [torch.from_numpy(raw[k].view(np.int16)).view(torch.bfloat16).to(dev) for k in wl.TIMESTEP_WEIGHTS]
+        bufs = mm.timestep_embed(t, *ws)
+        ms = time_calls(lambda: mm.timestep_embed(t, *ws, hidden=bufs[0], temb=bufs[1], tvec=bufs[2]), reps=50)
+        wbytes = sum(w.numel() * 2 for w in ws)
+        out[f"timestep_path_dt{cfg.t_dim}"] = {
+            "us": round(ms * 1e3, 2), "batch": cfg.batch, "weight_bytes": wbytes,
+            "GB_per_s": round(wbytes / (ms * 1e-3) / 1e9, 1), "launches": 3}
+    cfg = wl.LITE_480P
+    raw = wl.lite_inputs(cfg)
+    t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in raw.items()}
+    ym = torch.empty((1, cfg.n_merged, cfg.width), dtype=torch.bfloat16, device=dev)
+    yu = torch.empty((1, cfg.n_full, cfg.width), dtype=torch.bfloat16, device=dev)
+    half = cfg.flops / 2
+    ms_m = time_calls(lambda: mm.lite_merge(t["x"], t["w_merge"], t["b_merge"], cfg.grid, y=ym))
+    ms_u = time_calls(lambda: mm.lite_unpatchify(t["y"], t["w_unpatch"], t["b_unpatch"], cfg.grid, y=yu))
+    out["lite_merge_480p"] = {"ms": round(ms_m, 4), "tflops": round(half / (ms_m * 1e-3) / 1e12, 1),
+                              "shape": f"M={cfg.n_merged} N={cfg.width} K={4 * cfg.width}, bf16 in/out"}
+    out["lite_unpatchify_480p"] = {"ms": round(ms_u, 4), "tflops": round(half / (ms_u * 1e-3) / 1e12, 1),
+                                   "shape": f"M={cfg.n_merged} N={4 * cfg.width} K={cfg.width}, bf16 in/out"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +175,7 @@ def main():
     ap.add_argument("--act-dtype", choices=("f16", "bf16"), default="f16",
                     help="type of the 16-bit intermediates and MFMA operands")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the timing of the timestep path and Lite merge")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times): the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -226,6 +274,9 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "step_gpu_ms": round(float(np.mean(step_gpu_ms)), 4),
     }
+    if not args.no_next:
+        log("timestep path and Lite merge / unpatchify")
+        res["next_rows"] = next_rows(dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on this host)")
         res["cpu_baseline"] = cpu_baseline(cfg, raw)

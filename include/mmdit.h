@@ -177,10 +177,65 @@ int mmdit_linear(const void* x, const void* w, int x_dtype,
  *   mod[b] = W_mod tvec[b] + b_mod
  *
  * w_mod [6C, Dt] BF16;  b_mod [6C] BF16 or NULL;  tvec [B, Dt] t_dtype F32 | BF16;
- * mod   [B, 6C] f32.  Dt must be a multiple of 8.
+ * mod   [B, 6C] f32.  Dt must be a multiple of 8 and at most 16384 (1536 in the full
+ * model, 16 in Lite).
  * ------------------------------------------------------------------------------- */
 int mmdit_modulation(const void* w_mod, const void* b_mod, const void* tvec, int t_dtype,
                      float* mod, int64_t B, int64_t C6, int64_t Dt, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_timestep_embed -- timestep conditioning up to the shared bottleneck (Vimoo 1.0
+ * notes, section 2.2; the 16-wide Lite bottleneck, section 2.4).  Per batch item b:
+ *
+ *   e[b]      = [cos(t[b] f_0) .. cos(t[b] f_{h-1}), sin(t[b] f_0) .. sin(t[b] f_{h-1})],
+ *               h = freq_dim / 2, f_j = max_period^(-j / h)      (the pages fix only the
+ *               width, 256; the cosine-first layout and max_period 10000 are a reading)
+ *   hidden[b] = W1 e[b] + b1                     (the MLP's first layer, before its SiLU)
+ *   temb[b]   = W2 SiLU(hidden[b]) + b2          (the 3072-d timestep representation)
+ *   tvec[b]   = W3 SiLU(temb[b]) + b3            (the bottleneck shared by every block)
+ *
+ * SiLU(x) = x / (1 + exp(-x)).  t [B] f32 (timestep values as given, e.g. in [0, 1000]);
+ * w1 [Dh, freq_dim], w2 [Dh, Dh], w3 [Dt, Dh] and biases b1 [Dh], b2 [Dh], b3 [Dt] of
+ * w_dtype F32 | BF16 (biases may be NULL); outputs hidden, temb [B, Dh] and tvec [B, Dt]
+ * f32, all three caller-owned (hidden doubles as the scratch between the layers).
+ * freq_dim a multiple of 16 and Dh a multiple of 8, both <= 16384; Dt >= 1; max_period > 1.
+ * The angles t f_j are formed in double, so large timesteps keep full f32 accuracy.
+ * Outputs must not overlap each other or any input (MMDIT_ERR_ALIAS).
+ * ------------------------------------------------------------------------------- */
+int mmdit_timestep_embed(const float* t, int64_t B,
+                         const void* w1, const void* b1, const void* w2, const void* b2,
+                         const void* w3, const void* b3, int w_dtype,
+                         int64_t freq_dim, int64_t hidden_dim, int64_t Dt, float max_period,
+                         float* hidden, float* temb, float* tvec, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_lite_merge / mmdit_lite_unpatchify -- the Lite model's hidden-space 2x2 spatial
+ * merge before the backbone and its inverse after it (Vimoo 1.0 notes, section 2.4: four
+ * neighbouring hidden vectors of each 2x2 region are concatenated and mapped 4C -> C; the
+ * unpatchify projection expands each vector C -> 4C into four position-specific outputs;
+ * time is not merged).  The neighbour order is (dh, dw) = (0,0), (0,1), (1,0), (1,1), each
+ * neighbour's C channels contiguous (the pages fix only that the four are concatenated).
+ *
+ * Tokens of a batch item are the (t, h, w) grid flattened with w fastest; merged token
+ * (t, i, j) covers full-grid tokens (t, 2i+dh, 2j+dw).
+ *
+ *   merge:       y[b, (t,i,j)]  = W [x(t,2i,2j) | x(t,2i,2j+1) | x(t,2i+1,2j) | x(t,2i+1,2j+1)] + bias
+ *                x [B, T*H*W, C], w [C, 4C], bias [C] or NULL, y [B, T*(H/2)*(W/2), C]
+ *   unpatchify:  z = W x[b, (t,i,j)] + bias (4C values); y(t, 2i+dh, 2j+dw) = z[(2dh+dw)C .. +C]
+ *                x [B, T*(H/2)*(W/2), C], w [4C, C], bias [4C] or NULL, y [B, T*H*W, C]
+ *
+ * x and w BF16 | F16 (the same dtype; MFMA operands, fp32 accumulation), bias F32 | BF16,
+ * y F32 | BF16 | F16.  H and W even (odd grids, such as the 45-row 720p latent, are not
+ * defined by the pages and are rejected), C a multiple of 256, x and w below 2^31 bytes.
+ * The gather of the four neighbours happens inside the GEMM's loads and the scatter inside
+ * its stores: no regrouped copy of x or y is made.  y must not overlap x, w or bias.
+ * ------------------------------------------------------------------------------- */
+int mmdit_lite_merge(const void* x, int x_dtype, const void* w, const void* bias, int bias_dtype,
+                     void* y, int y_dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t C,
+                     void* stream);
+int mmdit_lite_unpatchify(const void* x, int x_dtype, const void* w, const void* bias, int bias_dtype,
+                          void* y, int y_dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t C,
+                          void* stream);
 
 /* ---------------------------------------------------------------------------------
  * mmdit_block_fwd -- one dual-stream MMDiT block forward (Vimoo 1.0 notes, section 2.2).

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert mm.abi_version() == 1
+    assert mm.abi_version() == 2
     assert L.mmdit_status_str(0) == b"MMDIT_OK"
     assert L.mmdit_status_str(ERR_ALIAS) == b"MMDIT_ERR_ALIAS"
     assert L.mmdit_status_str(99) == b"MMDIT_ERR_UNKNOWN"
@@ -147,3 +147,34 @@ def test_block_workspace_and_validation(L):
     st = L.mmdit_block_fwd(ctypes.byref(dims), ctypes.byref(sw), ctypes.byref(sw), p, p, mm.BF16, p, mm.BF16,
                            ctypes.byref(rope), 512, p, p, mm.F32, _fake(0x100000), 1024, 1, None)
     assert st == ERR_WS
+
+
+def test_timestep_embed_validation(L):
+    p, o1, o2, o3 = _fake(0x10000), _fake(0x900000), _fake(0xA00000), _fake(0xB00000)
+    args = lambda B, fd, dh, dt, wdt=mm.BF16, mp=10000.0, t=p, h=o1, e=o2, v=o3: (  # noqa: E731
+        t, B, p, None, p, None, p, None, wdt, fd, dh, dt, mp, h, e, v, None)
+    assert L.mmdit_timestep_embed(*args(2, 250, 3072, 1536)) == ERR_SHAPE     # freq_dim % 16
+    assert L.mmdit_timestep_embed(*args(2, 256, 3070, 1536)) == ERR_SHAPE     # hidden % 8
+    assert L.mmdit_timestep_embed(*args(2, 256, 3072, 0)) == ERR_SHAPE        # Dt >= 1
+    assert L.mmdit_timestep_embed(*args(2, 256, 3072, 16, mp=1.0)) == ERR_SHAPE
+    assert L.mmdit_timestep_embed(*args(2, 256, 3072, 16, wdt=mm.F16)) == ERR_DTYPE
+    assert L.mmdit_timestep_embed(*args(2, 256, 3072, 16, t=None)) == ERR_NULL
+    assert L.mmdit_timestep_embed(*args(2, 256, 3072, 16, h=_fake(0x900008))) == ERR_ALIGN
+    assert L.mmdit_timestep_embed(*args(2, 256, 3072, 16, e=o1)) == ERR_ALIAS  # outputs overlap
+    assert L.mmdit_timestep_embed(*args(2, 256, 3072, 16, v=p)) == ERR_ALIAS   # tvec over t / weights
+    assert L.mmdit_timestep_embed(*args(0, 256, 3072, 16, t=None)) == 0        # empty batch: no work
+
+
+def test_lite_merge_unpatchify_validation(L):
+    p, y = _fake(0x10000), _fake(0x90000000)
+    for fn in (L.mmdit_lite_merge, L.mmdit_lite_unpatchify):
+        assert fn(p, mm.BF16, p, None, mm.BF16, y, mm.F32, 1, 21, 45, 80, 3072, None) == ERR_SHAPE   # odd H
+        assert fn(p, mm.BF16, p, None, mm.BF16, y, mm.F32, 1, 21, 30, 51, 3072, None) == ERR_SHAPE   # odd W
+        assert fn(p, mm.BF16, p, None, mm.BF16, y, mm.F32, 1, 21, 30, 52, 3000, None) == ERR_SHAPE   # C % 256
+        assert fn(p, mm.F32, p, None, mm.BF16, y, mm.F32, 1, 21, 30, 52, 3072, None) == ERR_DTYPE
+        assert fn(p, mm.BF16, p, p, mm.F16, y, mm.F32, 1, 21, 30, 52, 3072, None) == ERR_DTYPE      # bias dtype
+        assert fn(None, mm.BF16, p, None, mm.BF16, y, mm.F32, 1, 21, 30, 52, 3072, None) == ERR_NULL
+        assert fn(p, mm.BF16, p, None, mm.BF16, _fake(0x90000008), mm.F32, 1, 21, 30, 52, 3072, None) == ERR_ALIGN
+        assert fn(p, mm.BF16, p, None, mm.BF16, p, mm.F32, 1, 21, 30, 52, 3072, None) == ERR_ALIAS
+        assert fn(p, mm.BF16, p, None, mm.BF16, y, mm.F32, 16, 21, 30, 52, 3072, None) == ERR_SHAPE  # > 2^31 B
+        assert fn(None, mm.BF16, None, None, mm.BF16, None, mm.F32, 0, 21, 30, 52, 3072, None) == 0  # empty

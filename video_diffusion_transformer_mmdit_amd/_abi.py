@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
                                   i64, vp, vp],
         "mmdit_linear": [vp, vp, i, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
         "mmdit_modulation": [vp, vp, vp, i, vp, i64, i64, i64, vp],
+        "mmdit_lite_merge": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
+        "mmdit_lite_unpatchify": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
+        "mmdit_timestep_embed": [vp, i64, vp, vp, vp, vp, vp, vp, i, i64, i64, i64, f, vp, vp, vp, vp],
         "mmdit_block_workspace_offsets": [ctypes.POINTER(BlockDims), i64, i64, i64, ctypes.POINTER(c_size_t)],
         "mmdit_block_fwd": [ctypes.POINTER(BlockDims), ctypes.POINTER(StreamWeights),
                             ctypes.POINTER(StreamWeights), vp, vp, i, vp, i, ctypes.POINTER(Rope3D), i64,
@@ -289,6 +292,70 @@ def modulation(w_mod: torch.Tensor, b_mod: Optional[torch.Tensor], tvec: torch.T
                                 B, C6, Dt, _stream(w_mod))
     _check(st, "mmdit_modulation")
     return out
+
+
+def timestep_embed(t: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
+                   b2: Optional[torch.Tensor], w3: torch.Tensor, b3: Optional[torch.Tensor], *,
+                   max_period: float = 10000.0, hidden: Optional[torch.Tensor] = None,
+                   temb: Optional[torch.Tensor] = None, tvec: Optional[torch.Tensor] = None):
+    """Timestep path: sinusoid(t) -> W1 -> SiLU -> W2 (= temb) -> SiLU -> W3 (= tvec).
+    t [B] f32; w1 [Dh, freq_dim], w2 [Dh, Dh], w3 [Dt, Dh] (f32 or bf16, contiguous).
+    Returns (hidden, temb, tvec), f32."""
+    _need_gpu(t, w1, b1, w2, b2, w3, b3, hidden, temb, tvec)
+    if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
+        raise MmditError("t must be a contiguous f32 [B] tensor")
+    dh, fd = w1.shape
+    dt = w3.shape[0]
+    if w2.shape != (dh, dh) or w3.shape[1] != dh:
+        raise MmditError("w1 [Dh, freq_dim], w2 [Dh, Dh], w3 [Dt, Dh] expected")
+    for nm, w in (("w1", w1), ("w2", w2), ("w3", w3), ("b1", b1), ("b2", b2), ("b3", b3)):
+        if w is not None and (w.dtype != w1.dtype or not w.is_contiguous()):
+            raise MmditError(f"{nm} must be contiguous and of w1's dtype")
+    B = t.shape[0]
+    dev = t.device
+    hidden = torch.empty((B, dh), dtype=torch.float32, device=dev) if hidden is None else hidden
+    temb = torch.empty((B, dh), dtype=torch.float32, device=dev) if temb is None else temb
+    tvec = torch.empty((B, dt), dtype=torch.float32, device=dev) if tvec is None else tvec
+    for nm, o, n in (("hidden", hidden, dh), ("temb", temb, dh), ("tvec", tvec, dt)):
+        if o.dtype != torch.float32 or o.shape != (B, n) or not o.is_contiguous():
+            raise MmditError(f"{nm} must be a contiguous f32 [B, {n}] tensor")
+    st = lib().mmdit_timestep_embed(t.data_ptr(), B, w1.data_ptr(), _ptr(b1), w2.data_ptr(), _ptr(b2),
+                                    w3.data_ptr(), _ptr(b3), _dt(w1), fd, dh, dt, max_period,
+                                    hidden.data_ptr(), temb.data_ptr(), tvec.data_ptr(), _stream(t))
+    _check(st, "mmdit_timestep_embed")
+    return hidden, temb, tvec
+
+
+def _lite(name: str, x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], grid: Sequence[int],
+          y: Optional[torch.Tensor], y_dtype, merge: bool) -> torch.Tensor:
+    _need_gpu(x, w, bias, y)
+    T, H, W = (int(g) for g in grid)
+    if x.dim() != 3 or not x.is_contiguous() or not w.is_contiguous() or w.dtype != x.dtype:
+        raise MmditError(f"{name}: x [B, n, C] and w must be contiguous and of one dtype")
+    B, n, C = x.shape
+    full, merged = T * H * W, T * (H // 2) * (W // 2)
+    if n != (full if merge else merged) or w.shape != ((C, 4 * C) if merge else (4 * C, C)):
+        raise MmditError(f"{name}: shapes do not match the (T, H, W) grid {grid}")
+    if y is None:
+        y = torch.empty((B, merged if merge else full, C), dtype=y_dtype, device=x.device)
+    fn = lib().mmdit_lite_merge if merge else lib().mmdit_lite_unpatchify
+    st = fn(x.data_ptr(), _dt(x), w.data_ptr(), _ptr(bias), _dt(bias) if bias is not None else BF16,
+            y.data_ptr(), _dt(y), B, T, H, W, C, _stream(x))
+    _check(st, f"mmdit_{name}")
+    return y
+
+
+def lite_merge(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], grid: Sequence[int], *,
+               y: Optional[torch.Tensor] = None, y_dtype=torch.bfloat16) -> torch.Tensor:
+    """Lite 2x2 merge: x [B, T*H*W, C] -> [B, T*(H/2)*(W/2), C] = concat4(x) w^T + bias; w [C, 4C]."""
+    return _lite("lite_merge", x, w, bias, grid, y, y_dtype, True)
+
+
+def lite_unpatchify(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], grid: Sequence[int], *,
+                    y: Optional[torch.Tensor] = None, y_dtype=torch.float32) -> torch.Tensor:
+    """Lite unpatchify: x [B, T*(H/2)*(W/2), C] -> [B, T*H*W, C]; w [4C, C]; ``grid`` is the
+    full (T, H, W) grid."""
+    return _lite("lite_unpatchify", x, w, bias, grid, y, y_dtype, False)
 
 
 STREAM_KEYS = ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm", "w_o", "b_o", "w_fc1", "b_fc1",

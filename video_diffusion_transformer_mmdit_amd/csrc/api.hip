@@ -67,7 +67,7 @@ const char* mmdit_status_str(int s) {
 
 const char* mmdit_last_error(void) { return g_last_error.c_str(); }
 
-int mmdit_abi_version(void) { return 1; }
+int mmdit_abi_version(void) { return 2; }
 
 int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
                       const float* gate, float* x_out, const float* shift, const float* scale,
@@ -234,12 +234,82 @@ int mmdit_modulation(const void* w_mod, const void* b_mod, const void* tvec, int
                      int64_t B, int64_t C6, int64_t Dt, void* stream) {
   g_last_error.clear();
   if (B < 0 || C6 < 0 || Dt < 8 || Dt % 8) return fail(MMDIT_ERR_SHAPE, "modulation: Dt must be a positive multiple of 8");
-  if (B * Dt > 16384) return fail(MMDIT_ERR_SHAPE, "modulation: B * Dt must be <= 16384");
+  if (Dt > 16384) return fail(MMDIT_ERR_SHAPE, "modulation: Dt must be <= 16384");
   if (t_dtype != MMDIT_F32 && t_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "modulation: tvec must be f32 or bf16");
   if (B == 0 || C6 == 0) return MMDIT_OK;
   if (!w_mod || !tvec || !mod) return fail(MMDIT_ERR_NULL, "modulation: w_mod, tvec, mod required");
   if (!aligned16(w_mod) || !aligned16(tvec) || !aligned16(mod)) return fail(MMDIT_ERR_ALIGN, "modulation: pointers must be 16-byte aligned");
   return launch_modulation(w_mod, b_mod, tvec, t_dtype, mod, B, C6, Dt, static_cast<hipStream_t>(stream));
+}
+
+static int lite_regroup(int layout, const char* name, const void* x, int x_dtype, const void* w,
+                        const void* bias, int bias_dtype, void* y, int y_dtype, int64_t B, int64_t T,
+                        int64_t H, int64_t W, int64_t C, void* stream) {
+  g_last_error.clear();
+  const std::string n(name);
+  if (B < 0 || T < 0 || H < 2 || W < 2 || H % 2 || W % 2)
+    return fail(MMDIT_ERR_SHAPE, n + ": the grid needs T >= 0 and an even H, W >= 2 (the merge is defined for even grids)");
+  if (C < 256 || C % 256) return fail(MMDIT_ERR_SHAPE, n + ": C must be a positive multiple of 256");
+  if (x_dtype != MMDIT_BF16 && x_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, n + ": x and w must be bf16 or f16");
+  if (bias && bias_dtype != MMDIT_F32 && bias_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, n + ": bias must be f32 or bf16");
+  if (!valid_dtype(y_dtype)) return fail(MMDIT_ERR_DTYPE, n + ": bad y dtype");
+  const int64_t M = B * T * (H / 2) * (W / 2);
+  if ((M + 256) * 4 * C * 2 >= ((int64_t)1 << 31) || (4 * C + 256) * C * 2 >= ((int64_t)1 << 31))
+    return fail(MMDIT_ERR_SHAPE, n + ": x or w too large for 32-bit buffer offsets");
+  if (M == 0) return MMDIT_OK;
+  if (!x || !w || !y) return fail(MMDIT_ERR_NULL, n + ": x, w, y required");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)))
+    return fail(MMDIT_ERR_ALIGN, n + ": pointers must be 16-byte aligned");
+  const size_t nx = (size_t)(4 * M * C) * 2, nw = (size_t)(4 * C * C) * 2;
+  const size_t ny = (size_t)(4 * M * C / (layout == GEMM_GATHER_X ? 4 : 1)) * dtype_size(y_dtype);
+  if (overlaps(y, ny, x, layout == GEMM_GATHER_X ? nx : nx / 4) || overlaps(y, ny, w, nw) ||
+      (bias && overlaps(y, ny, bias, (size_t)(layout == GEMM_GATHER_X ? C : 4 * C) * dtype_size(bias_dtype))))
+    return fail(MMDIT_ERR_ALIAS, n + ": y overlaps an input");
+  return launch_lite_regroup(layout, x, w, bias, bias_dtype, y, x_dtype, y_dtype, B, T, H, W, C,
+                             static_cast<hipStream_t>(stream));
+}
+
+int mmdit_lite_merge(const void* x, int x_dtype, const void* w, const void* bias, int bias_dtype, void* y,
+                     int y_dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t C, void* stream) {
+  return lite_regroup(GEMM_GATHER_X, "lite_merge", x, x_dtype, w, bias, bias_dtype, y, y_dtype, B, T, H, W, C, stream);
+}
+
+int mmdit_lite_unpatchify(const void* x, int x_dtype, const void* w, const void* bias, int bias_dtype, void* y,
+                          int y_dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t C, void* stream) {
+  return lite_regroup(GEMM_SCATTER_Y, "lite_unpatchify", x, x_dtype, w, bias, bias_dtype, y, y_dtype, B, T, H, W,
+                      C, stream);
+}
+
+int mmdit_timestep_embed(const float* t, int64_t B, const void* w1, const void* b1, const void* w2,
+                         const void* b2, const void* w3, const void* b3, int w_dtype, int64_t freq_dim,
+                         int64_t hidden_dim, int64_t Dt, float max_period, float* hidden, float* temb,
+                         float* tvec, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || freq_dim < 16 || freq_dim % 16 || hidden_dim < 8 || hidden_dim % 8 || Dt < 1)
+    return fail(MMDIT_ERR_SHAPE, "timestep_embed: freq_dim a positive multiple of 16, hidden_dim of 8, Dt >= 1");
+  if (freq_dim > 16384 || hidden_dim > 16384) return fail(MMDIT_ERR_SHAPE, "timestep_embed: freq_dim and hidden_dim must be <= 16384");
+  if (!(max_period > 1.f) || !(max_period < 3.0e38f)) return fail(MMDIT_ERR_SHAPE, "timestep_embed: max_period must be a finite value > 1");
+  if (w_dtype != MMDIT_F32 && w_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "timestep_embed: weights must be f32 or bf16");
+  if (B == 0) return MMDIT_OK;
+  if (!t || !w1 || !w2 || !w3 || !hidden || !temb || !tvec) return fail(MMDIT_ERR_NULL, "timestep_embed: t, w1, w2, w3, hidden, temb, tvec required");
+  const void* ps[] = {t, w1, w2, w3, b1, b2, b3, hidden, temb, tvec};
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return fail(MMDIT_ERR_ALIGN, "timestep_embed: pointers must be 16-byte aligned");
+  const size_t ws = dtype_size(w_dtype);
+  const size_t nh = (size_t)(B * hidden_dim) * 4, nt = (size_t)(B * Dt) * 4;
+  const void* outs[] = {hidden, temb, tvec};
+  const size_t nout[] = {nh, nh, nt};
+  const void* ins[] = {t, w1, w2, w3, b1, b2, b3};
+  const size_t nin[] = {(size_t)B * 4, (size_t)(hidden_dim * freq_dim) * ws, (size_t)(hidden_dim * hidden_dim) * ws,
+                        (size_t)(Dt * hidden_dim) * ws, (size_t)hidden_dim * ws, (size_t)hidden_dim * ws, (size_t)Dt * ws};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (ins[i] && overlaps(outs[o], nout[o], ins[i], nin[i])) return fail(MMDIT_ERR_ALIAS, "timestep_embed: an output overlaps an input");
+    for (int p = o + 1; p < 3; ++p)
+      if (overlaps(outs[o], nout[o], outs[p], nout[p])) return fail(MMDIT_ERR_ALIAS, "timestep_embed: outputs overlap");
+  }
+  return launch_timestep_embed(t, B, w1, b1, w2, b2, w3, b3, w_dtype, freq_dim, hidden_dim, Dt, max_period,
+                               hidden, temb, tvec, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

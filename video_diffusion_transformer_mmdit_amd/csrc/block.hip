@@ -23,7 +23,7 @@ static int validate_dims(const mmdit_block_dims* d, int64_t B, int64_t n_vis, in
   if (d->C > 8192 || d->F > 65536) return fail(MMDIT_ERR_SHAPE, "block: C <= 8192 and F <= 65536");
   if (d->Dt < 8 || d->Dt % 8) return fail(MMDIT_ERR_SHAPE, "block: Dt must be a positive multiple of 8");
   if (B < 1 || n_vis < 1 || n_cond < 0) return fail(MMDIT_ERR_SHAPE, "block: need B >= 1, n_vis >= 1, n_cond >= 0");
-  if (B * d->Dt > 16384) return fail(MMDIT_ERR_SHAPE, "block: B * Dt must be <= 16384");
+  if (d->Dt > 16384) return fail(MMDIT_ERR_SHAPE, "block: Dt must be <= 16384");
   if (d->qk_scale_head_stride != 0 && d->qk_scale_head_stride != d->D)
     return fail(MMDIT_ERR_SHAPE, "block: qk_scale_head_stride must be 0 or D");
   if (!(d->ln_eps >= 0.f) || !(d->qk_eps >= 0.f)) return fail(MMDIT_ERR_SHAPE, "block: eps must be >= 0");

@@ -137,11 +137,20 @@ struct GemmProblem {
   int64_t gate_stride;
   int64_t rows_per_batch;
 };
+// Operand layouts of the GEMM kernel: plain row-major x and y, or the Lite 2x2 regrouping.
+enum { GEMM_PLAIN = 0, GEMM_GATHER_X = 1, GEMM_SCATTER_Y = 2 };
+int launch_lite_regroup(int layout, const void* x, const void* w, const void* bias, int bias_dtype, void* y,
+                        int in_dtype, int y_dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t C,
+                        hipStream_t stream);
 // Runs one or two problems with equal N, K, dtypes and epilogue in one launch.
 int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dtype, int y_dtype,
                   int64_t N, int64_t K, int epilogue, int res_dtype, hipStream_t stream);
 int launch_modulation(const void* w_mod, const void* b_mod, const void* tvec, int t_dtype,
                       float* mod, int64_t B, int64_t C6, int64_t Dt, hipStream_t stream);
+int launch_timestep_embed(const float* t, int64_t B, const void* w1, const void* b1, const void* w2,
+                          const void* b2, const void* w3, const void* b3, int w_dtype, int64_t freq_dim,
+                          int64_t hidden_dim, int64_t Dt, float max_period, float* hidden, float* temb,
+                          float* tvec, hipStream_t stream);
 int launch_convert_bf16_to_f16(const void* src, void* dst, int64_t n, hipStream_t stream);
 
 }  // namespace mmdit

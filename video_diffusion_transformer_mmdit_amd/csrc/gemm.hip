@@ -1,22 +1,24 @@
 // y = epilogue(x W^T + bias): the per-stream projections of the MMDiT block (QKV, output,
 // FFN up with GELU, FFN down with the gated residual), Vimoo 1.0 notes section 2.2; their
-// cost is the linear term of the Wan report's workload model (section 4.3.1).
+// cost is the linear term of the Wan report's workload model (section 4.3.1).  The same
+// kernel runs the Lite model's 2x2 hidden-space merge and unpatchify (section 2.4), with the
+// neighbour gather folded into the x loads and the scatter back to the grid into the stores.
 //
 // gfx950 design:
-//   - 256 x 256 output tile per workgroup of 8 wave64s arranged 2 (M) x 4 (N); each wave
-//     owns 128 x 64 outputs = 4 x 2 tiles of v_mfma_f32_32x32x16_{bf16,f16}.  The MFMA
-//     computes C^T (A operand = W rows, B operand = x rows), so every lane ends up holding
-//     four consecutive output columns of one row and the epilogue stores 8 or 16 bytes at
-//     a time.
+//   - 256 x 256 output tile per workgroup of 4 wave64s arranged 2 (M) x 2 (N), one per SIMD;
+//     each wave owns 128 x 128 outputs = 4 x 4 tiles of v_mfma_f32_32x32x16_{bf16,f16} whose
+//     256 accumulator registers live in AGPRs.  The MFMA computes C^T (A operand = W rows,
+//     B operand = x rows), so every lane ends up holding four consecutive output columns of
+//     one row and the epilogue stores 8 or 16 bytes at a time.
 //   - K advances 32 at a time through four LDS stages (x tile and W tile, 16 KiB each, rows
 //     of 64 bytes, both K-contiguous so both MFMA operands are plain 16-byte LDS reads).
 //     Tiles move by LDS-DMA (buffer loads straight into LDS) three stages ahead, issued
 //     between the MFMAs; before the barrier that ends stage k each wave waits only for its
 //     loads of stage k+2, so stage k+1 is visible one stage early and the first fragments
-//     of the next stage are read while the current stage's last MFMAs run.  The eight stage
-//     buffers are distinct LDS objects addressed with compile-time stage indices, so the
-//     wait-count pass never stalls reads of one stage on the DMA into another (one object
-//     per stage: with one per operand tile it loses track and waits for every load).
+//     of the next stage are read while the current stage's last MFMAs run.  The four stage
+//     buffers are distinct LDS objects addressed with compile-time stage indices, and the
+//     DMA destinations pass through an opaque register copy, so the compiler's wait-count
+//     pass leaves every wait to the explicit per-stage ones.
 //   - LDS chunks are XOR-swizzled with (row / 4) % 4, which puts the 16 rows a 16-lane group
 //     of a fragment read touches on distinct bank groups; a DMA writes 16 bytes per lane in
 //     lane order, so each lane loads the logical chunk that belongs at its physical slot.
@@ -43,7 +45,18 @@ struct GemmArgs {
   int64_t tiles0;    // tiles of problem 0
   int64_t tiles;     // total tiles
   int64_t N, K;
+  // 2x2 spatial regrouping (GEMM_GATHER_X / GEMM_SCATTER_Y): hidden width C, full grid
+  // width W, merged grid width W/2 and merged tokens per frame (H/2)(W/2)
+  int c, w, w2, hw2;
 };
+
+// Row of the full (T, H, W) token grid holding the top-left neighbour of merged token m
+// (frames of all batch items follow one another, so batch and time fold into one index).
+__device__ __forceinline__ int merged_row0(int m, const GemmArgs& a) {
+  const int f = m / a.hw2, rem = m - f * a.hw2;
+  const int i = rem / a.w2, j = rem - i * a.w2;
+  return f * 4 * a.hw2 + 2 * i * a.w + 2 * j;
+}
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
@@ -124,7 +137,7 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* opaque_lds(__
   return (__attribute__((address_space(3))) void*)(uintptr_t)a;
 }
 
-template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT>
+template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs args) {
   // one LDS object per stage: x tile, then W tile
@@ -159,7 +172,11 @@ void gemm_kernel(GemmArgs args) {
   // 1 KiB loads each (lane l -> row 64w + 16i + l/4, physical chunk l % 4).  The immediate
   // offset i * 1024 moves the LDS destination and the source alike and is taken back out of
   // the per-lane offset, so all loads of a tile share one LDS base; the K position goes in
-  // the scalar offset.
+  // the scalar offset, which the range check ignores.
+  // GEMM_GATHER_X: logical x row m, K position k reads channel k % C of the full-grid token
+  // merged_row0(m) + (s / 2) W + s % 2, s = k / C (a K stage never straddles two neighbours
+  // as C is a multiple of 32).  The per-row part is per lane, the neighbour part scalar.
+  // Rows m >= M get an offset past the end of x, so they load zeros.
   const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * 2);
   const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * 2);
   int xo[4], wo[4];
@@ -167,17 +184,25 @@ void gemm_kernel(GemmArgs args) {
   for (int i = 0; i < 4; ++i) {
     const int row = 64 * wave + 16 * i + (lane >> 2);
     const int lc = (lane & 3) ^ swz(row);
-    xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - i * 1024;
+    if constexpr (LAYOUT == GEMM_GATHER_X)
+      xo[i] = (m0 + row < M ? merged_row0(m0 + row, args) * args.c * 2 + lc * 16 : 0x7FFF0000) - i * 1024;
+    else
+      xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - i * 1024;
     wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - i * 1024;
   }
   auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
+    int xso = k0 * 2;
+    if constexpr (LAYOUT == GEMM_GATHER_X) {
+      const int sg = __builtin_amdgcn_readfirstlane(k0 / args.c);
+      xso = (((sg >> 1) * args.w + (sg & 1)) * args.c + (k0 - sg * args.c)) * 2;
+    }
     const int so = k0 * 2;
     auto* lx = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 4096));
     auto* lw = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 4096));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], so, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], xso, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], xso, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], xso, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], xso, 3072, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[0], so, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[1], so, 1024, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[2], so, 2048, 0);
@@ -286,7 +311,21 @@ void gemm_kernel(GemmArgs args) {
   if (kt + 5 < nk) step(S1, TAIL, kt + 5);
 
   // ---- epilogue: lane holds C^T rows (output columns) 8 (e/4) + 4 g + e%4 of each 32 x 32
-  // tile at output row l32: four consecutive columns per e/4
+  // tile at output row l32: four consecutive columns per e/4.
+  // GEMM_SCATTER_Y: logical output row m, column n goes to column n % C of the full-grid
+  // token merged_row0(m) + (s / 2) W + s % 2, s = n / C; a 256-wide tile lies inside one s
+  // (C is a multiple of 256).
+  int64_t y_rows[4];
+  int s_col = 0;
+  if constexpr (LAYOUT == GEMM_SCATTER_Y) {
+    const int sg = n0 / args.c;
+    s_col = sg * args.c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 128 + i * 32 + l32;
+      y_rows[i] = m < M ? (int64_t)merged_row0(m, args) + (sg >> 1) * args.w + (sg & 1) : 0;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -313,15 +352,47 @@ void gemm_kernel(GemmArgs args) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = fmaf(gt[q], v[q], r[q]);
         }
-        store4<Y_DT>(P.y, m * N + n, v);
+        if constexpr (LAYOUT == GEMM_SCATTER_Y) store4<Y_DT>(P.y, y_rows[i] * args.c + (n - s_col), v);
+        else store4<Y_DT>(P.y, m * N + n, v);
       }
     }
   }
 }
 
-template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT>
+template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
 static void gemm_go(const GemmArgs& a, hipStream_t st) {
-  gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+  gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+}
+
+// Lite merge (GEMM_GATHER_X: y [B*T*(H/2)*(W/2), C] = gather4(x) W^T + b, W [C, 4C]) and
+// unpatchify (GEMM_SCATTER_Y: y [B*T*H*W, C] = scatter4(x W^T + b), W [4C, C]).
+int launch_lite_regroup(int layout, const void* x, const void* w, const void* bias, int bias_dtype, void* y,
+                        int in_dtype, int y_dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t C,
+                        hipStream_t stream) {
+  GemmArgs a{};
+  const int64_t M = B * T * (H / 2) * (W / 2);
+  const int64_t N = layout == GEMM_GATHER_X ? C : 4 * C;
+  const int64_t K = layout == GEMM_GATHER_X ? 4 * C : C;
+  if ((M + GBM) * K * 2 >= ((int64_t)1 << 31) || (N + GBN) * K * 2 >= ((int64_t)1 << 31))
+    return fail(MMDIT_ERR_SHAPE, "lite: tensors too large for 32-bit buffer offsets");
+  a.p[0].x = x; a.p[0].w = w; a.p[0].bias = bias; a.p[0].y = y; a.p[0].M = M; a.p[0].rows_per_batch = M;
+  a.tiles0 = a.tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+  a.N = N; a.K = K;
+  a.c = (int)C; a.w = (int)W; a.w2 = (int)(W / 2); a.hw2 = (int)((H / 2) * (W / 2));
+  if (a.tiles == 0) return MMDIT_OK;
+  const bool bf = bias_dtype == MMDIT_F32;
+#define LITE_CASE(L, IN, Y)                                                                   \
+  if (layout == L && in_dtype == IN && y_dtype == Y) {                                        \
+    if (bf) gemm_go<IN, MMDIT_F32, Y, MMDIT_EPI_NONE, MMDIT_F32, L>(a, stream);                \
+    else gemm_go<IN, MMDIT_BF16, Y, MMDIT_EPI_NONE, MMDIT_F32, L>(a, stream);                  \
+    return check_launch(L == GEMM_GATHER_X ? "lite_merge" : "lite_unpatchify");               \
+  }
+#define LITE_IN(L, IN) LITE_CASE(L, IN, MMDIT_F32) LITE_CASE(L, IN, MMDIT_BF16) LITE_CASE(L, IN, MMDIT_F16)
+  LITE_IN(GEMM_GATHER_X, MMDIT_BF16) LITE_IN(GEMM_GATHER_X, MMDIT_F16)
+  LITE_IN(GEMM_SCATTER_Y, MMDIT_BF16) LITE_IN(GEMM_SCATTER_Y, MMDIT_F16)
+#undef LITE_IN
+#undef LITE_CASE
+  return fail(MMDIT_ERR_DTYPE, "lite: unsupported dtype combination");
 }
 
 int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dtype, int y_dtype,

@@ -220,6 +220,90 @@ def block_inputs(cfg: BlockConfig, seed: Optional[int] = None,
     return out
 
 
+# --------------------------------------------------------------------------- timestep path
+@dataclasses.dataclass(frozen=True)
+class TimestepConfig:
+    """Timestep conditioning: 256-d sinusoid -> MLP(SiLU) -> hidden -> SiLU -> Linear t_dim
+    (Vimoo 1.0 notes, section 2.2; t_dim 16 in Lite, section 2.4)."""
+    name: str
+    batch: int
+    freq_dim: int = 256
+    hidden: int = 3072
+    t_dim: int = 1536
+    max_period: float = 10000.0
+    seed: int = 0
+
+
+TIMESTEP_FULL = TimestepConfig("timestep_b2_f256_h3072_dt1536", 2, t_dim=1536, seed=21)
+TIMESTEP_LITE = TimestepConfig("timestep_b2_f256_h3072_dt16", 2, t_dim=16, seed=22)
+TIMESTEP_WEIGHTS = ("w1", "b1", "w2", "b2", "w3", "b3")
+
+
+def timestep_inputs(cfg: TimestepConfig, seed: Optional[int] = None, weight_std: float = 0.02,
+                    weight_dtype: str = BF16) -> Dict[str, np.ndarray]:
+    """Timesteps t = 1000 * sigmoid(N(0, 1)) (logit-normal, the training distribution the Wan
+    report's reading guide gives for flow matching), stored f32; weights and biases
+    ~ N(0, weight_std).  Draw order: t, then w1, b1, w2, b2, w3, b3."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    z = _normal(rng, (cfg.batch,)).astype(np.float64)
+    out = {"t": (1000.0 / (1.0 + np.exp(-z))).astype(np.float32)}
+    shapes = {"w1": (cfg.hidden, cfg.freq_dim), "b1": (cfg.hidden,), "w2": (cfg.hidden, cfg.hidden),
+              "b2": (cfg.hidden,), "w3": (cfg.t_dim, cfg.hidden), "b3": (cfg.t_dim,)}
+    for nm in TIMESTEP_WEIGHTS:
+        out[nm] = _store(_normal(rng, shapes[nm], std=weight_std), weight_dtype)
+    return out
+
+
+# --------------------------------------------------------------------------- Lite 2x2 merge
+@dataclasses.dataclass(frozen=True)
+class LiteConfig:
+    """Lite hidden-space 2x2 merge before the backbone and unpatchify after it (Vimoo 1.0
+    notes, section 2.4) on a (T, H, W) grid of visual tokens of width C."""
+    name: str
+    width: int
+    grid: Tuple[int, int, int]
+    batch: int = 1
+    seed: int = 0
+
+    @property
+    def n_full(self) -> int:
+        t, h, w = self.grid
+        return t * h * w
+
+    @property
+    def merged_grid(self) -> Tuple[int, int, int]:
+        t, h, w = self.grid
+        return t, h // 2, w // 2
+
+    @property
+    def n_merged(self) -> int:
+        t, h, w = self.merged_grid
+        return t * h * w
+
+    @property
+    def flops(self) -> float:
+        """Merge and unpatchify each: 2 * merged tokens * C * 4C."""
+        return 2 * 2.0 * self.batch * self.n_merged * self.width * 4 * self.width
+
+
+LITE_480P = LiteConfig("lite480p_c3072_grid21x30x52", 3072, (21, 30, 52), seed=31)
+LITE_SMALL = LiteConfig("lite_small_c512_grid3x6x10_b2", 512, (3, 6, 10), batch=2, seed=32)
+
+
+def lite_inputs(cfg: LiteConfig, seed: Optional[int] = None, weight_std: float = 0.02) -> Dict[str, np.ndarray]:
+    """Hidden states x ~ N(0, 1) [B, T*H*W, C] and merged-grid states y ~ N(0, 1)
+    [B, T*(H/2)*(W/2), C]; merge weights [C, 4C] + [C] and unpatchify weights [4C, C] + [4C]
+    ~ N(0, weight_std).  All bf16.  Draw order: x, y, w_merge, b_merge, w_unpatch, b_unpatch."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    b, c = cfg.batch, cfg.width
+    return {"x": round_to_bf16_bits(_normal(rng, (b, cfg.n_full, c))),
+            "y": round_to_bf16_bits(_normal(rng, (b, cfg.n_merged, c))),
+            "w_merge": round_to_bf16_bits(_normal(rng, (c, 4 * c), std=weight_std)),
+            "b_merge": round_to_bf16_bits(_normal(rng, (c,), std=weight_std)),
+            "w_unpatch": round_to_bf16_bits(_normal(rng, (4 * c, c), std=weight_std)),
+            "b_unpatch": round_to_bf16_bits(_normal(rng, (4 * c,), std=weight_std))}
+
+
 def sample_rows(n: int, k: int, seed: int) -> np.ndarray:
     """Sorted distinct row indices for sampled comparisons; always keeps the first and the
     last row (tile edges and the ragged tail)."""
