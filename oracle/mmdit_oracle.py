@@ -32,7 +32,10 @@ design notes of the repository):
   r21 the timestep MLP and the bottleneck Linear carry biases, SiLU is x*sigmoid(x);
   r22 Lite merge concatenates the 2x2 neighbours in (dh, dw) row-major order, each
   neighbour's C channels contiguous; the unpatchify output splits the same way;
-  r23 Lite merge/unpatchify is defined for even H and W only (odd grids are rejected).
+  r23 Lite merge/unpatchify is defined for even H and W only (odd grids are rejected);
+  r24 FP8 is OCP E4M3 (largest 448), rounding to nearest with ties to even, saturating;
+  r25 8-bit scales are amax / qmax in float32 (qmax 448 for E4M3, 127 for INT8), an all-zero
+  group takes scale 1, and the value to round is x * (1/s) formed in float32.
 
 Further sources for the Lite parts: [Vimoo] section 2.4 "Vimoo 1.0-Lite" (2x2 hidden-space
 merge 4C -> C after the input projection, unpatchify C -> 4C after the backbone, time axis
@@ -376,6 +379,103 @@ def lite_unpatchify(y: np.ndarray, w: np.ndarray, b: Optional[np.ndarray],
     for s, (dh, dw) in enumerate(NEIGHBOURS):
         out[:, :, dh::2, dw::2, :] = z5[..., s * c:(s + 1) * c]
     return out.reshape(bsz, t_n * h_n * w_n, c)
+
+
+# ------------------------------------------------- 8-bit quantization  [Wan-zh 4.4.3]
+#
+# The Wan report (section 4.4.3) runs the DiT's GEMMs in FP8 with a per-tensor scale for the
+# weights and a per-token scale for the activations, and its attention with INT8 for Q K^T
+# and FP8 (E4M3) for P V, accumulating across blocks in FP32.  E4M3 below is the OCP FP8
+# format: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no infinities, largest finite 448.
+
+FP8_E4M3_MAX = 448.0
+INT8_MAX = 127.0
+
+
+def _round_half_even(v: np.ndarray) -> np.ndarray:
+    return np.round(v)   # numpy rounds halves to even
+
+
+def fp8_e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 value of each element (ties to even mantissa), saturating at +-448
+    (r24).  Normal numbers are 2^e (1 + m/8), e in [-6, 8]; below 2^-6 the spacing is the
+    subnormal step 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    out = np.empty_like(a)
+    sub = a < 2.0 ** -6
+    out[sub] = _round_half_even(a[sub] / 2.0 ** -9) * 2.0 ** -9
+    an = a[~sub]
+    e = np.floor(np.log2(an))
+    # guard the log2 rounding at exact powers of two
+    e = np.where(2.0 ** e > an, e - 1, e)
+    e = np.where(2.0 ** (e + 1) <= an, e + 1, e)
+    step = 2.0 ** (e - 3)
+    out[~sub] = _round_half_even(an / step) * step
+    out = np.minimum(out, FP8_E4M3_MAX)
+    return np.copysign(out, x)
+
+
+def fp8_e4m3_code(v: np.ndarray) -> np.ndarray:
+    """Bit pattern (uint8) of E4M3 values (as returned by fp8_e4m3_round)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sign = (np.signbit(v)).astype(np.uint8) << 7
+    code = np.zeros(a.shape, dtype=np.uint8)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.uint8)
+    an = a[~sub]
+    e = np.floor(np.log2(an))
+    e = np.where(2.0 ** e > an, e - 1, e)
+    e = np.where(2.0 ** (e + 1) <= an, e + 1, e)
+    m = np.rint((an / 2.0 ** e - 1.0) * 8).astype(np.int64)
+    code[~sub] = ((e.astype(np.int64) + 7) << 3 | m).astype(np.uint8)
+    return code | sign
+
+
+def fp8_e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """Value of each E4M3 bit pattern (0x7F / 0xFF, the NaN codes, never occur here)."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return s * mag
+
+
+def quant_scale(amax: np.ndarray, qmax: float) -> np.ndarray:
+    """Scale s = amax / qmax evaluated in float32, with an all-zero group given s = 1 (r25)."""
+    amax = np.asarray(amax, dtype=np.float32)
+    s = (amax / np.float32(qmax)).astype(np.float32)
+    return np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+
+
+def quantize_fp8(x: np.ndarray, per_row: bool):
+    """Symmetric FP8 E4M3 quantization with a scale per row (token) or one per tensor
+    (r25): s = amax / 448 in float32; the code is the E4M3 rounding of x * (1/s), that
+    product formed in float32.  Returns (values of the codes [same shape], scales
+    [rows] or [1])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    if per_row:
+        amax = np.max(np.abs(x32), axis=-1)
+    else:
+        amax = np.array([np.max(np.abs(x32))], dtype=np.float32)
+    s = quant_scale(amax, FP8_E4M3_MAX)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    inv_b = inv[..., None] if per_row else inv[0]
+    y = (x32 * inv_b).astype(np.float32)
+    y = np.clip(y, -FP8_E4M3_MAX, FP8_E4M3_MAX)
+    return fp8_e4m3_round(y), s
+
+
+def fp8_linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """The FP8 Linear of [Wan-zh] 4.4.3: x quantized per token, w per tensor, the product of
+    the quantized values taken exactly, then rescaled: y = (q_x q_w^T) s_x s_w + b.
+    x [M, K], w [N, K]."""
+    qx, sx = quantize_fp8(x, per_row=True)
+    qw, sw = quantize_fp8(w, per_row=False)
+    y = (qx @ qw.T) * sx.astype(np.float64)[:, None] * float(sw[0])
+    return y if b is None else y + b
 
 
 # ------------------------------------------------------------------ parity metric (r18)

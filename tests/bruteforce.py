@@ -201,3 +201,25 @@ def lite_unpatchify(y, w, b, grid):
                 part = (h % 2) * 2 + (x_ % 2)
                 out.append(z[part * c:(part + 1) * c])
     return out
+
+
+# ------------------------------------------------------------------ FP8 linear
+def fp8_linear(x, w, b, round_fp8):
+    """x: [M][K], w: [N][K] lists; ``round_fp8`` rounds one float to E4M3 (an independent
+    routine is passed in).  Per-row scales of x and one scale of w: amax / 448 in float32,
+    values scaled by the float32 reciprocal, rounded, multiplied exactly, rescaled."""
+    import numpy as np
+    f32 = np.float32
+
+    def quant(rows):
+        amax = f32(max(abs(f32(v)) for r in rows for v in r))
+        s = f32(amax / f32(448.0)) if amax > 0 else f32(1.0)
+        inv = f32(f32(1.0) / s)
+        return [[round_fp8(float(min(max(f32(f32(v) * inv), f32(-448.0)), f32(448.0)))) for v in r] for r in rows], float(s)
+
+    qw, sw = quant(w)
+    out = []
+    for r in x:
+        (qr,), sr = quant([r])
+        out.append([sum(a * c for a, c in zip(qr, wr)) * sr * sw + bb for wr, bb in zip(qw, b)])
+    return out

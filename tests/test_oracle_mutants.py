@@ -17,7 +17,8 @@ from tests import test_oracle_pins as pins
 ORIG = {name: getattr(om, name) for name in
         ("rope_angles", "rope_rotate", "token_positions", "rms_norm_heads", "softmax_attention",
          "modulate", "layer_norm", "linear", "gelu", "modulation", "joint_attention",
-         "timestep_sinusoid", "silu", "timestep_path", "lite_merge_gather", "lite_unpatchify")}
+         "timestep_sinusoid", "silu", "timestep_path", "lite_merge_gather", "lite_unpatchify",
+         "fp8_e4m3_round", "quantize_fp8", "fp8_linear", "quant_scale")}
 
 
 def _rope_sign(x, angles):
@@ -166,6 +167,37 @@ def _unpatchify_swapped_w(y, w, b, grid):
     return o5.reshape(out.shape)
 
 
+def _fp8_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    r = ORIG["fp8_e4m3_round"](x)
+    return np.where(np.abs(r) > np.abs(x), ORIG["fp8_e4m3_round"](x - np.sign(x) * np.abs(x) * 2.0 ** -4), r)
+
+
+def _fp8_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    r = ORIG["fp8_e4m3_round"](x)
+    up = ORIG["fp8_e4m3_round"](x * (1 + 2.0 ** -30))
+    return np.where(up != r, up, r)
+
+
+def _scale_int8_max(amax, qmax):
+    return ORIG["quant_scale"](amax, 127.0)
+
+
+def _fp8_linear_no_wscale(x, w, b):
+    qx, sx = om.quantize_fp8(x, per_row=True)
+    qw, _ = om.quantize_fp8(w, per_row=False)
+    y = (qx @ qw.T) * sx.astype(np.float64)[:, None]
+    return y if b is None else y + b
+
+
+def _fp8_linear_per_tensor_x(x, w, b):
+    qx, sx = om.quantize_fp8(x, per_row=False)
+    qw, sw = om.quantize_fp8(w, per_row=False)
+    y = (qx @ qw.T) * float(sx[0]) * float(sw[0])
+    return y if b is None else y + b
+
+
 MUTANTS = {
     "rope_sign": ("rope_rotate", _rope_sign),
     "rope_band_order": ("rope_angles", _band_order),
@@ -193,6 +225,11 @@ MUTANTS = {
     "merge_column_major": ("lite_merge_gather", _merge_column_major),
     "merge_channel_interleaved": ("lite_merge_gather", _merge_channel_interleaved),
     "unpatchify_swapped_w": ("lite_unpatchify", _unpatchify_swapped_w),
+    "fp8_truncate": ("fp8_e4m3_round", _fp8_truncate),
+    "fp8_ties_away": ("fp8_e4m3_round", _fp8_ties_away),
+    "fp8_scale_127": ("quant_scale", _scale_int8_max),
+    "fp8_linear_no_wscale": ("fp8_linear", _fp8_linear_no_wscale),
+    "fp8_linear_per_tensor_x": ("fp8_linear", _fp8_linear_per_tensor_x),
 }
 
 PIN_TESTS = [f for name, f in inspect.getmembers(pins, inspect.isfunction) if name.startswith("test_")]

@@ -542,3 +542,60 @@ def test_lite_selector_round_trip_and_odd_grid():
     np.testing.assert_array_equal(picked, x[0])
     with pytest.raises(ValueError):
         oracle.lite_merge_gather(np.zeros((1, 21 * 45 * 80, 2)), (21, 45, 80))
+
+
+# ------------------------------------------------------------------ FP8 (E4M3) quantization
+
+
+def _torch_fp8(v):
+    return torch.tensor(v, dtype=torch.float64).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_fp8_e4m3_rounding_closed_forms_and_library():
+    """OCP E4M3: largest 448, smallest subnormal 2^-9; ties go to the even mantissa; the
+    rounding agrees with torch's float8_e4m3fn conversion on every in-range test value."""
+    r = oracle.fp8_e4m3_round
+    cases = {448.0: 448.0, 460.0: 448.0, 240.0: 240.0, 17.0: 16.0, 19.0: 20.0, 1.0625: 1.0, 1.1875: 1.25,
+             2.0 ** -9: 2.0 ** -9, 2.0 ** -10: 0.0, 3 * 2.0 ** -10: 2 * 2.0 ** -9, 2.0 ** -6: 2.0 ** -6,
+             0.0: 0.0, -3.3: -3.25, -0.3: -0.3125}
+    for x, want in cases.items():
+        assert r(np.array([x]))[0] == want, (x, r(np.array([x]))[0], want)
+    codes = np.arange(127, dtype=np.uint8)                       # 0x00 .. 0x7E: the finite non-negatives
+    vals = oracle.fp8_e4m3_decode(codes)
+    assert vals[-1] == 448.0 and np.all(np.diff(vals) > 0) and vals[1] == 2.0 ** -9
+    np.testing.assert_array_equal(oracle.fp8_e4m3_code(vals), codes)
+    rng = np.random.default_rng(90)
+    mids = (vals[:-1] + vals[1:]) / 2
+    xs = np.concatenate([vals, -vals, mids, -mids, rng.uniform(-448, 448, 5000),
+                         rng.standard_normal(3000) * 2.0 ** rng.integers(-12, 6, 3000)])
+    xs = xs.astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(r(xs), _torch_fp8(xs))
+
+
+def test_fp8_quantization_per_row_and_per_tensor():
+    rng = np.random.default_rng(91)
+    x = rng.standard_normal((6, 40)) * np.array([1e-3, 0.5, 1, 10, 300, 0])[:, None]
+    q, s = oracle.quantize_fp8(x, per_row=True)
+    assert s.dtype == np.float32 and s[-1] == 1.0 and np.all(q[-1] == 0)          # all-zero row
+    amax = np.abs(x.astype(np.float32)).max(axis=1)
+    for i in range(5):
+        assert s[i] == np.float32(amax[i]) / np.float32(448)
+        assert np.abs(q[i]).max() == 448.0                                        # the row's amax lands on 448
+        err = np.abs(q[i] * s[i] - x[i])
+        assert np.all(err <= np.maximum(np.abs(x[i]) * 2.0 ** -4, 2.0 ** -10 * s[i]) * (1 + 1e-6))
+    qt, st = oracle.quantize_fp8(x, per_row=False)
+    assert st.shape == (1,) and st[0] == np.float32(amax.max()) / np.float32(448)
+    assert np.abs(qt).max() == 448.0
+
+
+def test_fp8_linear_against_bruteforce_loops():
+    rng = np.random.default_rng(92)
+    x = rng.standard_normal((5, 24))
+    w = rng.standard_normal((7, 24)) * 0.05
+    b = rng.standard_normal(7) * 0.1
+    got = oracle.fp8_linear(x, w, b)
+    ref = bf.fp8_linear(x.tolist(), w.tolist(), b.tolist(), lambda v: float(_torch_fp8(np.array([v]))[0]))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # and the quantization error stays within the E4M3 rounding bound of the exact product
+    exact = x @ w.T + b
+    assert np.max(np.abs(got - exact)) / np.sqrt(np.mean(exact ** 2)) < 0.2
