@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "joint-attn TFLOP/s + % bf16 MFMA peak; block tokens/s at 32760+512 tokens"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
 
 # HBM bytes per launch of the attention kernel at this workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
@@ -164,7 +165,37 @@ def next_rows(dev):
                               "shape": f"M={cfg.n_merged} N={cfg.width} K={4 * cfg.width}, bf16 in/out"}
     out["lite_unpatchify_480p"] = {"ms": round(ms_u, 4), "tflops": round(half / (ms_u * 1e-3) / 1e12, 1),
                                    "shape": f"M={cfg.n_merged} N={4 * cfg.width} K={cfg.width}, bf16 in/out"}
+    del t, ym, yu
+    out["fp8_gemm_480p"] = fp8_gemms(dev)
     return out
+
+
+def fp8_gemms(dev):
+    """The visual stream's four GEMM shapes at 480p (M = 32760) with FP8 operands (per-token
+    x scales, per-tensor W scale) beside the same shapes with f16 operands, and the
+    per-token quantization of the two activation widths."""
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    M = 32760
+    g = torch.Generator(device=dev).manual_seed(0)
+    res = {}
+    for name, N, K, epi in (("qkv", 9216, 3072, mm.EPI_NONE), ("out_proj", 3072, 3072, mm.EPI_NONE),
+                            ("ffn_up", 12288, 3072, mm.EPI_GELU), ("ffn_down", 3072, 12288, mm.EPI_NONE)):
+        x = torch.randn((M, K), generator=g, device=dev, dtype=torch.float16)
+        w = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float16) * 0.02)
+        xq, xs = mm.quantize_fp8(x)
+        wq, ws = mm.quantize_fp8(w, per_row=False)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        fl = 2.0 * M * N * K
+        ms8 = time_calls(lambda: mm.linear_fp8(xq, xs, wq, ws, None, epilogue=epi, y=y), reps=10)
+        ms16 = time_calls(lambda: mm.linear(x, w, None, epilogue=epi, y=y), reps=10)
+        msq = time_calls(lambda: mm.quantize_fp8(x, q=xq, scales=xs), reps=10)
+        res[name] = {"M": M, "N": N, "K": K, "fp8_ms": round(ms8, 4), "fp8_tflops": round(fl / ms8 / 1e9, 1),
+                     "fp8_frac_peak": round(fl / ms8 / 1e9 / PEAK_FP8_TFLOPS, 4),
+                     "f16_ms": round(ms16, 4), "f16_tflops": round(fl / ms16 / 1e9, 1),
+                     "quantize_x_ms": round(msq, 4), "quantize_x_GB_per_s": round(M * K * 3 / msq / 1e6, 1)}
+        del x, w, xq, wq, y
+    return res
 
 
 def main():

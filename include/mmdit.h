@@ -40,7 +40,9 @@
 extern "C" {
 #endif
 
-enum mmdit_dtype { MMDIT_F32 = 0, MMDIT_BF16 = 1, MMDIT_F16 = 2 };
+/* MMDIT_FP8_E4M3: the OCP 8-bit float (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * largest finite value 448, no infinities), accepted only where a call says so. */
+enum mmdit_dtype { MMDIT_F32 = 0, MMDIT_BF16 = 1, MMDIT_F16 = 2, MMDIT_FP8_E4M3 = 3 };
 
 enum mmdit_status {
   MMDIT_OK = 0,
@@ -168,6 +170,42 @@ int mmdit_linear(const void* x, const void* w, int x_dtype,
                  int epilogue, const void* res, int res_dtype,
                  const float* gate, int64_t gate_stride, int64_t rows_per_batch,
                  void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_quantize_fp8 -- symmetric FP8 E4M3 quantization, with one scale per row (per_row
+ * != 0: per-token activations) or one for the whole tensor (per_row == 0: weights), the
+ * scaling of the Wan report's FP8 GEMMs (section 4.4.3).
+ *
+ *   s = amax / 448 in f32 (amax over the row or the tensor; an all-zero group gets s = 1)
+ *   q = E4M3(clamp(x * (1/s), -448, 448)), rounded to nearest, ties to even
+ *
+ * x [rows, cols] x_dtype F32 | BF16 | F16, contiguous; q [rows, cols] E4M3 codes (bytes);
+ * scales [rows] (per_row) or [1] f32.  cols a multiple of 8.  The per-tensor form runs four
+ * kernels (clear, amax, quantize, scale) and uses scales[0] as its accumulator.  Outputs
+ * must not overlap x or each other.
+ * ------------------------------------------------------------------------------- */
+int mmdit_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row,
+                       void* q, float* scales, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * mmdit_linear_fp8 -- mmdit_linear on FP8 operands (Wan report, section 4.4.3: FP8 GEMM with
+ * per-tensor weight and per-token activation scales):
+ *
+ *   y = epilogue((xq wq^T) * x_scale[m] * w_scale[0] + bias)
+ *
+ * xq [M, K], wq [N, K] E4M3 codes (from mmdit_quantize_fp8); x_scale [M], w_scale [1] f32.
+ * The products of the codes are summed by the gfx950 8-bit MFMA (32 x 32 x 64) into f32;
+ * the hardware does not sum the 64 products of one instruction exactly (it deviates from the
+ * exact sum by up to ~4e-5 of the result's rms).  Everything else (bias, epilogues, res,
+ * gate, rows_per_batch, dtypes of bias / y / res, the 2^31-byte limit with one byte per
+ * element, alignment, aliasing) is as for mmdit_linear.  K a multiple of 64.
+ * ------------------------------------------------------------------------------- */
+int mmdit_linear_fp8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                     const void* bias, int bias_dtype, void* y, int y_dtype,
+                     int64_t M, int64_t N, int64_t K,
+                     int epilogue, const void* res, int res_dtype,
+                     const float* gate, int64_t gate_stride, int64_t rows_per_batch,
+                     void* stream);
 
 /* ---------------------------------------------------------------------------------
  * mmdit_modulation -- the per-(block, stream) modulation Linear: the shared timestep

@@ -178,3 +178,22 @@ def test_lite_merge_unpatchify_validation(L):
         assert fn(p, mm.BF16, p, None, mm.BF16, p, mm.F32, 1, 21, 30, 52, 3072, None) == ERR_ALIAS
         assert fn(p, mm.BF16, p, None, mm.BF16, y, mm.F32, 16, 21, 30, 52, 3072, None) == ERR_SHAPE  # > 2^31 B
         assert fn(None, mm.BF16, None, None, mm.BF16, None, mm.F32, 0, 21, 30, 52, 3072, None) == 0  # empty
+
+
+def test_fp8_validation(L):
+    p, y = _fake(0x10000), _fake(0x900000)
+    assert L.mmdit_quantize_fp8(p, mm.BF16, 4, 12, 1, y, _fake(0xA00000), None) == ERR_SHAPE      # cols % 8
+    assert L.mmdit_quantize_fp8(p, mm.FP8_E4M3, 4, 16, 1, y, _fake(0xA00000), None) == ERR_DTYPE
+    assert L.mmdit_quantize_fp8(p, mm.BF16, 4, 16, 1, None, _fake(0xA00000), None) == ERR_NULL
+    assert L.mmdit_quantize_fp8(p, mm.BF16, 4, 16, 1, _fake(0x900008), _fake(0xA00000), None) == ERR_ALIGN
+    assert L.mmdit_quantize_fp8(p, mm.BF16, 4, 16, 1, p, _fake(0xA00000), None) == ERR_ALIAS
+    assert L.mmdit_quantize_fp8(None, mm.BF16, 0, 16, 1, None, None, None) == 0
+    s = _fake(0xB00000)
+    assert L.mmdit_linear_fp8(p, s, p, s, None, mm.BF16, y, mm.F32, 10, 256, 100, mm.EPI_NONE, None, mm.F32,
+                              None, 0, 10, None) == ERR_SHAPE                                     # K % 64
+    assert L.mmdit_linear_fp8(p, None, p, s, None, mm.BF16, y, mm.F32, 10, 256, 128, mm.EPI_NONE, None, mm.F32,
+                              None, 0, 10, None) == ERR_NULL                                      # x_scale
+    assert L.mmdit_linear_fp8(p, s, p, s, None, mm.BF16, p, mm.F32, 10, 256, 128, mm.EPI_NONE, None, mm.F32,
+                              None, 0, 10, None) == ERR_ALIAS
+    assert L.mmdit_linear_fp8(p, s, p, s, None, mm.BF16, y, mm.F32, 1 << 24, 256, 256, mm.EPI_NONE, None, mm.F32,
+                              None, 0, 10, None) == ERR_SHAPE                                     # 2^31 bytes

@@ -14,7 +14,7 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import torch
 
-F32, BF16, F16 = 0, 1, 2
+F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 EPI_NONE, EPI_GELU, EPI_GATED_RES = 0, 1, 2
 WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_WQKV, WS_WO, WS_W1, WS_W2 = range(9)
 WS_COUNT = 9
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "mmdit_modulation": [vp, vp, vp, i, vp, i64, i64, i64, vp],
         "mmdit_lite_merge": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
         "mmdit_lite_unpatchify": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
+        "mmdit_quantize_fp8": [vp, i, i64, i64, i, vp, vp, vp],
+        "mmdit_linear_fp8": [vp, vp, vp, vp, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
         "mmdit_timestep_embed": [vp, i64, vp, vp, vp, vp, vp, vp, i, i64, i64, i64, f, vp, vp, vp, vp],
         "mmdit_block_workspace_offsets": [ctypes.POINTER(BlockDims), i64, i64, i64, ctypes.POINTER(c_size_t)],
         "mmdit_block_fwd": [ctypes.POINTER(BlockDims), ctypes.POINTER(StreamWeights),
@@ -277,6 +279,52 @@ def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None
                             epilogue, _ptr(res), _dt(res) if res is not None else F32, _ptr(gate), gs,
                             rows_per_batch or M, _stream(x))
     _check(st, "mmdit_linear")
+    return y
+
+
+def quantize_fp8(x: torch.Tensor, per_row: bool = True, q: Optional[torch.Tensor] = None,
+                 scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """FP8 E4M3 codes (torch.uint8, same shape as x) and f32 scales ([rows] per row, [1] per
+    tensor) of a contiguous 2-D x."""
+    _need_gpu(x, q, scales)
+    if x.dim() != 2 or not x.is_contiguous():
+        raise MmditError("x must be a contiguous [rows, cols] tensor")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty((rows if per_row else 1,), dtype=torch.float32, device=x.device) if scales is None else scales
+    if q.dtype != torch.uint8 or q.shape != (rows, cols) or scales.dtype != torch.float32:
+        raise MmditError("q must be uint8 [rows, cols] and scales f32")
+    st = lib().mmdit_quantize_fp8(x.data_ptr(), _dt(x), rows, cols, 1 if per_row else 0, q.data_ptr(),
+                                  scales.data_ptr(), _stream(x))
+    _check(st, "mmdit_quantize_fp8")
+    return q, scales
+
+
+def linear_fp8(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+               bias: Optional[torch.Tensor] = None, *, epilogue: int = EPI_NONE,
+               res: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+               rows_per_batch: Optional[int] = None, y: Optional[torch.Tensor] = None,
+               y_dtype=torch.bfloat16) -> torch.Tensor:
+    """y = epilogue((xq wq^T) x_scale[m] w_scale + bias) on E4M3 codes (uint8 tensors)."""
+    _need_gpu(xq, x_scale, wq, w_scale, bias, res, gate, y)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if xq.dtype != torch.uint8 or wq.dtype != torch.uint8 or wq.shape[1] != K:
+        raise MmditError("xq [M, K] and wq [N, K] must be uint8 E4M3 codes")
+    if not (xq.is_contiguous() and wq.is_contiguous()):
+        raise MmditError("xq and wq must be contiguous")
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=xq.device)
+    gs = 0
+    if gate is not None:
+        if gate.dtype != torch.float32 or gate.stride(-1) != 1:
+            raise MmditError("gate must be f32 with unit inner stride")
+        gs = gate.stride(0) if gate.dim() == 2 else N
+    st = lib().mmdit_linear_fp8(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(), _ptr(bias),
+                                _dt(bias) if bias is not None else BF16, y.data_ptr(), _dt(y), M, N, K, epilogue,
+                                _ptr(res), _dt(res) if res is not None else F32, _ptr(gate), gs,
+                                rows_per_batch or M, _stream(xq))
+    _check(st, "mmdit_linear_fp8")
     return y
 
 

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmmdit.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "block.hip", "gemm.hip", "joint_attention.hip", "modulate_ln.hip",
+SOURCES = ["api.hip", "block.hip", "gemm.hip", "joint_attention.hip", "modulate_ln.hip", "quant.hip",
            "modulation.hip", "qk_norm_rope.hip"]
 
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",

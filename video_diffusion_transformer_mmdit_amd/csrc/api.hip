@@ -230,6 +230,61 @@ int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, in
                        static_cast<hipStream_t>(stream));
 }
 
+int mmdit_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row, void* q,
+                       float* scales, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || cols < 8 || cols % 8 || cols > ((int64_t)1 << 30))
+    return fail(MMDIT_ERR_SHAPE, "quantize_fp8: cols must be a positive multiple of 8");
+  if (!valid_dtype(x_dtype)) return fail(MMDIT_ERR_DTYPE, "quantize_fp8: x must be f32, bf16 or f16");
+  if (rows == 0) return MMDIT_OK;
+  if (!x || !q || !scales) return fail(MMDIT_ERR_NULL, "quantize_fp8: x, q, scales required");
+  if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(scales) & 3))
+    return fail(MMDIT_ERR_ALIGN, "quantize_fp8: x and q must be 16-byte aligned, scales 4-byte aligned");
+  const size_t n = (size_t)(rows * cols), ns = (size_t)(per_row ? rows : 1) * 4;
+  if (overlaps(q, n, x, n * dtype_size(x_dtype)) || overlaps(scales, ns, x, n * dtype_size(x_dtype)) ||
+      overlaps(scales, ns, q, n))
+    return fail(MMDIT_ERR_ALIAS, "quantize_fp8: outputs overlap x or each other");
+  return launch_quantize_fp8(x, x_dtype, rows, cols, per_row ? 1 : 0, static_cast<uint8_t*>(q), scales,
+                             static_cast<hipStream_t>(stream));
+}
+
+int mmdit_linear_fp8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                     const void* bias, int bias_dtype, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                     int epilogue, const void* res, int res_dtype, const float* gate, int64_t gate_stride,
+                     int64_t rows_per_batch, void* stream) {
+  g_last_error.clear();
+  if (M < 0 || N < 0 || K < 64 || K % 64 || N % 4)
+    return fail(MMDIT_ERR_SHAPE, "linear_fp8: need M, N >= 0, N a multiple of 4 and K a positive multiple of 64");
+  if ((M + 256) * K >= ((int64_t)1 << 31) || (N + 256) * K >= ((int64_t)1 << 31))
+    return fail(MMDIT_ERR_SHAPE, "linear_fp8: x or w too large for 32-bit buffer offsets");
+  if (bias && bias_dtype != MMDIT_F32 && bias_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear_fp8: bias must be f32 or bf16");
+  if (!valid_dtype(y_dtype)) return fail(MMDIT_ERR_DTYPE, "linear_fp8: bad y dtype");
+  if (epilogue < MMDIT_EPI_NONE || epilogue > MMDIT_EPI_GATED_RES) return fail(MMDIT_ERR_SHAPE, "linear_fp8: bad epilogue");
+  if (epilogue == MMDIT_EPI_GATED_RES) {
+    if (res_dtype != MMDIT_F32 && res_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear_fp8: res must be f32 or bf16");
+    if (y_dtype == MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "linear_fp8: gated residual output must be f32 or bf16");
+    if (rows_per_batch < 1 || gate_stride < N || gate_stride % 4)
+      return fail(MMDIT_ERR_SHAPE, "linear_fp8: rows_per_batch >= 1 and gate_stride >= N, a multiple of 4");
+  }
+  if (M == 0 || N == 0) return MMDIT_OK;
+  if (!xq || !wq || !y || !x_scale || !w_scale) return fail(MMDIT_ERR_NULL, "linear_fp8: xq, x_scale, wq, w_scale, y required");
+  if (epilogue == MMDIT_EPI_GATED_RES && (!res || !gate)) return fail(MMDIT_ERR_NULL, "linear_fp8: res and gate required");
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || (bias && !aligned16(bias)) || (res && !aligned16(res)) ||
+      (gate && !aligned16(gate)) || (reinterpret_cast<uintptr_t>(x_scale) & 3) || (reinterpret_cast<uintptr_t>(w_scale) & 3))
+    return fail(MMDIT_ERR_ALIGN, "linear_fp8: pointers must be 16-byte aligned (scales 4-byte)");
+  const size_t ny = (size_t)(M * N) * dtype_size(y_dtype);
+  if (overlaps(y, ny, xq, (size_t)(M * K)) || overlaps(y, ny, wq, (size_t)(N * K)) ||
+      overlaps(y, ny, x_scale, (size_t)M * 4) || overlaps(y, ny, w_scale, 4) ||
+      (res && res != y && overlaps(y, ny, res, (size_t)(M * N) * dtype_size(res_dtype))))
+    return fail(MMDIT_ERR_ALIAS, "linear_fp8: y overlaps an input");
+  GemmProblem p{};
+  p.x = xq; p.w = wq; p.bias = bias; p.y = y; p.res = res; p.gate = gate; p.M = M;
+  p.gate_stride = gate_stride; p.rows_per_batch = rows_per_batch > 0 ? rows_per_batch : M;
+  p.x_scale = x_scale; p.w_scale = w_scale;
+  return launch_linear(&p, 1, MMDIT_FP8_E4M3, bias_dtype, y_dtype, N, K, epilogue, res_dtype,
+                       static_cast<hipStream_t>(stream));
+}
+
 int mmdit_modulation(const void* w_mod, const void* b_mod, const void* tvec, int t_dtype, float* mod,
                      int64_t B, int64_t C6, int64_t Dt, void* stream) {
   g_last_error.clear();

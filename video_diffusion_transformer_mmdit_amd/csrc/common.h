@@ -107,7 +107,7 @@ void set_error(const std::string& msg);
 int fail(int status, const std::string& msg);
 int check_launch(const char* what);
 
-inline int dtype_size(int dt) { return dt == MMDIT_F32 ? 4 : 2; }
+inline int dtype_size(int dt) { return dt == MMDIT_F32 ? 4 : dt == MMDIT_FP8_E4M3 ? 1 : 2; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Internal launchers (validated arguments only).
@@ -136,6 +136,8 @@ struct GemmProblem {
   int64_t M;
   int64_t gate_stride;
   int64_t rows_per_batch;
+  const float* x_scale;  // FP8 operands: [M] per-row scale of x
+  const float* w_scale;  // FP8 operands: [1] scale of all of W
 };
 // Operand layouts of the GEMM kernel: plain row-major x and y, or the Lite 2x2 regrouping.
 enum { GEMM_PLAIN = 0, GEMM_GATHER_X = 1, GEMM_SCATTER_Y = 2 };
@@ -145,6 +147,9 @@ int launch_lite_regroup(int layout, const void* x, const void* w, const void* bi
 // Runs one or two problems with equal N, K, dtypes and epilogue in one launch.
 int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dtype, int y_dtype,
                   int64_t N, int64_t K, int epilogue, int res_dtype, hipStream_t stream);
+// FP8 E4M3 quantization with a scale per row (per_row) or one for the whole tensor.
+int launch_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row, uint8_t* q,
+                        float* scales, hipStream_t stream);
 int launch_modulation(const void* w_mod, const void* b_mod, const void* tvec, int t_dtype,
                       float* mod, int64_t B, int64_t C6, int64_t Dt, hipStream_t stream);
 int launch_timestep_embed(const float* t, int64_t B, const void* w1, const void* b1, const void* w2,

@@ -60,6 +60,18 @@ __device__ __forceinline__ int merged_row0(int m, const GemmArgs& a) {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// FP8 E4M3 x E4M3, 32 x 32 x 64, unit block scales (the E8M0 exponent 127 is 2^0); each
+// operand is 32 bytes per lane, passed as two 16-byte halves.
+__device__ __forceinline__ f32x16 mfma_fp8(const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1,
+                                           const f32x16& c) {
+  const i32x8 a = __builtin_shufflevector(__builtin_bit_cast(i32x4, a0), __builtin_bit_cast(i32x4, a1), 0, 1, 2, 3, 4, 5, 6, 7);
+  const i32x8 b = __builtin_shufflevector(__builtin_bit_cast(i32x4, b0), __builtin_bit_cast(i32x4, b1), 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 template <int IN_DT>
 __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
   if constexpr (IN_DT == MMDIT_BF16)
@@ -140,6 +152,12 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* opaque_lds(__
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs args) {
+  // FP8 operands: one byte per element, so a 64-byte stage row holds 64 K values and each
+  // 32 x 32 output tile takes one 32 x 32 x 64 MFMA per stage instead of two 32 x 32 x 16.
+  constexpr bool FP8 = IN_DT == MMDIT_FP8_E4M3;
+  constexpr int ES = FP8 ? 1 : 2;
+  constexpr int KSTEP = 64 / ES;
+  static_assert(!FP8 || LAYOUT == GEMM_PLAIN, "FP8 operands use the plain layout");
   // one LDS object per stage: x tile, then W tile
   __shared__ __attribute__((aligned(16))) uint8_t lds_s0[2 * G_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_s1[2 * G_TILE_BYTES];
@@ -177,8 +195,8 @@ void gemm_kernel(GemmArgs args) {
   // merged_row0(m) + (s / 2) W + s % 2, s = k / C (a K stage never straddles two neighbours
   // as C is a multiple of 32).  The per-row part is per lane, the neighbour part scalar.
   // Rows m >= M get an offset past the end of x, so they load zeros.
-  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * 2);
-  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * 2);
+  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * ES);
+  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * ES);
   int xo[4], wo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -187,16 +205,16 @@ void gemm_kernel(GemmArgs args) {
     if constexpr (LAYOUT == GEMM_GATHER_X)
       xo[i] = (m0 + row < M ? merged_row0(m0 + row, args) * args.c * 2 + lc * 16 : 0x7FFF0000) - i * 1024;
     else
-      xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - i * 1024;
-    wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - i * 1024;
+      xo[i] = (m0 + row) * (int)K * ES + lc * 16 - i * 1024;
+    wo[i] = (n0 + row) * (int)K * ES + lc * 16 - i * 1024;
   }
   auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
-    int xso = k0 * 2;
+    int xso = k0 * ES;
     if constexpr (LAYOUT == GEMM_GATHER_X) {
       const int sg = __builtin_amdgcn_readfirstlane(k0 / args.c);
       xso = (((sg >> 1) * args.w + (sg & 1)) * args.c + (k0 - sg * args.c)) * 2;
     }
-    const int so = k0 * 2;
+    const int so = k0 * ES;
     auto* lx = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 4096));
     auto* lw = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 4096));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], xso, 0, 0);
@@ -233,7 +251,7 @@ void gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
 
-  const int nk = (int)(K / GBK);
+  const int nk = (int)(K / KSTEP);
   auto gbarrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -264,7 +282,7 @@ void gemm_kernel(GemmArgs args) {
     constexpr std::integral_constant<int, (CUR + 3) & 3> ahead{};
     // stage kt+3 goes into the buffers stage kt-1 used (every wave has passed the barrier
     // that ended stage kt-1)
-    if (MAIN || kt + 3 < nk) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * GBK);
+    if (MAIN || kt + 3 < nk) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP);
     uint4 wf1[4], xf1[4];
     read_slice(xbuf(cur), wbuf(cur), 1, wf1, xf1);
     mma(wf0, xf0);
@@ -278,37 +296,83 @@ void gemm_kernel(GemmArgs args) {
       if ((i < 4) || (i >= 16 && i < 24)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
       if (MAIN && i >= 4 && i < 12) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // this wave's loads of stage kt+2 have landed once at most the eight loads of stage kt+3
     // are outstanding; after the barrier stage kt+2 is in LDS for everyone
     if (MAIN || kt + 3 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
     gbarrier();
   };
+  // FP8: the whole 32-byte fragments of a stage (both 16-byte halves) are read one stage
+  // ahead into one of two register sets (stage parity), while the 16 MFMAs of the current
+  // stage run on the other.
+  uint4 fw8[2][4][2], fx8[2][4][2];
+  auto read8 = [&](const uint8_t* xs, const uint8_t* ws, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fw8[BUF][j][h] = *reinterpret_cast<const uint4*>(ws + (wn * 128 + j * 32) * 64 + cofs[h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fx8[BUF][i][h] = *reinterpret_cast<const uint4*>(xs + (wm * 128 + i * 32) * 64 + cofs[h]);
+    }
+  };
+  auto step8 = [&](auto cur_c, auto main_c, int kt) {
+    constexpr int CUR = decltype(cur_c)::value;
+    constexpr bool MAIN = decltype(main_c)::value;
+    constexpr std::integral_constant<int, (CUR + 1) & 3> next{};
+    constexpr std::integral_constant<int, (CUR + 3) & 3> ahead{};
+    constexpr std::integral_constant<int, CUR & 1> buf{};
+    constexpr std::integral_constant<int, (CUR + 1) & 1> nbuf{};
+    if (MAIN || kt + 3 < nk) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP);
+    if (MAIN || kt + 1 < nk) read8(xbuf(next), wbuf(next), nbuf);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = mfma_fp8(fw8[buf][j][0], fw8[buf][j][1], fx8[buf][i][0], fx8[buf][i][1], acc[j][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+      if (MAIN && i >= 2 && i < 10) __builtin_amdgcn_sched_group_barrier(0x010, 1, 2);
+    }
+    // the MFMAs only touch registers: keep the scheduler from moving them past the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    if (MAIN || kt + 3 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
+    gbarrier();
+  };
+  auto run = [&](auto cur_c, auto main_c, int kt) {
+    if constexpr (FP8) step8(cur_c, main_c, kt);
+    else step(cur_c, main_c, kt);
+  };
   constexpr std::true_type MAIN{};
   constexpr std::false_type TAIL{};
 
   dma(xbuf(S0), wbuf(S0), 0);
-  if (1 < nk) dma(xbuf(S1), wbuf(S1), GBK);
-  if (2 < nk) dma(xbuf(S2), wbuf(S2), 2 * GBK);
+  if (1 < nk) dma(xbuf(S1), wbuf(S1), KSTEP);
+  if (2 < nk) dma(xbuf(S2), wbuf(S2), 2 * KSTEP);
   // stages 0 and 1 must be in LDS; stage 2 may still be in flight
   if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
   else __builtin_amdgcn_s_waitcnt(0x0F70);
   gbarrier();
-  read_slice(xbuf(S0), wbuf(S0), 0, wf0, xf0);
+  if constexpr (FP8) read8(xbuf(S0), wbuf(S0), std::integral_constant<int, 0>{});
+  else read_slice(xbuf(S0), wbuf(S0), 0, wf0, xf0);
   int kt = 0;
   for (; kt + 6 < nk; kt += 4) {   // every step of the group has its stage kt+3
-    step(S0, MAIN, kt);
-    step(S1, MAIN, kt + 1);
-    step(S2, MAIN, kt + 2);
-    step(S3, MAIN, kt + 3);
+    run(S0, MAIN, kt);
+    run(S1, MAIN, kt + 1);
+    run(S2, MAIN, kt + 2);
+    run(S3, MAIN, kt + 3);
   }
   // at most six stages remain (kt % 4 == 0)
-  if (kt < nk) step(S0, TAIL, kt);
-  if (kt + 1 < nk) step(S1, TAIL, kt + 1);
-  if (kt + 2 < nk) step(S2, TAIL, kt + 2);
-  if (kt + 3 < nk) step(S3, TAIL, kt + 3);
-  if (kt + 4 < nk) step(S0, TAIL, kt + 4);
-  if (kt + 5 < nk) step(S1, TAIL, kt + 5);
+  if (kt < nk) run(S0, TAIL, kt);
+  if (kt + 1 < nk) run(S1, TAIL, kt + 1);
+  if (kt + 2 < nk) run(S2, TAIL, kt + 2);
+  if (kt + 3 < nk) run(S3, TAIL, kt + 3);
+  if (kt + 4 < nk) run(S0, TAIL, kt + 4);
+  if (kt + 5 < nk) run(S1, TAIL, kt + 5);
 
   // ---- epilogue: lane holds C^T rows (output columns) 8 (e/4) + 4 g + e%4 of each 32 x 32
   // tile at output row l32: four consecutive columns per e/4.
@@ -326,6 +390,16 @@ void gemm_kernel(GemmArgs args) {
       y_rows[i] = m < M ? (int64_t)merged_row0(m, args) + (sg >> 1) * args.w + (sg & 1) : 0;
     }
   }
+  // FP8: the product of the codes times the row's scale and W's scale
+  float rsc[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (FP8) {
+    const float sw = *P.w_scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + l32;
+      rsc[i] = m < M ? P.x_scale[m] * sw : 0.f;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -341,7 +415,8 @@ void gemm_kernel(GemmArgs args) {
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          v[q] = acc[j][i][4 * e4 + q] + bias[q];
+          if constexpr (FP8) v[q] = fmaf(acc[j][i][4 * e4 + q], rsc[i], bias[q]);
+          else v[q] = acc[j][i][4 * e4 + q] + bias[q];
           if constexpr (EPI == MMDIT_EPI_GELU) v[q] = gelu_erf(v[q]);
         }
         if constexpr (EPI == MMDIT_EPI_GATED_RES) {
@@ -401,10 +476,11 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   const int64_t nTn = (N + GBN - 1) / GBN;
   int64_t tiles[2] = {0, 0};
   // x and W are addressed through 32-bit buffer offsets, a tile's rows may run 256 past M
-  if (N % 4 || (N + GBN) * K * 2 >= ((int64_t)1 << 31))
-    return fail(MMDIT_ERR_SHAPE, "linear: need N a multiple of 4 and (N + 256) * K * 2 < 2^31");
+  const int64_t es = dtype_size(x_dtype);
+  if (N % 4 || (N + GBN) * K * es >= ((int64_t)1 << 31))
+    return fail(MMDIT_ERR_SHAPE, "linear: need N a multiple of 4 and (N + 256) * K * elem < 2^31");
   for (int i = 0; i < nprobs; ++i) {
-    if ((probs[i].M + GBM) * K * 2 >= ((int64_t)1 << 31))
+    if ((probs[i].M + GBM) * K * es >= ((int64_t)1 << 31))
       return fail(MMDIT_ERR_SHAPE, "linear: need (M + 256) * K * 2 < 2^31");
     a.p[i] = probs[i];
     tiles[i] = ((probs[i].M + GBM - 1) / GBM) * nTn;
@@ -435,6 +511,7 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   GEMM_CASE(IN, MMDIT_BF16, MMDIT_EPI_GATED_RES, MMDIT_BF16)
   GEMM_IN(MMDIT_BF16)
   GEMM_IN(MMDIT_F16)
+  GEMM_IN(MMDIT_FP8_E4M3)
 #undef GEMM_IN
 #undef GEMM_CASE
   return fail(MMDIT_ERR_DTYPE, "linear: unsupported dtype / epilogue combination");
