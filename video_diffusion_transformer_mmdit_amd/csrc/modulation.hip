@@ -23,13 +23,12 @@ enum { GEMV_IN_PLAIN = 0,      // x[b, k] as stored (dtype TDT)
 // WDT (bias the same dtype, or null).  Each group of LPR lanes owns ROWS rows and walks
 // them in 16-byte chunks; LPR < 64 serves short rows (K / 8 < 64) without idle lanes.
 // Consecutive row groups are consecutive in memory, so a wave reads one contiguous span.
-template <int IN, int TDT, int WDT, int LPR>
+template <int IN, int TDT, int WDT, int LPR, int ROWS>
 __global__ __launch_bounds__(MOD_THREADS) void gemv_kernel(
     const void* __restrict__ w, const void* __restrict__ bias, const void* __restrict__ x,
     float* __restrict__ y, int B, int64_t R, int K, double log_max_period) {
-  constexpr int ROWS = LPR == 64 ? 4 : 1;
   constexpr int GROUPS = 64 / LPR;
-  __shared__ float tv[MOD_MAX_T];
+  extern __shared__ float tv[];   // B * K floats
   for (int i = threadIdx.x; i < B * K; i += MOD_THREADS) {
     float v;
     if constexpr (IN == GEMV_IN_PLAIN) {
@@ -91,7 +90,9 @@ static int gemv_dispatch(const void* w, const void* bias, const void* x, float* 
     lpr = 1;
     while (lpr * 2 <= nch) lpr *= 2;
   }
-  const int64_t rows_per_block = (MOD_THREADS / 64) * (64 / lpr) * (lpr == 64 ? 4 : 1);
+  // four rows per lane group while that still leaves two workgroups per CU, else one
+  const int rows = (R / ((MOD_THREADS / 64) * (64 / lpr) * 4) >= 512) ? 4 : 1;
+  const int64_t rows_per_block = (MOD_THREADS / 64) * (64 / lpr) * rows;
   const dim3 grid((unsigned)((R + rows_per_block - 1) / rows_per_block));
   // The input vectors of at most MOD_MAX_T / K batch items fit in LDS at once.
   const int64_t bmax = MOD_MAX_T / K;
@@ -101,8 +102,12 @@ static int gemv_dispatch(const void* w, const void* bias, const void* x, float* 
     if constexpr (IN == GEMV_IN_SINUSOID) xb = static_cast<const float*>(x) + b0;
     else xb = static_cast<const char*>(x) + b0 * K * (TDT == MMDIT_F32 ? 4 : 2);
     float* yb = y + b0 * R;
-#define GEMV_CASE(L) \
-    case L: gemv_kernel<IN, TDT, WDT, L><<<grid, MOD_THREADS, 0, stream>>>(w, bias, xb, yb, bn, R, (int)K, log_max_period); break;
+    const size_t lds = (size_t)bn * K * sizeof(float);
+#define GEMV_CASE(L)                                                                                       \
+    case L:                                                                                                \
+      if (rows == 4) gemv_kernel<IN, TDT, WDT, L, 4><<<grid, MOD_THREADS, lds, stream>>>(w, bias, xb, yb, bn, R, (int)K, log_max_period); \
+      else gemv_kernel<IN, TDT, WDT, L, 1><<<grid, MOD_THREADS, lds, stream>>>(w, bias, xb, yb, bn, R, (int)K, log_max_period); \
+      break;
     switch (lpr) {
       GEMV_CASE(1) GEMV_CASE(2) GEMV_CASE(4) GEMV_CASE(8) GEMV_CASE(16) GEMV_CASE(32) GEMV_CASE(64)
     }
