@@ -35,7 +35,9 @@ design notes of the repository):
   r23 Lite merge/unpatchify is defined for even H and W only (odd grids are rejected);
   r24 FP8 is OCP E4M3 (largest 448), rounding to nearest with ties to even, saturating;
   r25 8-bit scales are amax / qmax in float32 (qmax 448 for E4M3, 127 for INT8), an all-zero
-  group takes scale 1, and the value to round is x * (1/s) formed in float32.
+  group takes scale 1, and the value to round is x * (1/s) formed in float32;
+  r26 / r27 the granularity of the 8-bit attention's scales and its probability rounding
+  (stated at joint_attention_8bit below).
 
 Further sources for the Lite parts: [Vimoo] section 2.4 "Vimoo 1.0-Lite" (2x2 hidden-space
 merge 4C -> C after the input projection, unpatchify C -> 4C after the backbone, time axis
@@ -476,6 +478,122 @@ def fp8_linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndar
     qw, sw = quantize_fp8(w, per_row=False)
     y = (qx @ qw.T) * sx.astype(np.float64)[:, None] * float(sw[0])
     return y if b is None else y + b
+
+
+# ---------------------------------------------- 8-bit joint attention  [Wan-zh 4.4.3]
+#
+# The Wan report (section 4.4.3) keeps S = Q K^T in INT8 and O = P V in FP8 (E4M3), with the
+# cross-block accumulation in FP32.  Readings taken where the page is silent:
+#   r26 Q^ has one INT8 scale per (token, head) and K^ one per (head, block of 64 consecutive
+#       keys of one stream); V has one FP8 scale per (head, channel) over all keys of both
+#       streams; each scale follows r25 (qmax 127 for INT8, 448 for E4M3; INT8 codes are
+#       rint(x * (1/s)) clamped to +-127, ties to even);
+#   r27 logits in log2 units y = RN32(acc * c) with c = RN32(s_q * RN32(s_k * RN32(scale *
+#       log2(e)))), acc the exact integer dot product; the row reference M = ceil(max_j y);
+#       P' = RN32(2^RN32(acc * c + 8 - M)) rounded to E4M3 (so P' <= 256); the row sum uses
+#       the same E4M3 values: O = (sum_j P'_j V^_j) / (sum_j P'_j), V^ the dequantized values.
+# The rounding decisions (codes, P') are taken in float32 as the kernel takes them.
+
+LOG2E = 1.4426950408889634
+ATT8_KEY_BLOCK = 64
+
+
+def quantize_int8(x: np.ndarray, axes) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric INT8 codes of x with one scale per group (the reduced ``axes``), r25 / r26.
+    Returns (codes as float64, scales float32 with the reduced axes kept as size 1)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=axes, keepdims=True)
+    s = quant_scale(amax, INT8_MAX)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    y = (x32 * inv).astype(np.float32)
+    return np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.float64), s
+
+
+def quantize_fp8_groups(x: np.ndarray, axes) -> Tuple[np.ndarray, np.ndarray]:
+    """FP8 E4M3 values of x with one scale per group (reduced ``axes``), r25."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=axes, keepdims=True)
+    s = quant_scale(amax, FP8_E4M3_MAX)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    y = np.clip((x32 * inv).astype(np.float32), -FP8_E4M3_MAX, FP8_E4M3_MAX)
+    return fp8_e4m3_round(y), s
+
+
+def attn8_quantize_stream(q: np.ndarray, k: np.ndarray):
+    """INT8 codes and scales of one stream's Q^ and K^ (r26).  q, k [B, n, H, D].
+    Returns q8 [B, n, H, D], sq [B, n, H], k8 [B, n, H, D], sk [B, H, ceil(n/64)]."""
+    b, n, h, d = q.shape
+    q8, sq = quantize_int8(q, axes=3)
+    nb = -(-n // ATT8_KEY_BLOCK)
+    k8 = np.empty_like(q8)
+    sk = np.empty((b, h, nb), dtype=np.float32)
+    for j in range(nb):
+        blk = k[:, j * ATT8_KEY_BLOCK:(j + 1) * ATT8_KEY_BLOCK]            # [B, <=64, H, D]
+        codes, s = quantize_int8(blk, axes=(1, 3))                          # s [B, 1, H, 1]
+        k8[:, j * ATT8_KEY_BLOCK:(j + 1) * ATT8_KEY_BLOCK] = codes
+        sk[:, :, j] = s[:, 0, :, 0]
+    return q8, sq[..., 0], k8, sk
+
+
+def attn8_quantize_v(v_vis: np.ndarray, v_cond: np.ndarray):
+    """FP8 E4M3 values of V with one scale per (batch, head, channel) over the keys of both
+    streams (r26).  Returns (v8_vis, v8_cond, sv [B, H, D])."""
+    n_vis = v_vis.shape[1]
+    v_all = np.concatenate([v_vis, v_cond], axis=1)
+    v8, sv = quantize_fp8_groups(v_all, axes=1)                             # sv [B, 1, H, D]
+    return v8[:, :n_vis], v8[:, n_vis:], sv[:, 0]
+
+
+def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
+                         scale: Optional[float] = None,
+                         vis_rows: Optional[np.ndarray] = None,
+                         cond_rows: Optional[np.ndarray] = None, chunk: int = 1024,
+                         return_lse: bool = False):
+    """The 8-bit joint attention of [Wan-zh] 4.4.3 under readings r26 / r27.  Inputs as for
+    joint_attention (Q^, K^ already normalised and rotated).  Returns (o_vis, o_cond) and,
+    with ``return_lse``, the natural-log row sums ln(sum_j 2^y_j) of the quantized weights,
+    i.e. ln(sum_j P'_j) + (M - 8) ln 2, laid out [B, H, n_cond + n_vis] ([cond | vis])."""
+    b, _, h, d = q_vis.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kc = np.float32(np.float32(scale) * np.float32(LOG2E))
+    qa, sqa, ka, ska = attn8_quantize_stream(q_vis, k_vis)
+    qc, sqc, kcd, skc = attn8_quantize_stream(q_cond, k_cond)
+    v8v, v8c, sv = attn8_quantize_v(v_vis, v_cond)
+    # keys in [vis | cond] order (any order gives the same result), each with its block scale
+    k8 = np.concatenate([ka, kcd], axis=1)                                  # [B, N, H, D]
+    v8 = np.concatenate([v8v, v8c], axis=1)
+    blk = lambda s_, n: np.repeat(s_, ATT8_KEY_BLOCK, axis=2)[:, :, :n]    # noqa: E731
+    skj = np.concatenate([blk(ska, k_vis.shape[1]), blk(skc, k_cond.shape[1])], axis=2)   # [B, H, N]
+    skcj = (skj * kc).astype(np.float32)
+
+    def run(q8, sq, rows):
+        if rows is not None:
+            q8, sq = q8[:, rows], sq[:, rows]
+        nq = q8.shape[1]
+        out = np.empty((b, nq, h, d), dtype=np.float64)
+        lse = np.empty((b, h, nq), dtype=np.float64)
+        for bi in range(b):
+            for hi in range(h):
+                kk = k8[bi, :, hi, :]
+                for i0 in range(0, nq, chunk):
+                    acc = q8[bi, i0:i0 + chunk, hi, :] @ kk.T                # exact integers
+                    c = (sq[bi, i0:i0 + chunk, hi][:, None] * skcj[bi, hi][None, :]).astype(np.float32)
+                    c = c.astype(np.float64)
+                    y = (acc * c).astype(np.float32)
+                    m = np.ceil(y.max(axis=1, keepdims=True).astype(np.float64))
+                    z = (acc * c + (8.0 - m)).astype(np.float32).astype(np.float64)
+                    p = fp8_e4m3_round(np.exp2(z).astype(np.float32))
+                    ell = p.sum(axis=1, keepdims=True)
+                    out[bi, i0:i0 + chunk, hi, :] = (p @ v8[bi, :, hi, :]) * sv[bi, hi][None, :] / ell
+                    lse[bi, hi, i0:i0 + chunk] = np.log(ell[:, 0]) + (m[:, 0] - 8.0) * math.log(2.0)
+        return out, lse
+
+    o_vis, lse_v = run(qa, sqa, vis_rows)
+    o_cond, lse_c = run(qc, sqc, cond_rows)
+    if return_lse:
+        return o_vis, o_cond, np.concatenate([lse_c, lse_v], axis=2)
+    return o_vis, o_cond
 
 
 # ------------------------------------------------------------------ parity metric (r18)

@@ -223,3 +223,49 @@ def fp8_linear(x, w, b, round_fp8):
         (qr,), sr = quant([r])
         out.append([sum(a * c for a, c in zip(qr, wr)) * sr * sw + bb for wr, bb in zip(qw, b)])
     return out
+
+
+# ------------------------------------------------------------------ 8-bit joint attention
+def attention_8bit(q_rows, k_rows, v_rows, seg_of_key, scale, round_fp8):
+    """One head, loops only.  q_rows: list of (vector, stream) queries; k_rows / v_rows: key
+    and value vectors in any order, seg_of_key[j] = (stream, position in that stream).
+    INT8: one scale per query row, one per 64-key block of a stream; V: one E4M3 scale per
+    channel over all keys.  Scales amax / qmax in float32, codes from x * (1/s) in float32.
+    Logits in log2 units rounded to float32; reference M = ceil of the row's max; weights
+    2^(logit - M + 8) rounded to float32 and then to E4M3; O = sum P V / sum P."""
+    import numpy as np
+    f32 = np.float32
+
+    def scale_of(vals, qmax):
+        amax = f32(max(abs(f32(v)) for v in vals))
+        return f32(amax / f32(qmax)) if amax > 0 else f32(1.0)
+
+    def int8(v, s):
+        inv = f32(f32(1.0) / s)
+        return [int(max(-127.0, min(127.0, float(np.rint(f32(f32(x) * inv)))))) for x in v]
+
+    # key block scales per (stream, block)
+    blocks = {}
+    for j, (sg, pos) in enumerate(seg_of_key):
+        blocks.setdefault((sg, pos // 64), []).extend(k_rows[j])
+    ks = {key: scale_of(vals, 127.0) for key, vals in blocks.items()}
+    k8 = [int8(k_rows[j], ks[(sg, pos // 64)]) for j, (sg, pos) in enumerate(seg_of_key)]
+    d = len(v_rows[0])
+    sv = [scale_of([v_rows[j][c] for j in range(len(v_rows))], 448.0) for c in range(d)]
+    v8 = [[round_fp8(float(min(max(f32(f32(v_rows[j][c]) * f32(f32(1.0) / sv[c])), f32(-448)), f32(448))))
+           for c in range(d)] for j in range(len(v_rows))]
+    kc = f32(f32(scale) * f32(1.4426950408889634))
+    outs = []
+    for qv, _ in q_rows:
+        sq = scale_of(qv, 127.0)
+        q8 = int8(qv, sq)
+        accs, cs = [], []
+        for j, (sg, pos) in enumerate(seg_of_key):
+            accs.append(sum(a * b for a, b in zip(q8, k8[j])))
+            cs.append(float(f32(sq * f32(ks[(sg, pos // 64)] * kc))))
+        y = [float(f32(a * c)) for a, c in zip(accs, cs)]
+        m = math.ceil(max(y))
+        p = [round_fp8(float(f32(2.0 ** float(f32(a * c + (8 - m)))))) for a, c in zip(accs, cs)]
+        ell = sum(p)
+        outs.append([sum(p[j] * v8[j][c] for j in range(len(p))) * float(sv[c]) / ell for c in range(d)])
+    return outs

@@ -18,7 +18,8 @@ ORIG = {name: getattr(om, name) for name in
         ("rope_angles", "rope_rotate", "token_positions", "rms_norm_heads", "softmax_attention",
          "modulate", "layer_norm", "linear", "gelu", "modulation", "joint_attention",
          "timestep_sinusoid", "silu", "timestep_path", "lite_merge_gather", "lite_unpatchify",
-         "fp8_e4m3_round", "quantize_fp8", "fp8_linear", "quant_scale")}
+         "fp8_e4m3_round", "quantize_fp8", "fp8_linear", "quant_scale",
+         "attn8_quantize_stream", "attn8_quantize_v", "quantize_int8", "joint_attention_8bit")}
 
 
 def _rope_sign(x, angles):
@@ -198,6 +199,65 @@ def _fp8_linear_per_tensor_x(x, w, b):
     return y if b is None else y + b
 
 
+def _att8_k_per_token(q, k):
+    q8, sq, _, _ = ORIG["attn8_quantize_stream"](q, k)
+    k8, skt = om.quantize_int8(k, axes=3)                 # per token, not per 64-key block
+    b, n, h, _ = k.shape
+    # keep the interface: one scale per block, taken from the block's first token
+    nb = -(-n // 64)
+    sk = np.stack([skt[:, min(j * 64, n - 1), :, 0] for j in range(nb)], axis=2)
+    return q8, sq, k8, sk
+
+
+def _att8_v_per_tensor(v_vis, v_cond):
+    n_vis = v_vis.shape[1]
+    v_all = np.concatenate([v_vis, v_cond], axis=1)
+    v8, sv = om.quantize_fp8_groups(v_all, axes=(1, 3))
+    return v8[:, :n_vis], v8[:, n_vis:], np.broadcast_to(sv[:, 0], (v_all.shape[0],) + v_all.shape[2:]).copy()
+
+
+def _int8_truncate(x, axes):
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=axes, keepdims=True)
+    s = om.quant_scale(amax, 127.0)
+    y = (x32 * (np.float32(1.0) / s).astype(np.float32)).astype(np.float32)
+    return np.clip(np.trunc(y), -127, 127).astype(np.float64), s
+
+
+def _att8_variant(floor=False, shift=8.0, exact_sum=False):
+    def f(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond, scale=None, vis_rows=None, cond_rows=None,
+          chunk=1024, return_lse=False):
+        b, _, h, d = q_vis.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        kc = np.float32(np.float32(scale) * np.float32(om.LOG2E))
+        qa, sqa, ka, ska = om.attn8_quantize_stream(q_vis, k_vis)
+        qc, sqc, kcd, skc = om.attn8_quantize_stream(q_cond, k_cond)
+        v8v, v8c, sv = om.attn8_quantize_v(v_vis, v_cond)
+        k8 = np.concatenate([ka, kcd], axis=1)
+        v8 = np.concatenate([v8v, v8c], axis=1)
+        blk = lambda s_, n: np.repeat(s_, 64, axis=2)[:, :, :n]  # noqa: E731
+        skcj = (np.concatenate([blk(ska, k_vis.shape[1]), blk(skc, k_cond.shape[1])], axis=2) * kc).astype(np.float32)
+
+        def run(q8, sq, rows):
+            if rows is not None:
+                q8, sq = q8[:, rows], sq[:, rows]
+            out = np.empty(q8.shape)
+            for bi in range(b):
+                for hi in range(h):
+                    acc = q8[bi, :, hi, :] @ k8[bi, :, hi, :].T
+                    c = (sq[bi, :, hi][:, None] * skcj[bi, hi][None, :]).astype(np.float32).astype(np.float64)
+                    y = (acc * c).astype(np.float32).astype(np.float64)
+                    m = (np.floor if floor else np.ceil)(y.max(axis=1, keepdims=True))
+                    z = (acc * c + (shift - m)).astype(np.float32).astype(np.float64)
+                    pe = np.exp2(z).astype(np.float32).astype(np.float64)
+                    p = om.fp8_e4m3_round(pe)
+                    ell = (pe if exact_sum else p).sum(axis=1, keepdims=True)
+                    out[bi, :, hi, :] = (p @ v8[bi, :, hi, :]) * sv[bi, hi][None, :] / ell
+            return out
+        return run(qa, sqa, vis_rows), run(qc, sqc, cond_rows)
+    return f
+
+
 MUTANTS = {
     "rope_sign": ("rope_rotate", _rope_sign),
     "rope_band_order": ("rope_angles", _band_order),
@@ -230,6 +290,12 @@ MUTANTS = {
     "fp8_scale_127": ("quant_scale", _scale_int8_max),
     "fp8_linear_no_wscale": ("fp8_linear", _fp8_linear_no_wscale),
     "fp8_linear_per_tensor_x": ("fp8_linear", _fp8_linear_per_tensor_x),
+    "att8_k_per_token": ("attn8_quantize_stream", _att8_k_per_token),
+    "att8_v_per_tensor": ("attn8_quantize_v", _att8_v_per_tensor),
+    "int8_truncate": ("quantize_int8", _int8_truncate),
+    "att8_floor_reference": ("joint_attention_8bit", _att8_variant(floor=True)),
+    "att8_no_shift": ("joint_attention_8bit", _att8_variant(shift=0.0)),
+    "att8_unquantized_row_sum": ("joint_attention_8bit", _att8_variant(exact_sum=True)),
 }
 
 PIN_TESTS = [f for name, f in inspect.getmembers(pins, inspect.isfunction) if name.startswith("test_")]

@@ -599,3 +599,75 @@ def test_fp8_linear_against_bruteforce_loops():
     # and the quantization error stays within the E4M3 rounding bound of the exact product
     exact = x @ w.T + b
     assert np.max(np.abs(got - exact)) / np.sqrt(np.mean(exact ** 2)) < 0.2
+
+
+# ------------------------------------------------------------------ 8-bit joint attention
+
+
+def test_int8_quantization_closed_forms():
+    rng = np.random.default_rng(93)
+    x = rng.standard_normal((5, 3, 128)) * np.array([1e-3, 1, 7])[None, :, None]
+    x[2, 1] = 0
+    q, s = oracle.quantize_int8(x, axes=2)
+    assert q.dtype == np.float64 and np.all(np.abs(q) <= 127) and np.all(q == np.round(q))
+    assert s[2, 1, 0] == 1.0 and np.all(q[2, 1] == 0)
+    amax = np.abs(x.astype(np.float32)).max(axis=2)
+    ok = amax > 0
+    assert np.all(np.abs(q).max(axis=2)[ok] == 127)                      # the amax lands on 127
+    np.testing.assert_array_equal(s[..., 0][ok], (amax / np.float32(127))[ok])
+    assert np.all(np.abs(q * s - x) <= s * 0.5 * (1 + 1e-6))             # half a step at most
+
+
+def _rand_streams(rng, nv, nc, h, d=128):
+    n = lambda sh: rng.standard_normal(sh)  # noqa: E731
+    return [n((1, nv, h, d)), n((1, nv, h, d)), n((1, nv, h, d)), n((1, nc, h, d)), n((1, nc, h, d)), n((1, nc, h, d))]
+
+
+def test_attention_8bit_against_bruteforce_loops():
+    rng = np.random.default_rng(94)
+    qv, kv, vv, qc, kc, vc = _rand_streams(rng, 70, 9, 1)            # 70 keys: a 64-block and a tail
+    ov, oc = oracle.joint_attention_8bit(qv, kv, vv, qc, kc, vc)
+    to = lambda a: [list(r) for r in a[0, :, 0, :]]  # noqa: E731
+    keys = to(kv) + to(kc)
+    vals = to(vv) + to(vc)
+    seg = [(0, j) for j in range(70)] + [(1, j) for j in range(9)]
+    fp8 = lambda v: float(_torch_fp8(np.array([v]))[0])  # noqa: E731
+    ref_v = bf.attention_8bit([(r, 0) for r in to(qv)[:12]], keys, vals, seg, 1 / math.sqrt(128), fp8)
+    ref_c = bf.attention_8bit([(r, 1) for r in to(qc)], keys, vals, seg, 1 / math.sqrt(128), fp8)
+    np.testing.assert_allclose(ov[0, :12, 0], ref_v, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oc[0, :, 0], ref_c, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_8bit_closed_forms():
+    """K = 0: every logit is 0, every weight 2^8 exactly, O = mean of the dequantized V.
+    One key: O = that key's dequantized value.  Equal value rows: O = the dequantized row."""
+    rng = np.random.default_rng(95)
+    qv, kv, vv, qc, kc, vc = _rand_streams(rng, 40, 7, 2)
+    ov, oc, lse = oracle.joint_attention_8bit(qv, 0 * kv, vv, qc, 0 * kc, vc, return_lse=True)
+    v8v, v8c, sv = oracle.attn8_quantize_v(vv, vc)
+    mean = np.concatenate([v8v, v8c], axis=1).mean(axis=1) * sv           # [B, H, D]
+    np.testing.assert_allclose(ov, np.broadcast_to(mean[:, None], ov.shape), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oc, np.broadcast_to(mean[:, None], oc.shape), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(47), rtol=1e-13)            # sum of 47 weights 2^0
+    e = np.zeros((1, 0, 2, 128))
+    o1, _ = oracle.joint_attention_8bit(qv[:, :1], kv[:, :1], vv[:, :1], e, e, e)
+    v8, _, s1 = oracle.attn8_quantize_v(vv[:, :1], e)
+    np.testing.assert_allclose(o1[0, 0], v8[0, 0] * s1[0], rtol=1e-14)
+    vrow = np.broadcast_to(vv[:, :1], vv.shape)
+    crow = np.broadcast_to(vv[:, :1], vc.shape)
+    oe, _ = oracle.joint_attention_8bit(qv, kv, vrow, qc, kc, crow)
+    v8, _, s2 = oracle.attn8_quantize_v(vrow, crow)
+    np.testing.assert_allclose(oe[0], np.broadcast_to(v8[0, :1] * s2[0], oe[0].shape), rtol=1e-13)
+
+
+def test_attention_8bit_stays_near_exact_attention():
+    """The 8-bit method approximates softmax attention: on N(0,1) inputs with logits of unit
+    spread its rms deviation is a few percent (the E4M3 rounding of P, 2^-4 relative, is the
+    main term) -- far from a wrong formula, which misses by order one."""
+    rng = np.random.default_rng(96)
+    qv, kv, vv, qc, kc, vc = _rand_streams(rng, 300, 40, 2)
+    a = oracle.joint_attention_8bit(qv, kv, vv, qc, kc, vc)
+    e = oracle.joint_attention(qv, kv, vv, qc, kc, vc)
+    for x, y in zip(a, e):
+        rms_err = np.sqrt(np.mean((x - y) ** 2)) / np.sqrt(np.mean(y ** 2))
+        assert 0.005 < rms_err < 0.06, rms_err
