@@ -167,7 +167,39 @@ def next_rows(dev):
                                    "shape": f"M={cfg.n_merged} N={4 * cfg.width} K={cfg.width}, bf16 in/out"}
     del t, ym, yu
     out["fp8_gemm_480p"] = fp8_gemms(dev)
+    out["attention_8bit"] = attention_8bit(dev)
     return out
+
+
+def attention_8bit(dev):
+    """The 8-bit joint attention at 480p and 720p (seeded N(0,1) Q^, K^, V in bf16, 24 heads):
+    operand quantization and the attention kernel timed separately, beside the 16-bit kernel
+    on the same inputs (Q^/K^ in f16 as the block feeds it)."""
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    import workloads as wl
+    res = {}
+    for cfg in (wl.ATTN_480P, wl.ATTN_720P):
+        raw = wl.attention_inputs(cfg)
+        t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in raw.items()}
+        ops = mm.attn8_quantize(t["q_vis"], t["k_vis"], t["v_vis"], t["q_cond"], t["k_cond"], t["v_cond"])
+        ov = torch.empty((1, cfg.n_vis, cfg.heads, 128), dtype=torch.float32, device=dev)
+        oc = torch.empty((1, cfg.n_cond, cfg.heads, 128), dtype=torch.float32, device=dev)
+        ms_q = time_calls(lambda: mm.attn8_quantize(t["q_vis"], t["k_vis"], t["v_vis"], t["q_cond"], t["k_cond"],
+                                                    t["v_cond"], out=ops), reps=5, warm=1)
+        ms_a = time_calls(lambda: mm.joint_attention_8bit(ops, o_vis=ov, o_cond=oc), reps=5, warm=1)
+        h16 = {k: t[k].to(torch.float16) for k in ("q_vis", "k_vis", "v_vis", "q_cond", "k_cond", "v_cond")}
+        ms_16 = time_calls(lambda: mm.joint_attention(h16["q_vis"], h16["k_vis"], h16["v_vis"], h16["q_cond"],
+                                                      h16["k_cond"], h16["v_cond"], o_vis=ov, o_cond=oc),
+                           reps=5, warm=1)
+        fl = cfg.attn_flops
+        res[cfg.name.split("_")[0]] = {
+            "tokens": cfg.n_tokens, "attention_ms": round(ms_a, 4), "tflops": round(fl / ms_a / 1e9, 1),
+            "frac_8bit_peak": round(fl / ms_a / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "quantize_ms": round(ms_q, 4), "f16_attention_ms": round(ms_16, 4),
+            "f16_tflops": round(fl / ms_16 / 1e9, 1)}
+        del t, ops, ov, oc, h16
+    return res
 
 
 def fp8_gemms(dev):

@@ -172,6 +172,60 @@ int mmdit_linear(const void* x, const void* w, int x_dtype,
                  void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * 8-bit joint attention (Wan report, section 4.4.3: INT8 for S = Q K^T, FP8 E4M3 for O = P V,
+ * f32 accumulation across key blocks), the same joint non-causal attention as
+ * mmdit_joint_attention (Vimoo 1.0 notes, section 2.2) on quantized operands.  The page
+ * does not fix the scale granularity; this library uses:
+ *   Q^: one INT8 scale per (token, head);  K^: one per (head, block of 64 consecutive keys
+ *   of one stream);  V: one E4M3 scale per (head, channel) over the keys of both streams.
+ * Each scale is amax / qmax in f32 (127 for INT8, 448 for E4M3; an all-zero group gets 1);
+ * codes are rint(x * (1/s)) clamped to +-127 (INT8) or E4M3(clamp(x * (1/s), +-448)).
+ *
+ * mmdit_attn8_stream: the quantized operands of one stream of n tokens, caller-owned:
+ *   q8       [B, n, H, D] INT8 codes (row stride H*D bytes)     q_scale [B, H, n] f32
+ *   k8       [B, n, H, D] INT8 codes                            k_scale [B, H, ceil(n/64)] f32
+ *   v8t      [B, H, D, np] E4M3 codes, np = 64 * ceil(n/64): channel-major; within each
+ *            64-key tile, key k = 32h + 8i + 4g + c (h, g in {0,1}; i, c in 0..3) sits at byte
+ *            16(2h + g) + 4i + c, the order in which the attention kernel holds its weights;
+ *            keys past n are zero codes.
+ * ------------------------------------------------------------------------------- */
+typedef struct {
+  void* q8;
+  float* q_scale;
+  void* k8;
+  float* k_scale;
+  void* v8t;
+} mmdit_attn8_stream;
+
+/* mmdit_attn8_quantize -- the operands above from 16-bit (or f32) Q^, K^, V of both streams
+ * (the same inputs as mmdit_joint_attention: [B, n, H, D] views with one token row stride
+ * in_row_stride, Q^/K^ already normalised and rotated); v_scale [B, H, D] f32 receives the
+ * V scales (it is also the kernel's amax accumulator).  D = 128.  A stream with n = 0 is
+ * skipped (its struct may be NULL).  Outputs must not overlap the inputs. */
+int mmdit_attn8_quantize(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
+                         const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
+                         int in_dtype, int64_t in_row_stride, int64_t B, int64_t H, int64_t D,
+                         const mmdit_attn8_stream* vis, const mmdit_attn8_stream* cond,
+                         float* v_scale, void* stream);
+
+/* mmdit_joint_attention_8bit -- for every batch item and head, with the codes and scales of
+ * mmdit_attn8_quantize, per query i and key j (keys of both streams):
+ *   y_ij = acc_ij * c_ij in log2 units, acc_ij the exact integer dot product of the codes,
+ *          c_ij = s_q[i] * (s_k[block of j] * (softmax_scale * log2 e)), all f32;
+ *   m_i  = an integer reference, at least ceil(y_ij) for every key seen (kept exact: raising
+ *          it rescales the accumulators by a power of two);
+ *   P'_ij = E4M3(2^(acc_ij c_ij + 8 - m_i)) (so P' <= 256), summed by the FP8 MFMA;
+ *   O_i  = s_v * (sum_j P'_ij V8_j) / (sum_j P'_ij).
+ * o_vis, o_cond, out_dtype, out_row_stride, lse as for mmdit_joint_attention (lse is
+ * ln(sum_j P'_ij) + (m_i - 8) ln 2).  D = 128. */
+int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis,
+                               const mmdit_attn8_stream* cond, int64_t n_cond,
+                               const float* v_scale, int64_t B, int64_t H, int64_t D,
+                               float softmax_scale,
+                               void* o_vis, void* o_cond, int out_dtype, int64_t out_row_stride,
+                               float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * mmdit_quantize_fp8 -- symmetric FP8 E4M3 quantization, with one scale per row (per_row
  * != 0: per-token activations) or one for the whole tensor (per_row == 0: weights), the
  * scaling of the Wan report's FP8 GEMMs (section 4.4.3).

@@ -197,3 +197,24 @@ def test_fp8_validation(L):
                               None, 0, 10, None) == ERR_ALIAS
     assert L.mmdit_linear_fp8(p, s, p, s, None, mm.BF16, y, mm.F32, 1 << 24, 256, 256, mm.EPI_NONE, None, mm.F32,
                               None, 0, 10, None) == ERR_SHAPE                                     # 2^31 bytes
+
+
+def test_attention_8bit_validation(L):
+    import ctypes as C
+    p = _fake(0x10000)
+    st = mm._abi.Attn8Stream(0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000)
+    bad = mm._abi.Attn8Stream(0x10000000, None, 0x30000000, 0x40000000, 0x50000000)
+    sv = _fake(0x60000000)
+    q = L.mmdit_attn8_quantize
+    assert q(p, p, p, 100, None, None, None, 0, mm.BF16, 3072, 1, 24, 64, C.byref(st), None, sv, None) == ERR_SHAPE
+    assert q(p, p, p, 100, None, None, None, 0, mm.FP8_E4M3, 3072, 1, 24, 128, C.byref(st), None, sv, None) == ERR_DTYPE
+    assert q(p, p, p, 100, None, None, None, 0, mm.BF16, 3000, 1, 24, 128, C.byref(st), None, sv, None) == ERR_ALIGN
+    assert q(p, p, p, 100, None, None, None, 0, mm.BF16, 3072, 1, 24, 128, C.byref(bad), None, sv, None) == ERR_NULL
+    assert q(p, p, p, 100, p, p, p, 5, mm.BF16, 3072, 1, 24, 128, C.byref(st), None, sv, None) == ERR_NULL
+    assert q(None, None, None, 0, None, None, None, 0, mm.BF16, 3072, 1, 24, 128, None, None, None, None) == 0
+    a = L.mmdit_joint_attention_8bit
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.0, p, None, mm.F32, 3072, None, None) == ERR_SHAPE
+    assert a(C.byref(st), 100, None, 0, None, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None) == ERR_NULL
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, p, None, mm.FP8_E4M3, 3072, None, None) == ERR_DTYPE
+    assert a(C.byref(st), 100, C.byref(st), 5, sv, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None) == ERR_NULL
+    assert a(C.byref(st), 100, None, 0, _fake(0x60000004), 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None) == ERR_ALIGN

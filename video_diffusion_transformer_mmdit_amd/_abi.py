@@ -40,6 +40,12 @@ class Rope3D(ctypes.Structure):
                    int(split[2]), float(base))
 
 
+class Attn8Stream(ctypes.Structure):
+    """Quantized operands of one stream for the 8-bit joint attention (device pointers)."""
+    _fields_ = [("q8", c_void_p), ("q_scale", c_void_p), ("k8", c_void_p), ("k_scale", c_void_p),
+                ("v8t", c_void_p)]
+
+
 class StreamWeights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm",
                                          "w_o", "b_o", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
@@ -86,6 +92,10 @@ def lib() -> ctypes.CDLL:
         "mmdit_lite_merge": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
         "mmdit_lite_unpatchify": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
         "mmdit_quantize_fp8": [vp, i, i64, i64, i, vp, vp, vp],
+        "mmdit_attn8_quantize": [vp, vp, vp, i64, vp, vp, vp, i64, i, i64, i64, i64, i64,
+                                 ctypes.POINTER(Attn8Stream), ctypes.POINTER(Attn8Stream), vp, vp],
+        "mmdit_joint_attention_8bit": [ctypes.POINTER(Attn8Stream), i64, ctypes.POINTER(Attn8Stream), i64, vp,
+                                       i64, i64, i64, f, vp, vp, i, i64, vp, vp],
         "mmdit_linear_fp8": [vp, vp, vp, vp, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
         "mmdit_timestep_embed": [vp, i64, vp, vp, vp, vp, vp, vp, i, i64, i64, i64, f, vp, vp, vp, vp],
         "mmdit_block_workspace_offsets": [ctypes.POINTER(BlockDims), i64, i64, i64, ctypes.POINTER(c_size_t)],
@@ -280,6 +290,81 @@ def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None
                             rows_per_batch or M, _stream(x))
     _check(st, "mmdit_linear")
     return y
+
+
+class Attn8Operands:
+    """Tensors of the 8-bit attention operands (mmdit_attn8_stream per stream + V scales)."""
+
+    def __init__(self, B: int, H: int, n_vis: int, n_cond: int, device):
+        self.B, self.H, self.n = B, H, (n_vis, n_cond)
+        self.t = []
+        for n in (n_vis, n_cond):
+            nb = (n + 63) // 64
+            self.t.append({
+                "q8": torch.empty((B, n, H, 128), dtype=torch.int8, device=device),
+                "q_scale": torch.empty((B, H, n), dtype=torch.float32, device=device),
+                "k8": torch.empty((B, n, H, 128), dtype=torch.int8, device=device),
+                "k_scale": torch.empty((B, H, nb), dtype=torch.float32, device=device),
+                "v8t": torch.empty((B, H, 128, nb * 64), dtype=torch.uint8, device=device)})
+        self.v_scale = torch.empty((B, H, 128), dtype=torch.float32, device=device)
+
+    def struct(self, s: int) -> Attn8Stream:
+        t = self.t[s]
+        return Attn8Stream(*(t[k].data_ptr() if t[k].numel() else None for k in ("q8", "q_scale", "k8", "k_scale", "v8t")))
+
+
+def attn8_quantize(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None,
+                   out: Optional[Attn8Operands] = None) -> Attn8Operands:
+    """INT8 Q/K and channel-major E4M3 V operands of the 8-bit joint attention from
+    [B, n, H, 128] views sharing one row stride (as joint_attention takes them)."""
+    ts = [t for t in (q_vis, k_vis, v_vis, q_cond, k_cond, v_cond) if t is not None]
+    _need_gpu(*ts)
+    B, n_vis, rs = _rows(q_vis, "q_vis")
+    H, D = q_vis.shape[2], q_vis.shape[3]
+    n_cond = 0 if q_cond is None else q_cond.shape[1]
+    for nm, t in zip(("k_vis", "v_vis", "q_cond", "k_cond", "v_cond"), (k_vis, v_vis, q_cond, k_cond, v_cond)):
+        if t is None:
+            continue
+        _, n, r = _rows(t, nm)
+        if t.dtype != q_vis.dtype or t.shape[0] != B or t.shape[2:] != q_vis.shape[2:]:
+            raise MmditError(f"{nm}: dtype / shape mismatch")
+        if n > 0 and r != rs and n != 1:
+            raise MmditError(f"{nm}: all inputs must share one row stride")
+    if out is None:
+        out = Attn8Operands(B, H, n_vis, n_cond, q_vis.device)
+    sv, sc = out.struct(0), out.struct(1)
+    st = lib().mmdit_attn8_quantize(q_vis.data_ptr(), k_vis.data_ptr(), v_vis.data_ptr(), n_vis,
+                                    _ptr(q_cond) if n_cond else None, _ptr(k_cond) if n_cond else None,
+                                    _ptr(v_cond) if n_cond else None, n_cond, _dt(q_vis), rs, B, H, D,
+                                    ctypes.byref(sv), ctypes.byref(sc), out.v_scale.data_ptr(), _stream(q_vis))
+    _check(st, "mmdit_attn8_quantize")
+    return out
+
+
+def joint_attention_8bit(ops: Attn8Operands, *, softmax_scale: Optional[float] = None, out_dtype=torch.float32,
+                         o_vis: Optional[torch.Tensor] = None, o_cond: Optional[torch.Tensor] = None,
+                         return_lse: bool = False):
+    """8-bit joint attention over the operands of attn8_quantize; outputs [B, n_s, H, 128]."""
+    B, H = ops.B, ops.H
+    n_vis, n_cond = ops.n
+    dev = ops.v_scale.device
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(128)
+    if o_vis is None:
+        o_vis = torch.empty((B, n_vis, H, 128), dtype=out_dtype, device=dev)
+    if o_cond is None and n_cond > 0:
+        o_cond = torch.empty((B, n_cond, H, 128), dtype=out_dtype, device=dev)
+    _, _, ors = _rows(o_vis, "o_vis")
+    lse = torch.empty((B, H, n_vis + n_cond), dtype=torch.float32, device=dev) if return_lse else None
+    sv, sc = ops.struct(0), ops.struct(1)
+    st = lib().mmdit_joint_attention_8bit(ctypes.byref(sv), n_vis, ctypes.byref(sc), n_cond, ops.v_scale.data_ptr(),
+                                          B, H, 128, softmax_scale, o_vis.data_ptr(),
+                                          _ptr(o_cond) if n_cond else None, _dt(o_vis), ors, _ptr(lse),
+                                          torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "mmdit_joint_attention_8bit")
+    if return_lse:
+        return o_vis, o_cond, lse
+    return o_vis, o_cond
 
 
 def quantize_fp8(x: torch.Tensor, per_row: bool = True, q: Optional[torch.Tensor] = None,

@@ -22,6 +22,7 @@ LIB = os.path.join(PKG, "libmmdit.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "block.hip", "gemm.hip", "joint_attention.hip", "modulate_ln.hip", "quant.hip",
+           "attn8_quant.hip", "joint_attention_8bit.hip",
            "modulation.hip", "qk_norm_rope.hip"]
 
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",

@@ -230,6 +230,88 @@ int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, in
                        static_cast<hipStream_t>(stream));
 }
 
+int mmdit_attn8_quantize(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
+                         const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
+                         int in_dtype, int64_t in_row_stride, int64_t B, int64_t H, int64_t D,
+                         const mmdit_attn8_stream* vis, const mmdit_attn8_stream* cond, float* v_scale,
+                         void* stream) {
+  g_last_error.clear();
+  if (B < 0 || H < 0 || n_vis < 0 || n_cond < 0) return fail(MMDIT_ERR_SHAPE, "attn8_quantize: negative size");
+  if (D != 128) return fail(MMDIT_ERR_SHAPE, "attn8_quantize: D must be 128");
+  if (!valid_dtype(in_dtype)) return fail(MMDIT_ERR_DTYPE, "attn8_quantize: inputs must be f32, bf16 or f16");
+  if (in_row_stride < H * D || in_row_stride % 8) return fail(MMDIT_ERR_ALIGN, "attn8_quantize: row stride >= H*D, a multiple of 8");
+  if (B == 0 || H == 0 || n_vis + n_cond == 0) return MMDIT_OK;
+  if (!v_scale) return fail(MMDIT_ERR_NULL, "attn8_quantize: v_scale required");
+  const void* qs[2] = {q_vis, q_cond};
+  const void* ks[2] = {k_vis, k_cond};
+  const void* vs[2] = {v_vis, v_cond};
+  const int64_t n[2] = {n_vis, n_cond};
+  const mmdit_attn8_stream* out[2] = {vis, cond};
+  const size_t es = dtype_size(in_dtype);
+  for (int s = 0; s < 2; ++s) {
+    if (n[s] == 0) continue;
+    const mmdit_attn8_stream* o = out[s];
+    if (!qs[s] || !ks[s] || !vs[s] || !o || !o->q8 || !o->q_scale || !o->k8 || !o->k_scale || !o->v8t)
+      return fail(MMDIT_ERR_NULL, "attn8_quantize: inputs and every output of a non-empty stream are required");
+    if (!aligned16(qs[s]) || !aligned16(ks[s]) || !aligned16(vs[s]) || !aligned16(o->q8) || !aligned16(o->k8) ||
+        !aligned16(o->v8t) || (reinterpret_cast<uintptr_t>(o->q_scale) & 3) || (reinterpret_cast<uintptr_t>(o->k_scale) & 3))
+      return fail(MMDIT_ERR_ALIGN, "attn8_quantize: tensors 16-byte aligned, scales 4-byte aligned");
+    const int64_t nb = (n[s] + 63) / 64;
+    if (B * H * 128 * nb * 64 >= ((int64_t)1 << 40) || (128 * nb * 64) >= ((int64_t)1 << 31))
+      return fail(MMDIT_ERR_SHAPE, "attn8_quantize: stream too long");
+    const size_t in_bytes = (size_t)((B * n[s] - 1) * in_row_stride + H * D) * es;
+    const void* outs[5] = {o->q8, o->q_scale, o->k8, o->k_scale, o->v8t};
+    const size_t nout[5] = {(size_t)(B * n[s] * H * D), (size_t)(B * H * n[s]) * 4, (size_t)(B * n[s] * H * D),
+                            (size_t)(B * H * nb) * 4, (size_t)(B * H * D * nb * 64)};
+    for (int i = 0; i < 5; ++i) {
+      for (int t = 0; t < 2; ++t)
+        if (n[t] > 0 && (overlaps(outs[i], nout[i], qs[t], (size_t)((B * n[t] - 1) * in_row_stride + H * D) * es) ||
+                         overlaps(outs[i], nout[i], ks[t], (size_t)((B * n[t] - 1) * in_row_stride + H * D) * es) ||
+                         overlaps(outs[i], nout[i], vs[t], (size_t)((B * n[t] - 1) * in_row_stride + H * D) * es)))
+          return fail(MMDIT_ERR_ALIAS, "attn8_quantize: an output overlaps an input");
+      if (overlaps(outs[i], nout[i], v_scale, (size_t)(B * H * D) * 4))
+        return fail(MMDIT_ERR_ALIAS, "attn8_quantize: an output overlaps v_scale");
+    }
+    (void)in_bytes;
+  }
+  if (reinterpret_cast<uintptr_t>(v_scale) & 15) return fail(MMDIT_ERR_ALIGN, "attn8_quantize: v_scale 16-byte aligned");
+  return launch_attn8_quantize(qs, ks, vs, n, in_dtype, in_row_stride, B, H, out, v_scale,
+                               static_cast<hipStream_t>(stream));
+}
+
+int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis, const mmdit_attn8_stream* cond,
+                               int64_t n_cond, const float* v_scale, int64_t B, int64_t H, int64_t D,
+                               float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
+                               int64_t out_row_stride, float* lse, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || H < 0 || n_vis < 0 || n_cond < 0) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: negative size");
+  if (D != 128) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: D must be 128");
+  if (!valid_dtype(out_dtype)) return fail(MMDIT_ERR_DTYPE, "joint_attention_8bit: bad out dtype");
+  if (out_row_stride < H * D || out_row_stride % 8) return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: out row stride >= H*D, a multiple of 8");
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 3.0e38f)) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: softmax_scale must be positive and finite");
+  if (B == 0 || H == 0 || n_vis + n_cond == 0) return MMDIT_OK;
+  const mmdit_attn8_stream* seg[2] = {vis, cond};
+  const int64_t n[2] = {n_vis, n_cond};
+  void* outs[2] = {o_vis, o_cond};
+  if (!v_scale) return fail(MMDIT_ERR_NULL, "joint_attention_8bit: v_scale required");
+  if (reinterpret_cast<uintptr_t>(v_scale) & 15) return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: v_scale 16-byte aligned");
+  for (int s = 0; s < 2; ++s) {
+    if (n[s] == 0) continue;
+    const mmdit_attn8_stream* o = seg[s];
+    if (!o || !o->q8 || !o->q_scale || !o->k8 || !o->k_scale || !o->v8t || !outs[s])
+      return fail(MMDIT_ERR_NULL, "joint_attention_8bit: every operand and the output of a non-empty stream are required");
+    if (!aligned16(o->q8) || !aligned16(o->k8) || !aligned16(o->v8t) || !aligned16(outs[s]) ||
+        (reinterpret_cast<uintptr_t>(o->q_scale) & 3) || (reinterpret_cast<uintptr_t>(o->k_scale) & 3))
+      return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: tensors 16-byte aligned, scales 4-byte aligned");
+    const int64_t nb = (n[s] + 63) / 64;
+    if ((n[s] + 64) * H * D >= ((int64_t)1 << 31) || 128 * nb * 64 >= ((int64_t)1 << 31))
+      return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: one stream spans 2 GiB or more per batch item");
+  }
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: lse 4-byte aligned");
+  return launch_joint_attention_8bit(seg, n, v_scale, B, H, softmax_scale, o_vis, o_cond, out_dtype, out_row_stride,
+                                     lse, static_cast<hipStream_t>(stream));
+}
+
 int mmdit_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row, void* q,
                        float* scales, void* stream) {
   g_last_error.clear();

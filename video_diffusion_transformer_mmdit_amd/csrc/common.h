@@ -147,6 +147,12 @@ int launch_lite_regroup(int layout, const void* x, const void* w, const void* bi
 // Runs one or two problems with equal N, K, dtypes and epilogue in one launch.
 int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dtype, int y_dtype,
                   int64_t N, int64_t K, int epilogue, int res_dtype, hipStream_t stream);
+int launch_attn8_quantize(const void* const* q, const void* const* k, const void* const* v, const int64_t* n,
+                          int in_dtype, int64_t stride, int64_t B, int64_t H, const mmdit_attn8_stream* const* out,
+                          float* v_scale, hipStream_t stream);
+int launch_joint_attention_8bit(const mmdit_attn8_stream* const* seg, const int64_t* n, const float* v_scale,
+                                int64_t B, int64_t H, float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
+                                int64_t out_stride, float* lse, hipStream_t stream);
 // FP8 E4M3 quantization with a scale per row (per_row) or one for the whole tensor.
 int launch_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row, uint8_t* q,
                         float* scales, hipStream_t stream);
