@@ -166,6 +166,7 @@ def next_rows(dev):
     out["lite_unpatchify_480p"] = {"ms": round(ms_u, 4), "tflops": round(half / (ms_u * 1e-3) / 1e12, 1),
                                    "shape": f"M={cfg.n_merged} N={4 * cfg.width} K={cfg.width}, bf16 in/out"}
     del t, ym, yu
+    out["lite_block_480p"] = lite_block(dev)
     out["fp8_gemm_480p"] = fp8_gemms(dev)
     out["attention_8bit"] = attention_8bit(dev)
     return out
@@ -200,6 +201,28 @@ def attention_8bit(dev):
             "f16_tflops": round(fl / ms_16 / 1e9, 1)}
         del t, ops, ov, oc, h16
     return res
+
+
+def lite_block(dev):
+    """One block of the Lite backbone at 480p: the 2x2-merged 21x15x26 = 8190 visual tokens +
+    512 conditioning tokens, the 16-wide timestep bottleneck, otherwise the block above."""
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    import workloads as wl
+    cfg = wl.BlockConfig("lite_block480p", 3072, 24, 128, 12288, 16, (21, 15, 26), 512, seed=6)
+    raw = wl.block_inputs(cfg)
+    t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in raw.items()}
+    wv = {k: t[f"vis.{k}"] for k in wl.STREAM_WEIGHTS}
+    wc = {k: t[f"cond.{k}"] for k in wl.STREAM_WEIGHTS}
+    dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, act_dtype=torch.float16)
+    rope = mm.Rope3D.make(cfg.grid)
+    ws = torch.empty(mm.block_workspace_bytes(dims, 1, cfg.n_vis, cfg.n_cond), dtype=torch.uint8, device=dev)
+    ov = torch.empty((1, cfg.n_vis, cfg.width), dtype=torch.float32, device=dev)
+    oc = torch.empty((1, cfg.n_cond, cfg.width), dtype=torch.float32, device=dev)
+    ms = time_calls(lambda: mm.block_fwd(dims, wv, wc, t["x_vis"], t["x_cond"], t["tvec"], rope, workspace=ws,
+                                         out_vis=ov, out_cond=oc), reps=10, warm=2)
+    return {"ms": round(ms, 4), "tokens": cfg.n_tokens, "tokens_per_s": round(cfg.n_tokens / (ms * 1e-3), 1),
+            "tflops": round(cfg.total_flops / (ms * 1e-3) / 1e12, 1)}
 
 
 def fp8_gemms(dev):

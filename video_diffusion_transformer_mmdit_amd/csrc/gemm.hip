@@ -4,7 +4,10 @@
 // kernel runs the Lite model's 2x2 hidden-space merge and unpatchify (section 2.4), with the
 // neighbour gather folded into the x loads and the scatter back to the grid into the stores.
 //
-// gfx950 design:
+// gfx950 design (two kernels share the tile, fragment layout, tile order and epilogue:
+// gemm_k64_kernel, two LDS stages of K = 64, for 16-bit operands in the plain layout with
+// K <= 4096; gemm_kernel, four LDS stages of 64 bytes per row, for long K, FP8 operands and
+// the Lite layouts):
 //   - 256 x 256 output tile per workgroup of 4 wave64s arranged 2 (M) x 2 (N), one per SIMD;
 //     each wave owns 128 x 128 outputs = 4 x 4 tiles of v_mfma_f32_32x32x16_{bf16,f16} whose
 //     256 accumulator registers live in AGPRs.  The MFMA computes C^T (A operand = W rows,
@@ -149,6 +152,90 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* opaque_lds(__
   return (__attribute__((address_space(3))) void*)(uintptr_t)a;
 }
 
+// Tile of this workgroup: tiles are renumbered so that each XCD (workgroups go round-robin
+// over the 8 XCDs) owns a contiguous run, rastered in groups of 8 M-tiles inside a problem.
+__device__ __forceinline__ void gemm_tile(const GemmArgs& args, int& pi, int& m0, int& n0) {
+  int64_t t = blockIdx.x;
+  if ((args.tiles & 7) == 0) t = (t & 7) * (args.tiles >> 3) + (t >> 3);
+  pi = t < args.tiles0 ? 0 : 1;
+  if (pi) t -= args.tiles0;
+  const int64_t M = args.p[pi].M, N = args.N;
+  const int64_t nTm = (M + GBM - 1) / GBM, nTn = (N + GBN - 1) / GBN;
+  const int64_t per_group = (int64_t)GROUP_M * nTn;
+  const int64_t grp = t / per_group;
+  const int64_t first_m = grp * GROUP_M;
+  const int64_t gm = (nTm - first_m) < GROUP_M ? (nTm - first_m) : GROUP_M;
+  const int64_t in_grp = t - grp * per_group;
+  m0 = (int)((first_m + in_grp % gm) * GBM);
+  n0 = (int)((in_grp / gm) * GBN);
+}
+
+// Epilogue of a 256 x 256 tile: bias, GELU or gated residual on the accumulators, one store.
+template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const GemmProblem& P, const f32x16 (&acc)[4][4],
+                                              int m0, int n0, int wm, int wn, int l32, int g) {
+  constexpr bool FP8 = IN_DT == MMDIT_FP8_E4M3;
+  const int64_t M = P.M, N = args.N;
+  // ---- epilogue: lane holds C^T rows (output columns) 8 (e/4) + 4 g + e%4 of each 32 x 32
+  // tile at output row l32: four consecutive columns per e/4.
+  // GEMM_SCATTER_Y: logical output row m, column n goes to column n % C of the full-grid
+  // token merged_row0(m) + (s / 2) W + s % 2, s = n / C; a 256-wide tile lies inside one s
+  // (C is a multiple of 256).
+  int64_t y_rows[4];
+  int s_col = 0;
+  if constexpr (LAYOUT == GEMM_SCATTER_Y) {
+    const int sg = n0 / args.c;
+    s_col = sg * args.c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 128 + i * 32 + l32;
+      y_rows[i] = m < M ? (int64_t)merged_row0(m, args) + (sg >> 1) * args.w + (sg & 1) : 0;
+    }
+  }
+  // FP8: the product of the codes times the row's scale and W's scale
+  float rsc[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (FP8) {
+    const float sw = *P.w_scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 32 + l32;
+      rsc[i] = m < M ? P.x_scale[m] * sw : 0.f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int64_t n = n0 + wn * 128 + j * 32 + 8 * e4 + 4 * g;
+      if (n >= N) continue;
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if (P.bias) load4<BIAS_DT>(P.bias, n, bias);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wm * 128 + i * 32 + l32;
+        if (m >= M) continue;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (FP8) v[q] = fmaf(acc[j][i][4 * e4 + q], rsc[i], bias[q]);
+          else v[q] = acc[j][i][4 * e4 + q] + bias[q];
+          if constexpr (EPI == MMDIT_EPI_GELU) v[q] = gelu_erf(v[q]);
+        }
+        if constexpr (EPI == MMDIT_EPI_GATED_RES) {
+          const int64_t b = m / P.rows_per_batch;
+          float r[4], gt[4];
+          load4<RES_DT>(P.res, m * N + n, r);
+          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(gt[q], v[q], r[q]);
+        }
+        if constexpr (LAYOUT == GEMM_SCATTER_Y) store4<Y_DT>(P.y, y_rows[i] * args.c + (n - s_col), v);
+        else store4<Y_DT>(P.y, m * N + n, v);
+      }
+    }
+  }
+}
+
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs args) {
@@ -164,22 +251,10 @@ void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_s2[2 * G_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_s3[2 * G_TILE_BYTES];
 
-  // ---- tile selection: XCD-contiguous runs, grouped raster inside a problem
-  int64_t t = blockIdx.x;
-  if ((args.tiles & 7) == 0) t = (t & 7) * (args.tiles >> 3) + (t >> 3);
-  const int pi = t < args.tiles0 ? 0 : 1;
-  if (pi) t -= args.tiles0;
+  int pi, m0, n0;
+  gemm_tile(args, pi, m0, n0);
   const GemmProblem& P = args.p[pi];
   const int64_t M = P.M, N = args.N, K = args.K;
-  const int64_t nTm = (M + GBM - 1) / GBM, nTn = (N + GBN - 1) / GBN;
-  const int64_t per_group = (int64_t)GROUP_M * nTn;
-  const int64_t grp = t / per_group;
-  const int64_t first_m = grp * GROUP_M;
-  const int64_t gm = (nTm - first_m) < GROUP_M ? (nTm - first_m) : GROUP_M;
-  const int64_t in_grp = t - grp * per_group;
-  const int64_t tm = first_m + in_grp % gm;
-  const int64_t tn = in_grp / gm;
-  const int m0 = (int)(tm * GBM), n0 = (int)(tn * GBN);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -374,68 +449,159 @@ void gemm_kernel(GemmArgs args) {
   if (kt + 4 < nk) run(S0, TAIL, kt + 4);
   if (kt + 5 < nk) run(S1, TAIL, kt + 5);
 
-  // ---- epilogue: lane holds C^T rows (output columns) 8 (e/4) + 4 g + e%4 of each 32 x 32
-  // tile at output row l32: four consecutive columns per e/4.
-  // GEMM_SCATTER_Y: logical output row m, column n goes to column n % C of the full-grid
-  // token merged_row0(m) + (s / 2) W + s % 2, s = n / C; a 256-wide tile lies inside one s
-  // (C is a multiple of 256).
-  int64_t y_rows[4];
-  int s_col = 0;
-  if constexpr (LAYOUT == GEMM_SCATTER_Y) {
-    const int sg = n0 / args.c;
-    s_col = sg * args.c;
+  gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, l32, g);
+}
+
+// 16-bit operands, plain layout: two LDS stages of K = 64 (64 KiB each, rows of 128 bytes,
+// chunks XOR-swizzled by row % 8).  The next stage's sixteen DMA loads per wave go out during
+// the first quarter of the current stage; before the last quarter every wave waits for them
+// and for its own reads of the current stage, and one barrier per 64 K follows, after which
+// the next stage's first fragments are read under the last quarter's MFMAs.
+template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT>
+__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_k64_kernel(GemmArgs args) {
+  constexpr int T64 = GBM * 128;   // one operand tile of one stage: 32 KiB
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * T64];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * T64];
+  int pi, m0, n0;
+  gemm_tile(args, pi, m0, n0);
+  const GemmProblem& P = args.p[pi];
+  const int64_t M = P.M, N = args.N, K = args.K;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  // DMA i of a wave fills rows 64 wave + 8 i .. +7 (lane l -> row + l / 8, physical chunk
+  // l % 8 = logical ^ (row % 8)); loads 0-3 and 4-7 each share one LDS base, the immediate
+  // offset (i % 4) * 1024 moving destination and source alike
+  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * 2);
+  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * 2);
+  int xo[8], wo[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + i * 32 + l32;
-      y_rows[i] = m < M ? (int64_t)merged_row0(m, args) + (sg >> 1) * args.w + (sg & 1) : 0;
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + (lane >> 3);
+    const int lc = (lane & 7) ^ (row & 7);
+    xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
+    wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
   }
-  // FP8: the product of the codes times the row's scale and W's scale
-  float rsc[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (FP8) {
-    const float sw = *P.w_scale;
+  auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
+    const int so = k0 * 2;
+    auto* lx0 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192));
+    auto* lx1 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192 + 4096));
+    auto* lw0 = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 8192));
+    auto* lw1 = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 8192 + 4096));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[3], so, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[4], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[5], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[6], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[7], so, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[3], so, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[4], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[5], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[6], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[7], so, 3072, 0);
+  };
+  auto xbuf = [&](auto st) -> uint8_t* { if constexpr (decltype(st)::value == 0) return lds_a; else return lds_b; };
+  auto wbuf = [&](auto st) -> uint8_t* { return xbuf(st) + T64; };
+  constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
+  int cofs[4];   // slice ks: logical chunk 2 ks + g of row l32 (+ a multiple of 32)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 128 + i * 32 + l32;
-      rsc[i] = m < M ? P.x_scale[m] * sw : 0.f;
+  for (int ks = 0; ks < 4; ++ks) cofs[ks] = l32 * 128 + (((2 * ks + g) ^ (l32 & 7)) << 4);
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
+  const int nk = (int)(K / 64);
+  auto gbarrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  uint4 wfa[4], xfa[4], wfb[4], xfb[4];
+  auto read_slice = [&](const uint8_t* xs, const uint8_t* ws, int ks, uint4 (&wf)[4], uint4 (&xf)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const uint4*>(ws + (wn * 128 + j * 32) * 128 + cofs[ks]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const uint4*>(xs + (wm * 128 + i * 32) * 128 + cofs[ks]);
+  };
+  auto mma = [&](const uint4 (&wf)[4], const uint4 (&xf)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wf[j], xf[i], acc[j][i]);
+  };
+  // 16 MFMAs with the next slice's 8 fragment reads among the first eight (and the stage's
+  // 16 DMA loads, two at a time, among MFMAs 2-9 when dma_here)
+  auto sched = [&](bool dma_here) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      if (dma_here && i >= 2 && i < 10) __builtin_amdgcn_sched_group_barrier(0x010, 2, 1);
     }
+  };
+  // stage kt in buffer cur, its slice 0 in wfa / xfa
+  auto step = [&](auto cur_c, int kt) {
+    constexpr int CUR = decltype(cur_c)::value;
+    constexpr std::integral_constant<int, CUR> cur{};
+    constexpr std::integral_constant<int, CUR ^ 1> oth{};
+    const bool more = kt + 1 < nk;
+    if (more) dma(xbuf(oth), wbuf(oth), (kt + 1) * 64);   // its last readers passed the previous barrier
+    read_slice(xbuf(cur), wbuf(cur), 1, wfb, xfb);
+    mma(wfa, xfa);
+    sched(true);
+    __builtin_amdgcn_sched_barrier(0);
+    read_slice(xbuf(cur), wbuf(cur), 2, wfa, xfa);
+    mma(wfb, xfb);
+    sched(false);
+    __builtin_amdgcn_sched_barrier(0);
+    read_slice(xbuf(cur), wbuf(cur), 3, wfb, xfb);
+    mma(wfa, xfa);
+    sched(false);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads of stage kt+1 have landed and its reads of stage kt are done; after
+    // the barrier both hold for every wave
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    gbarrier();
+    if (more) read_slice(xbuf(oth), wbuf(oth), 0, wfa, xfa);
+    mma(wfb, xfb);
+    sched(false);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  dma(xbuf(S0), wbuf(S0), 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  gbarrier();
+  read_slice(xbuf(S0), wbuf(S0), 0, wfa, xfa);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(S0, kt);
+    step(S1, kt + 1);
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int64_t n = n0 + wn * 128 + j * 32 + 8 * e4 + 4 * g;
-      if (n >= N) continue;
-      float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if (P.bias) load4<BIAS_DT>(P.bias, n, bias);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 128 + i * 32 + l32;
-        if (m >= M) continue;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (FP8) v[q] = fmaf(acc[j][i][4 * e4 + q], rsc[i], bias[q]);
-          else v[q] = acc[j][i][4 * e4 + q] + bias[q];
-          if constexpr (EPI == MMDIT_EPI_GELU) v[q] = gelu_erf(v[q]);
-        }
-        if constexpr (EPI == MMDIT_EPI_GATED_RES) {
-          const int64_t b = m / P.rows_per_batch;
-          float r[4], gt[4];
-          load4<RES_DT>(P.res, m * N + n, r);
-          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = fmaf(gt[q], v[q], r[q]);
-        }
-        if constexpr (LAYOUT == GEMM_SCATTER_Y) store4<Y_DT>(P.y, y_rows[i] * args.c + (n - s_col), v);
-        else store4<Y_DT>(P.y, m * N + n, v);
-      }
-    }
-  }
+  if (kt < nk) step(S0, kt);
+  gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, l32, g);
 }
 
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
 static void gemm_go(const GemmArgs& a, hipStream_t st) {
+  // The two-stage kernel prefetches one stage (three quarters of a stage's MFMAs) ahead: enough
+  // while the K panels of a tile group stay in L2; for long K (FFN down, K = 12288) the
+  // four-stage kernel's deeper prefetch measures faster.
+  if constexpr (IN_DT != MMDIT_FP8_E4M3 && LAYOUT == GEMM_PLAIN) {
+    if (a.K <= 4096) {
+      gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+      return;
+    }
+  }
   gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
 }
 
