@@ -152,3 +152,33 @@ def test_block_480p_sampled_parity():
         _check_intermediates(s, i, ref, act)
     assert_close("out_vis", got["out_vis"], ref["out_vis"], tol)
     assert_close("out_cond", got["out_cond"], ref["out_cond"], tol)
+
+
+@pytest.mark.timeout(600)
+def test_block_split_tail_tiles_parity():
+    """A size whose GEMMs leave a partial last round that includes visual-stream tiles (5500 +
+    77 tokens: 23 M-tiles, so the last rounds of the QKV (60 tiles, 4 K ranges each), out-
+    projection and FFN-down (20 tiles, 12 ranges) GEMMs are split over K and reduced separately,
+    while FFN up (80 tiles, 3 ranges) stays whole); sampled rows, most of them in the split
+    tiles' row range, and every conditioning row, against the oracle."""
+    cfg = wl.BlockConfig("block_split_c3072_h24_f12288_grid1x50x110_cond77", 3072, 24, 128, 12288, 1536,
+                         (1, 50, 110), 77, seed=13)
+    raw = wl.block_inputs(cfg)
+    dev, wv, wc = _dev_block(cfg, raw)
+    act = torch.float16
+    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, act)
+    rv = np.unique(np.concatenate([wl.sample_rows(cfg.n_vis, 48, seed=503), np.arange(4096, cfg.n_vis, 29)]))
+    rc = np.arange(cfg.n_cond)
+    got_v = to_host64(out_v[:, torch.from_numpy(rv).cuda()])
+    got_c = to_host64(out_c)
+    iv = _ws_views(dims, cfg, ws, 0, cfg.n_vis, rv)
+    ic = _ws_views(dims, cfg, ws, 1, cfg.n_cond, rc)
+    log("  oracle (float64) on sampled rows")
+    ref = oracle.block_forward(wl.to_f64(raw["x_vis"], wl.BF16), wl.to_f64(raw["x_cond"], wl.BF16),
+                               wl.to_f64(raw["tvec"], wl.BF16), _host_weights(raw, "vis"),
+                               _host_weights(raw, "cond"), cfg.grid, cfg.heads, cfg.ln_eps, cfg.qk_eps,
+                               vis_rows=rv, cond_rows=rc)
+    for s, i in (("vis", iv), ("cond", ic)):
+        _check_intermediates(s, i, ref, act)
+    assert_close("out_vis", got_v, ref["out_vis"], TOL[wl.BF16])
+    assert_close("out_cond", got_c, ref["out_cond"], TOL[wl.BF16])

@@ -16,8 +16,8 @@ import torch
 
 F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 EPI_NONE, EPI_GELU, EPI_GATED_RES = 0, 1, 2
-WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_WQKV, WS_WO, WS_W1, WS_W2 = range(9)
-WS_COUNT = 9
+WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_WQKV, WS_WO, WS_W1, WS_W2, WS_SPLIT = range(10)
+WS_COUNT = 10
 STAGES = ("mod_ln1", "qkv", "qk_norm_rope", "attention", "out_proj", "ln2", "ffn_up", "ffn_down")
 STAGE_COUNT = len(STAGES)
 

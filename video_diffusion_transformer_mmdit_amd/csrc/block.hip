@@ -32,6 +32,8 @@ static int validate_dims(const mmdit_block_dims* d, int64_t B, int64_t n_vis, in
   return MMDIT_OK;
 }
 
+constexpr size_t BLOCK_SPLIT_BYTES = (size_t)256 * 256 * 256 * 4;   // 256 tile partial sums, f32
+
 static void layout(const mmdit_block_dims* d, int64_t B, int64_t n_vis, int64_t n_cond, WsLayout* L) {
   size_t cur = 0;
   const size_t C = (size_t)d->C, F = (size_t)d->F;
@@ -41,7 +43,8 @@ static void layout(const mmdit_block_dims* d, int64_t B, int64_t n_vis, int64_t 
     const bool cvt = d->act_dtype != d->w_dtype;   // bf16 weights, f16 operands
     const size_t sz[MMDIT_WS_COUNT] = {(size_t)B * 6 * C * 4, n * C * 2, n * 3 * C * 2, n * C * 4, n * F * 2,
                                        cvt ? 3 * C * C * 2 : 0, cvt ? C * C * 2 : 0,
-                                       cvt ? F * C * 2 : 0, cvt ? C * F * 2 : 0};
+                                       cvt ? F * C * 2 : 0, cvt ? C * F * 2 : 0,
+                                       s == 0 ? BLOCK_SPLIT_BYTES : 0};
     for (int r = 0; r < MMDIT_WS_COUNT; ++r) {
       if (sz[r] == 0 && r >= MMDIT_WS_WQKV) { L->off[s][r] = SIZE_MAX; continue; }
       L->off[s][r] = cur;
@@ -138,6 +141,7 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
   }
   const int nstreams = n_cond > 0 ? 2 : 1;
   const int act = d.act_dtype;
+  float* split = reinterpret_cast<float*>(wsb + L.off[0][MMDIT_WS_SPLIT]);
 
   // S1 modulation vectors; S2 LN-modulate for the attention branch
   if ((st = mark(MMDIT_STAGE_MOD_LN1, 0))) return st;
@@ -165,7 +169,7 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
   // S3 QKV projection
   problems([&](int s, GemmProblem& q) { q.x = hbuf[s]; q.w = wqkv[s]; q.bias = ws[s]->b_qkv; q.y = qkv[s]; });
   if ((st = mark(MMDIT_STAGE_QKV, 0))) return st;
-  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, act, 3 * C, C, MMDIT_EPI_NONE, MMDIT_F32, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, act, 3 * C, C, MMDIT_EPI_NONE, MMDIT_F32, sm, split, BLOCK_SPLIT_BYTES))) return st;
   if ((st = mark(MMDIT_STAGE_QKV, 1))) return st;
   // S4 QK RMSNorm (+ RoPE on the visual stream), in place in the packed qkv rows
   if ((st = mark(MMDIT_STAGE_QK_NORM_ROPE, 0))) return st;
@@ -192,7 +196,7 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
     q.gate = mod[s] + 2 * C; q.gate_stride = 6 * C;
   });
   if ((st = mark(MMDIT_STAGE_OUT_PROJ, 0))) return st;
-  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, MMDIT_F32, C, C, MMDIT_EPI_GATED_RES, x_dtype, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, MMDIT_F32, C, C, MMDIT_EPI_GATED_RES, x_dtype, sm, split, BLOCK_SPLIT_BYTES))) return st;
   if ((st = mark(MMDIT_STAGE_OUT_PROJ, 1))) return st;
   if ((st = mark(MMDIT_STAGE_LN2, 0))) return st;
   // S7 LN-modulate for the FFN branch -> h2 in the qkv region
@@ -203,7 +207,7 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
   // S8 FFN up + GELU
   problems([&](int s, GemmProblem& q) { q.x = qkv[s]; q.w = w1[s]; q.bias = ws[s]->b_fc1; q.y = g[s]; });
   if ((st = mark(MMDIT_STAGE_FFN_UP, 0))) return st;
-  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, act, F, C, MMDIT_EPI_GELU, MMDIT_F32, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, act, F, C, MMDIT_EPI_GELU, MMDIT_F32, sm, split, BLOCK_SPLIT_BYTES))) return st;
   if ((st = mark(MMDIT_STAGE_FFN_UP, 1))) return st;
   // S9 FFN down with the FFN gate: out = x1 + gate_f (g W_2^T + b_2)
   problems([&](int s, GemmProblem& q) {
@@ -211,7 +215,7 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
     q.gate = mod[s] + 5 * C; q.gate_stride = 6 * C;
   });
   if ((st = mark(MMDIT_STAGE_FFN_DOWN, 0))) return st;
-  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, out_dtype, C, F, MMDIT_EPI_GATED_RES, MMDIT_F32, sm))) return st;
+  if ((st = launch_linear(p, nstreams, act, MMDIT_BF16, out_dtype, C, F, MMDIT_EPI_GATED_RES, MMDIT_F32, sm, split, BLOCK_SPLIT_BYTES))) return st;
   if ((st = mark(MMDIT_STAGE_FFN_DOWN, 1))) return st;
   return MMDIT_OK;
 }

@@ -145,8 +145,10 @@ int launch_lite_regroup(int layout, const void* x, const void* w, const void* bi
                         int in_dtype, int y_dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t C,
                         hipStream_t stream);
 // Runs one or two problems with equal N, K, dtypes and epilogue in one launch.
+// split_ws (optional, split_ws_bytes long): f32 scratch for the split tail (up to 64 MiB).
 int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dtype, int y_dtype,
-                  int64_t N, int64_t K, int epilogue, int res_dtype, hipStream_t stream);
+                  int64_t N, int64_t K, int epilogue, int res_dtype, hipStream_t stream,
+                  float* split_ws = nullptr, size_t split_ws_bytes = 0);
 int launch_attn8_quantize(const void* const* q, const void* const* k, const void* const* v, const int64_t* n,
                           int in_dtype, int64_t stride, int64_t B, int64_t H, const mmdit_attn8_stream* const* out,
                           float* v_scale, hipStream_t stream);

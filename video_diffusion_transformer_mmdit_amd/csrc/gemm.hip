@@ -42,11 +42,19 @@ constexpr int GBM = 256, GBN = 256, GBK = 32;
 constexpr int GTHREADS = 256;
 constexpr int GROUP_M = 8;
 constexpr int G_TILE_BYTES = 256 * GBK * 2;   // one operand tile of one stage: 16 KiB
+constexpr int64_t G_ROUND = 256;              // workgroups the chip runs at once (one per CU)
+constexpr size_t G_PART_BYTES = 256 * 256 * 4;   // f32 partial sums of one tile
 
 struct GemmArgs {
   GemmProblem p[2];
   int64_t tiles0;    // tiles of problem 0
   int64_t tiles;     // total tiles
+  // Split tail: workgroups [0, full) take one whole tile each; the remaining tiles (fewer than
+  // one round of the chip) are each cut into `split` K ranges taken by workgroups full + ...,
+  // which leave f32 partial sums in `part` for gemm_split_finish_kernel.  full == tiles: none.
+  int64_t full;
+  int split;
+  float* part;
   int64_t N, K;
   // 2x2 spatial regrouping (GEMM_GATHER_X / GEMM_SCATTER_Y): hidden width C, full grid
   // width W, merged grid width W/2 and merged tokens per frame (H/2)(W/2)
@@ -152,11 +160,11 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* opaque_lds(__
   return (__attribute__((address_space(3))) void*)(uintptr_t)a;
 }
 
-// Tile of this workgroup: tiles are renumbered so that each XCD (workgroups go round-robin
-// over the 8 XCDs) owns a contiguous run, rastered in groups of 8 M-tiles inside a problem.
-__device__ __forceinline__ void gemm_tile(const GemmArgs& args, int& pi, int& m0, int& n0) {
-  int64_t t = blockIdx.x;
-  if ((args.tiles & 7) == 0) t = (t & 7) * (args.tiles >> 3) + (t >> 3);
+// Tile of virtual index t: tiles are renumbered so that each XCD (workgroups go round-robin
+// over the 8 XCDs) owns a contiguous run of the whole-tile range, and rastered in groups of 8
+// M-tiles inside a problem.
+__device__ __forceinline__ void gemm_tile_of(const GemmArgs& args, int64_t t, int& pi, int& m0, int& n0) {
+  if (t < args.full && (args.full & 7) == 0) t = (t & 7) * (args.full >> 3) + (t >> 3);
   pi = t < args.tiles0 ? 0 : 1;
   if (pi) t -= args.tiles0;
   const int64_t M = args.p[pi].M, N = args.N;
@@ -168,6 +176,58 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, int& pi, int& m0
   const int64_t in_grp = t - grp * per_group;
   m0 = (int)((first_m + in_grp % gm) * GBM);
   n0 = (int)((in_grp / gm) * GBN);
+}
+
+// This workgroup's tile and its range [kb, ke) of K stages (nk stages in all); part_idx >= 0
+// for a split-tail workgroup (the index of its partial-sum slot).
+__device__ __forceinline__ void gemm_tile(const GemmArgs& args, int nk, int& pi, int& m0, int& n0, int& kb, int& ke,
+                                          int64_t& part_idx) {
+  const int64_t bid = blockIdx.x;
+  if (bid < args.full) {
+    gemm_tile_of(args, bid, pi, m0, n0);
+    kb = 0;
+    ke = nk;
+    part_idx = -1;
+  } else {
+    const int64_t r = (bid - args.full) / args.split;
+    const int sp = (int)((bid - args.full) - r * args.split);
+    gemm_tile_of(args, args.full + r, pi, m0, n0);
+    kb = (int)((int64_t)nk * sp / args.split);
+    ke = (int)((int64_t)nk * (sp + 1) / args.split);
+    part_idx = bid - args.full;
+  }
+}
+
+// Partial sums of one split workgroup: wave w's accumulator (j, i), element e, lane l at
+// part[((idx * 4 + w) * 16 + 4 j + i) * 16 + e) * 64 + l]: 64 consecutive floats per store
+// (stores straight from the accumulator registers; a float4 layout costs register spills).
+__device__ __forceinline__ void gemm_store_part(const GemmArgs& args, int64_t idx, int wave, int lane,
+                                                const f32x16 (&acc)[4][4]) {
+  float* base = args.part + ((idx * 4 + wave) * 16) * 16 * 64 + lane;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) base[((4 * j + i) * 16 + e) * 64] = acc[j][i][e];
+}
+
+// GELU or gated residual on four consecutive outputs (row m, columns n .. n + 3) that already
+// hold x W^T + b.
+template <int EPI, int RES_DT>
+__device__ __forceinline__ void gemm_epi_tail(const GemmProblem& P, int64_t N, int64_t m, int64_t n, float (&v)[4]) {
+  if constexpr (EPI == MMDIT_EPI_GELU) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = gelu_erf(v[q]);
+  }
+  if constexpr (EPI == MMDIT_EPI_GATED_RES) {
+    const int64_t b = m / P.rows_per_batch;
+    float r[4], gt[4];
+    load4<RES_DT>(P.res, m * N + n, r);
+    load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = fmaf(gt[q], v[q], r[q]);
+  }
 }
 
 // Epilogue of a 256 x 256 tile: bias, GELU or gated residual on the accumulators, one store.
@@ -251,8 +311,9 @@ void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_s2[2 * G_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_s3[2 * G_TILE_BYTES];
 
-  int pi, m0, n0;
-  gemm_tile(args, pi, m0, n0);
+  int pi, m0, n0, kb, ke;
+  int64_t part_idx;
+  gemm_tile(args, (int)(args.K / KSTEP), pi, m0, n0, kb, ke, part_idx);
   const GemmProblem& P = args.p[pi];
   const int64_t M = P.M, N = args.N, K = args.K;
 
@@ -284,6 +345,7 @@ void gemm_kernel(GemmArgs args) {
     wo[i] = (n0 + row) * (int)K * ES + lc * 16 - i * 1024;
   }
   auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
+    k0 += kb * KSTEP;
     int xso = k0 * ES;
     if constexpr (LAYOUT == GEMM_GATHER_X) {
       const int sg = __builtin_amdgcn_readfirstlane(k0 / args.c);
@@ -326,7 +388,7 @@ void gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
 
-  const int nk = (int)(K / KSTEP);
+  const int nk = ke - kb;   // stages of this workgroup (all of K unless it is a split-tail one)
   auto gbarrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -449,7 +511,8 @@ void gemm_kernel(GemmArgs args) {
   if (kt + 4 < nk) run(S0, TAIL, kt + 4);
   if (kt + 5 < nk) run(S1, TAIL, kt + 5);
 
-  gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, l32, g);
+  if (part_idx >= 0) gemm_store_part(args, part_idx, wave, lane, acc);
+  else gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, l32, g);
 }
 
 // 16-bit operands, plain layout: two LDS stages of K = 64 (64 KiB each, rows of 128 bytes,
@@ -463,8 +526,9 @@ void gemm_k64_kernel(GemmArgs args) {
   constexpr int T64 = GBM * 128;   // one operand tile of one stage: 32 KiB
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * T64];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * T64];
-  int pi, m0, n0;
-  gemm_tile(args, pi, m0, n0);
+  int pi, m0, n0, kb, ke;
+  int64_t part_idx;
+  gemm_tile(args, (int)(args.K / 64), pi, m0, n0, kb, ke, part_idx);
   const GemmProblem& P = args.p[pi];
   const int64_t M = P.M, N = args.N, K = args.K;
   const int tid = threadIdx.x;
@@ -485,7 +549,7 @@ void gemm_k64_kernel(GemmArgs args) {
     wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
   }
   auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
-    const int so = k0 * 2;
+    const int so = (k0 + kb * 64) * 2;
     auto* lx0 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192));
     auto* lx1 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192 + 4096));
     auto* lw0 = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 8192));
@@ -521,7 +585,7 @@ void gemm_k64_kernel(GemmArgs args) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
-  const int nk = (int)(K / 64);
+  const int nk = ke - kb;
   auto gbarrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -588,11 +652,54 @@ void gemm_k64_kernel(GemmArgs args) {
     step(S1, kt + 1);
   }
   if (kt < nk) step(S0, kt);
-  gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, l32, g);
+  if (part_idx >= 0) gemm_store_part(args, part_idx, wave, lane, acc);
+  else gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, l32, g);
+}
+
+// Tail tiles of a split launch: each thread sums, in K-range order, the `split` partial sums
+// of the four consecutive outputs (row m, columns n .. n + 3) that one GEMM lane held as
+// elements 4 e4 .. 4 e4 + 3 of one accumulator, and applies the tile epilogue to them;
+// G_SUM_WG workgroups per tail tile cover its 256 x 256 outputs.
+constexpr int G_SUM_WG = 64;   // 64 x 256 threads x 4 outputs = 256 x 256
+template <int BIAS_DT, int Y_DT, int EPI, int RES_DT>
+__global__ __launch_bounds__(GTHREADS) void gemm_split_finish_kernel(GemmArgs args) {
+  const int64_t tile = blockIdx.x / G_SUM_WG;
+  const int q = (blockIdx.x % G_SUM_WG) * GTHREADS + threadIdx.x;
+  const int lane = q & 63, e4 = (q >> 6) & 3, i = (q >> 8) & 3, j = (q >> 10) & 3, wave = q >> 12;
+  constexpr int64_t SLOT = G_PART_BYTES / 4;   // floats of one partial-sum slot
+  const float* base = args.part + tile * args.split * SLOT + ((wave * 16 + 4 * j + i) * 16 + 4 * e4) * 64 + lane;
+  float v[4] = {base[0], base[64], base[128], base[192]};
+#pragma unroll 2
+  for (int sp = 1; sp < args.split; ++sp) {
+    const float* b = base + sp * SLOT;
+    v[0] += b[0]; v[1] += b[64]; v[2] += b[128]; v[3] += b[192];
+  }
+  int pi, m0, n0;
+  gemm_tile_of(args, args.full + tile, pi, m0, n0);
+  const GemmProblem& P = args.p[pi];
+  // the accumulator element's place in the tile, as in the GEMM's epilogue
+  const int64_t m = m0 + (wave >> 1) * 128 + i * 32 + (lane & 31);
+  const int64_t n = n0 + (wave & 1) * 128 + j * 32 + 8 * e4 + 4 * (lane >> 5);
+  if (m >= P.M || n >= args.N) return;
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (P.bias) load4<BIAS_DT>(P.bias, n, bias);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] += bias[c];
+  gemm_epi_tail<EPI, RES_DT>(P, args.N, m, n, v);
+  store4<Y_DT>(P.y, m * args.N + n, v);
 }
 
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
 static void gemm_go(const GemmArgs& a, hipStream_t st) {
+  if constexpr (IN_DT != MMDIT_FP8_E4M3 && LAYOUT == GEMM_PLAIN) {
+    if (a.full < a.tiles) {   // split tail: whole tiles and K ranges of the tail tiles, then their sums
+      const int64_t grid = a.full + (a.tiles - a.full) * a.split;
+      if (a.K <= 4096) gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
+      else gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
+      gemm_split_finish_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)((a.tiles - a.full) * G_SUM_WG)), GTHREADS, 0, st>>>(a);
+      return;
+    }
+  }
   // The two-stage kernel prefetches one stage (three quarters of a stage's MFMAs) ahead: enough
   // while the K panels of a tile group stay in L2; for long K (FFN down, K = 12288) the
   // four-stage kernel's deeper prefetch measures faster.
@@ -618,6 +725,8 @@ int launch_lite_regroup(int layout, const void* x, const void* w, const void* bi
     return fail(MMDIT_ERR_SHAPE, "lite: tensors too large for 32-bit buffer offsets");
   a.p[0].x = x; a.p[0].w = w; a.p[0].bias = bias; a.p[0].y = y; a.p[0].M = M; a.p[0].rows_per_batch = M;
   a.tiles0 = a.tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+  a.full = a.tiles;
+  a.split = 1;
   a.N = N; a.K = K;
   a.c = (int)C; a.w = (int)W; a.w2 = (int)(W / 2); a.hw2 = (int)((H / 2) * (W / 2));
   if (a.tiles == 0) return MMDIT_OK;
@@ -637,7 +746,8 @@ int launch_lite_regroup(int layout, const void* x, const void* w, const void* bi
 }
 
 int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dtype, int y_dtype,
-                  int64_t N, int64_t K, int epilogue, int res_dtype, hipStream_t stream) {
+                  int64_t N, int64_t K, int epilogue, int res_dtype, hipStream_t stream, float* split_ws,
+                  size_t split_ws_bytes) {
   GemmArgs a{};
   const int64_t nTn = (N + GBN - 1) / GBN;
   int64_t tiles[2] = {0, 0};
@@ -655,7 +765,24 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   a.tiles = tiles[0] + tiles[1];
   a.N = N;
   a.K = K;
+  a.full = a.tiles;
+  a.split = 1;
   if (a.tiles == 0) return MMDIT_OK;
+  // Split tail: when the tiles fill R < 256 workgroup slots of the last round, cut each of
+  // those R tiles into S = 256 / R K ranges (each of at least 2 stages) so that the last round
+  // runs on (nearly) every CU instead of R of them.  Below 4 ranges the partial-sum pass costs
+  // about what the shorter last round saves, so such tails stay whole.
+  if (split_ws && x_dtype != MMDIT_FP8_E4M3 && a.tiles > G_ROUND) {
+    const int64_t R = a.tiles % G_ROUND;
+    const int64_t stages = K <= 4096 ? K / 64 : K / 32;
+    int64_t S = R ? G_ROUND / R : 0;
+    if (S > stages / 2) S = stages / 2;
+    if (R > 0 && S >= 4 && (size_t)(R * S) * G_PART_BYTES <= split_ws_bytes) {
+      a.full = a.tiles - R;
+      a.split = (int)S;
+      a.part = split_ws;
+    }
+  }
   if (a.tiles > 0x7fffffff) return fail(MMDIT_ERR_SHAPE, "linear: too many tiles");
   const int bdt = bias_dtype == MMDIT_F32 ? MMDIT_F32 : MMDIT_BF16;
 #define GEMM_CASE(IN, Y, EPI, RES)                                                            \
