@@ -230,69 +230,66 @@ __device__ __forceinline__ void gemm_epi_tail(const GemmProblem& P, int64_t N, i
   }
 }
 
-// Epilogue of a 256 x 256 tile: bias, GELU or gated residual on the accumulators, one store.
+// Epilogue of a 256 x 256 tile through LDS, so that the residual loads and the output stores
+// run along rows: wave w restages its 128 x 128 block a quarter (32 rows, accumulators i = q)
+// at a time as f32 in its own LDS region, rows 132 floats apart (the 4-float pad spreads the
+// rows one 16-lane group touches over distinct bank groups), then reads it back two rows per
+// instruction, 32 lanes x 4 columns per row, and applies the FP8 scales, bias, GELU or the
+// gated residual to four consecutive outputs per lane.  GEMM_SCATTER_Y: logical output row
+// m, column n goes to column n % C of the full-grid token merged_row0(m) + (s / 2) W + s % 2,
+// s = n / C (a 128-wide block lies inside one s, as C is a multiple of 256).  `region` holds
+// 32 x 132 floats; the caller has made every wave's reads of the K stages complete.
+constexpr int G_EPI_STRIDE = 132;                        // floats per restaged row
+constexpr int G_EPI_BYTES = 32 * G_EPI_STRIDE * 4;       // one wave's quarter block: 16.5 KiB
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& args, const GemmProblem& P, const f32x16 (&acc)[4][4],
-                                              int m0, int n0, int wm, int wn, int l32, int g) {
+__device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const GemmProblem& P,
+                                                   const f32x16 (&acc)[4][4], int m0, int n0, int wm, int wn,
+                                                   int lane, float* region) {
   constexpr bool FP8 = IN_DT == MMDIT_FP8_E4M3;
   const int64_t M = P.M, N = args.N;
-  // ---- epilogue: lane holds C^T rows (output columns) 8 (e/4) + 4 g + e%4 of each 32 x 32
-  // tile at output row l32: four consecutive columns per e/4.
-  // GEMM_SCATTER_Y: logical output row m, column n goes to column n % C of the full-grid
-  // token merged_row0(m) + (s / 2) W + s % 2, s = n / C; a 256-wide tile lies inside one s
-  // (C is a multiple of 256).
-  int64_t y_rows[4];
-  int s_col = 0;
-  if constexpr (LAYOUT == GEMM_SCATTER_Y) {
-    const int sg = n0 / args.c;
-    s_col = sg * args.c;
+  const int l32 = lane & 31, g = lane >> 5;
+  // this lane's four columns in the read phase, their bias
+  const int64_t n = n0 + wn * 128 + 4 * l32;
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (P.bias && n < N) load4<BIAS_DT>(P.bias, n, bias);
+  float sw = 1.f;
+  if constexpr (FP8) sw = *P.w_scale;
+  int sg = 0;
+  if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 128) / args.c;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + i * 32 + l32;
-      y_rows[i] = m < M ? (int64_t)merged_row0(m, args) + (sg >> 1) * args.w + (sg & 1) : 0;
-    }
-  }
-  // FP8: the product of the codes times the row's scale and W's scale
-  float rsc[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (FP8) {
-    const float sw = *P.w_scale;
+  for (int q = 0; q < 4; ++q) {
+    // accumulator (j, q) element e: row l32, column j * 32 + 8 (e / 4) + 4 g + e % 4 (single-
+    // float writes straight from the accumulator registers: a float4 write makes the
+    // compiler copy them out first)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 128 + i * 32 + l32;
-      rsc[i] = m < M ? P.x_scale[m] * sw : 0.f;
-    }
-  }
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int64_t n = n0 + wn * 128 + j * 32 + 8 * e4 + 4 * g;
-      if (n >= N) continue;
-      float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if (P.bias) load4<BIAS_DT>(P.bias, n, bias);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 128 + i * 32 + l32;
-        if (m >= M) continue;
+      for (int e = 0; e < 16; ++e) region[l32 * G_EPI_STRIDE + j * 32 + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[j][q][e];
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 32; r += 2) {
+      const int row = r + g;
+      const int64_t m = m0 + wm * 128 + q * 32 + row;
+      const float4 a = *reinterpret_cast<const float4*>(region + row * G_EPI_STRIDE + 4 * l32);
+      if (m < M && n < N) {
         float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (FP8) v[q] = fmaf(acc[j][i][4 * e4 + q], rsc[i], bias[q]);
-          else v[q] = acc[j][i][4 * e4 + q] + bias[q];
-          if constexpr (EPI == MMDIT_EPI_GELU) v[q] = gelu_erf(v[q]);
+        if constexpr (FP8) {
+          const float rs = P.x_scale[m] * sw;
+          v[0] = fmaf(a.x, rs, bias[0]); v[1] = fmaf(a.y, rs, bias[1]);
+          v[2] = fmaf(a.z, rs, bias[2]); v[3] = fmaf(a.w, rs, bias[3]);
+        } else {
+          v[0] = a.x + bias[0]; v[1] = a.y + bias[1]; v[2] = a.z + bias[2]; v[3] = a.w + bias[3];
         }
-        if constexpr (EPI == MMDIT_EPI_GATED_RES) {
-          const int64_t b = m / P.rows_per_batch;
-          float r[4], gt[4];
-          load4<RES_DT>(P.res, m * N + n, r);
-          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = fmaf(gt[q], v[q], r[q]);
+        gemm_epi_tail<EPI, RES_DT>(P, N, m, n, v);
+        if constexpr (LAYOUT == GEMM_SCATTER_Y) {
+          const int64_t yr = (int64_t)merged_row0((int)m, args) + (sg >> 1) * args.w + (sg & 1);
+          store4<Y_DT>(P.y, yr * args.c + (n - (int64_t)sg * args.c), v);
+        } else {
+          store4<Y_DT>(P.y, m * N + n, v);
         }
-        if constexpr (LAYOUT == GEMM_SCATTER_Y) store4<Y_DT>(P.y, y_rows[i] * args.c + (n - s_col), v);
-        else store4<Y_DT>(P.y, m * N + n, v);
       }
     }
+    __syncthreads();
   }
 }
 
@@ -511,8 +508,16 @@ void gemm_kernel(GemmArgs args) {
   if (kt + 4 < nk) run(S0, TAIL, kt + 4);
   if (kt + 5 < nk) run(S1, TAIL, kt + 5);
 
-  if (part_idx >= 0) gemm_store_part(args, part_idx, wave, lane, acc);
-  else gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, l32, g);
+  if (part_idx >= 0) {
+    gemm_store_part(args, part_idx, wave, lane, acc);
+  } else {
+    // every wave's fragment reads of the last stage are done after this barrier; wave w
+    // restages in stage buffer w
+    __syncthreads();
+    uint8_t* rb = wave == 0 ? lds_s0 : wave == 1 ? lds_s1 : wave == 2 ? lds_s2 : lds_s3;
+    gemm_epilogue_rows<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, lane,
+                                                                  reinterpret_cast<float*>(rb));
+  }
 }
 
 // 16-bit operands, plain layout: two LDS stages of K = 64 (64 KiB each, rows of 128 bytes,
@@ -536,15 +541,18 @@ void gemm_k64_kernel(GemmArgs args) {
   const int l32 = lane & 31, g = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
   // DMA i of a wave fills rows 64 wave + 8 i .. +7 (lane l -> row + l / 8, physical chunk
-  // l % 8 = logical ^ (row % 8)); loads 0-3 and 4-7 each share one LDS base, the immediate
-  // offset (i % 4) * 1024 moving destination and source alike
+  // l % 8 = logical ^ ((row / 2) % 8)); loads 0-3 and 4-7 each share one LDS base, the
+  // immediate offset (i % 4) * 1024 moving destination and source alike.  A 128-byte row
+  // spans half of the 64 LDS banks, so the 16 rows one 16-lane group of a 16-byte read
+  // touches fall in two bank halves by row parity; swizzling by row / 2 gives the 8 rows of
+  // each parity 8 distinct chunks (by row % 8 they would repeat after 4, a 2-way conflict).
   const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * 2);
   const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * 2);
   int xo[8], wo[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 64 * wave + 8 * i + (lane >> 3);
-    const int lc = (lane & 7) ^ (row & 7);
+    const int lc = (lane & 7) ^ ((row >> 1) & 7);
     xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
     wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
   }
@@ -577,7 +585,7 @@ void gemm_k64_kernel(GemmArgs args) {
   constexpr std::integral_constant<int, 1> S1{};
   int cofs[4];   // slice ks: logical chunk 2 ks + g of row l32 (+ a multiple of 32)
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) cofs[ks] = l32 * 128 + (((2 * ks + g) ^ (l32 & 7)) << 4);
+  for (int ks = 0; ks < 4; ++ks) cofs[ks] = l32 * 128 + (((2 * ks + g) ^ ((l32 >> 1) & 7)) << 4);
   f32x16 acc[4][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -652,8 +660,15 @@ void gemm_k64_kernel(GemmArgs args) {
     step(S1, kt + 1);
   }
   if (kt < nk) step(S0, kt);
-  if (part_idx >= 0) gemm_store_part(args, part_idx, wave, lane, acc);
-  else gemm_epilogue<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, l32, g);
+  if (part_idx >= 0) {
+    gemm_store_part(args, part_idx, wave, lane, acc);
+  } else {
+    // every wave's fragment reads of the last stage are done after this barrier; waves 0, 1
+    // restage in the first stage buffer, waves 2, 3 in the second
+    __syncthreads();
+    float* region = reinterpret_cast<float*>((wave < 2 ? lds_a : lds_b) + (wave & 1) * G_EPI_BYTES);
+    gemm_epilogue_rows<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, lane, region);
+  }
 }
 
 // Tail tiles of a split launch: each thread sums, in K-range order, the `split` partial sums
