@@ -341,7 +341,8 @@ void gemm_kernel(GemmArgs args) {
       xo[i] = (m0 + row) * (int)K * ES + lc * 16 - i * 1024;
     wo[i] = (n0 + row) * (int)K * ES + lc * 16 - i * 1024;
   }
-  auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
+  // part 0: the x tile's four loads, 1: W's, 2: both
+  auto dma = [&](uint8_t* xs, uint8_t* ws, int k0, int part = 2) {
     k0 += kb * KSTEP;
     int xso = k0 * ES;
     if constexpr (LAYOUT == GEMM_GATHER_X) {
@@ -351,14 +352,18 @@ void gemm_kernel(GemmArgs args) {
     const int so = k0 * ES;
     auto* lx = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 4096));
     auto* lw = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 4096));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], xso, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], xso, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], xso, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], xso, 3072, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[0], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[3], so, 3072, 0);
+    if (part != 1) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], xso, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], xso, 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], xso, 2048, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], xso, 3072, 0);
+    }
+    if (part != 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[0], so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[1], so, 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[2], so, 2048, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[3], so, 3072, 0);
+    }
   };
   auto xbuf = [&](auto s) -> uint8_t* {
     constexpr int v = decltype(s)::value;
@@ -416,19 +421,34 @@ void gemm_kernel(GemmArgs args) {
     constexpr std::integral_constant<int, (CUR + 3) & 3> ahead{};
     // stage kt+3 goes into the buffers stage kt-1 used (every wave has passed the barrier
     // that ended stage kt-1)
-    if (MAIN || kt + 3 < nk) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP);
+    const bool dma_here = MAIN || kt + 3 < nk;
     uint4 wf1[4], xf1[4];
     read_slice(xbuf(cur), wbuf(cur), 1, wf1, xf1);
-    mma(wf0, xf0);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 0: stage kt+3's DMA in two groups of four loads (x, then W), each before a row of
+    // four MFMAs; fenced, as left to the scheduler the second group issues in one burst that
+    // holds back the MFMAs behind it (in-order issue)
+    auto mrow = [&](int j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wf0[j], xf0[i], acc[j][i]);
+    };
+    if (dma_here) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mrow(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dma_here) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mrow(1);
+    mrow(2);
+    mrow(3);
+    __builtin_amdgcn_sched_barrier(0);
     // slice 0 of the next stage is read while this stage's second slice runs
     if (MAIN || kt + 1 < nk) read_slice(xbuf(next), wbuf(next), 0, wf0, xf0);
     mma(wf1, xf1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if ((i < 4) || (i >= 16 && i < 24)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      if (MAIN && i >= 4 && i < 12) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     // this wave's loads of stage kt+2 have landed once at most the eight loads of stage kt+3
@@ -556,6 +576,18 @@ void gemm_k64_kernel(GemmArgs args) {
     xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
     wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
   }
+  // the four loads of one LDS base (x rows 0-31 / 32-63 of the wave's 64, then W's)
+  auto dma_part = [&](uint8_t* xs, uint8_t* ws, int k0, auto part_c) {
+    constexpr int PART = decltype(part_c)::value;
+    const int so = (k0 + kb * 64) * 2;
+    const auto rs = PART < 2 ? rx : rw;
+    const int* o = (PART < 2 ? xo : wo) + (PART & 1) * 4;
+    auto* l = opaque_lds((__attribute__((address_space(3))) void*)((PART < 2 ? xs : ws) + wave * 8192 + (PART & 1) * 4096));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[3], so, 3072, 0);
+  };
   auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
     const int so = (k0 + kb * 64) * 2;
     auto* lx0 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192));
@@ -612,14 +644,12 @@ void gemm_k64_kernel(GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wf[j], xf[i], acc[j][i]);
   };
-  // 16 MFMAs with the next slice's 8 fragment reads among the first eight (and the stage's
-  // 16 DMA loads, two at a time, among MFMAs 2-9 when dma_here)
-  auto sched = [&](bool dma_here) {
+  // 16 MFMAs with the next slice's 8 fragment reads among the first eight
+  auto sched = [&]() {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      if (dma_here && i >= 2 && i < 10) __builtin_amdgcn_sched_group_barrier(0x010, 2, 1);
     }
   };
   // stage kt in buffer cur, its slice 0 in wfa / xfa
@@ -628,18 +658,39 @@ void gemm_k64_kernel(GemmArgs args) {
     constexpr std::integral_constant<int, CUR> cur{};
     constexpr std::integral_constant<int, CUR ^ 1> oth{};
     const bool more = kt + 1 < nk;
-    if (more) dma(xbuf(oth), wbuf(oth), (kt + 1) * 64);   // its last readers passed the previous barrier
     read_slice(xbuf(cur), wbuf(cur), 1, wfb, xfb);
-    mma(wfa, xfa);
-    sched(true);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 0: the next stage's DMA (its buffer's last readers passed the previous barrier) in
+    // four groups of four loads, one group before each row of four MFMAs; fenced, as left to
+    // the scheduler the sixteen loads issue in one burst that holds back the MFMAs behind them
+    // (in-order issue), 2-5 % slower
+    auto mrow = [&](int j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wfa[j], xfa[i], acc[j][i]);
+    };
+    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mrow(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mrow(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 2>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mrow(2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mrow(3);
     __builtin_amdgcn_sched_barrier(0);
     read_slice(xbuf(cur), wbuf(cur), 2, wfa, xfa);
     mma(wfb, xfb);
-    sched(false);
+    sched();
     __builtin_amdgcn_sched_barrier(0);
     read_slice(xbuf(cur), wbuf(cur), 3, wfb, xfb);
     mma(wfa, xfa);
-    sched(false);
+    sched();
     __builtin_amdgcn_sched_barrier(0);
     // this wave's loads of stage kt+1 have landed and its reads of stage kt are done; after
     // the barrier both hold for every wave
@@ -647,7 +698,7 @@ void gemm_k64_kernel(GemmArgs args) {
     gbarrier();
     if (more) read_slice(xbuf(oth), wbuf(oth), 0, wfa, xfa);
     mma(wfb, xfb);
-    sched(false);
+    sched();
     __builtin_amdgcn_sched_barrier(0);
   };
   dma(xbuf(S0), wbuf(S0), 0);
