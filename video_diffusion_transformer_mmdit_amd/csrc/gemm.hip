@@ -221,7 +221,8 @@ __device__ __forceinline__ void gemm_epi_tail(const GemmProblem& P, int64_t N, i
     for (int q = 0; q < 4; ++q) v[q] = gelu_erf(v[q]);
   }
   if constexpr (EPI == MMDIT_EPI_GATED_RES) {
-    const int64_t b = m / P.rows_per_batch;
+    // rows and rows per batch item are below 2^31 (the launch checks (M + 256) K < 2^31)
+    const int64_t b = (uint32_t)m / (uint32_t)P.rows_per_batch;
     float r[4], gt[4];
     load4<RES_DT>(P.res, m * N + n, r);
     load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
@@ -242,10 +243,13 @@ __device__ __forceinline__ void gemm_epi_tail(const GemmProblem& P, int64_t N, i
 constexpr int G_EPI_STRIDE = 132;                        // floats per restaged row
 constexpr int G_EPI_BYTES = 32 * G_EPI_STRIDE * 4;       // one wave's quarter block: 16.5 KiB
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
-__device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const GemmProblem& P,
+__device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const GemmProblem& Pk,
                                                    const f32x16 (&acc)[4][4], int m0, int n0, int wm, int wn,
                                                    int lane, float* region) {
   constexpr bool FP8 = IN_DT == MMDIT_FP8_E4M3;
+  // a private copy of the problem: read through the reference, its pointers were reloaded
+  // from the kernel arguments after every output store (one scalar load and wait per row)
+  const GemmProblem P = Pk;
   const int64_t M = P.M, N = args.N;
   const int l32 = lane & 31, g = lane >> 5;
   // this lane's four columns in the read phase, their bias
@@ -258,20 +262,25 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
   if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 128) / args.c;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    // accumulator (j, q) element e: row l32, column j * 32 + 8 (e / 4) + 4 g + e % 4 (single-
-    // float writes straight from the accumulator registers: a float4 write makes the
-    // compiler copy them out first)
+    // accumulator (j, q) element e: row l32, column j * 32 + 8 (e / 4) + 4 g + e % 4 (written
+    // element by element, which the compiler merges into 16-byte writes; spelled as float4
+    // writes, it copied the accumulators out first and spilled)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) region[l32 * G_EPI_STRIDE + j * 32 + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[j][q][e];
     __syncthreads();
-#pragma unroll 4
-    for (int r = 0; r < 32; r += 2) {
-      const int row = r + g;
-      const int64_t m = m0 + wm * 128 + q * 32 + row;
-      const float4 a = *reinterpret_cast<const float4*>(region + row * G_EPI_STRIDE + 4 * l32);
-      if (m < M && n < N) {
+    for (int r0 = 0; r0 < 32; r0 += 8) {
+      // four rows' reads in flight before the first store
+      float4 a4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        a4[k] = *reinterpret_cast<const float4*>(region + (r0 + 2 * k + g) * G_EPI_STRIDE + 4 * l32);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 a = a4[k];
+        const int64_t m = m0 + wm * 128 + q * 32 + r0 + 2 * k + g;
+        if (m >= M || n >= N) continue;
         float v[4];
         if constexpr (FP8) {
           const float rs = P.x_scale[m] * sw;
@@ -742,7 +751,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_split_finish_kernel(GemmArgs ar
   }
   int pi, m0, n0;
   gemm_tile_of(args, args.full + tile, pi, m0, n0);
-  const GemmProblem& P = args.p[pi];
+  const GemmProblem P = args.p[pi];
   // the accumulator element's place in the tile, as in the GEMM's epilogue
   const int64_t m = m0 + (wave >> 1) * 128 + i * 32 + (lane & 31);
   const int64_t n = n0 + (wave & 1) * 128 + j * 32 + 8 * e4 + 4 * (lane >> 5);
