@@ -380,8 +380,9 @@ typedef struct {
  *   MMDIT_WS_WQKV, MMDIT_WS_WO, MMDIT_WS_W1, MMDIT_WS_W2: f16 copies of w_qkv, w_o, w_fc1,
  *                   w_fc2 (act_dtype F16 only).
  *   MMDIT_WS_SPLIT  f32 64 MiB, stream 0 only: partial sums of the GEMM tiles of a launch's
- *                   last, partial round, each computed over K ranges by several workgroups
- *                   (its contents after the call are scratch). */
+ *                   last, partial round, each computed over K ranges by several workgroups,
+ *                   and likewise the attention's last-round query tiles computed over key
+ *                   ranges (its contents after the call are scratch). */
 enum { MMDIT_WS_MOD = 0, MMDIT_WS_H = 1, MMDIT_WS_QKV = 2, MMDIT_WS_X1 = 3, MMDIT_WS_G = 4,
        MMDIT_WS_WQKV = 5, MMDIT_WS_WO = 6, MMDIT_WS_W1 = 7, MMDIT_WS_W2 = 8, MMDIT_WS_SPLIT = 9,
        MMDIT_WS_COUNT = 10 };

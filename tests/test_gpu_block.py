@@ -159,8 +159,10 @@ def test_block_split_tail_tiles_parity():
     """A size whose GEMMs leave a partial last round that includes visual-stream tiles (5500 +
     77 tokens: 23 M-tiles, so the last rounds of the QKV (60 tiles, 4 K ranges each), out-
     projection and FFN-down (20 tiles, 12 ranges) GEMMs are split over K and reduced separately,
-    while FFN up (80 tiles, 3 ranges) stays whole); sampled rows, most of them in the split
-    tiles' row range, and every conditioning row, against the oracle."""
+    while FFN up (80 tiles, 3 ranges) stays whole; the attention's 528 (head, query tile) items
+    leave 16 for the last round, query tiles 20-21 of heads 16-23, each cut into 16 key ranges
+    and merged); sampled rows, most of them in the split tiles' row range, and every
+    conditioning row, against the oracle."""
     cfg = wl.BlockConfig("block_split_c3072_h24_f12288_grid1x50x110_cond77", 3072, 24, 128, 12288, 1536,
                          (1, 50, 110), 77, seed=13)
     raw = wl.block_inputs(cfg)

@@ -32,7 +32,9 @@ static int validate_dims(const mmdit_block_dims* d, int64_t B, int64_t n_vis, in
   return MMDIT_OK;
 }
 
-constexpr size_t BLOCK_SPLIT_BYTES = (size_t)256 * 256 * 256 * 4;   // 256 tile partial sums, f32
+// 256 GEMM tile partial sums (f32), also holding the attention's split-tail key-range results
+// (at most 256 x (256 x 128 + 512) floats)
+constexpr size_t BLOCK_SPLIT_BYTES = (size_t)256 * 256 * 256 * 4;
 
 static void layout(const mmdit_block_dims* d, int64_t B, int64_t n_vis, int64_t n_cond, WsLayout* L) {
   size_t cur = 0;
@@ -187,7 +189,8 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
     const uint16_t* qc = n_cond > 0 ? static_cast<const uint16_t*>(qkv[1]) : nullptr;
     if ((st = launch_joint_attention(qv, qv + C, qv + 2 * C, n_vis, qc, qc ? qc + C : nullptr, qc ? qc + 2 * C : nullptr,
                                      n_cond, act, act, 3 * C, B, H, 1.0f / sqrtf((float)d.D), hbuf[0],
-                                     n_cond > 0 ? hbuf[1] : nullptr, act, C, nullptr, sm))) return st;
+                                     n_cond > 0 ? hbuf[1] : nullptr, act, C, nullptr, sm, split,
+                                     BLOCK_SPLIT_BYTES))) return st;
   }
   if ((st = mark(MMDIT_STAGE_ATTENTION, 1))) return st;
   // S6 output projection with the attention gate: x1 = x + gate_a (O W_o^T + b_o), f32

@@ -124,7 +124,8 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
                            const void* q_cond, const void* k_cond, const void* v_cond,
                            int64_t n_cond, int qk_dtype, int v_dtype, int64_t in_stride, int64_t B, int64_t H,
                            float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
-                           int64_t out_stride, float* lse, hipStream_t stream);
+                           int64_t out_stride, float* lse, hipStream_t stream, float* split_ws = nullptr,
+                           size_t split_ws_bytes = 0);
 
 struct GemmProblem {
   const void* x;      // [M, K]

@@ -58,7 +58,20 @@ struct AttnArgs {
   int H;
   int nqt;
   float scale_log2;       // softmax_scale * log2(e)
+  // Work items are (batch item x head, query tile) pairs, nbh * nqt of them.  Split tail:
+  // workgroups [0, full) take items 0 .. full-1 over all keys; each of the remaining items
+  // (fewer than one round of the chip) is cut into `split` key ranges taken by workgroups
+  // full + ..., which leave f32 partial results in `part` for joint_attn_merge_kernel.
+  // full == nbh * nqt: none.
+  int nbh;
+  int full;
+  int split;
+  float* part;
 };
+
+constexpr int ATT_ROUND = 256;   // workgroups the chip runs at once (one per CU)
+// one key range's partial result for one query tile: O (256 x 128 f32) then (m, l) per query
+constexpr int64_t ATT_PART_FLOATS = 256 * 128 + 256 * 2;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
@@ -115,6 +128,21 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint8_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// (batch item x head, query tile) of work item i.  Items are dispatched round-robin over the
+// 8 XCDs (i % 8), each with its own L2; when the (batch, head) count allows, XCD x takes whole
+// heads x, x + 8, ... so that the 32 workgroups it runs at a time stream the same K and V
+// through one L2.
+__device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int& bh, int& qt) {
+  if ((a.nbh & 7) == 0) {
+    const int j = i >> 3;
+    bh = (i & 7) + 8 * (j / a.nqt);
+    qt = j % a.nqt;
+  } else {
+    bh = i / a.nqt;
+    qt = i % a.nqt;
+  }
+}
+
 template <int QK_DT, int V_DT, int OUT_DT, bool LSE>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void joint_attn_mfma_kernel(AttnArgs a) {
@@ -130,20 +158,15 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave index in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
-  // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8), each with its own L2.
-  // When the (batch, head) count allows, XCD x takes whole heads x, x + 8, ... so that the 32
-  // workgroups it runs at a time stream the same K and V through one L2.
   int qt, bh;
+  int slot = -1;   // a split-tail workgroup's partial-result slot
   {
-    const int bid = blockIdx.x, nbh = gridDim.x / a.nqt;
-    if ((nbh & 7) == 0) {
-      const int i = bid >> 3;
-      bh = (bid & 7) + 8 * (i / a.nqt);
-      qt = i % a.nqt;
-    } else {
-      bh = bid / a.nqt;
-      qt = bid % a.nqt;
+    int item = blockIdx.x;
+    if (item >= a.full) {
+      slot = item - a.full;
+      item = a.full + slot / a.split;
     }
+    attn_item(a, item, bh, qt);
   }
   const int h = bh % a.H;
   const int64_t b = bh / a.H;
@@ -183,6 +206,13 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   }
   const int t_vis = (int)((n_vis + ATT_BN - 1) / ATT_BN);
   const int ntiles = t_vis + (int)((n_cond + ATT_BN - 1) / ATT_BN);
+  // this workgroup's key tiles [jbeg, jend): all of them, or one range of a split-tail item
+  int jbeg = 0, jend = ntiles;
+  if (slot >= 0) {
+    const int sp = slot % a.split;
+    jbeg = (int)((int64_t)ntiles * sp / a.split);
+    jend = (int)((int64_t)ntiles * (sp + 1) / a.split);
+  }
   auto tile_seg = [&](int jt, int& sg, int& t) { sg = jt < t_vis ? 0 : 1; t = sg ? jt - t_vis : jt; };
   auto tile_rows = [&](int sg, int t) {
     const int64_t r = a.n_seg[sg] - (int64_t)t * ATT_BN;
@@ -323,8 +353,8 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       // group 0: V_{j+1} into the other V stage; group 1: K_{j+2} into this K stage (its last
       // reader, group 1's M(j-1), is behind the barrier).  Past the last tile: a reload of the
       // last one into a stage nobody reads again.
-      if constexpr (GRP == 0) dma_tile(jt + 1 < ntiles ? jt + 1 : ntiles - 1, vbuf(oth));
-      else dma_tile(jt + 2 < ntiles ? jt + 2 : ntiles - 1, kbuf(cur));
+      if constexpr (GRP == 0) dma_tile(jt + 1 < jend ? jt + 1 : jend - 1, vbuf(oth));
+      else dma_tile(jt + 2 < jend ? jt + 2 : jend - 1, kbuf(cur));
       compute_s(kbuf(oth), sn);
       const uint8_t* vb = vbuf(cur);
 #pragma unroll
@@ -365,9 +395,9 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       // S and mx hold logit - m_run.  The first tile sets the running max exactly; later the
       // max is only raised when a logit exceeds it by more than 2^8 (lazy rescale)
       const float dl = mx * ce;
-      if (jt == 0 || __any(dl > ATT_RESCALE_LOG2)) {
-        const float delta = jt == 0 ? dl : fmaxf(dl, 0.f);
-        if (jt != 0) {
+      if (jt == jbeg || __any(dl > ATT_RESCALE_LOG2)) {
+        const float delta = jt == jbeg ? dl : fmaxf(dl, 0.f);
+        if (jt != jbeg) {
           const float alpha = __builtin_amdgcn_exp2f(-delta);
           l_run *= alpha;
 #pragma unroll
@@ -416,26 +446,26 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     // prologue: group 1 loads K_0 and K_1; S_0 is an M phase of its own in which group 0
     // starts loading V_0
     if constexpr (GRP == 1) {
-      dma_tile(0, lds_k0);
-      if (ntiles > 1) dma_tile(1, lds_k1);
+      dma_tile(jbeg, lds_k0);
+      if (jbeg + 1 < jend) dma_tile(jbeg + 1, lds_k1);
       __builtin_amdgcn_s_waitcnt(0xF70);
     }
     __syncthreads();
     if constexpr (GRP == 1) phase_barrier();   // group 1 runs one phase behind
-    if constexpr (GRP == 0) dma_tile(0, lds_v0);
+    if constexpr (GRP == 0) dma_tile(jbeg, lds_v0);
     f32x16 sa[2], sb[2];
     init_s(sa, 0.f);
     compute_s(lds_k0, sa);
     asm volatile("" ::"v"(sa[0]), "v"(sa[1]));
     phase_barrier();
-    int jt = 0;
-    for (; jt + 1 < ntiles; jt += 2) {
+    int jt = jbeg;
+    for (; jt + 1 < jend; jt += 2) {
       phase_v(S0, jt, sa, sb);
       phase_m(S0, jt, sb);
       phase_v(S1, jt + 1, sb, sa);
       phase_m(S1, jt + 1, sa);
     }
-    if (jt < ntiles) {
+    if (jt < jend) {
       phase_v(S0, jt, sa, sb);
       phase_m(S0, jt, sb);
     }
@@ -446,6 +476,18 @@ void joint_attn_mfma_kernel(AttnArgs a) {
 
     // ---- finish: combine the two half-wave partial sums, normalise, store
     const float l_tot = xhalf_sum(l_run);
+    if (slot >= 0) {   // a key range of a split-tail item: unnormalised O, running max and sum
+      float* pb = a.part + (int64_t)slot * ATT_PART_FLOATS;
+      const int ql = wave * 32 + l32;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          *reinterpret_cast<float4*>(pb + ql * 128 + dt * 32 + 8 * e4 + 4 * g) =
+              make_float4(o[dt][4 * e4], o[dt][4 * e4 + 1], o[dt][4 * e4 + 2], o[dt][4 * e4 + 3]);
+      if (g == 0) *reinterpret_cast<float2*>(pb + 256 * 128 + 2 * ql) = make_float2(m_run, l_tot);
+      return;
+    }
     if (qi >= N) return;
     const float inv = 1.0f / l_tot;
     const bool is_cond = qi < n_cond;
@@ -549,9 +591,61 @@ __global__ __launch_bounds__(64) void joint_attn_f32_kernel(AttnArgsF32 a) {
   }
 }
 
+// Split-tail items: per query, the `split` key ranges' results (O_s relative to their own
+// running max m_s, sums l_s, log2 units) combine as O = sum_s 2^(m_s - M) O_s / L with
+// M = max_s m_s and L = sum_s 2^(m_s - M) l_s; then the output row and, if asked, the LSE.
+// One thread per query and four dims; 32 workgroups of 256 threads per item.
+template <int OUT_DT, bool LSE>
+__global__ __launch_bounds__(256) void joint_attn_merge_kernel(AttnArgs a) {
+  const int r = blockIdx.x >> 5;                       // tail item
+  const int t = (blockIdx.x & 31) * 256 + threadIdx.x;
+  const int ql = t >> 5, d0 = (t & 31) * 4;            // query in the tile, first dim
+  int bh, qt;
+  attn_item(a, a.full + r, bh, qt);
+  const int64_t qi = (int64_t)qt * ATT_BM + ql;
+  if (qi >= a.N) return;
+  const float* pb = a.part + (int64_t)r * a.split * ATT_PART_FLOATS;
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < a.split; ++sp) mmax = fmaxf(mmax, pb[sp * ATT_PART_FLOATS + 256 * 128 + 2 * ql]);
+  float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < a.split; ++sp) {
+    const float* ps = pb + sp * ATT_PART_FLOATS;
+    const float w = exp2f(ps[256 * 128 + 2 * ql] - mmax);
+    l = fmaf(w, ps[256 * 128 + 2 * ql + 1], l);
+    const float4 o = *reinterpret_cast<const float4*>(ps + ql * 128 + d0);
+    acc[0] = fmaf(w, o.x, acc[0]); acc[1] = fmaf(w, o.y, acc[1]);
+    acc[2] = fmaf(w, o.z, acc[2]); acc[3] = fmaf(w, o.w, acc[3]);
+  }
+  const float inv = 1.0f / l;
+  const int h = bh % a.H;
+  const int64_t b = bh / a.H;
+  const int64_t n_cond = a.n_seg[1], n_vis = a.n_seg[0];
+  const bool is_cond = qi < n_cond;
+  const int64_t row = is_cond ? b * n_cond + qi : b * n_vis + (qi - n_cond);
+  void* obase = is_cond ? a.o[1] : a.o[0];
+  const int64_t off = row * a.out_stride + (int64_t)h * ATT_D + d0;
+  const float v0 = acc[0] * inv, v1 = acc[1] * inv, v2 = acc[2] * inv, v3 = acc[3] * inv;
+  if constexpr (OUT_DT == MMDIT_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(obase) + off) = make_float4(v0, v1, v2, v3);
+  } else if constexpr (OUT_DT == MMDIT_BF16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + off) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + off) = make_uint2(cvt_pk_f16(v0, v1), cvt_pk_f16(v2, v3));
+  }
+  if constexpr (LSE) {
+    if (d0 == 0) a.lse[(b * a.H + h) * a.N + qi] = (mmax + log2f(l)) * 0.69314718055994530942f;
+  }
+}
+
 template <int QK, int V>
 static int attn_go(const AttnArgs& a, dim3 grid, int out_dtype, bool has_lse, hipStream_t stream) {
-#define ATT_GO(O, L) joint_attn_mfma_kernel<QK, V, O, L><<<grid, ATT_THREADS, 0, stream>>>(a)
+  const int tail = a.nbh * a.nqt - a.full;   // split-tail items
+  const dim3 mgrid((unsigned)(tail * 32));
+#define ATT_GO(O, L)                                                                        \
+  do {                                                                                      \
+    joint_attn_mfma_kernel<QK, V, O, L><<<grid, ATT_THREADS, 0, stream>>>(a);              \
+    if (tail > 0) joint_attn_merge_kernel<O, L><<<mgrid, 256, 0, stream>>>(a);             \
+  } while (0)
   if (out_dtype == MMDIT_F32) { if (has_lse) ATT_GO(MMDIT_F32, true); else ATT_GO(MMDIT_F32, false); }
   else if (out_dtype == MMDIT_BF16) { if (has_lse) ATT_GO(MMDIT_BF16, true); else ATT_GO(MMDIT_BF16, false); }
   else if (out_dtype == MMDIT_F16) { if (has_lse) ATT_GO(MMDIT_F16, true); else ATT_GO(MMDIT_F16, false); }
@@ -564,7 +658,8 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
                            const void* q_cond, const void* k_cond, const void* v_cond,
                            int64_t n_cond, int qk_dtype, int v_dtype, int64_t in_stride, int64_t B, int64_t H,
                            float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
-                           int64_t out_stride, float* lse, hipStream_t stream) {
+                           int64_t out_stride, float* lse, hipStream_t stream, float* split_ws,
+                           size_t split_ws_bytes) {
   const int64_t N = n_vis + n_cond;
   if (B == 0 || H == 0 || N == 0) return MMDIT_OK;
   const bool has_lse = lse != nullptr;
@@ -584,8 +679,26 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
     a.H = (int)H;
     a.nqt = (int)((N + ATT_BM - 1) / ATT_BM);
     a.scale_log2 = softmax_scale * 1.44269504088896340736f;
-    const int64_t blocks = (int64_t)a.nqt * H * B;
-    if (blocks > 0x7fffffff) return fail(MMDIT_ERR_SHAPE, "joint_attention: grid too large");
+    const int64_t items = (int64_t)a.nqt * H * B;
+    if (items > 0x7fffffff) return fail(MMDIT_ERR_SHAPE, "joint_attention: grid too large");
+    a.nbh = (int)(H * B);
+    a.full = (int)items;
+    a.split = 1;
+    // Split tail: when the items fill R < 256 workgroup slots of the last round, cut each of
+    // those R items into S = 256 / R key ranges (at most one per key tile) so that the last
+    // round runs on (nearly) every CU instead of R of them; a merge kernel combines them.
+    const int64_t ntiles = (n_vis + ATT_BN - 1) / ATT_BN + (n_cond + ATT_BN - 1) / ATT_BN;
+    if (split_ws && items > ATT_ROUND) {
+      const int64_t R = items % ATT_ROUND;
+      int64_t S = R ? ATT_ROUND / R : 0;
+      if (S > ntiles) S = ntiles;
+      if (R > 0 && S >= 2 && (size_t)(R * S * ATT_PART_FLOATS) * 4 <= split_ws_bytes) {
+        a.full = (int)(items - R);
+        a.split = (int)S;
+        a.part = split_ws;
+      }
+    }
+    const int64_t blocks = a.full + (items - a.full) * a.split;
     const dim3 grid((unsigned)blocks);
     if (qk_dtype == MMDIT_F16 && v_dtype == MMDIT_F16) return attn_go<MMDIT_F16, MMDIT_F16>(a, grid, out_dtype, has_lse, stream);
     if (qk_dtype == MMDIT_F16 && v_dtype == MMDIT_BF16) return attn_go<MMDIT_F16, MMDIT_BF16>(a, grid, out_dtype, has_lse, stream);
