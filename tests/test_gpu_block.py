@@ -158,8 +158,8 @@ def test_block_480p_sampled_parity():
 def test_block_split_tail_tiles_parity():
     """A size whose GEMMs leave a partial last round that includes visual-stream tiles (5500 +
     77 tokens: 23 M-tiles, so the last rounds of the QKV (60 tiles, 4 K ranges each), out-
-    projection and FFN-down (20 tiles, 12 ranges) GEMMs are split over K and reduced separately,
-    while FFN up (80 tiles, 3 ranges) stays whole; the attention's 528 (head, query tile) items
+    projection and FFN-down (20 tiles, 12 ranges) and FFN-up + GELU (80 tiles, 3 ranges) GEMMs
+    are split over K and reduced separately; the attention's 528 (head, query tile) items
     leave 16 for the last round, query tiles 20-21 of heads 16-23, each cut into 16 key ranges
     and merged); sampled rows, most of them in the split tiles' row range, and every
     conditioning row, against the oracle."""

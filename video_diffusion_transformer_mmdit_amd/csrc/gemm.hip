@@ -844,15 +844,14 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   a.split = 1;
   if (a.tiles == 0) return MMDIT_OK;
   // Split tail: when the tiles fill R < 256 workgroup slots of the last round, cut each of
-  // those R tiles into S = 256 / R K ranges (each of at least 2 stages) so that the last round
-  // runs on (nearly) every CU instead of R of them.  Below 4 ranges the partial-sum pass costs
-  // about what the shorter last round saves, so such tails stay whole.
+  // those R tiles into S = 256 / R K ranges (at least 2, each of at least 2 stages) so that
+  // the last round runs on (nearly) every CU instead of R of them.
   if (split_ws && x_dtype != MMDIT_FP8_E4M3 && a.tiles > G_ROUND) {
     const int64_t R = a.tiles % G_ROUND;
     const int64_t stages = K <= 4096 ? K / 64 : K / 32;
     int64_t S = R ? G_ROUND / R : 0;
     if (S > stages / 2) S = stages / 2;
-    if (R > 0 && S >= 4 && (size_t)(R * S) * G_PART_BYTES <= split_ws_bytes) {
+    if (R > 0 && S >= 2 && (size_t)(R * S) * G_PART_BYTES <= split_ws_bytes) {
       a.full = a.tiles - R;
       a.split = (int)S;
       a.part = split_ws;

@@ -593,9 +593,9 @@ __global__ __launch_bounds__(64) void joint_attn_f32_kernel(AttnArgsF32 a) {
 
 // Split-tail items: per query, the `split` key ranges' results (O_s relative to their own
 // running max m_s, sums l_s, log2 units) combine as O = sum_s 2^(m_s - M) O_s / L with
-// M = max_s m_s and L = sum_s 2^(m_s - M) l_s; then the output row and, if asked, the LSE.
+// M = max_s m_s and L = sum_s 2^(m_s - M) l_s (calls that ask for the LSE are not split).
 // One thread per query and four dims; 32 workgroups of 256 threads per item.
-template <int OUT_DT, bool LSE>
+template <int OUT_DT>
 __global__ __launch_bounds__(256) void joint_attn_merge_kernel(AttnArgs a) {
   const int r = blockIdx.x >> 5;                       // tail item
   const int t = (blockIdx.x & 31) * 256 + threadIdx.x;
@@ -632,9 +632,6 @@ __global__ __launch_bounds__(256) void joint_attn_merge_kernel(AttnArgs a) {
   } else {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + off) = make_uint2(cvt_pk_f16(v0, v1), cvt_pk_f16(v2, v3));
   }
-  if constexpr (LSE) {
-    if (d0 == 0) a.lse[(b * a.H + h) * a.N + qi] = (mmax + log2f(l)) * 0.69314718055994530942f;
-  }
 }
 
 template <int QK, int V>
@@ -644,7 +641,7 @@ static int attn_go(const AttnArgs& a, dim3 grid, int out_dtype, bool has_lse, hi
 #define ATT_GO(O, L)                                                                        \
   do {                                                                                      \
     joint_attn_mfma_kernel<QK, V, O, L><<<grid, ATT_THREADS, 0, stream>>>(a);              \
-    if (tail > 0) joint_attn_merge_kernel<O, L><<<mgrid, 256, 0, stream>>>(a);             \
+    if constexpr (!L) if (tail > 0) joint_attn_merge_kernel<O><<<mgrid, 256, 0, stream>>>(a);  \
   } while (0)
   if (out_dtype == MMDIT_F32) { if (has_lse) ATT_GO(MMDIT_F32, true); else ATT_GO(MMDIT_F32, false); }
   else if (out_dtype == MMDIT_BF16) { if (has_lse) ATT_GO(MMDIT_BF16, true); else ATT_GO(MMDIT_BF16, false); }
@@ -688,7 +685,7 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
     // those R items into S = 256 / R key ranges (at most one per key tile) so that the last
     // round runs on (nearly) every CU instead of R of them; a merge kernel combines them.
     const int64_t ntiles = (n_vis + ATT_BN - 1) / ATT_BN + (n_cond + ATT_BN - 1) / ATT_BN;
-    if (split_ws && items > ATT_ROUND) {
+    if (split_ws && !has_lse && items > ATT_ROUND) {
       const int64_t R = items % ATT_ROUND;
       int64_t S = R ? ATT_ROUND / R : 0;
       if (S > ntiles) S = ntiles;
