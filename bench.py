@@ -31,12 +31,14 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
 
-# HBM bytes per launch of the attention kernel at this workload, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
-# for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel
-# source they were taken on: a different joint_attention.hip reports traffic as null.
-ATTN_COUNTERS = {"source_sha256": "2c9deed0ab938ea4",
-                 "fetch_kib": 1113838.0, "write_kib": 199696.6, "fetch_scale": 2.0, "write_scale": 1.0}
+# HBM bytes per attention stage of the block at this workload (joint_attn_mfma_kernel plus the
+# merge kernel of its split tail, the two launches the stage's events bracket), from two
+# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+# same counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only
+# for the kernel source they were taken on: a different joint_attention.hip reports null.
+ATTN_COUNTERS = {"source_sha256": "2b26186b20c577f0",
+                 "fetch_kib": 1156482.4 + 15814.3, "write_kib": 227855.5 + 3056.0,
+                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def attention_traffic_bytes():
@@ -350,7 +352,7 @@ def main():
                    "global_batch": 1, "seq_len": cfg.n_tokens, "parallelism": "none (1 GPU)",
                    "inputs_and_weights": "bf16", "mfma_operands": args.act_dtype,
                    "accumulate": "f32", "output_dtype": "f32"},
-        "roofline": {"bound": "mfma", "kernel": "joint_attn_mfma_kernel",
+        "roofline": {"bound": "mfma", "kernel": "joint_attn_mfma_kernel (+ joint_attn_merge_kernel of its split tail)",
                      "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attention_traffic_bytes(),
                      "flops_per_launch": cfg.attn_flops, "avg_launch_ms": round(attn_ms, 4)},
