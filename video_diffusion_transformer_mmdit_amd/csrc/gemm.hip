@@ -5,14 +5,13 @@
 // neighbour gather folded into the x loads and the scatter back to the grid into the stores.
 //
 // gfx950 design (two kernels share the tile, fragment layout, tile order and epilogue:
-// gemm_k64_kernel, two LDS stages of K = 64, for 16-bit operands in the plain layout with
-// K <= 4096; gemm_kernel, four LDS stages of 64 bytes per row, for long K, FP8 operands and
-// the Lite layouts):
+// gemm_k64_kernel, two LDS stages of K = 64, for 16-bit operands in the plain layout;
+// gemm_kernel, four LDS stages of 64 bytes per row, for FP8 operands and the Lite layouts):
 //   - 256 x 256 output tile per workgroup of 4 wave64s arranged 2 (M) x 2 (N), one per SIMD;
 //     each wave owns 128 x 128 outputs = 4 x 4 tiles of v_mfma_f32_32x32x16_{bf16,f16} whose
 //     256 accumulator registers live in AGPRs.  The MFMA computes C^T (A operand = W rows,
 //     B operand = x rows), so every lane ends up holding four consecutive output columns of
-//     one row and the epilogue stores 8 or 16 bytes at a time.
+//     one row, 32 rows apart from its neighbours'.
 //   - K advances 32 at a time through four LDS stages (x tile and W tile, 16 KiB each, rows
 //     of 64 bytes, both K-contiguous so both MFMA operands are plain 16-byte LDS reads).
 //     Tiles move by LDS-DMA (buffer loads straight into LDS) three stages ahead, issued
@@ -30,8 +29,10 @@
 //   - Tiles are renumbered so that each XCD (workgroups go round-robin over the 8 XCDs) owns
 //     a contiguous run of tiles, and runs are rastered in groups of 8 M-tiles, keeping the
 //     x and W panels that concurrent workgroups of one XCD share inside its L2.
-//   - Epilogues (bias, GELU, gated residual) are applied on the accumulators before the only
-//     store of y.
+//   - The epilogue restages each wave's block through LDS (free after the last stage) and
+//     applies bias, GELU or the gated residual along rows, before the only store of y.
+//   - A launch whose last round would leave CUs idle cuts that round's tiles into K ranges
+//     (split tail) and sums them in a small elementwise kernel that applies the epilogue.
 #include <type_traits>
 
 #include "common.h"
@@ -769,20 +770,17 @@ static void gemm_go(const GemmArgs& a, hipStream_t st) {
   if constexpr (IN_DT != MMDIT_FP8_E4M3 && LAYOUT == GEMM_PLAIN) {
     if (a.full < a.tiles) {   // split tail: whole tiles and K ranges of the tail tiles, then their sums
       const int64_t grid = a.full + (a.tiles - a.full) * a.split;
-      if (a.K <= 4096) gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
-      else gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
+      gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
       gemm_split_finish_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)((a.tiles - a.full) * G_SUM_WG)), GTHREADS, 0, st>>>(a);
       return;
     }
   }
-  // The two-stage kernel prefetches one stage (three quarters of a stage's MFMAs) ahead: enough
-  // while the K panels of a tile group stay in L2; for long K (FFN down, K = 12288) the
-  // four-stage kernel's deeper prefetch measures faster.
+  // 16-bit operands in the plain layout (K a multiple of 64): the two-stage K = 64 kernel, at
+  // every K (with its DMA fenced in groups it also beats the four-stage kernel at K = 6144 and
+  // 12288); the four-stage kernel serves FP8 operands and the Lite layouts.
   if constexpr (IN_DT != MMDIT_FP8_E4M3 && LAYOUT == GEMM_PLAIN) {
-    if (a.K <= 4096) {
-      gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
-      return;
-    }
+    gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+    return;
   }
   gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
 }
@@ -848,7 +846,7 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   // the last round runs on (nearly) every CU instead of R of them.
   if (split_ws && x_dtype != MMDIT_FP8_E4M3 && a.tiles > G_ROUND) {
     const int64_t R = a.tiles % G_ROUND;
-    const int64_t stages = K <= 4096 ? K / 64 : K / 32;
+    const int64_t stages = K / 64;   // K = 64 stages of the two-stage kernel
     int64_t S = R ? G_ROUND / R : 0;
     if (S > stages / 2) S = stages / 2;
     if (R > 0 && S >= 2 && (size_t)(R * S) * G_PART_BYTES <= split_ws_bytes) {
