@@ -62,6 +62,9 @@ def test_modulate_ln(xdt, ydt, branch, C, N):
     (260, 256, 1024, torch.bfloat16, mm.EPI_GELU, torch.float32),
     (1, 256, 64, torch.bfloat16, mm.EPI_NONE, torch.float32),
     (40, 300, 128, torch.bfloat16, mm.EPI_NONE, torch.float32),
+    # odd counts of K = 64 stages past the first (the two-stage loop's trailing stage)
+    (200, 512, 192, torch.float16, mm.EPI_GELU, torch.float16),
+    (129, 260, 320, torch.bfloat16, mm.EPI_NONE, torch.float32),
 ])
 def test_linear(M, N, K, dt, epi, ydt):
     x = _rand((M, K), 7, 1.0, dt)
