@@ -5,8 +5,8 @@
 // neighbour gather folded into the x loads and the scatter back to the grid into the stores.
 //
 // gfx950 design (two kernels share the tile, fragment layout, tile order and epilogue:
-// gemm_k64_kernel, two LDS stages of K = 64, for 16-bit operands in the plain layout;
-// gemm_kernel, four LDS stages of 64 bytes per row, for FP8 operands and the Lite layouts):
+// gemm_k64_kernel, two LDS stages of K = 64, for 16-bit operands in every layout;
+// gemm_kernel, four LDS stages of 64 bytes per row, for FP8 operands):
 //   - 256 x 256 output tile per workgroup of 4 wave64s arranged 2 (M) x 2 (N), one per SIMD;
 //     each wave owns 128 x 128 outputs = 4 x 4 tiles of v_mfma_f32_32x32x16_{bf16,f16} whose
 //     256 accumulator registers live in AGPRs.  The MFMA computes C^T (A operand = W rows,
@@ -550,12 +550,16 @@ void gemm_kernel(GemmArgs args) {
   }
 }
 
-// 16-bit operands, plain layout: two LDS stages of K = 64 (64 KiB each, rows of 128 bytes,
-// chunks XOR-swizzled by row % 8).  The next stage's sixteen DMA loads per wave go out during
-// the first quarter of the current stage; before the last quarter every wave waits for them
-// and for its own reads of the current stage, and one barrier per 64 K follows, after which
-// the next stage's first fragments are read under the last quarter's MFMAs.
-template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT>
+// 16-bit operands, any layout: two LDS stages of K = 64 (64 KiB each, rows of 128 bytes,
+// chunks XOR-swizzled by (row / 2) % 8).  The next stage's sixteen DMA loads per wave go out
+// during the first quarter of the current stage; before the last quarter every wave waits for
+// them and for its own reads of the current stage, and one barrier per 64 K follows, after
+// which the next stage's first fragments are read under the last quarter's MFMAs.
+// GEMM_GATHER_X: x row m, K position k reads channel k % C of the full-grid token
+// merged_row0(m) + (s / 2) W + s % 2, s = k / C (a 64-wide K stage never straddles two
+// neighbours, as C is a multiple of 256): the per-row part is per lane, the neighbour part
+// scalar.  GEMM_SCATTER_Y is the epilogue's.
+template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_k64_kernel(GemmArgs args) {
   constexpr int T64 = GBM * 128;   // one operand tile of one stage: 32 KiB
@@ -583,13 +587,26 @@ void gemm_k64_kernel(GemmArgs args) {
   for (int i = 0; i < 8; ++i) {
     const int row = 64 * wave + 8 * i + (lane >> 3);
     const int lc = (lane & 7) ^ ((row >> 1) & 7);
-    xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
+    // rows past M: an offset past the end of x, so they load zeros
+    if constexpr (LAYOUT == GEMM_GATHER_X)
+      xo[i] = (m0 + row < M ? merged_row0(m0 + row, args) * args.c * 2 + lc * 16 : 0x7FFF0000) - (i & 3) * 1024;
+    else
+      xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
     wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
   }
+  // scalar byte offset of K position k0 in x (the neighbour's token, then the channel)
+  auto x_soff = [&](int k0) {
+    if constexpr (LAYOUT == GEMM_GATHER_X) {
+      const int sg = __builtin_amdgcn_readfirstlane(k0 / args.c);
+      return (((sg >> 1) * args.w + (sg & 1)) * args.c + (k0 - sg * args.c)) * 2;
+    } else {
+      return k0 * 2;
+    }
+  };
   // the four loads of one LDS base (x rows 0-31 / 32-63 of the wave's 64, then W's)
   auto dma_part = [&](uint8_t* xs, uint8_t* ws, int k0, auto part_c) {
     constexpr int PART = decltype(part_c)::value;
-    const int so = (k0 + kb * 64) * 2;
+    const int so = PART < 2 ? x_soff(k0 + kb * 64) : (k0 + kb * 64) * 2;
     const auto rs = PART < 2 ? rx : rw;
     const int* o = (PART < 2 ? xo : wo) + (PART & 1) * 4;
     auto* l = opaque_lds((__attribute__((address_space(3))) void*)((PART < 2 ? xs : ws) + wave * 8192 + (PART & 1) * 4096));
@@ -600,18 +617,19 @@ void gemm_k64_kernel(GemmArgs args) {
   };
   auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
     const int so = (k0 + kb * 64) * 2;
+    const int xso = x_soff(k0 + kb * 64);
     auto* lx0 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192));
     auto* lx1 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192 + 4096));
     auto* lw0 = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 8192));
     auto* lw1 = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 8192 + 4096));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[0], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[3], so, 3072, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[4], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[5], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[6], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[7], so, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[0], xso, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[1], xso, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[2], xso, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[3], xso, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[4], xso, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[5], xso, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[6], xso, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[7], xso, 3072, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[0], so, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[1], so, 1024, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[2], so, 2048, 0);
@@ -728,7 +746,7 @@ void gemm_k64_kernel(GemmArgs args) {
     // restage in the first stage buffer, waves 2, 3 in the second
     __syncthreads();
     float* region = reinterpret_cast<float*>((wave < 2 ? lds_a : lds_b) + (wave & 1) * G_EPI_BYTES);
-    gemm_epilogue_rows<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, lane, region);
+    gemm_epilogue_rows<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, lane, region);
   }
 }
 
@@ -767,22 +785,22 @@ __global__ __launch_bounds__(GTHREADS) void gemm_split_finish_kernel(GemmArgs ar
 
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
 static void gemm_go(const GemmArgs& a, hipStream_t st) {
-  if constexpr (IN_DT != MMDIT_FP8_E4M3 && LAYOUT == GEMM_PLAIN) {
-    if (a.full < a.tiles) {   // split tail: whole tiles and K ranges of the tail tiles, then their sums
-      const int64_t grid = a.full + (a.tiles - a.full) * a.split;
-      gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
-      gemm_split_finish_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)((a.tiles - a.full) * G_SUM_WG)), GTHREADS, 0, st>>>(a);
-      return;
+  // 16-bit operands (K a multiple of 64), plain or Lite layout: the two-stage K = 64 kernel,
+  // at every K (with its DMA fenced in groups it also beats the four-stage kernel at K = 6144
+  // and 12288); the four-stage kernel serves FP8 operands.
+  if constexpr (IN_DT != MMDIT_FP8_E4M3) {
+    if constexpr (LAYOUT == GEMM_PLAIN) {
+      if (a.full < a.tiles) {   // split tail: whole tiles and K ranges of the tail tiles, then their sums
+        const int64_t grid = a.full + (a.tiles - a.full) * a.split;
+        gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
+        gemm_split_finish_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)((a.tiles - a.full) * G_SUM_WG)), GTHREADS, 0, st>>>(a);
+        return;
+      }
     }
+    gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+  } else {
+    gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
   }
-  // 16-bit operands in the plain layout (K a multiple of 64): the two-stage K = 64 kernel, at
-  // every K (with its DMA fenced in groups it also beats the four-stage kernel at K = 6144 and
-  // 12288); the four-stage kernel serves FP8 operands and the Lite layouts.
-  if constexpr (IN_DT != MMDIT_FP8_E4M3 && LAYOUT == GEMM_PLAIN) {
-    gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
-    return;
-  }
-  gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
 }
 
 // Lite merge (GEMM_GATHER_X: y [B*T*(H/2)*(W/2), C] = gather4(x) W^T + b, W [C, 4C]) and
