@@ -5,24 +5,21 @@
 // neighbour gather folded into the x loads and the scatter back to the grid into the stores.
 //
 // gfx950 design (two kernels share the tile, fragment layout, tile order and epilogue:
-// gemm_k64_kernel, two LDS stages of K = 64, for 16-bit operands in every layout;
-// gemm_kernel, four LDS stages of 64 bytes per row, for FP8 operands):
+// gemm_k64_kernel for 16-bit operands in every layout, gemm_fp8_kernel for FP8 operands):
 //   - 256 x 256 output tile per workgroup of 4 wave64s arranged 2 (M) x 2 (N), one per SIMD;
-//     each wave owns 128 x 128 outputs = 4 x 4 tiles of v_mfma_f32_32x32x16_{bf16,f16} whose
-//     256 accumulator registers live in AGPRs.  The MFMA computes C^T (A operand = W rows,
-//     B operand = x rows), so every lane ends up holding four consecutive output columns of
-//     one row, 32 rows apart from its neighbours'.
-//   - K advances 32 at a time through four LDS stages (x tile and W tile, 16 KiB each, rows
-//     of 64 bytes, both K-contiguous so both MFMA operands are plain 16-byte LDS reads).
-//     Tiles move by LDS-DMA (buffer loads straight into LDS) three stages ahead, issued
-//     between the MFMAs; before the barrier that ends stage k each wave waits only for its
-//     loads of stage k+2, so stage k+1 is visible one stage early and the first fragments
-//     of the next stage are read while the current stage's last MFMAs run.  The four stage
-//     buffers are distinct LDS objects addressed with compile-time stage indices, and the
-//     DMA destinations pass through an opaque register copy, so the compiler's wait-count
-//     pass leaves every wait to the explicit per-stage ones.
-//   - LDS chunks are XOR-swizzled with (row / 4) % 4, which puts the 16 rows a 16-lane group
-//     of a fragment read touches on distinct bank groups; a DMA writes 16 bytes per lane in
+//     each wave owns 128 x 128 outputs = 4 x 4 tiles of 32 x 32 MFMAs whose 256 accumulator
+//     registers live in AGPRs.  The MFMA computes C^T (A operand = W rows, B operand = x
+//     rows), so every lane ends up holding four consecutive output columns of one row, 32
+//     rows apart from its neighbours'.
+//   - x and W tiles are K-contiguous in LDS, so both MFMA operands are plain 16-byte LDS
+//     reads, and move by LDS-DMA (buffer loads straight into LDS) issued between the MFMAs.
+//     16-bit: two stages of K = 64 (rows of 128 bytes), one barrier per stage, the next
+//     stage's loads in four fenced groups.  FP8: four stages of 64 bytes per row, the DMA
+//     three stages ahead.  Stage buffers are distinct LDS objects addressed with compile-time
+//     indices, and the DMA destinations pass through an opaque register copy, so the
+//     compiler's wait-count pass leaves every wait to the explicit per-stage ones.
+//   - 16-byte LDS chunks are XOR-swizzled by row so that the 16 rows a 16-lane group of a
+//     fragment read touches fall on distinct bank groups; a DMA writes 16 bytes per lane in
 //     lane order, so each lane loads the logical chunk that belongs at its physical slot.
 //     Rows past the end of x or W fail the buffer descriptor's range check and arrive as
 //     zeros.
@@ -30,7 +27,8 @@
 //     a contiguous run of tiles, and runs are rastered in groups of 8 M-tiles, keeping the
 //     x and W panels that concurrent workgroups of one XCD share inside its L2.
 //   - The epilogue restages each wave's block through LDS (free after the last stage) and
-//     applies bias, GELU or the gated residual along rows, before the only store of y.
+//     applies the FP8 scales, bias, GELU or the gated residual along rows, before the only
+//     store of y.
 //   - A launch whose last round would leave CUs idle cuts that round's tiles into K ranges
 //     (split tail) and sums them in a small elementwise kernel that applies the epilogue.
 #include <type_traits>
@@ -303,15 +301,12 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
   }
 }
 
-template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
+// FP8 operands (E4M3 codes, one byte per element): four LDS stages of K = 64, rows of 64
+// bytes; each 32 x 32 output tile takes one 32 x 32 x 64 MFMA per stage.
+template <int BIAS_DT, int Y_DT, int EPI, int RES_DT>
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_kernel(GemmArgs args) {
-  // FP8 operands: one byte per element, so a 64-byte stage row holds 64 K values and each
-  // 32 x 32 output tile takes one 32 x 32 x 64 MFMA per stage instead of two 32 x 32 x 16.
-  constexpr bool FP8 = IN_DT == MMDIT_FP8_E4M3;
-  constexpr int ES = FP8 ? 1 : 2;
-  constexpr int KSTEP = 64 / ES;
-  static_assert(!FP8 || LAYOUT == GEMM_PLAIN, "FP8 operands use the plain layout");
+void gemm_fp8_kernel(GemmArgs args) {
+  constexpr int KSTEP = 64;   // K values per stage (64 bytes per row)
   // one LDS object per stage: x tile, then W tile
   __shared__ __attribute__((aligned(16))) uint8_t lds_s0[2 * G_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_s1[2 * G_TILE_BYTES];
@@ -333,47 +328,29 @@ void gemm_kernel(GemmArgs args) {
   // 1 KiB loads each (lane l -> row 64w + 16i + l/4, physical chunk l % 4).  The immediate
   // offset i * 1024 moves the LDS destination and the source alike and is taken back out of
   // the per-lane offset, so all loads of a tile share one LDS base; the K position goes in
-  // the scalar offset, which the range check ignores.
-  // GEMM_GATHER_X: logical x row m, K position k reads channel k % C of the full-grid token
-  // merged_row0(m) + (s / 2) W + s % 2, s = k / C (a K stage never straddles two neighbours
-  // as C is a multiple of 32).  The per-row part is per lane, the neighbour part scalar.
-  // Rows m >= M get an offset past the end of x, so they load zeros.
-  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * ES);
-  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * ES);
+  // the scalar offset, which the range check ignores.  Rows past M or N load zeros.
+  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K);
+  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K);
   int xo[4], wo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 64 * wave + 16 * i + (lane >> 2);
     const int lc = (lane & 3) ^ swz(row);
-    if constexpr (LAYOUT == GEMM_GATHER_X)
-      xo[i] = (m0 + row < M ? merged_row0(m0 + row, args) * args.c * 2 + lc * 16 : 0x7FFF0000) - i * 1024;
-    else
-      xo[i] = (m0 + row) * (int)K * ES + lc * 16 - i * 1024;
-    wo[i] = (n0 + row) * (int)K * ES + lc * 16 - i * 1024;
+    xo[i] = (m0 + row) * (int)K + lc * 16 - i * 1024;
+    wo[i] = (n0 + row) * (int)K + lc * 16 - i * 1024;
   }
-  // part 0: the x tile's four loads, 1: W's, 2: both
-  auto dma = [&](uint8_t* xs, uint8_t* ws, int k0, int part = 2) {
-    k0 += kb * KSTEP;
-    int xso = k0 * ES;
-    if constexpr (LAYOUT == GEMM_GATHER_X) {
-      const int sg = __builtin_amdgcn_readfirstlane(k0 / args.c);
-      xso = (((sg >> 1) * args.w + (sg & 1)) * args.c + (k0 - sg * args.c)) * 2;
-    }
-    const int so = k0 * ES;
+  auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
+    const int so = k0 + kb * KSTEP;
     auto* lx = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 4096));
     auto* lw = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 4096));
-    if (part != 1) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], xso, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], xso, 1024, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], xso, 2048, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], xso, 3072, 0);
-    }
-    if (part != 0) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[0], so, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[1], so, 1024, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[2], so, 2048, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[3], so, 3072, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], so, 3072, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[3], so, 3072, 0);
   };
   auto xbuf = [&](auto s) -> uint8_t* {
     constexpr int v = decltype(s)::value;
@@ -386,11 +363,11 @@ void gemm_kernel(GemmArgs args) {
   constexpr std::integral_constant<int, 2> S2{};
   constexpr std::integral_constant<int, 3> S3{};
 
-  // ---- fragment reads: row base + l32 of a tile, logical chunk 2 ks + g; the swizzle of
-  // row base + l32 (base a multiple of 32) depends on l32 only
+  // ---- fragment reads: row base + l32 of a tile, 16-byte half h = chunk 2 h + g; the swizzle
+  // of row base + l32 (base a multiple of 32) depends on l32 only
   int cofs[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) cofs[ks] = l32 * 64 + (((2 * ks + g) ^ swz(l32)) << 4);
+  for (int h = 0; h < 2; ++h) cofs[h] = l32 * 64 + (((2 * h + g) ^ swz(l32)) << 4);
 
   f32x16 acc[4][4];   // [n tile][m tile] of C^T
 #pragma unroll
@@ -400,76 +377,15 @@ void gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
 
-  const int nk = ke - kb;   // stages of this workgroup (all of K unless it is a split-tail one)
+  const int nk = ke - kb;   // stages of this workgroup
   auto gbarrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // Fragments of k16 slice 0 of the current stage, read during the previous stage.
-  uint4 wf0[4], xf0[4];
-  auto read_slice = [&](const uint8_t* xs, const uint8_t* ws, int ks, uint4 (&wf)[4], uint4 (&xf)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const uint4*>(ws + (wn * 128 + j * 32) * 64 + cofs[ks]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const uint4*>(xs + (wm * 128 + i * 32) * 64 + cofs[ks]);
-  };
-  auto mma = [&](const uint4 (&wf)[4], const uint4 (&xf)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wf[j], xf[i], acc[j][i]);
-  };
-  // One K stage.  At its start stages kt and kt+1 are in LDS for every wave.  MAIN: stage
-  // kt+3 exists (load it; at the end wait with its loads in flight); otherwise the tail
-  // decides at run time.
-  auto step = [&](auto cur_c, auto main_c, int kt) {
-    constexpr int CUR = decltype(cur_c)::value;
-    constexpr bool MAIN = decltype(main_c)::value;
-    constexpr std::integral_constant<int, CUR> cur{};
-    constexpr std::integral_constant<int, (CUR + 1) & 3> next{};
-    constexpr std::integral_constant<int, (CUR + 3) & 3> ahead{};
-    // stage kt+3 goes into the buffers stage kt-1 used (every wave has passed the barrier
-    // that ended stage kt-1)
-    const bool dma_here = MAIN || kt + 3 < nk;
-    uint4 wf1[4], xf1[4];
-    read_slice(xbuf(cur), wbuf(cur), 1, wf1, xf1);
-    __builtin_amdgcn_sched_barrier(0);
-    // slice 0: stage kt+3's DMA in two groups of four loads (x, then W), each before a row of
-    // four MFMAs; fenced, as left to the scheduler the second group issues in one burst that
-    // holds back the MFMAs behind it (in-order issue)
-    auto mrow = [&](int j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wf0[j], xf0[i], acc[j][i]);
-    };
-    if (dma_here) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mrow(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (dma_here) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mrow(1);
-    mrow(2);
-    mrow(3);
-    __builtin_amdgcn_sched_barrier(0);
-    // slice 0 of the next stage is read while this stage's second slice runs
-    if (MAIN || kt + 1 < nk) read_slice(xbuf(next), wbuf(next), 0, wf0, xf0);
-    mma(wf1, xf1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // this wave's loads of stage kt+2 have landed once at most the eight loads of stage kt+3
-    // are outstanding; after the barrier stage kt+2 is in LDS for everyone
-    if (MAIN || kt + 3 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
-    gbarrier();
-  };
-  // FP8: the whole 32-byte fragments of a stage (both 16-byte halves) are read one stage
-  // ahead into one of two register sets (stage parity), while the 16 MFMAs of the current
-  // stage run on the other.
+  // The whole 32-byte fragments of a stage (both 16-byte halves) are read one stage ahead into
+  // one of two register sets (stage parity), while the 16 MFMAs of the current stage run on
+  // the other.
   uint4 fw8[2][4][2], fx8[2][4][2];
   auto read8 = [&](const uint8_t* xs, const uint8_t* ws, auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
@@ -481,7 +397,11 @@ void gemm_kernel(GemmArgs args) {
       for (int i = 0; i < 4; ++i) fx8[BUF][i][h] = *reinterpret_cast<const uint4*>(xs + (wm * 128 + i * 32) * 64 + cofs[h]);
     }
   };
-  auto step8 = [&](auto cur_c, auto main_c, int kt) {
+  // One K stage.  At its start stages kt and kt+1 are in LDS for every wave.  MAIN: stage
+  // kt+3 exists (load it; at the end wait with its loads in flight); otherwise the tail
+  // decides at run time.  Stage kt+3 goes into the buffers stage kt-1 used (every wave has
+  // passed the barrier that ended stage kt-1).
+  auto step = [&](auto cur_c, auto main_c, int kt) {
     constexpr int CUR = decltype(cur_c)::value;
     constexpr bool MAIN = decltype(main_c)::value;
     constexpr std::integral_constant<int, (CUR + 1) & 3> next{};
@@ -495,6 +415,8 @@ void gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[j][i] = mfma_fp8(fw8[buf][j][0], fw8[buf][j][1], fx8[buf][i][0], fx8[buf][i][1], acc[j][i]);
+    // one fragment read after each MFMA, the eight DMA loads among MFMAs 2-9 (fencing the DMA
+    // in two groups as in the 16-bit kernel measured ~1 % slower here)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
@@ -503,13 +425,11 @@ void gemm_kernel(GemmArgs args) {
     }
     // the MFMAs only touch registers: keep the scheduler from moving them past the barrier
     __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads of stage kt+2 have landed once at most the eight loads of stage kt+3
+    // are outstanding; after the barrier stage kt+2 is in LDS for everyone
     if (MAIN || kt + 3 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
     gbarrier();
-  };
-  auto run = [&](auto cur_c, auto main_c, int kt) {
-    if constexpr (FP8) step8(cur_c, main_c, kt);
-    else step(cur_c, main_c, kt);
   };
   constexpr std::true_type MAIN{};
   constexpr std::false_type TAIL{};
@@ -521,22 +441,21 @@ void gemm_kernel(GemmArgs args) {
   if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
   else __builtin_amdgcn_s_waitcnt(0x0F70);
   gbarrier();
-  if constexpr (FP8) read8(xbuf(S0), wbuf(S0), std::integral_constant<int, 0>{});
-  else read_slice(xbuf(S0), wbuf(S0), 0, wf0, xf0);
+  read8(xbuf(S0), wbuf(S0), std::integral_constant<int, 0>{});
   int kt = 0;
   for (; kt + 6 < nk; kt += 4) {   // every step of the group has its stage kt+3
-    run(S0, MAIN, kt);
-    run(S1, MAIN, kt + 1);
-    run(S2, MAIN, kt + 2);
-    run(S3, MAIN, kt + 3);
+    step(S0, MAIN, kt);
+    step(S1, MAIN, kt + 1);
+    step(S2, MAIN, kt + 2);
+    step(S3, MAIN, kt + 3);
   }
   // at most six stages remain (kt % 4 == 0)
-  if (kt < nk) run(S0, TAIL, kt);
-  if (kt + 1 < nk) run(S1, TAIL, kt + 1);
-  if (kt + 2 < nk) run(S2, TAIL, kt + 2);
-  if (kt + 3 < nk) run(S3, TAIL, kt + 3);
-  if (kt + 4 < nk) run(S0, TAIL, kt + 4);
-  if (kt + 5 < nk) run(S1, TAIL, kt + 5);
+  if (kt < nk) step(S0, TAIL, kt);
+  if (kt + 1 < nk) step(S1, TAIL, kt + 1);
+  if (kt + 2 < nk) step(S2, TAIL, kt + 2);
+  if (kt + 3 < nk) step(S3, TAIL, kt + 3);
+  if (kt + 4 < nk) step(S0, TAIL, kt + 4);
+  if (kt + 5 < nk) step(S1, TAIL, kt + 5);
 
   if (part_idx >= 0) {
     gemm_store_part(args, part_idx, wave, lane, acc);
@@ -545,8 +464,8 @@ void gemm_kernel(GemmArgs args) {
     // restages in stage buffer w
     __syncthreads();
     uint8_t* rb = wave == 0 ? lds_s0 : wave == 1 ? lds_s1 : wave == 2 ? lds_s2 : lds_s3;
-    gemm_epilogue_rows<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, lane,
-                                                                  reinterpret_cast<float*>(rb));
+    gemm_epilogue_rows<MMDIT_FP8_E4M3, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, lane,
+                                                                             reinterpret_cast<float*>(rb));
   }
 }
 
@@ -786,8 +705,8 @@ __global__ __launch_bounds__(GTHREADS) void gemm_split_finish_kernel(GemmArgs ar
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
 static void gemm_go(const GemmArgs& a, hipStream_t st) {
   // 16-bit operands (K a multiple of 64), plain or Lite layout: the two-stage K = 64 kernel,
-  // at every K (with its DMA fenced in groups it also beats the four-stage kernel at K = 6144
-  // and 12288); the four-stage kernel serves FP8 operands.
+  // at every K (with its DMA fenced in groups it also beat a four-stage 16-bit kernel at
+  // K = 6144 and 12288); FP8 operands take the four-stage FP8 kernel.
   if constexpr (IN_DT != MMDIT_FP8_E4M3) {
     if constexpr (LAYOUT == GEMM_PLAIN) {
       if (a.full < a.tiles) {   // split tail: whole tiles and K ranges of the tail tiles, then their sums
@@ -799,7 +718,8 @@ static void gemm_go(const GemmArgs& a, hipStream_t st) {
     }
     gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
   } else {
-    gemm_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+    static_assert(LAYOUT == GEMM_PLAIN, "FP8 operands use the plain layout");
+    gemm_fp8_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
   }
 }
 
