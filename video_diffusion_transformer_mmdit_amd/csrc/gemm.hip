@@ -24,7 +24,7 @@
 //     Rows past the end of x or W fail the buffer descriptor's range check and arrive as
 //     zeros.
 //   - Tiles are renumbered so that each XCD (workgroups go round-robin over the 8 XCDs) owns
-//     a contiguous run of tiles, and runs are rastered in groups of 8 M-tiles, keeping the
+//     a contiguous run of tiles, and runs are rastered in bands of 4 M-tiles, keeping the
 //     x and W panels that concurrent workgroups of one XCD share inside its L2.
 //   - The epilogue restages each wave's block through LDS (free after the last stage) and
 //     applies the FP8 scales, bias, GELU or the gated residual along rows, before the only
@@ -39,7 +39,7 @@ namespace mmdit {
 
 constexpr int GBM = 256, GBN = 256, GBK = 32;
 constexpr int GTHREADS = 256;
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;   // M-tiles per raster band (4 measured ~1 % faster than 2, 8 or 16)
 constexpr int G_TILE_BYTES = 256 * GBK * 2;   // one operand tile of one stage: 16 KiB
 constexpr int64_t G_ROUND = 256;              // workgroups the chip runs at once (one per CU)
 constexpr size_t G_PART_BYTES = 256 * 256 * 4;   // f32 partial sums of one tile
