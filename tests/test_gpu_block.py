@@ -184,3 +184,32 @@ def test_block_split_tail_tiles_parity():
         _check_intermediates(s, i, ref, act)
     assert_close("out_vis", got_v, ref["out_vis"], TOL[wl.BF16])
     assert_close("out_cond", got_c, ref["out_cond"], TOL[wl.BF16])
+
+@pytest.mark.timeout(600)
+def test_block_batch2_attention_split_tail_parity():
+    """Batch 2, so the attention's (batch item x head) count is 48: 1400 + 77 tokens make 6
+    query tiles, 288 (batch x head, query tile) items, and the last round's 32 items (query
+    tiles 2-5 of batch item 1, heads 16-23) are each cut into 8 key ranges and merged.
+    Sampled visual rows, most of them in that range, and every conditioning row, of both
+    batch items against the oracle."""
+    cfg = wl.BlockConfig("block_b2_c3072_h24_f12288_grid2x20x35_cond77", 3072, 24, 128, 12288, 1536,
+                         (2, 20, 35), 77, batch=2, seed=17)
+    raw = wl.block_inputs(cfg)
+    dev, wv, wc = _dev_block(cfg, raw)
+    act = torch.float16
+    dims, out_v, out_c, ws = _run_block(cfg, dev, wv, wc, act)
+    rv = np.unique(np.concatenate([wl.sample_rows(cfg.n_vis, 16, seed=505), np.arange(400, cfg.n_vis, 23)]))
+    rc = np.arange(cfg.n_cond)
+    got_v = to_host64(out_v[:, torch.from_numpy(rv).cuda()])
+    got_c = to_host64(out_c)
+    iv = _ws_views(dims, cfg, ws, 0, cfg.n_vis, rv)
+    ic = _ws_views(dims, cfg, ws, 1, cfg.n_cond, rc)
+    log("  oracle (float64) on sampled rows")
+    ref = oracle.block_forward(wl.to_f64(raw["x_vis"], wl.BF16), wl.to_f64(raw["x_cond"], wl.BF16),
+                               wl.to_f64(raw["tvec"], wl.BF16), _host_weights(raw, "vis"),
+                               _host_weights(raw, "cond"), cfg.grid, cfg.heads, cfg.ln_eps, cfg.qk_eps,
+                               vis_rows=rv, cond_rows=rc)
+    for s, i in (("vis", iv), ("cond", ic)):
+        _check_intermediates(s, i, ref, act)
+    assert_close("out_vis", got_v, ref["out_vis"], TOL[wl.BF16])
+    assert_close("out_cond", got_c, ref["out_cond"], TOL[wl.BF16])
