@@ -217,13 +217,20 @@ int mmdit_attn8_quantize(const void* q_vis, const void* k_vis, const void* v_vis
  *   P'_ij = E4M3(2^(acc_ij c_ij + 8 - m_i)) (so P' <= 256), summed by the FP8 MFMA;
  *   O_i  = s_v * (sum_j P'_ij V8_j) / (sum_j P'_ij).
  * o_vis, o_cond, out_dtype, out_row_stride, lse as for mmdit_joint_attention (lse is
- * ln(sum_j P'_ij) + (m_i - 8) ln 2).  D = 128. */
+ * ln(sum_j P'_ij) + (m_i - 8) ln 2).  D = 128.
+ * workspace (optional, device memory, 256-byte aligned, caller-owned, contents scratch):
+ * when the (batch x head, 256-query tile) items leave the GPU's last round of 256
+ * workgroups partly empty and no lse is asked for, those items are split over key ranges
+ * whose results go there (up to 256 x 33280 floats = 34 MB) and are merged: the ranges' sums
+ * combine with exact power-of-two weights 2^(m_s - max m), so O changes only by the f32
+ * summation order.  NULL or too small: no split.  Calls that share a workspace must not
+ * overlap. */
 int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis,
                                const mmdit_attn8_stream* cond, int64_t n_cond,
                                const float* v_scale, int64_t B, int64_t H, int64_t D,
                                float softmax_scale,
                                void* o_vis, void* o_cond, int out_dtype, int64_t out_row_stride,
-                               float* lse, void* stream);
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * mmdit_quantize_fp8 -- symmetric FP8 E4M3 quantization, with one scale per row (per_row

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert mm.abi_version() == 3
+    assert mm.abi_version() == 4
     assert L.mmdit_status_str(0) == b"MMDIT_OK"
     assert L.mmdit_status_str(ERR_ALIAS) == b"MMDIT_ERR_ALIAS"
     assert L.mmdit_status_str(99) == b"MMDIT_ERR_UNKNOWN"
@@ -215,8 +215,10 @@ def test_attention_8bit_validation(L):
     assert q(p, p, p, 100, p, p, p, 5, mm.BF16, 3072, 1, 24, 128, C.byref(st), None, sv, None) == ERR_NULL
     assert q(None, None, None, 0, None, None, None, 0, mm.BF16, 3072, 1, 24, 128, None, None, None, None) == 0
     a = L.mmdit_joint_attention_8bit
-    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.0, p, None, mm.F32, 3072, None, None) == ERR_SHAPE
-    assert a(C.byref(st), 100, None, 0, None, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None) == ERR_NULL
-    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, p, None, mm.FP8_E4M3, 3072, None, None) == ERR_DTYPE
-    assert a(C.byref(st), 100, C.byref(st), 5, sv, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None) == ERR_NULL
-    assert a(C.byref(st), 100, None, 0, _fake(0x60000004), 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None) == ERR_ALIGN
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.0, p, None, mm.F32, 3072, None, None, 0, None) == ERR_SHAPE
+    assert a(C.byref(st), 100, None, 0, None, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None, 0, None) == ERR_NULL
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, p, None, mm.FP8_E4M3, 3072, None, None, 0, None) == ERR_DTYPE
+    assert a(C.byref(st), 100, C.byref(st), 5, sv, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None, 0, None) == ERR_NULL
+    assert a(C.byref(st), 100, None, 0, _fake(0x60000004), 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None, 0, None) == ERR_ALIGN
+
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, _fake(0x60000010), 1 << 20, None) == ERR_ALIGN

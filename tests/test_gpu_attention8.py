@@ -133,3 +133,27 @@ def test_attention_8bit_zero_keys_give_mean_of_values():
     mean = np.concatenate([v8v, v8c], axis=1).mean(axis=1) * sv
     assert_close("o_vis", to_host64(ov), np.broadcast_to(mean[:, None], ov.shape), 1e-4)
     assert_close("o_cond", to_host64(oc), np.broadcast_to(mean[:, None], oc.shape), 1e-4)
+
+
+def test_attention_8bit_split_tail_with_workspace():
+    """Batch 2, 24 heads, 1400 + 77 tokens: 288 (batch x head, query tile) items leave 32 for
+    the last round, which a workspace lets the kernel cut into 8 key ranges each and merge.
+    Each range takes its own integer reference, so a weight's E4M3 code is the same as in one
+    pass up to the format's range at the bottom; the output is held to the same bars against
+    the oracle, and against the same call without a workspace (one pass per item)."""
+    cfg = wl.AttnConfig("a8_split_b2_h24_grid2x20x35_cond77", wl.BF16, 24, 128, (2, 20, 35), 77, seed=45, batch=2)
+    dev, f64 = _inputs(cfg)
+    ops = mm.attn8_quantize(dev["q_vis"], dev["k_vis"], dev["v_vis"], dev["q_cond"], dev["k_cond"], dev["v_cond"])
+    ws = torch.empty(mm.ATTN8_SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+    ov, oc = mm.joint_attention_8bit(ops, workspace=ws)
+    uv, uc = mm.joint_attention_8bit(ops)
+    torch.cuda.synchronize()
+    _close8("o_vis split vs one pass", to_host64(ov), to_host64(uv))
+    _close8("o_cond split vs one pass", to_host64(oc), to_host64(uc))
+    rows_v = np.unique(np.concatenate([wl.sample_rows(cfg.n_vis, 24, seed=9), np.arange(400, cfg.n_vis, 37)]))
+    rows_c = np.arange(cfg.n_cond)
+    log("  oracle rows")
+    rv, rc = oracle.joint_attention_8bit(f64["q_vis"], f64["k_vis"], f64["v_vis"], f64["q_cond"], f64["k_cond"],
+                                         f64["v_cond"], vis_rows=rows_v, cond_rows=rows_c)
+    _close8("o_vis[rows]", to_host64(ov)[:, rows_v], rv)
+    _close8("o_cond[rows]", to_host64(oc)[:, rows_c], rc)

@@ -95,7 +95,7 @@ def lib() -> ctypes.CDLL:
         "mmdit_attn8_quantize": [vp, vp, vp, i64, vp, vp, vp, i64, i, i64, i64, i64, i64,
                                  ctypes.POINTER(Attn8Stream), ctypes.POINTER(Attn8Stream), vp, vp],
         "mmdit_joint_attention_8bit": [ctypes.POINTER(Attn8Stream), i64, ctypes.POINTER(Attn8Stream), i64, vp,
-                                       i64, i64, i64, f, vp, vp, i, i64, vp, vp],
+                                       i64, i64, i64, f, vp, vp, i, i64, vp, vp, ctypes.c_size_t, vp],
         "mmdit_linear_fp8": [vp, vp, vp, vp, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
         "mmdit_timestep_embed": [vp, i64, vp, vp, vp, vp, vp, vp, i, i64, i64, i64, f, vp, vp, vp, vp],
         "mmdit_block_workspace_offsets": [ctypes.POINTER(BlockDims), i64, i64, i64, ctypes.POINTER(c_size_t)],
@@ -341,10 +341,17 @@ def attn8_quantize(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None,
     return out
 
 
+# bytes of key-range results the 8-bit attention's split tail can use: 256 slots of
+# 256 x 128 outputs plus (m, l) for 256 queries, f32
+ATTN8_SPLIT_BYTES = 256 * (256 * 128 + 256 * 2) * 4
+
+
 def joint_attention_8bit(ops: Attn8Operands, *, softmax_scale: Optional[float] = None, out_dtype=torch.float32,
                          o_vis: Optional[torch.Tensor] = None, o_cond: Optional[torch.Tensor] = None,
-                         return_lse: bool = False):
-    """8-bit joint attention over the operands of attn8_quantize; outputs [B, n_s, H, 128]."""
+                         return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """8-bit joint attention over the operands of attn8_quantize; outputs [B, n_s, H, 128].
+    ``workspace`` (optional device bytes, 256-byte aligned) lets a partly empty last round of
+    workgroups split its items over key ranges (ATTN8_SPLIT_BYTES is always enough)."""
     B, H = ops.B, ops.H
     n_vis, n_cond = ops.n
     dev = ops.v_scale.device
@@ -360,6 +367,7 @@ def joint_attention_8bit(ops: Attn8Operands, *, softmax_scale: Optional[float] =
     st = lib().mmdit_joint_attention_8bit(ctypes.byref(sv), n_vis, ctypes.byref(sc), n_cond, ops.v_scale.data_ptr(),
                                           B, H, 128, softmax_scale, o_vis.data_ptr(),
                                           _ptr(o_cond) if n_cond else None, _dt(o_vis), ors, _ptr(lse),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                           torch.cuda.current_stream(dev).cuda_stream)
     _check(st, "mmdit_joint_attention_8bit")
     if return_lse:

@@ -67,7 +67,7 @@ const char* mmdit_status_str(int s) {
 
 const char* mmdit_last_error(void) { return g_last_error.c_str(); }
 
-int mmdit_abi_version(void) { return 3; }
+int mmdit_abi_version(void) { return 4; }
 
 int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
                       const float* gate, float* x_out, const float* shift, const float* scale,
@@ -282,9 +282,12 @@ int mmdit_attn8_quantize(const void* q_vis, const void* k_vis, const void* v_vis
 int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis, const mmdit_attn8_stream* cond,
                                int64_t n_cond, const float* v_scale, int64_t B, int64_t H, int64_t D,
                                float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
-                               int64_t out_row_stride, float* lse, void* stream) {
+                               int64_t out_row_stride, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   g_last_error.clear();
   if (B < 0 || H < 0 || n_vis < 0 || n_cond < 0) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: negative size");
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: workspace must be 256-byte aligned");
   if (D != 128) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: D must be 128");
   if (!valid_dtype(out_dtype)) return fail(MMDIT_ERR_DTYPE, "joint_attention_8bit: bad out dtype");
   if (out_row_stride < H * D || out_row_stride % 8) return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: out row stride >= H*D, a multiple of 8");
@@ -309,7 +312,8 @@ int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis, con
   }
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: lse 4-byte aligned");
   return launch_joint_attention_8bit(seg, n, v_scale, B, H, softmax_scale, o_vis, o_cond, out_dtype, out_row_stride,
-                                     lse, static_cast<hipStream_t>(stream));
+                                     lse, static_cast<hipStream_t>(stream), static_cast<float*>(workspace),
+                                     workspace ? workspace_bytes : 0);
 }
 
 int mmdit_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row, void* q,

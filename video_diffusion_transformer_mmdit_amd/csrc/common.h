@@ -155,7 +155,8 @@ int launch_attn8_quantize(const void* const* q, const void* const* k, const void
                           float* v_scale, hipStream_t stream);
 int launch_joint_attention_8bit(const mmdit_attn8_stream* const* seg, const int64_t* n, const float* v_scale,
                                 int64_t B, int64_t H, float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
-                                int64_t out_stride, float* lse, hipStream_t stream);
+                                int64_t out_stride, float* lse, hipStream_t stream, float* split_ws = nullptr,
+                                size_t split_ws_bytes = 0);
 // FP8 E4M3 quantization with a scale per row (per_row) or one for the whole tensor.
 int launch_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row, uint8_t* q,
                         float* scales, hipStream_t stream);

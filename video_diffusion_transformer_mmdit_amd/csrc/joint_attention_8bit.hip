@@ -51,7 +51,32 @@ struct Attn8Args {
   int H;
   int nqt;
   float scale_log2;         // softmax_scale * log2(e)
+  // Split tail, as in the 16-bit kernel: workgroups [0, full) take items (batch x head, query
+  // tile) 0 .. full-1 over all keys; each remaining item is cut into `split` key ranges whose
+  // partial results go to `part` for joint_attn_8bit_merge_kernel.  full == nbh * nqt: none.
+  int nbh;
+  int full;
+  int split;
+  float* part;
 };
+
+constexpr int A8_ROUND = 256;   // workgroups the chip runs at once (one per CU)
+// one key range's partial result for one query tile: O (256 x 128 f32, V scale applied) then
+// (m, l) per query
+constexpr int64_t A8_PART_FLOATS = 256 * 128 + 256 * 2;
+
+// (batch x head, query tile) of work item i; XCD x (i % 8) takes whole heads x, x + 8, ...
+// when the (batch, head) count allows
+__device__ __forceinline__ void attn8_item(const Attn8Args& a, int i, int& bh, int& qt) {
+  if ((a.nbh & 7) == 0) {
+    const int j = i >> 3;
+    bh = (i & 7) + 8 * (j / a.nqt);
+    qt = j % a.nqt;
+  } else {
+    bh = i / a.nqt;
+    qt = i % a.nqt;
+  }
+}
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -96,16 +121,14 @@ void joint_attn_8bit_kernel(Attn8Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   int qt, bh;
+  int slot = -1;   // a split-tail workgroup's partial-result slot
   {
-    const int bid = blockIdx.x, nbh = gridDim.x / a.nqt;
-    if ((nbh & 7) == 0) {   // XCD x (bid % 8) takes whole heads x, x + 8, ...
-      const int i = bid >> 3;
-      bh = (bid & 7) + 8 * (i / a.nqt);
-      qt = i % a.nqt;
-    } else {
-      bh = bid / a.nqt;
-      qt = bid % a.nqt;
+    int item = blockIdx.x;
+    if (item >= a.full) {
+      slot = item - a.full;
+      item = a.full + slot / a.split;
     }
+    attn8_item(a, item, bh, qt);
   }
   const int h = bh % a.H;
   const int64_t b = bh / a.H;
@@ -133,6 +156,13 @@ void joint_attn_8bit_kernel(Attn8Args a) {
   const int t_vis = (int)((n_vis + A8_BN - 1) / A8_BN);
   const int t_cond = (int)((n_cond + A8_BN - 1) / A8_BN);
   const int ntiles = t_vis + t_cond;
+  // this workgroup's key tiles [jbeg, jend): all of them, or one range of a split-tail item
+  int jbeg = 0, jend = ntiles;
+  if (slot >= 0) {
+    const int sp = slot % a.split;
+    jbeg = (int)((int64_t)ntiles * sp / a.split);
+    jend = (int)((int64_t)ntiles * (sp + 1) / a.split);
+  }
   auto tile_seg = [&](int jt, int& sg, int& t) { sg = jt < t_vis ? 0 : 1; t = sg ? jt - t_vis : jt; };
   auto kbuf = [&](auto stage) -> uint8_t* { if constexpr (decltype(stage)::value == 0) return lds_k0; else return lds_k1; };
   auto vbuf = [&](auto stage) -> uint8_t* { if constexpr (decltype(stage)::value == 0) return lds_v0; else return lds_v1; };
@@ -233,8 +263,8 @@ void joint_attn_8bit_kernel(Attn8Args a) {
       constexpr int CUR = decltype(cur_c)::value;
       constexpr std::integral_constant<int, CUR> cur{};
       constexpr std::integral_constant<int, CUR ^ 1> oth{};
-      if constexpr (GRP == 0) dma_tile(jt + 1 < ntiles ? jt + 1 : ntiles - 1, vbuf(oth));
-      else dma_tile(jt + 2 < ntiles ? jt + 2 : ntiles - 1, kbuf(cur));
+      if constexpr (GRP == 0) dma_tile(jt + 1 < jend ? jt + 1 : jend - 1, vbuf(oth));
+      else dma_tile(jt + 2 < jend ? jt + 2 : jend - 1, kbuf(cur));
       compute_s(kbuf(oth), sn);
       const uint8_t* vb = vbuf(cur);
 #pragma unroll
@@ -254,11 +284,11 @@ void joint_attn_8bit_kernel(Attn8Args a) {
       phase_barrier();
     };
     // the K scale of the tile the next V phase works on, loaded one phase ahead
-    float sk_next = k_scale(0);
+    float sk_next = k_scale(jbeg);
     // V(j): integer row max, integer reference, P'_j = E4M3(2^(acc c + 8 - m))
     auto phase_v = [&](auto cur_c, int jt, i32x16 (&s)[2]) {
       const float skt = sk_next;
-      sk_next = k_scale(jt + 1 < ntiles ? jt + 1 : jt);
+      sk_next = k_scale(jt + 1 < jend ? jt + 1 : jt);
       int sg, t;
       tile_seg(jt, sg, t);
       const int64_t rows = a.n_seg[sg] - (int64_t)t * A8_BN;
@@ -279,9 +309,9 @@ void joint_attn_8bit_kernel(Attn8Args a) {
       const int mx = xhalf_max_i(max(max(m4[0], m4[1]), max(m4[2], m4[3])));
       const float ci = sq * (skt * kc);
       const float mt = ceilf((float)mx * ci);
-      if (jt == 0 || __any(mt > m_run)) {
-        const float mnew = jt == 0 ? mt : fmaxf(m_run, mt);
-        if (jt != 0) {
+      if (jt == jbeg || __any(mt > m_run)) {
+        const float mnew = jt == jbeg ? mt : fmaxf(m_run, mt);
+        if (jt != jbeg) {
           const int sh = (int)(m_run - mnew);   // <= 0: an exact power-of-two rescale
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt)
@@ -315,25 +345,25 @@ void joint_attn_8bit_kernel(Attn8Args a) {
     };
 
     if constexpr (GRP == 1) {
-      dma_tile(0, lds_k0);
-      if (ntiles > 1) dma_tile(1, lds_k1);
+      dma_tile(jbeg, lds_k0);
+      if (jbeg + 1 < jend) dma_tile(jbeg + 1, lds_k1);
       __builtin_amdgcn_s_waitcnt(0xF70);
     }
     __syncthreads();
     if constexpr (GRP == 1) phase_barrier();
-    if constexpr (GRP == 0) dma_tile(0, lds_v0);
+    if constexpr (GRP == 0) dma_tile(jbeg, lds_v0);
     i32x16 sa[2], sb[2];
     compute_s(lds_k0, sa);
     asm volatile("" ::"v"(sa[0]), "v"(sa[1]));
     phase_barrier();
-    int jt = 0;
-    for (; jt + 1 < ntiles; jt += 2) {
+    int jt = jbeg;
+    for (; jt + 1 < jend; jt += 2) {
       phase_v(S0, jt, sa);
       phase_m(S0, jt, sb);
       phase_v(S1, jt + 1, sb);
       phase_m(S1, jt + 1, sa);
     }
-    if (jt < ntiles) {
+    if (jt < jend) {
       phase_v(S0, jt, sa);
       phase_m(S0, jt, sb);
     }
@@ -343,6 +373,23 @@ void joint_attn_8bit_kernel(Attn8Args a) {
     }
 
     // ---- finish: O = s_v * acc / ell; every row of the ones product holds the row sum
+    const float* svp = a.sv + ((int64_t)b * a.H + h) * A8_DIM;
+    if (slot >= 0) {   // a key range of a split-tail item: s_v * acc, running max and sum
+      float* pb = a.part + (int64_t)slot * A8_PART_FLOATS;
+      const int ql = wave * 32 + l32;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int d0 = dt * 32 + 8 * e4 + 4 * g;
+          const float4 sv = *reinterpret_cast<const float4*>(svp + d0);
+          *reinterpret_cast<float4*>(pb + ql * 128 + d0) =
+              make_float4(o[dt][4 * e4] * sv.x, o[dt][4 * e4 + 1] * sv.y, o[dt][4 * e4 + 2] * sv.z,
+                          o[dt][4 * e4 + 3] * sv.w);
+        }
+      if (g == 0) *reinterpret_cast<float2*>(pb + 256 * 128 + 2 * ql) = make_float2(m_run, ol[0]);
+      return;
+    }
     if (qi >= N) return;
     const float ell = ol[0];
     const float inv = 1.0f / ell;
@@ -350,7 +397,6 @@ void joint_attn_8bit_kernel(Attn8Args a) {
     const int64_t row = is_cond ? b * n_cond + qi : b * n_vis + (qi - n_cond);
     void* obase = is_cond ? a.o[1] : a.o[0];
     const int64_t ooff = row * a.out_stride + (int64_t)h * A8_DIM;
-    const float* svp = a.sv + ((int64_t)b * a.H + h) * A8_DIM;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -377,9 +423,54 @@ void joint_attn_8bit_kernel(Attn8Args a) {
   else run(std::integral_constant<int, 0>{});
 }
 
+// Split-tail items: per query, the `split` key ranges' results (s_v * acc_s relative to 2^(m_s
+// - 8), sums l_s; the m_s are integers) combine as O = sum_s 2^(m_s - M) O_s / L, M = max_s
+// m_s, L = sum_s 2^(m_s - M) l_s: every weight is an exact power of two, as in the rescale.
+// One thread per query and four dims; 32 workgroups of 256 threads per item.  Calls that
+// ask for the LSE are not split.
+template <int OUT_DT>
+__global__ __launch_bounds__(256) void joint_attn_8bit_merge_kernel(Attn8Args a) {
+  const int r = blockIdx.x >> 5;
+  const int t = (blockIdx.x & 31) * 256 + threadIdx.x;
+  const int ql = t >> 5, d0 = (t & 31) * 4;
+  int bh, qt;
+  attn8_item(a, a.full + r, bh, qt);
+  const int64_t qi = (int64_t)qt * A8_BM + ql;
+  if (qi >= a.N) return;
+  const float* pb = a.part + (int64_t)r * a.split * A8_PART_FLOATS;
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < a.split; ++sp) mmax = fmaxf(mmax, pb[sp * A8_PART_FLOATS + 256 * 128 + 2 * ql]);
+  float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < a.split; ++sp) {
+    const float* ps = pb + sp * A8_PART_FLOATS;
+    const float w = __builtin_ldexpf(1.0f, (int)(ps[256 * 128 + 2 * ql] - mmax));
+    l = fmaf(w, ps[256 * 128 + 2 * ql + 1], l);
+    const float4 o = *reinterpret_cast<const float4*>(ps + ql * 128 + d0);
+    acc[0] = fmaf(w, o.x, acc[0]); acc[1] = fmaf(w, o.y, acc[1]);
+    acc[2] = fmaf(w, o.z, acc[2]); acc[3] = fmaf(w, o.w, acc[3]);
+  }
+  const float inv = 1.0f / l;
+  const int h = bh % a.H;
+  const int64_t b = bh / a.H;
+  const int64_t n_cond = a.n_seg[1], n_vis = a.n_seg[0];
+  const bool is_cond = qi < n_cond;
+  const int64_t row = is_cond ? b * n_cond + qi : b * n_vis + (qi - n_cond);
+  void* obase = is_cond ? a.o[1] : a.o[0];
+  const int64_t off = row * a.out_stride + (int64_t)h * A8_DIM + d0;
+  const float v0 = acc[0] * inv, v1 = acc[1] * inv, v2 = acc[2] * inv, v3 = acc[3] * inv;
+  if constexpr (OUT_DT == MMDIT_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(obase) + off) = make_float4(v0, v1, v2, v3);
+  } else if constexpr (OUT_DT == MMDIT_BF16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + off) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(obase) + off) = make_uint2(pack_f16x2(v0, v1), pack_f16x2(v2, v3));
+  }
+}
+
 int launch_joint_attention_8bit(const mmdit_attn8_stream* const* seg, const int64_t* n, const float* v_scale,
                                 int64_t B, int64_t H, float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
-                                int64_t out_stride, float* lse, hipStream_t stream) {
+                                int64_t out_stride, float* lse, hipStream_t stream, float* split_ws,
+                                size_t split_ws_bytes) {
   const int64_t N = n[0] + n[1];
   if (B == 0 || H == 0 || N == 0) return MMDIT_OK;
   Attn8Args a{};
@@ -399,11 +490,34 @@ int launch_joint_attention_8bit(const mmdit_attn8_stream* const* seg, const int6
   a.H = (int)H;
   a.nqt = (int)((N + A8_BM - 1) / A8_BM);
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
-  const int64_t blocks = (int64_t)a.nqt * H * B;
-  if (blocks > 0x7fffffff) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: grid too large");
-  const dim3 grid((unsigned)blocks);
+  const int64_t items = (int64_t)a.nqt * H * B;
+  if (items > 0x7fffffff) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: grid too large");
   const bool L = lse != nullptr;
-#define A8_GO(O, LS) joint_attn_8bit_kernel<O, LS><<<grid, A8_THREADS, 0, stream>>>(a)
+  a.nbh = (int)(H * B);
+  a.full = (int)items;
+  a.split = 1;
+  // Split tail (with a workspace and no LSE): when the items fill R < 256 workgroup slots of
+  // the last round, cut each of those R items into S = 256 / R key ranges (at most one per
+  // key tile), merged afterwards
+  const int64_t ntiles = (n[0] + A8_BN - 1) / A8_BN + (n[1] + A8_BN - 1) / A8_BN;
+  if (split_ws && !L && items > A8_ROUND) {
+    const int64_t R = items % A8_ROUND;
+    int64_t S = R ? A8_ROUND / R : 0;
+    if (S > ntiles) S = ntiles;
+    if (R > 0 && S >= 2 && (size_t)(R * S * A8_PART_FLOATS) * 4 <= split_ws_bytes) {
+      a.full = (int)(items - R);
+      a.split = (int)S;
+      a.part = split_ws;
+    }
+  }
+  const int tail = (int)(items - a.full);
+  const dim3 grid((unsigned)(a.full + (int64_t)tail * a.split));
+  const dim3 mgrid((unsigned)(tail * 32));
+#define A8_GO(O, LS)                                                                            \
+  do {                                                                                          \
+    joint_attn_8bit_kernel<O, LS><<<grid, A8_THREADS, 0, stream>>>(a);                         \
+    if constexpr (!LS) if (tail > 0) joint_attn_8bit_merge_kernel<O><<<mgrid, 256, 0, stream>>>(a); \
+  } while (0)
   if (out_dtype == MMDIT_F32) { if (L) A8_GO(MMDIT_F32, true); else A8_GO(MMDIT_F32, false); }
   else if (out_dtype == MMDIT_BF16) { if (L) A8_GO(MMDIT_BF16, true); else A8_GO(MMDIT_BF16, false); }
   else if (out_dtype == MMDIT_F16) { if (L) A8_GO(MMDIT_F16, true); else A8_GO(MMDIT_F16, false); }
