@@ -182,8 +182,8 @@ def attention_8bit(dev):
     import video_diffusion_transformer_mmdit_amd as mm
     import workloads as wl
     res = {}
-    # key-range results of the 8-bit kernel's split tail (allocated once, outside the timing)
-    ws = torch.empty(mm.ATTN8_SPLIT_BYTES, dtype=torch.uint8, device=dev)
+    # key-range results of the kernels' split tails (allocated once, outside the timing)
+    ws = torch.empty(mm.ATTN_SPLIT_BYTES, dtype=torch.uint8, device=dev)
     for cfg in (wl.ATTN_480P, wl.ATTN_720P):
         raw = wl.attention_inputs(cfg)
         t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in raw.items()}
@@ -195,7 +195,8 @@ def attention_8bit(dev):
         ms_a = time_calls(lambda: mm.joint_attention_8bit(ops, o_vis=ov, o_cond=oc, workspace=ws), reps=5, warm=1)
         h16 = {k: t[k].to(torch.float16) for k in ("q_vis", "k_vis", "v_vis", "q_cond", "k_cond", "v_cond")}
         ms_16 = time_calls(lambda: mm.joint_attention(h16["q_vis"], h16["k_vis"], h16["v_vis"], h16["q_cond"],
-                                                      h16["k_cond"], h16["v_cond"], o_vis=ov, o_cond=oc),
+                                                      h16["k_cond"], h16["v_cond"], o_vis=ov, o_cond=oc,
+                                                      workspace=ws),
                            reps=5, warm=1)
         fl = cfg.attn_flops
         res[cfg.name.split("_")[0]] = {

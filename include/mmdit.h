@@ -135,6 +135,12 @@ int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_ro
  * o_vis, o_cond  [B, n_s, H, D] out_dtype F32 | BF16 | F16, row stride out_row_stride.
  * lse         optional f32 [B, H, n_cond + n_vis], cond rows first: the natural-log
  *             sum of exp(scaled logits) of each query row, or NULL.
+ * workspace   optional device memory (256-byte aligned, caller-owned, contents scratch):
+ *             with 16-bit operands, no lse and a last round of 256 workgroups that the
+ *             (batch x head, 256-query tile) items fill only partly, those items are split
+ *             over key ranges whose results go there (up to 256 x 33280 floats = 34 MB) and
+ *             are merged (O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s).  NULL or too
+ *             small: no split.  Calls that share a workspace must not overlap.
  * D must be 128; n_vis + n_cond >= 1; a stream with n_s = 0 may pass NULL pointers.
  * ------------------------------------------------------------------------------- */
 int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
@@ -142,7 +148,7 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
                           int qk_dtype, int v_dtype, int64_t in_row_stride,
                           int64_t B, int64_t H, int64_t D, float softmax_scale,
                           void* o_vis, void* o_cond, int out_dtype, int64_t out_row_stride,
-                          float* lse, void* stream);
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * mmdit_linear -- y = epilogue(x W^T + bias) on bf16 / f16 MFMA, fp32 accumulate.  The

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert mm.abi_version() == 4
+    assert mm.abi_version() == 5
     assert L.mmdit_status_str(0) == b"MMDIT_OK"
     assert L.mmdit_status_str(ERR_ALIAS) == b"MMDIT_ERR_ALIAS"
     assert L.mmdit_status_str(99) == b"MMDIT_ERR_UNKNOWN"
@@ -77,7 +77,8 @@ def test_qk_norm_rope_validation(L):
 def test_joint_attention_validation(L):
     p, o = _fake(0x10000), _fake(0x900000)
     f = L.mmdit_joint_attention
-    args = [p, p, p, 10, p, p, p, 3, mm.BF16, mm.BF16, 256, 1, 2, 128, 0.088, o, _fake(0xA00000), mm.F32, 256, None, None]
+    args = [p, p, p, 10, p, p, p, 3, mm.BF16, mm.BF16, 256, 1, 2, 128, 0.088, o, _fake(0xA00000), mm.F32, 256, None,
+            None, 0, None]
     a = list(args); a[13] = 96
     assert f(*a) == ERR_SHAPE
     a = list(args); a[3] = 0; a[7] = 0
@@ -94,6 +95,8 @@ def test_joint_attention_validation(L):
     assert f(*a) == ERR_SHAPE
     a = list(args); a[10] = 100
     assert f(*a) == ERR_SHAPE                                       # row stride < H*D
+    a = list(args); a[20] = _fake(0xB00010); a[21] = 1 << 20
+    assert f(*a) == ERR_ALIGN                                       # workspace not 256-byte aligned
 
 
 def test_linear_modulate_modulation_validation(L):

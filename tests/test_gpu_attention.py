@@ -226,3 +226,23 @@ def test_attention_operand_dtype_combinations(qk, v):
     r_v, r_c = _oracle_attn(qv, kv, vv, qc, kc, vc)
     assert_close("o_vis", to_host64(o_v), r_v, 1e-2)
     assert_close("o_cond", to_host64(o_c), r_c, 1e-2)
+
+
+def test_attention_split_tail_with_workspace():
+    """B = 2, 24 heads, 1400 + 77 tokens: 288 (batch x head, query tile) items leave 32 for the
+    last round, which a workspace lets the kernel cut into 8 key ranges each and merge.  The
+    output matches the oracle at the 16-bit bar and the same call without a workspace to
+    within the f16 rounding of P (each range rounds exp2 against its own running max)."""
+    B, nv, nc, H, D = 2, 1400, 77, 24, 128
+    qv, kv, vv = (_rand((B, nv, H, D), s) for s in (11, 12, 13))
+    qc, kc, vc = (_rand((B, nc, H, D), s) for s in (14, 15, 16))
+    ws = torch.empty(mm.ATTN_SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+    o_v, o_c = mm.joint_attention(qv, kv, vv, qc, kc, vc, workspace=ws)
+    u_v, u_c = mm.joint_attention(qv, kv, vv, qc, kc, vc)
+    torch.cuda.synchronize()
+    assert_close("o_vis split vs one pass", to_host64(o_v), to_host64(u_v), 5e-3)
+    assert_close("o_cond split vs one pass", to_host64(o_c), to_host64(u_c), 5e-3)
+    for b in range(B):
+        r_v, r_c = _oracle_attn(*(t[b:b + 1].contiguous() for t in (qv, kv, vv, qc, kc, vc)))
+        assert_close(f"o_vis[b={b}]", to_host64(o_v[b:b + 1]), r_v, 2e-2)
+        assert_close(f"o_cond[b={b}]", to_host64(o_c[b:b + 1]), r_c, 2e-2)

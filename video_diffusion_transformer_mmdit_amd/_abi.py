@@ -86,7 +86,7 @@ def lib() -> ctypes.CDLL:
         "mmdit_qk_norm_rope": [vp, vp, i, i64, vp, vp, i, i64, vp, vp, i, i64, i64, i64, i64, i64, f,
                                ctypes.POINTER(Rope3D), vp],
         "mmdit_joint_attention": [vp, vp, vp, i64, vp, vp, vp, i64, i, i, i64, i64, i64, i64, f, vp, vp, i,
-                                  i64, vp, vp],
+                                  i64, vp, vp, ctypes.c_size_t, vp],
         "mmdit_linear": [vp, vp, i, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
         "mmdit_modulation": [vp, vp, vp, i, vp, i64, i64, i64, vp],
         "mmdit_lite_merge": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
@@ -227,12 +227,20 @@ def qk_norm_rope(q: torch.Tensor, k: torch.Tensor, q_scale: torch.Tensor, k_scal
     return q_out, k_out
 
 
+# bytes of key-range results the attention kernels' split tails can use: 256 slots of
+# 256 x 128 outputs plus (m, l) for 256 queries, f32
+ATTN_SPLIT_BYTES = 256 * (256 * 128 + 256 * 2) * 4
+ATTN8_SPLIT_BYTES = ATTN_SPLIT_BYTES
+
+
 def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, *,
                     softmax_scale: Optional[float] = None, out_dtype=torch.float32,
                     o_vis: Optional[torch.Tensor] = None, o_cond: Optional[torch.Tensor] = None,
-                    return_lse: bool = False):
+                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
     """softmax(Q K^T * scale) V over [cond | vis] per head, outputs split per stream.
-    Inputs [B, N_s, H, D] views with one common row stride."""
+    Inputs [B, N_s, H, D] views with one common row stride.  ``workspace`` (optional device
+    bytes, 256-byte aligned; ATTN_SPLIT_BYTES is always enough) lets a partly empty last
+    round of workgroups split its items over key ranges."""
     ts = [t for t in (q_vis, k_vis, v_vis, q_cond, k_cond, v_cond) if t is not None]
     _need_gpu(*ts)
     B, n_vis, rs = _rows(q_vis, "q_vis")
@@ -260,7 +268,9 @@ def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, 
                                      _ptr(q_cond) if n_cond else None, _ptr(k_cond) if n_cond else None,
                                      _ptr(v_cond) if n_cond else None, n_cond, _dt(q_vis), _dt(v_vis), rs, B, H, D,
                                      softmax_scale, o_vis.data_ptr(), _ptr(o_cond) if n_cond else None,
-                                     _dt(o_vis), ors, _ptr(lse), _stream(q_vis))
+                                     _dt(o_vis), ors, _ptr(lse), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                     _stream(q_vis))
     _check(st, "mmdit_joint_attention")
     if return_lse:
         return o_vis, o_cond, lse
@@ -341,9 +351,7 @@ def attn8_quantize(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None,
     return out
 
 
-# bytes of key-range results the 8-bit attention's split tail can use: 256 slots of
-# 256 x 128 outputs plus (m, l) for 256 queries, f32
-ATTN8_SPLIT_BYTES = 256 * (256 * 128 + 256 * 2) * 4
+
 
 
 def joint_attention_8bit(ops: Attn8Operands, *, softmax_scale: Optional[float] = None, out_dtype=torch.float32,

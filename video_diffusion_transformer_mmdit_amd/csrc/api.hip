@@ -67,7 +67,7 @@ const char* mmdit_status_str(int s) {
 
 const char* mmdit_last_error(void) { return g_last_error.c_str(); }
 
-int mmdit_abi_version(void) { return 4; }
+int mmdit_abi_version(void) { return 5; }
 
 int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
                       const float* gate, float* x_out, const float* shift, const float* scale,
@@ -154,9 +154,12 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
                           const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
                           int qk_dtype, int v_dtype, int64_t in_row_stride, int64_t B, int64_t H, int64_t D,
                           float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
-                          int64_t out_row_stride, float* lse, void* stream) {
+                          int64_t out_row_stride, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   g_last_error.clear();
   if (D != 128) return fail(MMDIT_ERR_SHAPE, "joint_attention: D must be 128");
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(MMDIT_ERR_ALIGN, "joint_attention: workspace must be 256-byte aligned");
   if (B < 0 || H < 1 || n_vis < 0 || n_cond < 0 || n_vis + n_cond < 1)
     return fail(MMDIT_ERR_SHAPE, "joint_attention: need B >= 0, H >= 1, n_vis + n_cond >= 1");
   if (in_row_stride < H * D || out_row_stride < H * D) return fail(MMDIT_ERR_SHAPE, "joint_attention: row stride < H*D");
@@ -191,7 +194,8 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
     return fail(MMDIT_ERR_ALIAS, "joint_attention: o_vis and o_cond overlap");
   return launch_joint_attention(q_vis, k_vis, v_vis, n_vis, q_cond, k_cond, v_cond, n_cond, qk_dtype, v_dtype,
                                 in_row_stride, B, H, softmax_scale, o_vis, o_cond, out_dtype,
-                                out_row_stride, lse, static_cast<hipStream_t>(stream));
+                                out_row_stride, lse, static_cast<hipStream_t>(stream), static_cast<float*>(workspace),
+                                workspace ? workspace_bytes : 0);
 }
 
 int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, int bias_dtype,
