@@ -140,7 +140,8 @@ int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_ro
  *             (batch x head, 256-query tile) items fill only partly, those items are split
  *             over key ranges whose results go there (up to 256 x 33280 floats = 34 MB) and
  *             are merged (O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s).  NULL or too
- *             small: no split.  Calls that share a workspace must not overlap.
+ *             small: no split.  Calls that share a workspace must not overlap.  The
+ *             workspace must not overlap any input, output or lse (MMDIT_ERR_ALIAS).
  * D must be 128; n_vis + n_cond >= 1; a stream with n_s = 0 may pass NULL pointers.
  * ------------------------------------------------------------------------------- */
 int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
@@ -230,7 +231,8 @@ int mmdit_attn8_quantize(const void* q_vis, const void* k_vis, const void* v_vis
  * whose results go there (up to 256 x 33280 floats = 34 MB) and are merged: the ranges' sums
  * combine with exact power-of-two weights 2^(m_s - max m), so O changes only by the f32
  * summation order.  NULL or too small: no split.  Calls that share a workspace must not
- * overlap. */
+ * overlap.  Outputs, lse and workspace must be disjoint from every operand (codes, scales,
+ * v_scale) and from one another (MMDIT_ERR_ALIAS). */
 int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis,
                                const mmdit_attn8_stream* cond, int64_t n_cond,
                                const float* v_scale, int64_t B, int64_t H, int64_t D,

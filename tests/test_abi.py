@@ -97,6 +97,14 @@ def test_joint_attention_validation(L):
     assert f(*a) == ERR_SHAPE                                       # row stride < H*D
     a = list(args); a[20] = _fake(0xB00010); a[21] = 1 << 20
     assert f(*a) == ERR_ALIGN                                       # workspace not 256-byte aligned
+    a = list(args); a[20] = p; a[21] = 1 << 20
+    assert f(*a) == ERR_ALIAS                                       # workspace on top of the inputs
+    a = list(args); a[20] = _fake(0x8FFF00); a[21] = 1 << 20
+    assert f(*a) == ERR_ALIAS                                       # workspace running into o_vis
+    a = list(args); a[20] = _fake(0xA00000); a[21] = 256
+    assert f(*a) == ERR_ALIAS                                       # workspace on o_cond
+    a = list(args); a[19] = _fake(0xC00000); a[20] = _fake(0xC00000); a[21] = 256
+    assert f(*a) == ERR_ALIAS                                       # workspace on lse
 
 
 def test_linear_modulate_modulation_validation(L):
@@ -223,5 +231,38 @@ def test_attention_8bit_validation(L):
     assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, p, None, mm.FP8_E4M3, 3072, None, None, 0, None) == ERR_DTYPE
     assert a(C.byref(st), 100, C.byref(st), 5, sv, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None, 0, None) == ERR_NULL
     assert a(C.byref(st), 100, None, 0, _fake(0x60000004), 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, None, 0, None) == ERR_ALIGN
+    o = _fake(0x70000000)
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, _fake(0x10000000), None, mm.F32, 3072, None, None, 0,
+             None) == ERR_ALIAS                                     # output on the Q codes
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, o, None, mm.F32, 3072, None, _fake(0x50000000),
+             1 << 20, None) == ERR_ALIAS                            # workspace on the V codes
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, o, None, mm.F32, 3072, None, o, 1 << 20,
+             None) == ERR_ALIAS                                     # workspace on the output
+    assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, o, None, mm.F32, 3072, _fake(0x7F000000),
+             _fake(0x7F000000), 256, None) == ERR_ALIAS             # workspace on lse
 
     assert a(C.byref(st), 100, None, 0, sv, 1, 24, 128, 0.088, p, None, mm.F32, 3072, None, _fake(0x60000010), 1 << 20, None) == ERR_ALIGN
+
+def test_binding_rejects_host_or_foreign_workspace_before_any_launch():
+    """A workspace (or output) that is not a GPU tensor on the inputs' device raises in the
+    binding: its host address would otherwise reach the split-tail kernels, which write
+    through it."""
+    import torch
+    from video_diffusion_transformer_mmdit_amd import _abi
+    cuda0 = torch.device("cuda", 0)
+    host = torch.empty(256, dtype=torch.uint8)
+    with pytest.raises(mm.MmditError, match="workspace must be a GPU tensor"):
+        _abi._on_device(cuda0, workspace=host)
+    with pytest.raises(mm.MmditError, match="o_vis must be a GPU tensor"):
+        _abi._on_device(cuda0, o_vis=host)
+    with pytest.raises(mm.MmditError, match="must be a GPU tensor"):
+        _abi._on_device(torch.device("cpu"), workspace=host)
+    _abi._on_device(cuda0, workspace=None, o_cond=None)       # absent tensors are fine
+    with pytest.raises(mm.MmditError, match="contiguous"):
+        _abi._workspace_bytes(torch.empty((4, 64), dtype=torch.uint8)[:, ::2])
+    assert _abi._workspace_bytes(torch.empty(300, dtype=torch.float32)) == 1200
+    # through the public entry points (host inputs fail first here; on a GPU box the
+    # workspace check is reached, see test_gpu_attention)
+    q = torch.empty((1, 8, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(mm.MmditError):
+        mm.joint_attention(q, q, q, workspace=host)

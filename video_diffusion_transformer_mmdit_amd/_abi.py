@@ -153,6 +153,24 @@ def _need_gpu(*ts):
             raise MmditError("tensors must live on the GPU")
 
 
+def _on_device(device: torch.device, **named):
+    """Every given tensor must be a GPU tensor on ``device`` (the device the kernels run on):
+    a host or other-device pointer handed to a kernel would be written through."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda or device.type != "cuda" or t.device != device:
+            raise MmditError(f"{name} must be a GPU tensor on {device} (got {t.device})")
+
+
+def _workspace_bytes(workspace: Optional[torch.Tensor]) -> int:
+    if workspace is None:
+        return 0
+    if not workspace.is_contiguous():
+        raise MmditError("workspace must be contiguous")
+    return workspace.numel() * workspace.element_size()
+
+
 def _rows(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
     """[B, N, H, D] view with contiguous (H, D) and batch items N rows apart ->
     (B, N, row_stride)."""
@@ -243,6 +261,9 @@ def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, 
     round of workgroups split its items over key ranges."""
     ts = [t for t in (q_vis, k_vis, v_vis, q_cond, k_cond, v_cond) if t is not None]
     _need_gpu(*ts)
+    _on_device(q_vis.device, k_vis=k_vis, v_vis=v_vis, q_cond=q_cond, k_cond=k_cond, v_cond=v_cond,
+               o_vis=o_vis, o_cond=o_cond, workspace=workspace)
+    ws_bytes = _workspace_bytes(workspace)
     B, n_vis, rs = _rows(q_vis, "q_vis")
     H, D = q_vis.shape[2], q_vis.shape[3]
     n_cond = 0 if q_cond is None else q_cond.shape[1]
@@ -268,9 +289,7 @@ def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, 
                                      _ptr(q_cond) if n_cond else None, _ptr(k_cond) if n_cond else None,
                                      _ptr(v_cond) if n_cond else None, n_cond, _dt(q_vis), _dt(v_vis), rs, B, H, D,
                                      softmax_scale, o_vis.data_ptr(), _ptr(o_cond) if n_cond else None,
-                                     _dt(o_vis), ors, _ptr(lse), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                     _stream(q_vis))
+                                     _dt(o_vis), ors, _ptr(lse), _ptr(workspace), ws_bytes, _stream(q_vis))
     _check(st, "mmdit_joint_attention")
     if return_lse:
         return o_vis, o_cond, lse
@@ -363,6 +382,8 @@ def joint_attention_8bit(ops: Attn8Operands, *, softmax_scale: Optional[float] =
     B, H = ops.B, ops.H
     n_vis, n_cond = ops.n
     dev = ops.v_scale.device
+    _on_device(dev, v_scale=ops.v_scale, o_vis=o_vis, o_cond=o_cond, workspace=workspace)
+    ws_bytes = _workspace_bytes(workspace)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128)
     if o_vis is None:
@@ -375,8 +396,7 @@ def joint_attention_8bit(ops: Attn8Operands, *, softmax_scale: Optional[float] =
     st = lib().mmdit_joint_attention_8bit(ctypes.byref(sv), n_vis, ctypes.byref(sc), n_cond, ops.v_scale.data_ptr(),
                                           B, H, 128, softmax_scale, o_vis.data_ptr(),
                                           _ptr(o_cond) if n_cond else None, _dt(o_vis), ors, _ptr(lse),
-                                          _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                          torch.cuda.current_stream(dev).cuda_stream)
+                                          _ptr(workspace), ws_bytes, torch.cuda.current_stream(dev).cuda_stream)
     _check(st, "mmdit_joint_attention_8bit")
     if return_lse:
         return o_vis, o_cond, lse
@@ -511,12 +531,13 @@ STREAM_KEYS = ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm", "w_o", "b
                "w_fc2", "b_fc2")
 
 
-def _stream_weights(w: Dict[str, torch.Tensor]) -> StreamWeights:
+def _stream_weights(w: Dict[str, torch.Tensor], device: torch.device) -> StreamWeights:
     sw = StreamWeights()
     for k in STREAM_KEYS:
         t = w.get(k)
         if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
             raise MmditError(f"weight {k} must be contiguous bf16")
+        _on_device(device, **{f"weight {k}": t})
         setattr(sw, k, None if t is None else t.data_ptr())
     return sw
 
@@ -541,6 +562,7 @@ def block_fwd(dims: BlockDims, w_vis: Dict[str, torch.Tensor], w_cond: Dict[str,
     ``stage_events``: optional 2 * STAGE_COUNT raw hipEvent_t handles (ints or None)
     recorded around each stage on the current stream."""
     _need_gpu(x_vis, x_cond, tvec, workspace)
+    _on_device(x_vis.device, x_cond=x_cond, tvec=tvec, workspace=workspace, out_vis=out_vis, out_cond=out_cond)
     B, n_vis, C = x_vis.shape
     n_cond = 0 if x_cond is None else x_cond.shape[1]
     need = block_workspace_bytes(dims, B, n_vis, n_cond)
@@ -552,11 +574,11 @@ def block_fwd(dims: BlockDims, w_vis: Dict[str, torch.Tensor], w_cond: Dict[str,
         out_vis = torch.empty((B, n_vis, C), dtype=out_dtype, device=x_vis.device)
     if out_cond is None and n_cond > 0:
         out_cond = torch.empty((B, n_cond, C), dtype=out_dtype, device=x_vis.device)
-    swv, swc = _stream_weights(w_vis), _stream_weights(w_cond)
+    swv, swc = _stream_weights(w_vis, x_vis.device), _stream_weights(w_cond, x_vis.device)
     args = (ctypes.byref(dims), ctypes.byref(swv), ctypes.byref(swc), x_vis.data_ptr(),
             _ptr(x_cond) if n_cond else None, _dt(x_vis), tvec.data_ptr(), _dt(tvec),
             ctypes.byref(rope), n_cond, out_vis.data_ptr(), _ptr(out_cond) if n_cond else None,
-            _dt(out_vis), workspace.data_ptr(), workspace.numel(), B, _stream(x_vis))
+            _dt(out_vis), workspace.data_ptr(), _workspace_bytes(workspace), B, _stream(x_vis))
     if stage_events is None:
         _check(lib().mmdit_block_fwd(*args), "mmdit_block_fwd")
     else:

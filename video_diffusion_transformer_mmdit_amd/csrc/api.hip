@@ -192,6 +192,19 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
   if (n_vis > 0 && n_cond > 0 &&
       overlaps(o_vis, span(B * n_vis, hd, out_row_stride, out_dtype), o_cond, span(B * n_cond, hd, out_row_stride, out_dtype)))
     return fail(MMDIT_ERR_ALIAS, "joint_attention: o_vis and o_cond overlap");
+  // the split tail writes key-range results into the workspace while other workgroups read the
+  // inputs and write the outputs: it must be disjoint from all of them
+  if (workspace && workspace_bytes > 0) {
+    for (int i = 0; i < 6; ++i)
+      if (nin[i] > 0 && overlaps(workspace, workspace_bytes, ins[i],
+                                 span(B * nin[i], hd, in_row_stride, i % 3 == 2 ? v_dtype : qk_dtype)))
+        return fail(MMDIT_ERR_ALIAS, "joint_attention: workspace overlaps an input");
+    for (int o = 0; o < 2; ++o)
+      if (nout[o] > 0 && overlaps(workspace, workspace_bytes, outs[o], span(B * nout[o], hd, out_row_stride, out_dtype)))
+        return fail(MMDIT_ERR_ALIAS, "joint_attention: workspace overlaps an output");
+    if (lse && overlaps(workspace, workspace_bytes, lse, (size_t)(B * H * (n_vis + n_cond)) * 4))
+      return fail(MMDIT_ERR_ALIAS, "joint_attention: workspace overlaps lse");
+  }
   return launch_joint_attention(q_vis, k_vis, v_vis, n_vis, q_cond, k_cond, v_cond, n_cond, qk_dtype, v_dtype,
                                 in_row_stride, B, H, softmax_scale, o_vis, o_cond, out_dtype,
                                 out_row_stride, lse, static_cast<hipStream_t>(stream), static_cast<float*>(workspace),
@@ -315,6 +328,38 @@ int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis, con
       return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: one stream spans 2 GiB or more per batch item");
   }
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: lse 4-byte aligned");
+  // outputs (and the split tail's workspace) must be disjoint from every operand and from
+  // one another: other workgroups are still reading the operands while they are written
+  {
+    const size_t nlse = lse ? (size_t)(B * H * (n_vis + n_cond)) * 4 : 0;
+    const size_t nvs = (size_t)(B * H * D) * 4;
+    size_t nout[2] = {0, 0};
+    for (int s = 0; s < 2; ++s) nout[s] = n[s] > 0 ? span(B * n[s], H * D, out_row_stride, out_dtype) : 0;
+    struct Span { const void* p; size_t n; };
+    Span ops[11];
+    int nops = 0;
+    for (int s = 0; s < 2; ++s) {
+      if (n[s] == 0) continue;
+      const mmdit_attn8_stream* o = seg[s];
+      const int64_t nb = (n[s] + 63) / 64;
+      ops[nops++] = {o->q8, (size_t)(B * n[s] * H * D)};
+      ops[nops++] = {o->q_scale, (size_t)(B * H * n[s]) * 4};
+      ops[nops++] = {o->k8, (size_t)(B * n[s] * H * D)};
+      ops[nops++] = {o->k_scale, (size_t)(B * H * nb) * 4};
+      ops[nops++] = {o->v8t, (size_t)(B * H * D * nb * 64)};
+    }
+    ops[nops++] = {v_scale, nvs};
+    const Span wr[4] = {{outs[0], nout[0]}, {outs[1], nout[1]}, {lse, nlse},
+                        {workspace, workspace ? workspace_bytes : 0}};
+    for (int w = 0; w < 4; ++w) {
+      for (int i = 0; i < nops; ++i)
+        if (overlaps(wr[w].p, wr[w].n, ops[i].p, ops[i].n))
+          return fail(MMDIT_ERR_ALIAS, "joint_attention_8bit: an output or the workspace overlaps an operand");
+      for (int v = w + 1; v < 4; ++v)
+        if (overlaps(wr[w].p, wr[w].n, wr[v].p, wr[v].n))
+          return fail(MMDIT_ERR_ALIAS, "joint_attention_8bit: outputs, lse and workspace must not overlap");
+    }
+  }
   return launch_joint_attention_8bit(seg, n, v_scale, B, H, softmax_scale, o_vis, o_cond, out_dtype, out_row_stride,
                                      lse, static_cast<hipStream_t>(stream), static_cast<float*>(workspace),
                                      workspace ? workspace_bytes : 0);
