@@ -488,11 +488,13 @@ def fp8_linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndar
 #       keys of one stream); V has one FP8 scale per (head, channel) over all keys of both
 #       streams; each scale follows r25 (qmax 127 for INT8, 448 for E4M3; INT8 codes are
 #       rint(x * (1/s)) clamped to +-127, ties to even);
-#   r27 logits in log2 units y = RN32(acc * c) with c = RN32(s_q * RN32(s_k * RN32(scale *
-#       log2(e)))), acc the exact integer dot product; the row reference M = ceil(max_j y);
-#       P' = RN32(2^RN32(acc * c + 8 - M)) rounded to E4M3 (so P' <= 256); the row sum uses
-#       the same E4M3 values: O = (sum_j P'_j V^_j) / (sum_j P'_j), V^ the dequantized values.
-# The rounding decisions (codes, P') are taken in float32 as the kernel takes them.
+#   r27 logits in log2 units y = acc * s_q * s_k * scale * log2(e), acc the exact integer dot
+#       product of the codes and s_q, s_k the float32 scales of r25; the row reference is the
+#       integer M = ceil(max_j y); each weight is the E4M3 rounding of the exact value
+#       2^(y + 8 - M) (so P' <= 256); the row sum adds the same E4M3 weights:
+#       O = (sum_j P'_j V^_j) / (sum_j P'_j), V^ the dequantized values.
+# The codes and scales of Q, K and V are the r25 rule (an f32 product rounded); everything
+# after them (logits, reference, weights, sums) is evaluated in float64.
 
 LOG2E = 1.4426950408889634
 ATT8_KEY_BLOCK = 64
@@ -556,7 +558,7 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
     b, _, h, d = q_vis.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    kc = np.float32(np.float32(scale) * np.float32(LOG2E))
+    kc = float(scale) * LOG2E
     qa, sqa, ka, ska = attn8_quantize_stream(q_vis, k_vis)
     qc, sqc, kcd, skc = attn8_quantize_stream(q_cond, k_cond)
     v8v, v8c, sv = attn8_quantize_v(v_vis, v_cond)
@@ -565,7 +567,7 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
     v8 = np.concatenate([v8v, v8c], axis=1)
     blk = lambda s_, n: np.repeat(s_, ATT8_KEY_BLOCK, axis=2)[:, :, :n]    # noqa: E731
     skj = np.concatenate([blk(ska, k_vis.shape[1]), blk(skc, k_cond.shape[1])], axis=2)   # [B, H, N]
-    skcj = (skj * kc).astype(np.float32)
+    skcj = skj.astype(np.float64) * kc
 
     def run(q8, sq, rows):
         if rows is not None:
@@ -578,12 +580,10 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
                 kk = k8[bi, :, hi, :]
                 for i0 in range(0, nq, chunk):
                     acc = q8[bi, i0:i0 + chunk, hi, :] @ kk.T                # exact integers
-                    c = (sq[bi, i0:i0 + chunk, hi][:, None] * skcj[bi, hi][None, :]).astype(np.float32)
-                    c = c.astype(np.float64)
-                    y = (acc * c).astype(np.float32)
-                    m = np.ceil(y.max(axis=1, keepdims=True).astype(np.float64))
-                    z = (acc * c + (8.0 - m)).astype(np.float32).astype(np.float64)
-                    p = fp8_e4m3_round(np.exp2(z).astype(np.float32))
+                    c = sq[bi, i0:i0 + chunk, hi].astype(np.float64)[:, None] * skcj[bi, hi][None, :]
+                    y = acc * c                                              # log2 units
+                    m = np.ceil(y.max(axis=1, keepdims=True))
+                    p = fp8_e4m3_round(np.exp2(y + (8.0 - m)))
                     ell = p.sum(axis=1, keepdims=True)
                     out[bi, i0:i0 + chunk, hi, :] = (p @ v8[bi, :, hi, :]) * sv[bi, hi][None, :] / ell
                     lse[bi, hi, i0:i0 + chunk] = np.log(ell[:, 0]) + (m[:, 0] - 8.0) * math.log(2.0)

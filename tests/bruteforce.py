@@ -231,8 +231,8 @@ def attention_8bit(q_rows, k_rows, v_rows, seg_of_key, scale, round_fp8):
     and value vectors in any order, seg_of_key[j] = (stream, position in that stream).
     INT8: one scale per query row, one per 64-key block of a stream; V: one E4M3 scale per
     channel over all keys.  Scales amax / qmax in float32, codes from x * (1/s) in float32.
-    Logits in log2 units rounded to float32; reference M = ceil of the row's max; weights
-    2^(logit - M + 8) rounded to float32 and then to E4M3; O = sum P V / sum P."""
+    Logits in log2 units acc * s_q * s_k * scale * log2(e) as python floats; reference M =
+    ceil of the row's max; weights 2^(logit - M + 8) rounded to E4M3; O = sum P V / sum P."""
     import numpy as np
     f32 = np.float32
 
@@ -254,18 +254,17 @@ def attention_8bit(q_rows, k_rows, v_rows, seg_of_key, scale, round_fp8):
     sv = [scale_of([v_rows[j][c] for j in range(len(v_rows))], 448.0) for c in range(d)]
     v8 = [[round_fp8(float(min(max(f32(f32(v_rows[j][c]) * f32(f32(1.0) / sv[c])), f32(-448)), f32(448))))
            for c in range(d)] for j in range(len(v_rows))]
-    kc = f32(f32(scale) * f32(1.4426950408889634))
+    kc = float(scale) * math.log2(math.e)
     outs = []
     for qv, _ in q_rows:
         sq = scale_of(qv, 127.0)
         q8 = int8(qv, sq)
-        accs, cs = [], []
+        y = []
         for j, (sg, pos) in enumerate(seg_of_key):
-            accs.append(sum(a * b for a, b in zip(q8, k8[j])))
-            cs.append(float(f32(sq * f32(ks[(sg, pos // 64)] * kc))))
-        y = [float(f32(a * c)) for a, c in zip(accs, cs)]
+            acc = sum(a * b for a, b in zip(q8, k8[j]))                  # python int, exact
+            y.append(acc * float(sq) * float(ks[(sg, pos // 64)]) * kc)
         m = math.ceil(max(y))
-        p = [round_fp8(float(f32(2.0 ** float(f32(a * c + (8 - m)))))) for a, c in zip(accs, cs)]
+        p = [round_fp8(2.0 ** (yj + 8 - m)) for yj in y]
         ell = sum(p)
         outs.append([sum(p[j] * v8[j][c] for j in range(len(p))) * float(sv[c]) / ell for c in range(d)])
     return outs

@@ -229,14 +229,14 @@ def _att8_variant(floor=False, shift=8.0, exact_sum=False):
           chunk=1024, return_lse=False):
         b, _, h, d = q_vis.shape
         scale = 1.0 / math.sqrt(d) if scale is None else scale
-        kc = np.float32(np.float32(scale) * np.float32(om.LOG2E))
+        kc = float(scale) * om.LOG2E
         qa, sqa, ka, ska = om.attn8_quantize_stream(q_vis, k_vis)
         qc, sqc, kcd, skc = om.attn8_quantize_stream(q_cond, k_cond)
         v8v, v8c, sv = om.attn8_quantize_v(v_vis, v_cond)
         k8 = np.concatenate([ka, kcd], axis=1)
         v8 = np.concatenate([v8v, v8c], axis=1)
         blk = lambda s_, n: np.repeat(s_, 64, axis=2)[:, :, :n]  # noqa: E731
-        skcj = (np.concatenate([blk(ska, k_vis.shape[1]), blk(skc, k_cond.shape[1])], axis=2) * kc).astype(np.float32)
+        skcj = np.concatenate([blk(ska, k_vis.shape[1]), blk(skc, k_cond.shape[1])], axis=2).astype(np.float64) * kc
 
         def run(q8, sq, rows):
             if rows is not None:
@@ -245,11 +245,10 @@ def _att8_variant(floor=False, shift=8.0, exact_sum=False):
             for bi in range(b):
                 for hi in range(h):
                     acc = q8[bi, :, hi, :] @ k8[bi, :, hi, :].T
-                    c = (sq[bi, :, hi][:, None] * skcj[bi, hi][None, :]).astype(np.float32).astype(np.float64)
-                    y = (acc * c).astype(np.float32).astype(np.float64)
+                    c = sq[bi, :, hi].astype(np.float64)[:, None] * skcj[bi, hi][None, :]
+                    y = acc * c
                     m = (np.floor if floor else np.ceil)(y.max(axis=1, keepdims=True))
-                    z = (acc * c + (shift - m)).astype(np.float32).astype(np.float64)
-                    pe = np.exp2(z).astype(np.float32).astype(np.float64)
+                    pe = np.exp2(y + (shift - m))
                     p = om.fp8_e4m3_round(pe)
                     ell = (pe if exact_sum else p).sum(axis=1, keepdims=True)
                     out[bi, :, hi, :] = (p @ v8[bi, :, hi, :]) * sv[bi, hi][None, :] / ell
