@@ -1,15 +1,19 @@
 """GPU parity of the 8-bit joint attention (INT8 Q K^T, FP8 E4M3 P V, f32 accumulation)
 against the float64 oracle's definition of the same quantized method.
 
-The operand codes and scales are integer-valued decisions taken in f32 on both sides and are
-compared bit for bit.  For the attention output the codes are identical and the integer
-products exact; what separates the two sides is
+The operand codes and scales (the quantization rule, an f32 product rounded) are compared bit
+for bit.  For the attention output the codes are identical and the integer products exact;
+the oracle then evaluates the logits, the integer reference, the weights 2^(y + 8 - M) and
+their E4M3 rounding in float64.  What separates the kernel from it is
   (a) the FP8 MFMA's inexact sum of its 64 products (up to ~1e-4 of its result's rms), and
-  (b) the f32 value of 2^(acc c + 8 - m) that decides each weight's E4M3 code: the kernel
-      forms it against its running integer reference and with the hardware exp2, so a value
-      within an f32 ulp of an E4M3 rounding boundary can land one E4M3 step (1/16 to 1/8 of
-      the weight) away.  One such weight moves its row by (step) |V_j - O| / sum P', which at
-      ~1.4 k keys reaches a few 1e-3 of the output's rms and shrinks as the sequence grows.
+  (b) the kernel's f32 logits (its factor s_q s_k scale log2(e) and the product with the
+      integer dot product are rounded to f32, and exp2 is the hardware's): a weight whose exact
+      value lies within a few f32 ulps of an E4M3 rounding boundary can land one E4M3 step
+      (1/16 to 1/8 of the weight) away, and a row maximum within an f32 ulp of an integer can
+      move the reference M by one, which rescales every weight of the row by 2 exactly and
+      changes only weights in E4M3's subnormal range (below 2^-6 of the 2^8 ceiling).  One
+      stepped weight moves its row by (step) |V_j - O| / sum P', a few 1e-3 of the output's
+      rms at ~1.4 k keys, less as the sequence grows.
 Bars: rms(err) / rms <= 2e-4 (systematic errors, which move every element) and
 max|err| / rms <= 1e-2 (single E4M3 steps; a wrong formula or layout misses by order one,
 and the method's own deviation from exact attention, logged, is ~4 % rms and ~25 % max)."""
@@ -22,7 +26,7 @@ import torch
 import oracle
 import video_diffusion_transformer_mmdit_amd as mm
 import workloads as wl
-from tests.util import assert_close, log, to_dev, to_host64
+from tests.util import assert_close, log, parity_rows, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 TOL_ATT8 = 1e-2
@@ -44,13 +48,17 @@ def _inputs(cfg, seed=None):
     return dev, f64
 
 
-def _unpermute_v(v8t, n):
-    """v8t [B, H, D, np] in the kernel's key order -> codes [B, n, H, D]."""
+def _logical_v(v8t):
+    """v8t [B, H, D, np] in the kernel's key order -> [B, H, D, np] in key order."""
     k = np.arange(v8t.shape[-1])
     t, kk = k // 64, k % 64
     pos = 16 * (2 * (kk >> 5) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 3) + (kk & 3)
-    logical = v8t[..., t * 64 + pos]                       # [B, H, D, np] in key order
-    return np.transpose(logical[..., :n], (0, 3, 1, 2))
+    return v8t[..., t * 64 + pos]
+
+
+def _unpermute_v(v8t, n):
+    """v8t [B, H, D, np] in the kernel's key order -> codes [B, n, H, D]."""
+    return np.transpose(_logical_v(v8t)[..., :n], (0, 3, 1, 2))
 
 
 def _check_operands(ops, f64, n_vis, n_cond):
@@ -68,10 +76,11 @@ def _check_operands(ops, f64, n_vis, n_cond):
         np.testing.assert_array_equal(t["k_scale"].cpu().numpy(), sk)
         got_v = _unpermute_v(t["v8t"].cpu().numpy(), n)
         np.testing.assert_array_equal(got_v, oracle.fp8_e4m3_code(v8))
-        pad = t["v8t"].cpu().numpy()
-        if pad.shape[-1] > n:                              # padding keys hold zero codes
-            k = np.arange(pad.shape[-1])
-            assert np.all(pad[..., k % 64 >= 0][..., :0] == 0)
+        # keys past n in the last 64-key block are multiplied by P' = 0 in the FP8 MFMA: their
+        # codes must be +0 (a NaN code would poison the whole row)
+        tail = _logical_v(t["v8t"].cpu().numpy())[..., n:]
+        assert tail.shape[-1] == (-n) % 64
+        assert np.all(tail == 0), "padding keys must hold zero codes"
     np.testing.assert_array_equal(ops.v_scale.cpu().numpy(), sv)
 
 
@@ -103,23 +112,32 @@ def test_attention_8bit_matches_oracle(cfg):
         f"max {oracle.rel_max_err(to_host64(ov), ev):.3e}")
 
 
-def test_attention_8bit_480p_sampled_rows():
-    """The 480p workload (32760 visual + 512 conditioning tokens, 24 heads) in the launch the
-    bench times, every operand code checked and sampled query rows against the oracle."""
-    cfg = wl.ATTN_480P
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,n_rows_v,n_rows_c", [(wl.ATTN_480P, 192, 64), (wl.ATTN_720P, 96, 32)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_attention_8bit_full_size_sampled_rows(cfg, n_rows_v, n_rows_c):
+    """The 480p and 720p workloads (32760 / 75600 visual + 512 conditioning tokens, 24 heads)
+    in the launch the bench times (with the split-tail workspace): every operand code checked,
+    and sampled query rows (the first and last 32, a band over the last query tiles, seeded
+    random rows) of every head against the oracle."""
     dev, f64 = _inputs(cfg)
     ops = mm.attn8_quantize(dev["q_vis"], dev["k_vis"], dev["v_vis"], dev["q_cond"], dev["k_cond"], dev["v_cond"])
-    ov, oc = mm.joint_attention_8bit(ops)
+    ws = torch.empty(mm.ATTN8_SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+    ov, oc = mm.joint_attention_8bit(ops, workspace=ws)
     torch.cuda.synchronize()
     log("  operands")
     _check_operands(ops, f64, cfg.n_vis, cfg.n_cond)
-    rows_v = wl.sample_rows(cfg.n_vis, 48, seed=7)
-    rows_c = wl.sample_rows(cfg.n_cond, 16, seed=8)
-    log("  oracle rows")
+    rows_v = parity_rows(cfg.n_vis, n_rows_v, seed=7, bands=[(cfg.n_vis - 1536, cfg.n_vis, 97)])
+    rows_c = parity_rows(cfg.n_cond, n_rows_c, seed=8)
+    got_v, got_c = to_host64(ov)[:, rows_v], to_host64(oc)[:, rows_c]
+    del dev, ops, ov, oc, ws
+    torch.cuda.empty_cache()
+    log(f"  oracle rows: {rows_v.size} visual, {rows_c.size} conditioning")
     rv, rc = oracle.joint_attention_8bit(f64["q_vis"], f64["k_vis"], f64["v_vis"], f64["q_cond"], f64["k_cond"],
                                          f64["v_cond"], vis_rows=rows_v, cond_rows=rows_c)
-    _close8("o_vis[rows]", to_host64(ov)[:, rows_v], rv)
-    _close8("o_cond[rows]", to_host64(oc)[:, rows_c], rc)
+    _close8("o_vis[rows]", got_v, rv)
+    _close8("o_cond[rows]", got_c, rc)
 
 
 def test_attention_8bit_zero_keys_give_mean_of_values():

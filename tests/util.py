@@ -68,3 +68,20 @@ def assert_close_stored(name, got, ref, dtype, tol):
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert e <= tol, f"{name}: {e:.3e} > {tol:.0e}"
     return e
+
+
+def parity_rows(n: int, k: int, seed: int, bands=()) -> np.ndarray:
+    """Sorted distinct query rows of a sampled full-size comparison: the first and last 32
+    rows, every row of each (start, stop, step) band, then seeded random rows until there
+    are k in all (every row when k >= n)."""
+    if k >= n:
+        return np.arange(n)
+    must = [np.arange(min(32, n)), np.arange(max(0, n - 32), n)]
+    for a, b, s in bands:
+        must.append(np.arange(max(0, a), min(n, b), s))
+    must = np.unique(np.concatenate(must))
+    rest = np.setdiff1d(np.arange(n), must)
+    extra = max(0, k - must.size)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(rest, size=min(extra, rest.size), replace=False)
+    return np.unique(np.concatenate([must, pick]))
