@@ -275,3 +275,33 @@ def test_host_workspace_or_output_raises_before_launch():
     with pytest.raises(mm.MmditError, match="o_vis must be a GPU tensor"):
         mm.joint_attention_8bit(ops, o_vis=torch.empty((1, 300, 2, 128)))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("B,n_vis,n_cond", [(1, 1000, 77), (2, 333, 5), (1, 64, 0)])
+def test_nan_rows_past_each_segment_are_never_read(B, n_vis, n_cond):
+    """Q/K/V of each stream are views of buffers whose rows past the segment (and past the last
+    batch item) are NaN: the kernels' partial tiles must take zeros there (their loads stop at
+    the segment's end), so every output is finite and matches the oracle.  The 8-bit path's
+    quantizer and attention read the same views."""
+    H, D, pad = 3, 128, 300
+    def padded(n, seed):
+        full = torch.full((B * n + pad, 3, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        full[:B * n] = _rand((B * n, 3, H, D), seed)
+        return full[:B * n].view(B, n, 3, H, D)
+    pv, pc = padded(n_vis, 61), padded(n_cond, 62)
+    qv, kv, vv = pv[:, :, 0], pv[:, :, 1], pv[:, :, 2]
+    qc, kc, vc = (pc[:, :, 0], pc[:, :, 1], pc[:, :, 2]) if n_cond else (None, None, None)
+    ws = torch.empty(mm.ATTN_SPLIT_BYTES, dtype=torch.uint8, device="cuda")
+    o_v, o_c = mm.joint_attention(qv, kv, vv, qc, kc, vc, workspace=ws)
+    ops = mm.attn8_quantize(qv, kv, vv, qc, kc, vc)
+    e_v, e_c = mm.joint_attention_8bit(ops, workspace=ws)
+    torch.cuda.synchronize()
+    for nm, t in (("o_vis", o_v), ("o_cond", o_c), ("o8_vis", e_v), ("o8_cond", e_c)):
+        if t is not None and t.numel():
+            assert torch.isfinite(t).all(), f"{nm}: non-finite output (a padding row was read)"
+    for b in range(B):
+        f = lambda t: to_host64(t[b:b + 1]) if t is not None else np.zeros((1, 0, H, D))  # noqa: E731
+        r_v, r_c = oracle.joint_attention(f(qv), f(kv), f(vv), f(qc), f(kc), f(vc))
+        assert_close(f"o_vis[b={b}]", f(o_v), r_v, 2e-2)
+        if n_cond:
+            assert_close(f"o_cond[b={b}]", f(o_c), r_c, 2e-2)

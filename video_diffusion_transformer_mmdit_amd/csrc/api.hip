@@ -1,5 +1,6 @@
 // extern "C" entry points of libmmdit: argument validation, then dispatch to the kernels.
 // Every check runs before anything is enqueued, so a rejected call touches no HIP state.
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -15,6 +16,18 @@ int fail(int status, const std::string& msg) {
   g_last_error = std::string(mmdit_status_str(status)) + ": " + msg;
   return status;
 }
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];   // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MMDIT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -37,6 +50,7 @@ static size_t span(int64_t rows, int64_t row_elems, int64_t stride, int dt) {
 
 int validate_rope(const mmdit_rope3d* r, int64_t N, int64_t D) {
   if (r->T < 1 || r->H < 1 || r->W < 1) return fail(MMDIT_ERR_SHAPE, "rope: T, H, W must be >= 1");
+  if (!extents_ok({r->T, r->H, r->W})) return fail(MMDIT_ERR_SHAPE, "rope: T * H * W too large");
   if (r->d_t < 0 || r->d_h < 0 || r->d_w < 0 || (r->d_t & 1) || (r->d_h & 1) || (r->d_w & 1))
     return fail(MMDIT_ERR_SHAPE, "rope: band widths must be even and >= 0");
   if ((int64_t)r->d_t + r->d_h + r->d_w != D) return fail(MMDIT_ERR_SHAPE, "rope: d_t + d_h + d_w != D");
@@ -77,6 +91,7 @@ int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch
   if (B < 0 || N < 0 || C < 8 || C % 8 || C > 8192)
     return fail(MMDIT_ERR_SHAPE, "modulate_ln: need B, N >= 0 and C a multiple of 8 in [8, 8192]");
   if (mod_stride < C) return fail(MMDIT_ERR_SHAPE, "modulate_ln: mod_stride < C");
+  if (!extents_ok({B, N, C}) || !extents_ok({B, mod_stride})) return fail(MMDIT_ERR_SHAPE, "modulate_ln: sizes too large");
   if (!(eps >= 0.f)) return fail(MMDIT_ERR_SHAPE, "modulate_ln: eps must be >= 0");
   if (x_dtype != MMDIT_F32 && x_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "modulate_ln: x must be f32 or bf16");
   if (branch && branch_dtype != MMDIT_F32 && branch_dtype != MMDIT_BF16)
@@ -107,6 +122,8 @@ int mmdit_qk_norm_rope(const void* q, const void* k, int in_dtype, int64_t in_ro
   g_last_error.clear();
   if (D != 128) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: D must be 128");
   if (B < 0 || N < 0 || H < 1 || H > 4096) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: need B, N >= 0, 1 <= H <= 4096");
+  if (!extents_ok({B, N, in_row_stride}) || !extents_ok({B, N, out_row_stride}))
+    return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: sizes too large");
   if (in_row_stride < H * D || out_row_stride < H * D) return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: row stride < H*D");
   if (scale_head_stride != 0 && scale_head_stride != D)
     return fail(MMDIT_ERR_SHAPE, "qk_norm_rope: scale_head_stride must be 0 or D");
@@ -160,8 +177,14 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
   if (D != 128) return fail(MMDIT_ERR_SHAPE, "joint_attention: D must be 128");
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(MMDIT_ERR_ALIGN, "joint_attention: workspace must be 256-byte aligned");
-  if (B < 0 || H < 1 || n_vis < 0 || n_cond < 0 || n_vis + n_cond < 1)
+  if (!extents_ok({B}) || !extents_ok({H}) || !extents_ok({n_vis}) || !extents_ok({n_cond}))
+    return fail(MMDIT_ERR_SHAPE, "joint_attention: sizes must be >= 0 and below 2^31");
+  if (H < 1 || n_vis + n_cond < 1)
     return fail(MMDIT_ERR_SHAPE, "joint_attention: need B >= 0, H >= 1, n_vis + n_cond >= 1");
+  if (H > 4096 || !extents_ok({B, n_vis, in_row_stride}) || !extents_ok({B, n_cond, in_row_stride}) ||
+      !extents_ok({B, n_vis, out_row_stride}) || !extents_ok({B, n_cond, out_row_stride}) ||
+      !extents_ok({B, H, n_vis + n_cond}))
+    return fail(MMDIT_ERR_SHAPE, "joint_attention: sizes too large");
   if (in_row_stride < H * D || out_row_stride < H * D) return fail(MMDIT_ERR_SHAPE, "joint_attention: row stride < H*D");
   if (!(softmax_scale > 0.f)) return fail(MMDIT_ERR_SHAPE, "joint_attention: softmax_scale must be > 0");
   if (!valid_dtype(qk_dtype) || !valid_dtype(v_dtype) || ((qk_dtype == MMDIT_F32) != (v_dtype == MMDIT_F32)))
@@ -216,9 +239,10 @@ int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, in
                  const void* res, int res_dtype, const float* gate, int64_t gate_stride,
                  int64_t rows_per_batch, void* stream) {
   g_last_error.clear();
-  if (M < 0 || N < 0 || K < 64 || K % 64 || N % 4)
+  if (!extents_ok({M}) || !extents_ok({N}) || !extents_ok({K}) || K < 64 || K % 64 || N % 4)
     return fail(MMDIT_ERR_SHAPE, "linear: need M, N >= 0, N a multiple of 4 and K a positive multiple of 64");
-  if ((M + 256) * K * 2 >= ((int64_t)1 << 31) || (N + 256) * K * 2 >= ((int64_t)1 << 31))
+  if (!extents_ok({M + 256, K}) || !extents_ok({N + 256, K}) || !extents_ok({M, N}) || !extents_ok({rows_per_batch}) ||
+      !extents_ok({gate_stride}) || (M + 256) * K * 2 >= ((int64_t)1 << 31) || (N + 256) * K * 2 >= ((int64_t)1 << 31))
     return fail(MMDIT_ERR_SHAPE, "linear: x or w too large for 32-bit buffer offsets");
   if (x_dtype != MMDIT_BF16 && x_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "linear: x/w must be bf16 or f16");
   if (bias && bias_dtype != MMDIT_F32 && bias_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear: bias must be f32 or bf16");
@@ -253,9 +277,13 @@ int mmdit_attn8_quantize(const void* q_vis, const void* k_vis, const void* v_vis
                          const mmdit_attn8_stream* vis, const mmdit_attn8_stream* cond, float* v_scale,
                          void* stream) {
   g_last_error.clear();
-  if (B < 0 || H < 0 || n_vis < 0 || n_cond < 0) return fail(MMDIT_ERR_SHAPE, "attn8_quantize: negative size");
+  if (!extents_ok({B}) || !extents_ok({H}) || !extents_ok({n_vis}) || !extents_ok({n_cond}) || !extents_ok({in_row_stride}))
+    return fail(MMDIT_ERR_SHAPE, "attn8_quantize: sizes must be >= 0 and below 2^31");
   if (D != 128) return fail(MMDIT_ERR_SHAPE, "attn8_quantize: D must be 128");
   if (!valid_dtype(in_dtype)) return fail(MMDIT_ERR_DTYPE, "attn8_quantize: inputs must be f32, bf16 or f16");
+  if (H > 4096 || !extents_ok({B, n_vis + 64, in_row_stride}) || !extents_ok({B, n_cond + 64, in_row_stride}) ||
+      !extents_ok({B, H, 128, n_vis + 64}) || !extents_ok({B, H, 128, n_cond + 64}))
+    return fail(MMDIT_ERR_SHAPE, "attn8_quantize: sizes too large");
   if (in_row_stride < H * D || in_row_stride % 8) return fail(MMDIT_ERR_ALIGN, "attn8_quantize: row stride >= H*D, a multiple of 8");
   if (B == 0 || H == 0 || n_vis + n_cond == 0) return MMDIT_OK;
   if (!v_scale) return fail(MMDIT_ERR_NULL, "attn8_quantize: v_scale required");
@@ -302,10 +330,14 @@ int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis, con
                                int64_t out_row_stride, float* lse, void* workspace, size_t workspace_bytes,
                                void* stream) {
   g_last_error.clear();
-  if (B < 0 || H < 0 || n_vis < 0 || n_cond < 0) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: negative size");
+  if (!extents_ok({B}) || !extents_ok({H}) || !extents_ok({n_vis}) || !extents_ok({n_cond}) || !extents_ok({out_row_stride}))
+    return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: sizes must be >= 0 and below 2^31");
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: workspace must be 256-byte aligned");
   if (D != 128) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: D must be 128");
+  if (H > 4096 || !extents_ok({B, n_vis + 64, H, D}) || !extents_ok({B, n_cond + 64, H, D}) ||
+      !extents_ok({B, n_vis, out_row_stride}) || !extents_ok({B, n_cond, out_row_stride}))
+    return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: sizes too large");
   if (!valid_dtype(out_dtype)) return fail(MMDIT_ERR_DTYPE, "joint_attention_8bit: bad out dtype");
   if (out_row_stride < H * D || out_row_stride % 8) return fail(MMDIT_ERR_ALIGN, "joint_attention_8bit: out row stride >= H*D, a multiple of 8");
   if (!(softmax_scale > 0.f) || !(softmax_scale < 3.0e38f)) return fail(MMDIT_ERR_SHAPE, "joint_attention_8bit: softmax_scale must be positive and finite");
@@ -371,6 +403,7 @@ int mmdit_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, i
   if (rows < 0 || cols < 8 || cols % 8 || cols > ((int64_t)1 << 30))
     return fail(MMDIT_ERR_SHAPE, "quantize_fp8: cols must be a positive multiple of 8");
   if (!valid_dtype(x_dtype)) return fail(MMDIT_ERR_DTYPE, "quantize_fp8: x must be f32, bf16 or f16");
+  if (!extents_ok({rows, cols})) return fail(MMDIT_ERR_SHAPE, "quantize_fp8: sizes too large");
   if (rows == 0) return MMDIT_OK;
   if (!x || !q || !scales) return fail(MMDIT_ERR_NULL, "quantize_fp8: x, q, scales required");
   if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(scales) & 3))
@@ -388,9 +421,10 @@ int mmdit_linear_fp8(const void* xq, const float* x_scale, const void* wq, const
                      int epilogue, const void* res, int res_dtype, const float* gate, int64_t gate_stride,
                      int64_t rows_per_batch, void* stream) {
   g_last_error.clear();
-  if (M < 0 || N < 0 || K < 64 || K % 64 || N % 4)
+  if (!extents_ok({M}) || !extents_ok({N}) || !extents_ok({K}) || K < 64 || K % 64 || N % 4)
     return fail(MMDIT_ERR_SHAPE, "linear_fp8: need M, N >= 0, N a multiple of 4 and K a positive multiple of 64");
-  if ((M + 256) * K >= ((int64_t)1 << 31) || (N + 256) * K >= ((int64_t)1 << 31))
+  if (!extents_ok({M + 256, K}) || !extents_ok({N + 256, K}) || !extents_ok({M, N}) || !extents_ok({rows_per_batch}) ||
+      !extents_ok({gate_stride}) || (M + 256) * K >= ((int64_t)1 << 31) || (N + 256) * K >= ((int64_t)1 << 31))
     return fail(MMDIT_ERR_SHAPE, "linear_fp8: x or w too large for 32-bit buffer offsets");
   if (bias && bias_dtype != MMDIT_F32 && bias_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "linear_fp8: bias must be f32 or bf16");
   if (!valid_dtype(y_dtype)) return fail(MMDIT_ERR_DTYPE, "linear_fp8: bad y dtype");
@@ -425,6 +459,7 @@ int mmdit_modulation(const void* w_mod, const void* b_mod, const void* tvec, int
   g_last_error.clear();
   if (B < 0 || C6 < 0 || Dt < 8 || Dt % 8) return fail(MMDIT_ERR_SHAPE, "modulation: Dt must be a positive multiple of 8");
   if (Dt > 16384) return fail(MMDIT_ERR_SHAPE, "modulation: Dt must be <= 16384");
+  if (!extents_ok({B, C6}) || !extents_ok({C6, Dt})) return fail(MMDIT_ERR_SHAPE, "modulation: sizes too large");
   if (t_dtype != MMDIT_F32 && t_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "modulation: tvec must be f32 or bf16");
   if (B == 0 || C6 == 0) return MMDIT_OK;
   if (!w_mod || !tvec || !mod) return fail(MMDIT_ERR_NULL, "modulation: w_mod, tvec, mod required");
@@ -440,6 +475,7 @@ static int lite_regroup(int layout, const char* name, const void* x, int x_dtype
   if (B < 0 || T < 0 || H < 2 || W < 2 || H % 2 || W % 2)
     return fail(MMDIT_ERR_SHAPE, n + ": the grid needs T >= 0 and an even H, W >= 2 (the merge is defined for even grids)");
   if (C < 256 || C % 256) return fail(MMDIT_ERR_SHAPE, n + ": C must be a positive multiple of 256");
+  if (!extents_ok({B, T, H, W, C})) return fail(MMDIT_ERR_SHAPE, n + ": sizes too large");
   if (x_dtype != MMDIT_BF16 && x_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, n + ": x and w must be bf16 or f16");
   if (bias && bias_dtype != MMDIT_F32 && bias_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, n + ": bias must be f32 or bf16");
   if (!valid_dtype(y_dtype)) return fail(MMDIT_ERR_DTYPE, n + ": bad y dtype");
@@ -478,6 +514,8 @@ int mmdit_timestep_embed(const float* t, int64_t B, const void* w1, const void* 
   if (B < 0 || freq_dim < 16 || freq_dim % 16 || hidden_dim < 8 || hidden_dim % 8 || Dt < 1)
     return fail(MMDIT_ERR_SHAPE, "timestep_embed: freq_dim a positive multiple of 16, hidden_dim of 8, Dt >= 1");
   if (freq_dim > 16384 || hidden_dim > 16384) return fail(MMDIT_ERR_SHAPE, "timestep_embed: freq_dim and hidden_dim must be <= 16384");
+  if (!extents_ok({B, hidden_dim}) || !extents_ok({B, Dt}) || !extents_ok({Dt, hidden_dim}))
+    return fail(MMDIT_ERR_SHAPE, "timestep_embed: sizes too large");
   if (!(max_period > 1.f) || !(max_period < 3.0e38f)) return fail(MMDIT_ERR_SHAPE, "timestep_embed: max_period must be a finite value > 1");
   if (w_dtype != MMDIT_F32 && w_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "timestep_embed: weights must be f32 or bf16");
   if (B == 0) return MMDIT_OK;

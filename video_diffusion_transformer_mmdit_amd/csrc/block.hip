@@ -23,6 +23,8 @@ static int validate_dims(const mmdit_block_dims* d, int64_t B, int64_t n_vis, in
   if (d->C > 8192 || d->F > 65536) return fail(MMDIT_ERR_SHAPE, "block: C <= 8192 and F <= 65536");
   if (d->Dt < 8 || d->Dt % 8) return fail(MMDIT_ERR_SHAPE, "block: Dt must be a positive multiple of 8");
   if (B < 1 || n_vis < 1 || n_cond < 0) return fail(MMDIT_ERR_SHAPE, "block: need B >= 1, n_vis >= 1, n_cond >= 0");
+  if (!extents_ok({B, n_vis, d->F}) || !extents_ok({B, n_cond, d->F}) || !extents_ok({B, 6, d->C}))
+    return fail(MMDIT_ERR_SHAPE, "block: sizes too large");
   if (d->Dt > 16384) return fail(MMDIT_ERR_SHAPE, "block: Dt must be <= 16384");
   if (d->qk_scale_head_stride != 0 && d->qk_scale_head_stride != d->D)
     return fail(MMDIT_ERR_SHAPE, "block: qk_scale_head_stride must be 0 or D");
@@ -88,6 +90,8 @@ int mmdit_block_fwd_events(const mmdit_block_dims* dims, const mmdit_stream_weig
                            size_t workspace_bytes, int64_t B, void* stream, void* const* events) {
   set_error("");
   if (!rope) return fail(MMDIT_ERR_NULL, "block: rope is required (visual grid)");
+  if (rope->T < 1 || rope->H < 1 || rope->W < 1 || !extents_ok({rope->T, rope->H, rope->W}))
+    return fail(MMDIT_ERR_SHAPE, "block: the visual grid must be non-empty and of a representable size");
   const int64_t n_vis = rope->T * rope->H * rope->W;
   int st = validate_dims(dims, B, n_vis, n_cond);
   if (st) return st;

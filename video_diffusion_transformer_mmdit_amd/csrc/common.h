@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <initializer_list>
 #include <string>
 
 #include "../../include/mmdit.h"
@@ -108,7 +109,23 @@ int fail(int status, const std::string& msg);
 int check_launch(const char* what);
 
 inline int dtype_size(int dt) { return dt == MMDIT_F32 ? 4 : dt == MMDIT_FP8_E4M3 ? 1 : 2; }
+
+// Compute units of the current device (queried once per device; 256 on MI355X).  The split-tail
+// heuristics size a launch's last round by it: one persistent-size workgroup per CU.
+int device_cu_count();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Size guard of the argument validators: every extent lies in [0, 2^31) and their product
+// (a zero extent counting as one) stays below 2^40, so that the validators' byte-span
+// arithmetic on such products cannot overflow int64.
+inline bool extents_ok(std::initializer_list<int64_t> xs) {
+  int64_t p = 1;
+  for (const int64_t x : xs) {
+    if (x < 0 || x >= ((int64_t)1 << 31)) return false;
+    if (__builtin_mul_overflow(p, x > 0 ? x : (int64_t)1, &p) || p >= ((int64_t)1 << 40)) return false;
+  }
+  return true;
+}
 
 // Internal launchers (validated arguments only).
 int launch_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
@@ -126,6 +143,10 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
                            float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
                            int64_t out_stride, float* lse, hipStream_t stream, float* split_ws = nullptr,
                            size_t split_ws_bytes = 0);
+
+// Bytes of key-range results the attention's split tail uses with an unlimited workspace (0:
+// the call does not split).
+size_t joint_attention_split_bytes(int64_t n_vis, int64_t n_cond, int64_t B, int64_t H, int qk_dtype, bool has_lse);
 
 struct GemmProblem {
   const void* x;      // [M, K]

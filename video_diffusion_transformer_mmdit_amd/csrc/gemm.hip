@@ -41,7 +41,6 @@ constexpr int GBM = 256, GBN = 256, GBK = 32;
 constexpr int GTHREADS = 256;
 constexpr int GROUP_M = 4;   // M-tiles per raster band (4 measured ~1 % faster than 2, 8 or 16)
 constexpr int G_TILE_BYTES = 256 * GBK * 2;   // one operand tile of one stage: 16 KiB
-constexpr int64_t G_ROUND = 256;              // workgroups the chip runs at once (one per CU)
 constexpr size_t G_PART_BYTES = 256 * 256 * 4;   // f32 partial sums of one tile
 
 struct GemmArgs {
@@ -230,6 +229,22 @@ __device__ __forceinline__ void gemm_epi_tail(const GemmProblem& P, int64_t N, i
   }
 }
 
+// Raw residual values of one lane's four consecutive outputs (f32: 16 bytes, bf16: 8 bytes),
+// loaded ahead of the rows that use them.
+template <int RES_DT> struct ResRaw;
+template <> struct ResRaw<MMDIT_F32> { float4 v; };
+template <> struct ResRaw<MMDIT_BF16> { uint2 v; };
+template <int RES_DT>
+__device__ __forceinline__ void res_load(const void* base, int64_t idx, ResRaw<RES_DT>& r) {
+  if constexpr (RES_DT == MMDIT_F32) r.v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+  else r.v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+}
+template <int RES_DT>
+__device__ __forceinline__ void res_unpack(const ResRaw<RES_DT>& r, float (&v)[4]) {
+  if constexpr (RES_DT == MMDIT_F32) { v[0] = r.v.x; v[1] = r.v.y; v[2] = r.v.z; v[3] = r.v.w; }
+  else { v[0] = lo_bf16(r.v.x); v[1] = hi_bf16(r.v.x); v[2] = lo_bf16(r.v.y); v[3] = hi_bf16(r.v.y); }
+}
+
 // Epilogue of a 256 x 256 tile through LDS, so that the residual loads and the output stores
 // run along rows: wave w restages its 128 x 128 block a quarter (32 rows, accumulators i = q)
 // at a time as f32 in its own LDS region, rows 132 floats apart (the 4-float pad spreads the
@@ -239,6 +254,10 @@ __device__ __forceinline__ void gemm_epi_tail(const GemmProblem& P, int64_t N, i
 // m, column n goes to column n % C of the full-grid token merged_row0(m) + (s / 2) W + s % 2,
 // s = n / C (a 128-wide block lies inside one s, as C is a multiple of 256).  `region` holds
 // 32 x 132 floats; the caller has made every wave's reads of the K stages complete.
+// Gated residual: the residual of a group of four rows is loaded while the previous group is
+// computed (the quarter's first group before its restaging), so the loads of consecutive
+// groups overlap instead of each group waiting a full memory round trip (all CUs finish their
+// K loops together, and the row-by-row epilogue was bound by the load latency of that burst).
 constexpr int G_EPI_STRIDE = 132;                        // floats per restaged row
 constexpr int G_EPI_BYTES = 32 * G_EPI_STRIDE * 4;       // one wave's quarter block: 16.5 KiB
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
@@ -259,8 +278,19 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
   if constexpr (FP8) sw = *P.w_scale;
   int sg = 0;
   if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 128) / args.c;
+  constexpr bool GRES = EPI == MMDIT_EPI_GATED_RES;
+  // residual of rows r0 + 2 k + g (k = 0..3) of quarter q
+  auto res_group = [&](int q, int r0, ResRaw<RES_DT> (&rr)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t m = m0 + wm * 128 + q * 32 + r0 + 2 * k + g;
+      if (m < M && n < N) res_load<RES_DT>(P.res, m * N + n, rr[k]);
+    }
+  };
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
+    ResRaw<RES_DT> rc[4], rn[4];
+    if constexpr (GRES) res_group(q, 0, rc);
     // accumulator (j, q) element e: row l32, column j * 32 + 8 (e / 4) + 4 g + e % 4 (written
     // element by element, which the compiler merges into 16-byte writes; spelled as float4
     // writes, it copied the accumulators out first and spilled)
@@ -269,7 +299,11 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
 #pragma unroll
       for (int e = 0; e < 16; ++e) region[l32 * G_EPI_STRIDE + j * 32 + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[j][q][e];
     __syncthreads();
+#pragma unroll
     for (int r0 = 0; r0 < 32; r0 += 8) {
+      if constexpr (GRES) {
+        if (r0 + 8 < 32) res_group(q, r0 + 8, rn);
+      }
       // four rows' reads in flight before the first store
       float4 a4[4];
 #pragma unroll
@@ -288,13 +322,26 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
         } else {
           v[0] = a.x + bias[0]; v[1] = a.y + bias[1]; v[2] = a.z + bias[2]; v[3] = a.w + bias[3];
         }
-        gemm_epi_tail<EPI, RES_DT>(P, N, m, n, v);
+        if constexpr (GRES) {
+          const int64_t b = (uint32_t)m / (uint32_t)P.rows_per_batch;
+          float r[4], gt[4];
+          res_unpack<RES_DT>(rc[k], r);
+          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = fmaf(gt[c], v[c], r[c]);
+        } else {
+          gemm_epi_tail<EPI, RES_DT>(P, N, m, n, v);
+        }
         if constexpr (LAYOUT == GEMM_SCATTER_Y) {
           const int64_t yr = (int64_t)merged_row0((int)m, args) + (sg >> 1) * args.w + (sg & 1);
           store4<Y_DT>(P.y, yr * args.c + (n - (int64_t)sg * args.c), v);
         } else {
           store4<Y_DT>(P.y, m * N + n, v);
         }
+      }
+      if constexpr (GRES) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rc[k] = rn[k];
       }
     }
     __syncthreads();
@@ -779,14 +826,17 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   a.full = a.tiles;
   a.split = 1;
   if (a.tiles == 0) return MMDIT_OK;
-  // Split tail: when the tiles fill R < 256 workgroup slots of the last round, cut each of
-  // those R tiles into S = 256 / R K ranges (at least 2, each of at least 2 stages) so that
-  // the last round runs on (nearly) every CU instead of R of them.
-  if (split_ws && x_dtype != MMDIT_FP8_E4M3 && a.tiles > G_ROUND) {
-    const int64_t R = a.tiles % G_ROUND;
+  // Split tail: when the tiles fill R < P workgroup slots of the last round (P = the CU
+  // count, one workgroup per CU), cut each of those R tiles into S = P / R K ranges (at
+  // least 2, each of at least 2 stages) so that the last round runs on (nearly) every CU
+  // instead of R of them.
+  const int64_t round = device_cu_count();
+  if (split_ws && x_dtype != MMDIT_FP8_E4M3 && a.tiles > round) {
+    const int64_t R = a.tiles % round;
     const int64_t stages = K / 64;   // K = 64 stages of the two-stage kernel
-    int64_t S = R ? G_ROUND / R : 0;
+    int64_t S = R ? round / R : 0;
     if (S > stages / 2) S = stages / 2;
+    if (R > 0 && S > (int64_t)(split_ws_bytes / ((size_t)R * G_PART_BYTES))) S = (int64_t)(split_ws_bytes / ((size_t)R * G_PART_BYTES));
     if (R > 0 && S >= 2 && (size_t)(R * S) * G_PART_BYTES <= split_ws_bytes) {
       a.full = a.tiles - R;
       a.split = (int)S;

@@ -69,7 +69,6 @@ struct AttnArgs {
   float* part;
 };
 
-constexpr int ATT_ROUND = 256;   // workgroups the chip runs at once (one per CU)
 // one key range's partial result for one query tile: O (256 x 128 f32) then (m, l) per query
 constexpr int64_t ATT_PART_FLOATS = 256 * 128 + 256 * 2;
 
@@ -651,6 +650,20 @@ static int attn_go(const AttnArgs& a, dim3 grid, int out_dtype, bool has_lse, hi
   return check_launch("joint_attention");
 }
 
+size_t joint_attention_split_bytes(int64_t n_vis, int64_t n_cond, int64_t B, int64_t H, int qk_dtype, bool has_lse) {
+  const int64_t N = n_vis + n_cond;
+  if (qk_dtype == MMDIT_F32 || has_lse || B < 1 || H < 1 || n_vis < 0 || n_cond < 0 || N < 1) return 0;
+  const int64_t items = ((N + ATT_BM - 1) / ATT_BM) * H * B;
+  const int64_t round = device_cu_count();
+  if (items <= round) return 0;
+  const int64_t R = items % round;
+  if (R == 0) return 0;
+  const int64_t ntiles = (n_vis + ATT_BN - 1) / ATT_BN + (n_cond + ATT_BN - 1) / ATT_BN;
+  int64_t S = round / R;
+  if (S > ntiles) S = ntiles;
+  return S >= 2 ? (size_t)(R * S * ATT_PART_FLOATS) * 4 : 0;
+}
+
 int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
                            const void* q_cond, const void* k_cond, const void* v_cond,
                            int64_t n_cond, int qk_dtype, int v_dtype, int64_t in_stride, int64_t B, int64_t H,
@@ -681,14 +694,17 @@ int launch_joint_attention(const void* q_vis, const void* k_vis, const void* v_v
     a.nbh = (int)(H * B);
     a.full = (int)items;
     a.split = 1;
-    // Split tail: when the items fill R < 256 workgroup slots of the last round, cut each of
-    // those R items into S = 256 / R key ranges (at most one per key tile) so that the last
-    // round runs on (nearly) every CU instead of R of them; a merge kernel combines them.
+    // Split tail: when the items fill R < P workgroup slots of the last round (P = the CU
+    // count, one workgroup per CU), cut each of those R items into S = P / R key ranges (at
+    // most one per key tile) so that the last round runs on (nearly) every CU instead of R of
+    // them; a merge kernel combines them.
     const int64_t ntiles = (n_vis + ATT_BN - 1) / ATT_BN + (n_cond + ATT_BN - 1) / ATT_BN;
-    if (split_ws && !has_lse && items > ATT_ROUND) {
-      const int64_t R = items % ATT_ROUND;
-      int64_t S = R ? ATT_ROUND / R : 0;
+    const int64_t round = device_cu_count();
+    if (split_ws && !has_lse && items > round) {
+      const int64_t R = items % round;
+      int64_t S = R ? round / R : 0;
       if (S > ntiles) S = ntiles;
+      if (R > 0 && S > (int64_t)(split_ws_bytes / ((size_t)R * ATT_PART_FLOATS * 4))) S = (int64_t)(split_ws_bytes / ((size_t)R * ATT_PART_FLOATS * 4));
       if (R > 0 && S >= 2 && (size_t)(R * S * ATT_PART_FLOATS) * 4 <= split_ws_bytes) {
         a.full = (int)(items - R);
         a.split = (int)S;

@@ -60,7 +60,6 @@ struct Attn8Args {
   float* part;
 };
 
-constexpr int A8_ROUND = 256;   // workgroups the chip runs at once (one per CU)
 // one key range's partial result for one query tile: O (256 x 128 f32, V scale applied) then
 // (m, l) per query
 constexpr int64_t A8_PART_FLOATS = 256 * 128 + 256 * 2;
@@ -496,14 +495,16 @@ int launch_joint_attention_8bit(const mmdit_attn8_stream* const* seg, const int6
   a.nbh = (int)(H * B);
   a.full = (int)items;
   a.split = 1;
-  // Split tail (with a workspace and no LSE): when the items fill R < 256 workgroup slots of
-  // the last round, cut each of those R items into S = 256 / R key ranges (at most one per
-  // key tile), merged afterwards
+  // Split tail (with a workspace and no LSE): when the items fill R < P workgroup slots of
+  // the last round (P = the CU count, one workgroup per CU), cut each of those R items into
+  // S = P / R key ranges (at most one per key tile), merged afterwards
   const int64_t ntiles = (n[0] + A8_BN - 1) / A8_BN + (n[1] + A8_BN - 1) / A8_BN;
-  if (split_ws && !L && items > A8_ROUND) {
-    const int64_t R = items % A8_ROUND;
-    int64_t S = R ? A8_ROUND / R : 0;
+  const int64_t round = device_cu_count();
+  if (split_ws && !L && items > round) {
+    const int64_t R = items % round;
+    int64_t S = R ? round / R : 0;
     if (S > ntiles) S = ntiles;
+    if (R > 0 && S > (int64_t)(split_ws_bytes / ((size_t)R * A8_PART_FLOATS * 4))) S = (int64_t)(split_ws_bytes / ((size_t)R * A8_PART_FLOATS * 4));
     if (R > 0 && S >= 2 && (size_t)(R * S * A8_PART_FLOATS) * 4 <= split_ws_bytes) {
       a.full = (int)(items - R);
       a.split = (int)S;
