@@ -550,11 +550,13 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
                          scale: Optional[float] = None,
                          vis_rows: Optional[np.ndarray] = None,
                          cond_rows: Optional[np.ndarray] = None, chunk: int = 1024,
-                         return_lse: bool = False):
+                         return_lse: bool = False, return_row_sums: bool = False):
     """The 8-bit joint attention of [Wan-zh] 4.4.3 under readings r26 / r27.  Inputs as for
     joint_attention (Q^, K^ already normalised and rotated).  Returns (o_vis, o_cond) and,
     with ``return_lse``, the natural-log row sums ln(sum_j 2^y_j) of the quantized weights,
-    i.e. ln(sum_j P'_j) + (M - 8) ln 2, laid out [B, H, n_cond + n_vis] ([cond | vis])."""
+    i.e. ln(sum_j P'_j) + (M - 8) ln 2, laid out [B, H, n_cond + n_vis] ([cond | vis]); with
+    ``return_row_sums``, the sums sum_j P'_j themselves ([B, H, rows] per stream, in the
+    order of the returned rows)."""
     b, _, h, d = q_vis.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -575,6 +577,7 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
         nq = q8.shape[1]
         out = np.empty((b, nq, h, d), dtype=np.float64)
         lse = np.empty((b, h, nq), dtype=np.float64)
+        sums = np.empty((b, h, nq), dtype=np.float64)
         for bi in range(b):
             for hi in range(h):
                 kk = k8[bi, :, hi, :]
@@ -587,13 +590,17 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
                     ell = p.sum(axis=1, keepdims=True)
                     out[bi, i0:i0 + chunk, hi, :] = (p @ v8[bi, :, hi, :]) * sv[bi, hi][None, :] / ell
                     lse[bi, hi, i0:i0 + chunk] = np.log(ell[:, 0]) + (m[:, 0] - 8.0) * math.log(2.0)
-        return out, lse
+                    sums[bi, hi, i0:i0 + chunk] = ell[:, 0]
+        return out, lse, sums
 
-    o_vis, lse_v = run(qa, sqa, vis_rows)
-    o_cond, lse_c = run(qc, sqc, cond_rows)
+    o_vis, lse_v, sum_v = run(qa, sqa, vis_rows)
+    o_cond, lse_c, sum_c = run(qc, sqc, cond_rows)
+    res = (o_vis, o_cond)
     if return_lse:
-        return o_vis, o_cond, np.concatenate([lse_c, lse_v], axis=2)
-    return o_vis, o_cond
+        res = res + (np.concatenate([lse_c, lse_v], axis=2),)
+    if return_row_sums:
+        res = res + (sum_v, sum_c)
+    return res
 
 
 # ------------------------------------------------------------------ parity metric (r18)
