@@ -138,6 +138,98 @@ def time_calls(fn, reps: int = 20, warm: int = 3) -> float:
     return a.elapsed_time(b) / reps
 
 
+def attention_configs(dev):
+    """The four attention workloads on their own: seeded Q, K, V in the workload's dtype ->
+    qk_norm_rope (Q^/K^ in f16 for the 16-bit workloads, f32 for the fp32 one) -> joint
+    attention (with the split-tail workspace), each timed with events over repeated calls.
+    The fp32 workload (40 tokens, 2 heads) is launch-bound; it is reported for completeness."""
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    import workloads as wl
+    res = {}
+    ws = torch.empty(mm.ATTN_SPLIT_BYTES, dtype=torch.uint8, device=dev)
+    for cfg, reps in ((wl.ATTN_TINY, 50), (wl.ATTN_LAYER, 50), (wl.ATTN_480P, 10), (wl.ATTN_720P, 5)):
+        raw = wl.attention_inputs(cfg)
+        if cfg.dtype == wl.F32:
+            t = {k: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev) for k, v in raw.items()}
+            qk_dt = torch.float32
+        else:
+            t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in raw.items()}
+            qk_dt = torch.float16
+        rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
+        qv, kv = mm.qk_norm_rope(t["q_vis"], t["k_vis"], t["gq_vis"], t["gk_vis"], rope=rope, eps=cfg.qk_eps,
+                                 out_dtype=qk_dt)
+        qc, kc = mm.qk_norm_rope(t["q_cond"], t["k_cond"], t["gq_cond"], t["gk_cond"], eps=cfg.qk_eps, out_dtype=qk_dt)
+        ov = torch.empty((cfg.batch, cfg.n_vis, cfg.heads, 128), dtype=torch.float32, device=dev)
+        oc = torch.empty((cfg.batch, cfg.n_cond, cfg.heads, 128), dtype=torch.float32, device=dev)
+
+        def norm():
+            mm.qk_norm_rope(t["q_vis"], t["k_vis"], t["gq_vis"], t["gk_vis"], rope=rope, eps=cfg.qk_eps,
+                            q_out=qv, k_out=kv)
+            mm.qk_norm_rope(t["q_cond"], t["k_cond"], t["gq_cond"], t["gk_cond"], eps=cfg.qk_eps, q_out=qc, k_out=kc)
+
+        ms_n = time_calls(norm, reps=reps)
+        ms_a = time_calls(lambda: mm.joint_attention(qv, kv, t["v_vis"], qc, kc, t["v_cond"], o_vis=ov, o_cond=oc,
+                                                     workspace=ws), reps=reps)
+        el_in = 4 if cfg.dtype == wl.F32 else 2
+        el_out = 4 if cfg.dtype == wl.F32 else 2
+        nbytes = 2 * cfg.n_tokens * cfg.batch * cfg.heads * 128 * (el_in + el_out)   # read Q, K; write Q^, K^
+        fl = cfg.attn_flops
+        res[cfg.name] = {
+            "tokens": cfg.n_tokens, "dtype": cfg.dtype, "attention_ms": round(ms_a, 4),
+            "attention_tflops": round(fl / ms_a / 1e9, 3 if fl < 1e10 else 1),
+            "attention_frac_bf16_peak": round(fl / ms_a / 1e9 / PEAK_BF16_TFLOPS, 5),
+            "qk_norm_rope_ms": round(ms_n, 4), "qk_norm_rope_GB_per_s": round(nbytes / ms_n / 1e6, 1),
+            "qk_norm_rope_frac_hbm": round(nbytes / ms_n / 1e6 / PEAK_HBM_GBS, 4)}
+        if cfg.dtype == wl.F32:
+            res[cfg.name]["note"] = "launch-bound (40 tokens, 2 heads; fp32 VALU kernel)"
+        del t, qv, kv, qc, kc, ov, oc
+    del ws
+    return res
+
+
+def memory_bound_kernels(dev):
+    """The block's memory-bound kernels at the 480p visual stream's shapes, alone: the
+    modulation GEMV (one stream's W_mod 18432 x 1536 bf16), LN-modulate before attention (x
+    bf16 -> h f16) and before the FFN (x1 f32 -> h2 f16), and QK-RMSNorm + 3D RoPE in place on
+    the packed q|k|v rows (f16).  Algorithmic bytes: each tensor read or written once."""
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    import workloads as wl
+    cfg = wl.BLOCK_480P
+    C, N = cfg.width, cfg.n_vis
+    g = torch.Generator(device=dev).manual_seed(7)
+    out = {}
+    w = (torch.randn((6 * C, cfg.t_dim), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    bm = (torch.randn((6 * C,), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    tv = torch.randn((1, cfg.t_dim), generator=g, device=dev).to(torch.bfloat16)
+    mod = torch.empty((1, 6 * C), dtype=torch.float32, device=dev)
+    ms = time_calls(lambda: mm.modulation(w, bm, tv, out=mod), reps=50)
+    nb = w.numel() * 2
+    out["modulation_gemv"] = {"ms": round(ms, 4), "bytes": nb, "GB_per_s": round(nb / ms / 1e6, 1),
+                              "frac_hbm": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    x = torch.randn((1, N, C), generator=g, device=dev).to(torch.bfloat16)
+    x1 = torch.randn((1, N, C), generator=g, device=dev)
+    h = torch.empty((1, N, C), dtype=torch.float16, device=dev)
+    shift, scale = mod[:, :C], mod[:, C:2 * C]
+    for name, src, el in (("modulate_ln_attention", x, 2), ("modulate_ln_ffn", x1, 4)):
+        ms = time_calls(lambda: mm.modulate_ln(src, shift, scale, y=h), reps=20)
+        nb = N * C * (el + 2)
+        out[name] = {"ms": round(ms, 4), "bytes": nb, "GB_per_s": round(nb / ms / 1e6, 1),
+                     "frac_hbm": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    del x, x1, h
+    qkv = torch.randn((1, N, 3, cfg.heads, 128), generator=g, device=dev).to(torch.float16)
+    gq = (1 + 0.1 * torch.randn((128,), generator=g, device=dev)).to(torch.bfloat16)
+    gk = (1 + 0.1 * torch.randn((128,), generator=g, device=dev)).to(torch.bfloat16)
+    rope = mm.Rope3D.make(cfg.grid)
+    q, k = qkv[:, :, 0], qkv[:, :, 1]
+    ms = time_calls(lambda: mm.qk_norm_rope(q, k, gq, gk, rope=rope, q_out=q, k_out=k), reps=20)
+    nb = 4 * N * C * 2
+    out["qk_norm_rope"] = {"ms": round(ms, 4), "bytes": nb, "GB_per_s": round(nb / ms / 1e6, 1),
+                           "frac_hbm": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def next_rows(dev):
     """The conditioning path that produces tvec (full 1536-d and Lite 16-d bottleneck) and the
     Lite 2x2 merge / unpatchify at 480p, timed on their own (not part of the block step)."""
@@ -268,6 +360,8 @@ def main():
                     help="type of the 16-bit intermediates and MFMA operands")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the timing of the timestep path and Lite merge")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload attention records and the memory-bound kernels alone")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times): the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -366,6 +460,17 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "step_gpu_ms": round(float(np.mean(step_gpu_ms)), 4),
     }
+    # memory-bound stages of the step, from the same events (algorithmic bytes of both streams)
+    n_tok = cfg.n_tokens
+    stage_bytes = {"qk_norm_rope": 4 * n_tok * cfg.width * 2,                    # q, k read + written (f16)
+                   "ln2": n_tok * cfg.width * (4 + 2)}                             # x1 f32 -> h2 f16
+    res["memory_bound_stages"] = {
+        k: {"ms": round(stage_avg[k], 4), "bytes": b, "GB_per_s": round(b / stage_avg[k] / 1e6, 1),
+            "frac_hbm": round(b / stage_avg[k] / 1e6 / PEAK_HBM_GBS, 4)} for k, b in stage_bytes.items()}
+    if not args.no_configs:
+        log("attention workloads 1-4 and memory-bound kernels alone")
+        res["attention_configs"] = attention_configs(dev)
+        res["memory_bound_kernels"] = memory_bound_kernels(dev)
     if not args.no_next:
         log("timestep path and Lite merge / unpatchify")
         res["next_rows"] = next_rows(dev)
