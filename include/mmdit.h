@@ -152,6 +152,29 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * mmdit_joint_attention_noalloc -- mmdit_joint_attention for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments and results as mmdit_joint_attention without the workspace: the split tail's
+ * key-range results go to a static scratch array inside the library, MMDIT_NOALLOC_SCRATCH_BYTES
+ * (34,078,720 bytes: 256 slots of one 256-query tile) on each GPU the library runs on, held
+ * until the process ends.  The GPU is the one that runs `stream` (the current device for the
+ * null stream); the first call on a GPU takes the scratch's address there, making that device
+ * current for the lookup and restoring the caller's.  No call allocates or frees memory.  The scratch is shared by every call on
+ * a GPU and keeps the last call's contents (nothing in it needs to start at zero): calls that
+ * overlap in time on one GPU (different streams, or threads without ordering) race and must be
+ * serialised by the caller.  A call whose split tail would need more than the scratch holds
+ * (possible only on a device with more than 256 compute units) returns MMDIT_ERR_WORKSPACE
+ * before anything is enqueued.
+ * ------------------------------------------------------------------------------- */
+#define MMDIT_NOALLOC_SCRATCH_BYTES ((size_t)34078720)
+int mmdit_joint_attention_noalloc(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
+                                  const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
+                                  int qk_dtype, int v_dtype, int64_t in_row_stride,
+                                  int64_t B, int64_t H, int64_t D, float softmax_scale,
+                                  void* o_vis, void* o_cond, int out_dtype, int64_t out_row_stride,
+                                  float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * mmdit_linear -- y = epilogue(x W^T + bias) on bf16 / f16 MFMA, fp32 accumulate.  The
  * per-stream projections of the block (QKV, output, FFN) all run through this GEMM.
  *

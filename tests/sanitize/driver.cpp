@@ -71,6 +71,8 @@ int main() {
   EXPECT(ja(10, 3, 256, 1, 2, p, o2, nullptr, nullptr, 0), MMDIT_ERR_ALIAS);
   EXPECT(ja(BIG, BIG, BIG, BIG, BIG, o, o2, nullptr, nullptr, 0), ANYERR);
   EXPECT(ja(BIG / 2, 3, 256, 3, 2, o, o2, nullptr, nullptr, 0), ANYERR);
+  EXPECT(mmdit_joint_attention_noalloc(p, p, p, 10, p, p, p, 3, MMDIT_BF16, MMDIT_BF16, 256, 1, 2, 128, 0.088f, p, o2,
+                                       MMDIT_F32, 256, nullptr, nullptr), ANYERR);       // alias, or no device
   mmdit_attn8_stream st{fk(0x10000000), ff(0x20000000), fk(0x30000000), ff(0x40000000), fk(0x50000000)};
   EXPECT(mmdit_attn8_quantize(p, p, p, 100, nullptr, nullptr, nullptr, 0, MMDIT_BF16, 3072, 1, 24, 128, &st, nullptr,
                               ff(0x60000000), nullptr), OK);

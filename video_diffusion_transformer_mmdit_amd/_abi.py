@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
                                ctypes.POINTER(Rope3D), vp],
         "mmdit_joint_attention": [vp, vp, vp, i64, vp, vp, vp, i64, i, i, i64, i64, i64, i64, f, vp, vp, i,
                                   i64, vp, vp, ctypes.c_size_t, vp],
+        "mmdit_joint_attention_noalloc": [vp, vp, vp, i64, vp, vp, vp, i64, i, i, i64, i64, i64, i64, f, vp, vp, i,
+                                          i64, vp, vp],
         "mmdit_linear": [vp, vp, i, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
         "mmdit_modulation": [vp, vp, vp, i, vp, i64, i64, i64, vp],
         "mmdit_lite_merge": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
@@ -294,6 +296,47 @@ def joint_attention(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, 
     if return_lse:
         return o_vis, o_cond, lse
     return o_vis, o_cond
+
+
+def joint_attention_noalloc(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_cond=None, *,
+                            softmax_scale: Optional[float] = None, o_vis: torch.Tensor, o_cond: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None):
+    """mmdit_joint_attention_noalloc: joint_attention whose split tail uses the library's static
+    scratch (no allocation anywhere: the caller passes every output, ``o_vis`` / ``o_cond`` and
+    optionally ``lse`` [B, H, n_cond + n_vis] f32).  Calls on one GPU must not overlap in time."""
+    ts = [t for t in (q_vis, k_vis, v_vis, q_cond, k_cond, v_cond) if t is not None]
+    _need_gpu(*ts)
+    _on_device(q_vis.device, k_vis=k_vis, v_vis=v_vis, q_cond=q_cond, k_cond=k_cond, v_cond=v_cond,
+               o_vis=o_vis, o_cond=o_cond, lse=lse)
+    B, n_vis, rs = _rows(q_vis, "q_vis")
+    H, D = q_vis.shape[2], q_vis.shape[3]
+    n_cond = 0 if q_cond is None else q_cond.shape[1]
+    for nm, t in zip(("k_vis", "v_vis", "q_cond", "k_cond", "v_cond"), (k_vis, v_vis, q_cond, k_cond, v_cond)):
+        if t is None:
+            continue
+        _, n, r = _rows(t, nm)
+        ref_dt = v_vis.dtype if nm.startswith("v") else q_vis.dtype
+        if t.dtype != ref_dt or t.shape[0] != B or t.shape[2:] != q_vis.shape[2:]:
+            raise MmditError(f"{nm}: dtype / shape mismatch")
+        if n > 0 and r != rs and not (n == 1 or rs == 0):
+            raise MmditError(f"{nm}: all inputs must share one row stride")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    _, _, ors = _rows(o_vis, "o_vis")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H, n_vis + n_cond)):
+        raise MmditError("lse must be a contiguous f32 [B, H, n_cond + n_vis] tensor")
+    st = lib().mmdit_joint_attention_noalloc(q_vis.data_ptr(), k_vis.data_ptr(), v_vis.data_ptr(), n_vis,
+                                             _ptr(q_cond) if n_cond else None, _ptr(k_cond) if n_cond else None,
+                                             _ptr(v_cond) if n_cond else None, n_cond, _dt(q_vis), _dt(v_vis), rs,
+                                             B, H, D, softmax_scale, o_vis.data_ptr(),
+                                             _ptr(o_cond) if n_cond else None, _dt(o_vis), ors, _ptr(lse),
+                                             _stream(q_vis))
+    _check(st, "mmdit_joint_attention_noalloc")
+    return o_vis, o_cond
+
+
+NOALLOC_SCRATCH_BYTES = 34078720
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,

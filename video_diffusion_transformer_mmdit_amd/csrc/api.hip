@@ -3,6 +3,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -59,6 +60,44 @@ int validate_rope(const mmdit_rope3d* r, int64_t N, int64_t D) {
   return MMDIT_OK;
 }
 
+// Scratch of mmdit_joint_attention_noalloc: the key-range results of the attention's split
+// tail (at most 256 slots of one 256-query tile's unnormalised O, 256 x 128 f32, and (m, l)
+// per query).  Each device holds its own copy for the life of the process; its address is
+// taken once per device, with that device current, and only that address reaches the kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)256 * (256 * 128 + 256 * 2) * 4;
+static_assert(NOALLOC_SCRATCH_BYTES == MMDIT_NOALLOC_SCRATCH_BYTES, "scratch size and header disagree");
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// The scratch address on the device that runs `stream` (the current device for the null
+// stream).  The first call on a device makes that device current for the lookup and then
+// restores the caller's.
+static int noalloc_scratch(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MMDIT_ERR_HIP, std::string("noalloc: device of the stream: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(MMDIT_ERR_HIP, "noalloc: device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess || !p)
+      return fail(MMDIT_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MMDIT_OK;
+}
+
 }  // namespace mmdit
 
 using namespace mmdit;
@@ -81,7 +120,7 @@ const char* mmdit_status_str(int s) {
 
 const char* mmdit_last_error(void) { return g_last_error.c_str(); }
 
-int mmdit_abi_version(void) { return 5; }
+int mmdit_abi_version(void) { return 6; }
 
 int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
                       const float* gate, float* x_out, const float* shift, const float* scale,
@@ -232,6 +271,27 @@ int mmdit_joint_attention(const void* q_vis, const void* k_vis, const void* v_vi
                                 in_row_stride, B, H, softmax_scale, o_vis, o_cond, out_dtype,
                                 out_row_stride, lse, static_cast<hipStream_t>(stream), static_cast<float*>(workspace),
                                 workspace ? workspace_bytes : 0);
+}
+
+int mmdit_joint_attention_noalloc(const void* q_vis, const void* k_vis, const void* v_vis, int64_t n_vis,
+                                  const void* q_cond, const void* k_cond, const void* v_cond, int64_t n_cond,
+                                  int qk_dtype, int v_dtype, int64_t in_row_stride, int64_t B, int64_t H,
+                                  int64_t D, float softmax_scale, void* o_vis, void* o_cond, int out_dtype,
+                                  int64_t out_row_stride, float* lse, void* stream) {
+  g_last_error.clear();
+  if (!extents_ok({B}) || !extents_ok({H}) || !extents_ok({n_vis}) || !extents_ok({n_cond}))
+    return fail(MMDIT_ERR_SHAPE, "joint_attention_noalloc: sizes must be >= 0 and below 2^31");
+  const size_t need = joint_attention_split_bytes(n_vis, n_cond, B, H, qk_dtype, lse != nullptr);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(MMDIT_ERR_WORKSPACE, "joint_attention_noalloc: the split tail needs " + std::to_string(need) +
+                                         " bytes of scratch; the static scratch holds " +
+                                         std::to_string(NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  const int st = noalloc_scratch(stream, &ws);
+  if (st) return st;
+  return mmdit_joint_attention(q_vis, k_vis, v_vis, n_vis, q_cond, k_cond, v_cond, n_cond, qk_dtype, v_dtype,
+                               in_row_stride, B, H, D, softmax_scale, o_vis, o_cond, out_dtype, out_row_stride,
+                               lse, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int mmdit_linear(const void* x, const void* w, int x_dtype, const void* bias, int bias_dtype,
