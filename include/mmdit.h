@@ -175,6 +175,18 @@ int mmdit_joint_attention_noalloc(const void* q_vis, const void* k_vis, const vo
                                   float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * mmdit_cast -- elementwise dtype change, y[i] = x[i] rounded to y_dtype (nearest even).
+ * Not a step of the pages' method: it lets bf16 inputs reach the 16-bit attention kernel as
+ * f16 operands (a bf16 V converted inside the kernel costs its MFMA-only phase 16
+ * conversions per key tile), the same conversion the block applies to its weights.
+ *
+ * x [n] x_dtype, y [n] y_dtype: F32 | BF16 | F16, two different types; both 16-byte aligned.
+ * y may be x itself when both types are 16-bit (in place); any other overlap is refused
+ * (MMDIT_ERR_ALIAS).  n may be 0.
+ * ------------------------------------------------------------------------------- */
+int mmdit_cast(const void* x, int x_dtype, void* y, int y_dtype, int64_t n, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * mmdit_linear -- y = epilogue(x W^T + bias) on bf16 / f16 MFMA, fp32 accumulate.  The
  * per-stream projections of the block (QKV, output, FFN) all run through this GEMM.
  *

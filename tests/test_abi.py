@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert mm.abi_version() == 6
+    assert mm.abi_version() == 7
     assert L.mmdit_status_str(0) == b"MMDIT_OK"
     assert L.mmdit_status_str(ERR_ALIAS) == b"MMDIT_ERR_ALIAS"
     assert L.mmdit_status_str(99) == b"MMDIT_ERR_UNKNOWN"
@@ -210,6 +210,19 @@ def test_fp8_validation(L):
                               None, 0, 10, None) == ERR_ALIAS
     assert L.mmdit_linear_fp8(p, s, p, s, None, mm.BF16, y, mm.F32, 1 << 24, 256, 256, mm.EPI_NONE, None, mm.F32,
                               None, 0, 10, None) == ERR_SHAPE                                     # 2^31 bytes
+
+
+def test_cast_validation(L):
+    p, y = _fake(0x10000), _fake(0x900000)
+    assert L.mmdit_cast(p, mm.BF16, y, mm.F16, -1, None) == ERR_SHAPE
+    assert L.mmdit_cast(p, mm.BF16, y, mm.F16, 1 << 31, None) == ERR_SHAPE
+    assert L.mmdit_cast(p, mm.BF16, y, mm.BF16, 16, None) == ERR_DTYPE                  # same type
+    assert L.mmdit_cast(p, mm.FP8_E4M3, y, mm.F16, 16, None) == ERR_DTYPE
+    assert L.mmdit_cast(None, mm.BF16, y, mm.F16, 16, None) == ERR_NULL
+    assert L.mmdit_cast(_fake(0x10008), mm.BF16, y, mm.F16, 16, None) == ERR_ALIGN
+    assert L.mmdit_cast(p, mm.F32, _fake(0x10010), mm.F16, 16, None) == ERR_ALIAS        # partial overlap
+    assert L.mmdit_cast(p, mm.F32, p, mm.F16, 16, None) == ERR_ALIAS                     # in place across sizes
+    assert L.mmdit_cast(None, mm.BF16, None, mm.F16, 0, None) == 0
 
 
 def test_attention_8bit_validation(L):

@@ -110,3 +110,28 @@ def test_linear_full_width_shapes():
         y = mm.linear(x, w, None, y_dtype=torch.float32)
         torch.cuda.synchronize()
         assert_close(f"y[{N}x{K}]", to_host64(y), to_host64(x) @ to_host64(w).T, 1e-4)
+
+
+@pytest.mark.parametrize("src,dst", [(torch.bfloat16, torch.float16), (torch.float16, torch.bfloat16),
+                                     (torch.float32, torch.float16), (torch.float32, torch.bfloat16),
+                                     (torch.bfloat16, torch.float32)])
+@pytest.mark.parametrize("n", [0, 5, 8 * 1000 + 3, 3 * 1024 * 1024])
+def test_cast_matches_round_to_nearest_even(src, dst, n):
+    """mmdit_cast against the CPU's round-to-nearest-even conversion, bit for bit (values span
+    f16's subnormal and overflow ranges)."""
+    g = torch.Generator().manual_seed(n + 7)
+    x = (torch.randn(n, generator=g) * torch.exp2(torch.randint(-20, 18, (n,), generator=g).float())).to(src)
+    y = mm.cast(x.cuda(), dst)
+    torch.cuda.synchronize()
+    ref = x.to(dst)
+    assert torch.equal(y.cpu().view(torch.int16 if dst != torch.float32 else torch.int32),
+                       ref.view(torch.int16 if dst != torch.float32 else torch.int32))
+
+
+def test_cast_in_place_bf16_to_f16():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(4099, generator=g).to(torch.bfloat16)
+    d = x.cuda()
+    mm.cast(d, torch.float16, out=d.view(torch.float16))
+    torch.cuda.synchronize()
+    assert torch.equal(d.view(torch.float16).cpu(), x.to(torch.float16))

@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
         "mmdit_joint_attention_noalloc": [vp, vp, vp, i64, vp, vp, vp, i64, i, i, i64, i64, i64, i64, f, vp, vp, i,
                                           i64, vp, vp],
         "mmdit_linear": [vp, vp, i, vp, i, vp, i, i64, i64, i64, i, vp, i, vp, i64, i64, vp],
+        "mmdit_cast": [vp, i, vp, i, i64, vp],
         "mmdit_modulation": [vp, vp, vp, i, vp, i64, i64, i64, vp],
         "mmdit_lite_merge": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
         "mmdit_lite_unpatchify": [vp, i, vp, vp, i, vp, i, i64, i64, i64, i64, i64, vp],
@@ -337,6 +338,21 @@ def joint_attention_noalloc(q_vis, k_vis, v_vis, q_cond=None, k_cond=None, v_con
 
 
 NOALLOC_SCRATCH_BYTES = 34078720
+
+
+def cast(x: torch.Tensor, dtype: torch.dtype, *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mmdit_cast: a contiguous copy of ``x`` in ``dtype`` (f32, bf16 or f16; rounding to
+    nearest even), into ``out`` if given (``out`` may be ``x`` for a 16-bit to 16-bit cast)."""
+    _need_gpu(x)
+    if not x.is_contiguous():
+        raise MmditError("cast: x must be contiguous")
+    if out is None:
+        out = torch.empty(x.shape, dtype=dtype, device=x.device)
+    _on_device(x.device, out=out)
+    if out.dtype != dtype or not out.is_contiguous() or out.numel() != x.numel():
+        raise MmditError("cast: out must be a contiguous tensor of dtype with x's element count")
+    _check(lib().mmdit_cast(x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), x.numel(), _stream(x)), "mmdit_cast")
+    return out
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, *,

@@ -120,7 +120,7 @@ const char* mmdit_status_str(int s) {
 
 const char* mmdit_last_error(void) { return g_last_error.c_str(); }
 
-int mmdit_abi_version(void) { return 6; }
+int mmdit_abi_version(void) { return 7; }
 
 int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
                       const float* gate, float* x_out, const float* shift, const float* scale,
@@ -455,6 +455,20 @@ int mmdit_joint_attention_8bit(const mmdit_attn8_stream* vis, int64_t n_vis, con
   return launch_joint_attention_8bit(seg, n, v_scale, B, H, softmax_scale, o_vis, o_cond, out_dtype, out_row_stride,
                                      lse, static_cast<hipStream_t>(stream), static_cast<float*>(workspace),
                                      workspace ? workspace_bytes : 0);
+}
+
+int mmdit_cast(const void* x, int x_dtype, void* y, int y_dtype, int64_t n, void* stream) {
+  g_last_error.clear();
+  if (!extents_ok({n})) return fail(MMDIT_ERR_SHAPE, "cast: n must be >= 0 and below 2^31");
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype) || x_dtype == y_dtype)
+    return fail(MMDIT_ERR_DTYPE, "cast: x and y must be two different dtypes of f32, bf16, f16");
+  if (n == 0) return MMDIT_OK;
+  if (!x || !y) return fail(MMDIT_ERR_NULL, "cast: x and y required");
+  if (!aligned16(x) || !aligned16(y)) return fail(MMDIT_ERR_ALIGN, "cast: x and y must be 16-byte aligned");
+  const size_t nx = (size_t)n * dtype_size(x_dtype), ny = (size_t)n * dtype_size(y_dtype);
+  const bool in_place = x == y && nx == ny;
+  if (!in_place && overlaps(x, nx, y, ny)) return fail(MMDIT_ERR_ALIAS, "cast: y overlaps x (only an exact in-place cast between 16-bit types is allowed)");
+  return launch_cast(x, x_dtype, y, y_dtype, n, static_cast<hipStream_t>(stream));
 }
 
 int mmdit_quantize_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int per_row, void* q,

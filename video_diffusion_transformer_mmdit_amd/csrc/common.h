@@ -188,5 +188,6 @@ int launch_timestep_embed(const float* t, int64_t B, const void* w1, const void*
                           int64_t hidden_dim, int64_t Dt, float max_period, float* hidden, float* temb,
                           float* tvec, hipStream_t stream);
 int launch_convert_bf16_to_f16(const void* src, void* dst, int64_t n, hipStream_t stream);
+int launch_cast(const void* src, int src_dtype, void* dst, int dst_dtype, int64_t n, hipStream_t stream);
 
 }  // namespace mmdit

@@ -149,22 +149,42 @@ int launch_timestep_embed(const float* t, int64_t B, const void* w1, const void*
   return gemv_dispatch<GEMV_IN_SILU, MMDIT_F32, MMDIT_F32>(w3, b3, temb, tvec, B, Dt, hidden_dim, 0.0, stream);
 }
 
-// bf16 -> f16, 8 elements per thread (n a multiple of 8).
-__global__ __launch_bounds__(256) void convert_bf16_f16_kernel(const uint16_t* __restrict__ src,
-                                                               uint16_t* __restrict__ dst, int64_t n8) {
+// Elementwise dtype change, 8 elements per thread with 16-byte accesses; the last n % 8
+// elements one per thread of the last workgroup.  Rounding to 16 bits is to nearest even.
+template <int IN, int OUT>
+__global__ __launch_bounds__(256) void cast_kernel(const void* __restrict__ src, void* __restrict__ dst,
+                                                   int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  float v[8];
-  load8<MMDIT_BF16>(src, i * 8, v);
-  store8<MMDIT_F16>(dst, i * 8, v);
+  const int64_t n8 = n / 8;
+  if (i < n8) {
+    float v[8];
+    load8<IN>(src, i * 8, v);
+    store8<OUT>(dst, i * 8, v);
+  } else if (i - n8 < n % 8) {
+    const int64_t e = n8 * 8 + (i - n8);
+    store1<OUT>(dst, e, load1<IN>(src, e));
+  }
+}
+
+template <int IN, int OUT>
+static int cast_go(const void* src, void* dst, int64_t n, hipStream_t stream) {
+  const int64_t threads = n / 8 + n % 8;
+  if (threads == 0) return MMDIT_OK;
+  cast_kernel<IN, OUT><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, stream>>>(src, dst, n);
+  return check_launch("cast");
+}
+
+int launch_cast(const void* src, int src_dtype, void* dst, int dst_dtype, int64_t n, hipStream_t stream) {
+#define MMDIT_CAST(I, O) if (src_dtype == I && dst_dtype == O) return cast_go<I, O>(src, dst, n, stream)
+  MMDIT_CAST(MMDIT_BF16, MMDIT_F16); MMDIT_CAST(MMDIT_F16, MMDIT_BF16);
+  MMDIT_CAST(MMDIT_BF16, MMDIT_F32); MMDIT_CAST(MMDIT_F16, MMDIT_F32);
+  MMDIT_CAST(MMDIT_F32, MMDIT_BF16); MMDIT_CAST(MMDIT_F32, MMDIT_F16);
+#undef MMDIT_CAST
+  return fail(MMDIT_ERR_DTYPE, "cast: unsupported dtype pair");
 }
 
 int launch_convert_bf16_to_f16(const void* src, void* dst, int64_t n, hipStream_t stream) {
-  const int64_t n8 = n / 8;
-  if (n8 == 0) return MMDIT_OK;
-  convert_bf16_f16_kernel<<<dim3((unsigned)((n8 + 255) / 256)), 256, 0, stream>>>(
-      static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), n8);
-  return check_launch("convert_bf16_f16");
+  return cast_go<MMDIT_BF16, MMDIT_F16>(src, dst, n, stream);
 }
 
 }  // namespace mmdit
