@@ -36,8 +36,8 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only
 # for the kernel source they were taken on: a different joint_attention.hip reports null.
-ATTN_COUNTERS = {"source_sha256": "2b26186b20c577f0",
-                 "fetch_kib": 1163401.3 + 15814.3, "write_kib": 227852.8 + 3056.0,
+ATTN_COUNTERS = {"source_sha256": "a185da4d81ba65ed",
+                 "fetch_kib": 1171374.6 + 15814.2, "write_kib": 227851.7 + 3056.0,
                  "fetch_scale": 2.0, "write_scale": 1.0}
 
 

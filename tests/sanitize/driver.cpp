@@ -73,6 +73,10 @@ int main() {
   EXPECT(ja(BIG / 2, 3, 256, 3, 2, o, o2, nullptr, nullptr, 0), ANYERR);
   EXPECT(mmdit_joint_attention_noalloc(p, p, p, 10, p, p, p, 3, MMDIT_BF16, MMDIT_BF16, 256, 1, 2, 128, 0.088f, p, o2,
                                        MMDIT_F32, 256, nullptr, nullptr), ANYERR);       // alias, or no device
+  EXPECT(mmdit_cast(p, MMDIT_BF16, fk(0x90000000), MMDIT_F16, 1000, nullptr), OK);
+  EXPECT(mmdit_cast(p, MMDIT_BF16, p, MMDIT_F16, 1000, nullptr), OK);                       // in place
+  EXPECT(mmdit_cast(p, MMDIT_F32, p, MMDIT_F16, 1000, nullptr), MMDIT_ERR_ALIAS);
+  EXPECT(mmdit_cast(p, MMDIT_BF16, fk(0x90000000), MMDIT_F16, BIG, nullptr), ANYERR);
   mmdit_attn8_stream st{fk(0x10000000), ff(0x20000000), fk(0x30000000), ff(0x40000000), fk(0x50000000)};
   EXPECT(mmdit_attn8_quantize(p, p, p, 100, nullptr, nullptr, nullptr, 0, MMDIT_BF16, 3072, 1, 24, 128, &st, nullptr,
                               ff(0x60000000), nullptr), OK);

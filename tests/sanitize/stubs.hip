@@ -38,4 +38,5 @@ int launch_timestep_embed(const float*, int64_t, const void*, const void*, const
   ++g_launches; return MMDIT_OK;
 }
 int launch_convert_bf16_to_f16(const void*, void*, int64_t, hipStream_t) { ++g_launches; return MMDIT_OK; }
+int launch_cast(const void*, int, void*, int, int64_t, hipStream_t) { ++g_launches; return MMDIT_OK; }
 }  // namespace mmdit

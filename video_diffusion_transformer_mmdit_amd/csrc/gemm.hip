@@ -4,12 +4,13 @@
 // kernel runs the Lite model's 2x2 hidden-space merge and unpatchify (section 2.4), with the
 // neighbour gather folded into the x loads and the scatter back to the grid into the stores.
 //
-// gfx950 design (two kernels share the tile, fragment layout, tile order and epilogue:
-// gemm_k64_kernel for 16-bit operands in every layout, gemm_fp8_kernel for FP8 operands):
-//   - 256 x 256 output tile per workgroup of 4 wave64s arranged 2 (M) x 2 (N), one per SIMD;
-//     each wave owns 128 x 128 outputs = 4 x 4 tiles of 32 x 32 MFMAs whose 256 accumulator
-//     registers live in AGPRs.  The MFMA computes C^T (A operand = W rows, B operand = x
-//     rows), so every lane ends up holding four consecutive output columns of one row, 32
+// gfx950 design (two kernels share the tile, fragment layout and tile order: gemm_k64_kernel
+// for 16-bit operands in every layout, gemm_fp8_kernel for FP8 operands):
+//   - 256 x 256 output tile per workgroup.  16-bit: 8 wave64s, two per SIMD, arranged 2 (M)
+//     x 4 (N), each owning 128 x 64 outputs = 4 x 2 tiles of 32 x 32 MFMAs (128 accumulator
+//     registers).  FP8: 4 wave64s, one per SIMD, 2 x 2, each 128 x 128 outputs (256
+//     accumulator registers in AGPRs).  The MFMA computes C^T (A operand = W rows, B operand
+//     = x rows), so every lane ends up holding four consecutive output columns of one row, 32
 //     rows apart from its neighbours'.
 //   - x and W tiles are K-contiguous in LDS, so both MFMA operands are plain 16-byte LDS
 //     reads, and move by LDS-DMA (buffer loads straight into LDS) issued between the MFMAs.
@@ -210,6 +211,19 @@ __device__ __forceinline__ void gemm_store_part(const GemmArgs& args, int64_t id
       for (int e = 0; e < 16; ++e) base[((4 * j + i) * 16 + e) * 64] = acc[j][i][e];
 }
 
+// The same for the 8-wave kernel: wave w's accumulator (j, i) (j < 2), element e, lane l at
+// part[((idx * 8 + w) * 8 + 4 j + i) * 16 + e) * 64 + l].
+__device__ __forceinline__ void gemm_store_part8(const GemmArgs& args, int64_t idx, int wave, int lane,
+                                                 const f32x16 (&acc)[2][4]) {
+  float* base = args.part + ((idx * 8 + wave) * 8) * 16 * 64 + lane;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) base[((4 * j + i) * 16 + e) * 64] = acc[j][i][e];
+}
+
 // GELU or gated residual on four consecutive outputs (row m, columns n .. n + 3) that already
 // hold x W^T + b.
 template <int EPI, int RES_DT>
@@ -322,6 +336,85 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
         } else {
           v[0] = a.x + bias[0]; v[1] = a.y + bias[1]; v[2] = a.z + bias[2]; v[3] = a.w + bias[3];
         }
+        if constexpr (GRES) {
+          const int64_t b = (uint32_t)m / (uint32_t)P.rows_per_batch;
+          float r[4], gt[4];
+          res_unpack<RES_DT>(rc[k], r);
+          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = fmaf(gt[c], v[c], r[c]);
+        } else {
+          gemm_epi_tail<EPI, RES_DT>(P, N, m, n, v);
+        }
+        if constexpr (LAYOUT == GEMM_SCATTER_Y) {
+          const int64_t yr = (int64_t)merged_row0((int)m, args) + (sg >> 1) * args.w + (sg & 1);
+          store4<Y_DT>(P.y, yr * args.c + (n - (int64_t)sg * args.c), v);
+        } else {
+          store4<Y_DT>(P.y, m * N + n, v);
+        }
+      }
+      if constexpr (GRES) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rc[k] = rn[k];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Epilogue of the 8-wave kernel (16-bit operands): wave w restages its 128 x 64 block a quarter
+// (32 rows, accumulators i = q) at a time as f32 in its own LDS region (rows 68 floats apart),
+// reads it back four rows per instruction, 16 lanes x 4 columns per row, and applies bias, GELU
+// or the gated residual (residual rows loaded one group ahead, as above).  GEMM_SCATTER_Y: as
+// above (a 64-wide block lies inside one s).  `region` holds 32 x 68 floats.
+constexpr int G8_EPI_STRIDE = 68;                       // floats per restaged row
+constexpr int G8_EPI_BYTES = 32 * G8_EPI_STRIDE * 4;    // one wave's quarter block: 8.5 KiB
+template <int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
+__device__ __forceinline__ void gemm_epilogue_rows8(const GemmArgs& args, const GemmProblem& Pk,
+                                                    const f32x16 (&acc)[2][4], int m0, int n0, int wm, int wn,
+                                                    int lane, float* region) {
+  const GemmProblem P = Pk;   // a private copy (see gemm_epilogue_rows)
+  const int64_t M = P.M, N = args.N;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const int64_t n = n0 + wn * 64 + 4 * c16;
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (P.bias && n < N) load4<BIAS_DT>(P.bias, n, bias);
+  int sg = 0;
+  if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 64) / args.c;
+  constexpr bool GRES = EPI == MMDIT_EPI_GATED_RES;
+  // residual of rows r0 + 4 k + r4 (k = 0..3) of quarter q
+  auto res_group = [&](int q, int r0, ResRaw<RES_DT> (&rr)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t m = m0 + wm * 128 + q * 32 + r0 + 4 * k + r4;
+      if (m < M && n < N) res_load<RES_DT>(P.res, m * N + n, rr[k]);
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ResRaw<RES_DT> rc[4], rn[4];
+    if constexpr (GRES) res_group(q, 0, rc);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) region[l32 * G8_EPI_STRIDE + j * 32 + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[j][q][e];
+    __syncthreads();
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += 16) {
+      if constexpr (GRES) {
+        if (r0 + 16 < 32) res_group(q, r0 + 16, rn);
+      }
+      float4 a4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        a4[k] = *reinterpret_cast<const float4*>(region + (r0 + 4 * k + r4) * G8_EPI_STRIDE + 4 * c16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 a = a4[k];
+        const int64_t m = m0 + wm * 128 + q * 32 + r0 + 4 * k + r4;
+        if (m >= M || n >= N) continue;
+        float v[4] = {a.x + bias[0], a.y + bias[1], a.z + bias[2], a.w + bias[3]};
         if constexpr (GRES) {
           const int64_t b = (uint32_t)m / (uint32_t)P.rows_per_batch;
           float r[4], gt[4];
@@ -516,17 +609,23 @@ void gemm_fp8_kernel(GemmArgs args) {
   }
 }
 
-// 16-bit operands, any layout: two LDS stages of K = 64 (64 KiB each, rows of 128 bytes,
-// chunks XOR-swizzled by (row / 2) % 8).  The next stage's sixteen DMA loads per wave go out
-// during the first quarter of the current stage; before the last quarter every wave waits for
-// them and for its own reads of the current stage, and one barrier per 64 K follows, after
-// which the next stage's first fragments are read under the last quarter's MFMAs.
+// 16-bit operands, any layout: 8 wave64s, two per SIMD, arranged 2 (M) x 4 (N), each owning
+// 128 x 64 outputs = 4 x 2 tiles of 32 x 32 MFMAs (128 accumulator registers, so two waves fit
+// a SIMD).  While one wave of a SIMD waits for its fragment reads, the other issues MFMAs;
+// the 4-wave form (one wave per SIMD, 128 x 128 each) kept the matrix pipe busy only 50-56 %
+// of the time, stalling on its own reads.  Two LDS stages of K = 64 (64 KiB each, rows of 128
+// bytes, chunks XOR-swizzled by (row / 2) % 8).  The next stage's eight DMA loads per wave
+// go out in two fenced groups during the first quarter of the current stage; before the last
+// quarter every wave waits for them and for its own reads of the current stage, and one
+// barrier per 64 K follows, after which the next stage's first fragments are read under the
+// last quarter's MFMAs.
 // GEMM_GATHER_X: x row m, K position k reads channel k % C of the full-grid token
 // merged_row0(m) + (s / 2) W + s % 2, s = k / C (a 64-wide K stage never straddles two
 // neighbours, as C is a multiple of 256): the per-row part is per lane, the neighbour part
 // scalar.  GEMM_SCATTER_Y is the epilogue's.
+constexpr int G8_THREADS = 512;
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
-__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(G8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_k64_kernel(GemmArgs args) {
   constexpr int T64 = GBM * 128;   // one operand tile of one stage: 32 KiB
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * T64];
@@ -539,26 +638,26 @@ void gemm_k64_kernel(GemmArgs args) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
-  // DMA i of a wave fills rows 64 wave + 8 i .. +7 (lane l -> row + l / 8, physical chunk
-  // l % 8 = logical ^ ((row / 2) % 8)); loads 0-3 and 4-7 each share one LDS base, the
-  // immediate offset (i % 4) * 1024 moving destination and source alike.  A 128-byte row
-  // spans half of the 64 LDS banks, so the 16 rows one 16-lane group of a 16-byte read
-  // touches fall in two bank halves by row parity; swizzling by row / 2 gives the 8 rows of
-  // each parity 8 distinct chunks (by row % 8 they would repeat after 4, a 2-way conflict).
+  const int wm = wave >> 2, wn = wave & 3;
+  // DMA i (0..3) of a wave fills rows 32 wave + 8 i .. +7 of the x tile, and of the W tile
+  // (lane l -> row + l / 8, physical chunk l % 8 = logical ^ ((row / 2) % 8)); the four loads
+  // of a tile share one LDS base, the immediate offset i * 1024 moving destination and source
+  // alike.  A 128-byte row spans half of the 64 LDS banks, so the 16 rows one 16-lane group
+  // of a 16-byte read touches fall in two bank halves by row parity; swizzling by row / 2
+  // gives the 8 rows of each parity 8 distinct chunks.
   const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K * 2);
   const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K * 2);
-  int xo[8], wo[8];
+  int xo[4], wo[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
     const int lc = (lane & 7) ^ ((row >> 1) & 7);
     // rows past M: an offset past the end of x, so they load zeros
     if constexpr (LAYOUT == GEMM_GATHER_X)
-      xo[i] = (m0 + row < M ? merged_row0(m0 + row, args) * args.c * 2 + lc * 16 : 0x7FFF0000) - (i & 3) * 1024;
+      xo[i] = (m0 + row < M ? merged_row0(m0 + row, args) * args.c * 2 + lc * 16 : 0x7FFF0000) - i * 1024;
     else
-      xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
-    wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - (i & 3) * 1024;
+      xo[i] = (m0 + row) * (int)K * 2 + lc * 16 - i * 1024;
+    wo[i] = (n0 + row) * (int)K * 2 + lc * 16 - i * 1024;
   }
   // scalar byte offset of K position k0 in x (the neighbour's token, then the channel)
   auto x_soff = [&](int k0) {
@@ -569,41 +668,21 @@ void gemm_k64_kernel(GemmArgs args) {
       return k0 * 2;
     }
   };
-  // the four loads of one LDS base (x rows 0-31 / 32-63 of the wave's 64, then W's)
-  auto dma_part = [&](uint8_t* xs, uint8_t* ws, int k0, auto part_c) {
-    constexpr int PART = decltype(part_c)::value;
-    const int so = PART < 2 ? x_soff(k0 + kb * 64) : (k0 + kb * 64) * 2;
-    const auto rs = PART < 2 ? rx : rw;
-    const int* o = (PART < 2 ? xo : wo) + (PART & 1) * 4;
-    auto* l = opaque_lds((__attribute__((address_space(3))) void*)((PART < 2 ? xs : ws) + wave * 8192 + (PART & 1) * 4096));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[0], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, o[3], so, 3072, 0);
+  auto dma_x = [&](uint8_t* xs, int k0) {
+    const int so = x_soff(k0 + kb * 64);
+    auto* l = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 4096));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, l, 16, xo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, l, 16, xo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, l, 16, xo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, l, 16, xo[3], so, 3072, 0);
   };
-  auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
+  auto dma_w = [&](uint8_t* ws, int k0) {
     const int so = (k0 + kb * 64) * 2;
-    const int xso = x_soff(k0 + kb * 64);
-    auto* lx0 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192));
-    auto* lx1 = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 8192 + 4096));
-    auto* lw0 = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 8192));
-    auto* lw1 = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 8192 + 4096));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[0], xso, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[1], xso, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[2], xso, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx0, 16, xo[3], xso, 3072, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[4], xso, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[5], xso, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[6], xso, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx1, 16, xo[7], xso, 3072, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[0], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw0, 16, wo[3], so, 3072, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[4], so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[5], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[6], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw1, 16, wo[7], so, 3072, 0);
+    auto* l = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 4096));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, l, 16, wo[0], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, l, 16, wo[1], so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, l, 16, wo[2], so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, l, 16, wo[3], so, 3072, 0);
   };
   auto xbuf = [&](auto st) -> uint8_t* { if constexpr (decltype(st)::value == 0) return lds_a; else return lds_b; };
   auto wbuf = [&](auto st) -> uint8_t* { return xbuf(st) + T64; };
@@ -612,9 +691,9 @@ void gemm_k64_kernel(GemmArgs args) {
   int cofs[4];   // slice ks: logical chunk 2 ks + g of row l32 (+ a multiple of 32)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) cofs[ks] = l32 * 128 + (((2 * ks + g) ^ ((l32 >> 1) & 7)) << 4);
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];   // [n tile][m tile] of C^T
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -625,25 +704,25 @@ void gemm_k64_kernel(GemmArgs args) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  uint4 wfa[4], xfa[4], wfb[4], xfb[4];
-  auto read_slice = [&](const uint8_t* xs, const uint8_t* ws, int ks, uint4 (&wf)[4], uint4 (&xf)[4]) {
+  uint4 wfa[2], xfa[4], wfb[2], xfb[4];
+  auto read_slice = [&](const uint8_t* xs, const uint8_t* ws, int ks, uint4 (&wf)[2], uint4 (&xf)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const uint4*>(ws + (wn * 128 + j * 32) * 128 + cofs[ks]);
+    for (int j = 0; j < 2; ++j) wf[j] = *reinterpret_cast<const uint4*>(ws + (wn * 64 + j * 32) * 128 + cofs[ks]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const uint4*>(xs + (wm * 128 + i * 32) * 128 + cofs[ks]);
   };
-  auto mma = [&](const uint4 (&wf)[4], const uint4 (&xf)[4]) {
+  auto mma = [&](const uint4 (&wf)[2], const uint4 (&xf)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wf[j], xf[i], acc[j][i]);
   };
-  // 16 MFMAs with the next slice's 8 fragment reads among the first eight
+  // 8 MFMAs with the next slice's 6 fragment reads among them
   auto sched = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
   };
   // stage kt in buffer cur, its slice 0 in wfa / xfa
@@ -655,28 +734,17 @@ void gemm_k64_kernel(GemmArgs args) {
     read_slice(xbuf(cur), wbuf(cur), 1, wfb, xfb);
     __builtin_amdgcn_sched_barrier(0);
     // slice 0: the next stage's DMA (its buffer's last readers passed the previous barrier) in
-    // four groups of four loads, one group before each row of four MFMAs; fenced, as left to
-    // the scheduler the sixteen loads issue in one burst that holds back the MFMAs behind them
-    // (in-order issue), 2-5 % slower
-    auto mrow = [&](int j) {
+    // two fenced groups of four loads, one before each half of the slice's MFMAs (left to the
+    // scheduler the loads issue in one burst that holds back the MFMAs behind them)
+    if (more) dma_x(xbuf(oth), (kt + 1) * 64);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = mfma32<IN_DT>(wfa[j], xfa[i], acc[j][i]);
-    };
-    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 0>{});
+    for (int i = 0; i < 4; ++i) acc[0][i] = mfma32<IN_DT>(wfa[0], xfa[i], acc[0][i]);
     __builtin_amdgcn_sched_barrier(0);
-    mrow(0);
+    if (more) dma_w(wbuf(oth), (kt + 1) * 64);
     __builtin_amdgcn_sched_barrier(0);
-    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 1>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mrow(1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 2>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mrow(2);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) dma_part(xbuf(oth), wbuf(oth), (kt + 1) * 64, std::integral_constant<int, 3>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mrow(3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[1][i] = mfma32<IN_DT>(wfa[1], xfa[i], acc[1][i]);
     __builtin_amdgcn_sched_barrier(0);
     read_slice(xbuf(cur), wbuf(cur), 2, wfa, xfa);
     mma(wfb, xfb);
@@ -695,7 +763,8 @@ void gemm_k64_kernel(GemmArgs args) {
     sched();
     __builtin_amdgcn_sched_barrier(0);
   };
-  dma(xbuf(S0), wbuf(S0), 0);
+  dma_x(xbuf(S0), 0);
+  dma_w(wbuf(S0), 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   gbarrier();
   read_slice(xbuf(S0), wbuf(S0), 0, wfa, xfa);
@@ -706,28 +775,28 @@ void gemm_k64_kernel(GemmArgs args) {
   }
   if (kt < nk) step(S0, kt);
   if (part_idx >= 0) {
-    gemm_store_part(args, part_idx, wave, lane, acc);
+    gemm_store_part8(args, part_idx, wave, lane, acc);
   } else {
-    // every wave's fragment reads of the last stage are done after this barrier; waves 0, 1
-    // restage in the first stage buffer, waves 2, 3 in the second
+    // every wave's fragment reads of the last stage are done after this barrier; waves 0-3
+    // restage in the first stage buffer, waves 4-7 in the second
     __syncthreads();
-    float* region = reinterpret_cast<float*>((wave < 2 ? lds_a : lds_b) + (wave & 1) * G_EPI_BYTES);
-    gemm_epilogue_rows<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, lane, region);
+    float* region = reinterpret_cast<float*>((wave < 4 ? lds_a : lds_b) + (wave & 3) * G8_EPI_BYTES);
+    gemm_epilogue_rows8<BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT>(args, P, acc, m0, n0, wm, wn, lane, region);
   }
 }
 
-// Tail tiles of a split launch: each thread sums, in K-range order, the `split` partial sums
-// of the four consecutive outputs (row m, columns n .. n + 3) that one GEMM lane held as
-// elements 4 e4 .. 4 e4 + 3 of one accumulator, and applies the tile epilogue to them;
-// G_SUM_WG workgroups per tail tile cover its 256 x 256 outputs.
+// Tail tiles of a split launch (16-bit kernel): each thread sums, in K-range order, the `split`
+// partial sums of the four consecutive outputs (row m, columns n .. n + 3) that one GEMM lane
+// held as elements 4 e4 .. 4 e4 + 3 of one accumulator, and applies the tile epilogue to
+// them; G_SUM_WG workgroups per tail tile cover its 256 x 256 outputs.
 constexpr int G_SUM_WG = 64;   // 64 x 256 threads x 4 outputs = 256 x 256
 template <int BIAS_DT, int Y_DT, int EPI, int RES_DT>
 __global__ __launch_bounds__(GTHREADS) void gemm_split_finish_kernel(GemmArgs args) {
   const int64_t tile = blockIdx.x / G_SUM_WG;
   const int q = (blockIdx.x % G_SUM_WG) * GTHREADS + threadIdx.x;
-  const int lane = q & 63, e4 = (q >> 6) & 3, i = (q >> 8) & 3, j = (q >> 10) & 3, wave = q >> 12;
+  const int lane = q & 63, e4 = (q >> 6) & 3, i = (q >> 8) & 3, j = (q >> 10) & 1, wave = q >> 11;
   constexpr int64_t SLOT = G_PART_BYTES / 4;   // floats of one partial-sum slot
-  const float* base = args.part + tile * args.split * SLOT + ((wave * 16 + 4 * j + i) * 16 + 4 * e4) * 64 + lane;
+  const float* base = args.part + tile * args.split * SLOT + ((wave * 8 + 4 * j + i) * 16 + 4 * e4) * 64 + lane;
   float v[4] = {base[0], base[64], base[128], base[192]};
 #pragma unroll 2
   for (int sp = 1; sp < args.split; ++sp) {
@@ -738,8 +807,8 @@ __global__ __launch_bounds__(GTHREADS) void gemm_split_finish_kernel(GemmArgs ar
   gemm_tile_of(args, args.full + tile, pi, m0, n0);
   const GemmProblem P = args.p[pi];
   // the accumulator element's place in the tile, as in the GEMM's epilogue
-  const int64_t m = m0 + (wave >> 1) * 128 + i * 32 + (lane & 31);
-  const int64_t n = n0 + (wave & 1) * 128 + j * 32 + 8 * e4 + 4 * (lane >> 5);
+  const int64_t m = m0 + (wave >> 2) * 128 + i * 32 + (lane & 31);
+  const int64_t n = n0 + (wave & 3) * 64 + j * 32 + 8 * e4 + 4 * (lane >> 5);
   if (m >= P.M || n >= args.N) return;
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   if (P.bias) load4<BIAS_DT>(P.bias, n, bias);
@@ -758,12 +827,12 @@ static void gemm_go(const GemmArgs& a, hipStream_t st) {
     if constexpr (LAYOUT == GEMM_PLAIN) {
       if (a.full < a.tiles) {   // split tail: whole tiles and K ranges of the tail tiles, then their sums
         const int64_t grid = a.full + (a.tiles - a.full) * a.split;
-        gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)grid), GTHREADS, 0, st>>>(a);
+        gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)grid), G8_THREADS, 0, st>>>(a);
         gemm_split_finish_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)((a.tiles - a.full) * G_SUM_WG)), GTHREADS, 0, st>>>(a);
         return;
       }
     }
-    gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+    gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), G8_THREADS, 0, st>>>(a);
   } else {
     static_assert(LAYOUT == GEMM_PLAIN, "FP8 operands use the plain layout");
     gemm_fp8_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
