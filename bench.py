@@ -37,7 +37,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
 # same counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only
 # for the kernel source they were taken on: a different joint_attention.hip reports null.
 ATTN_COUNTERS = {"source_sha256": "a185da4d81ba65ed",
-                 "fetch_kib": 1171374.6 + 15814.2, "write_kib": 227851.7 + 3056.0,
+                 "fetch_kib": 1167653.5 + 15813.8, "write_kib": 227854.4 + 3056.0,
                  "fetch_scale": 2.0, "write_scale": 1.0}
 
 
