@@ -82,7 +82,7 @@ typedef struct {
  *         (mod_stride in elements, >= C; pass 6*C to read straight from an mmdit
  *         modulation buffer).  gate is required iff branch is given.
  * x_out   [B, N, C] f32 receives x' (may be NULL).
- * y       [B, N, C] y_dtype F32 | BF16 | F16.
+ * y       [B, N, C] y_dtype F32 | BF16 | F16; an f16 y saturates at +-65504 (NaN stays NaN).
  * C must be a multiple of 8 and at most 8192.  N may be 0.  Outputs must not overlap
  * inputs.
  * ------------------------------------------------------------------------------- */
@@ -199,8 +199,8 @@ int mmdit_cast(const void* x, int x_dtype, void* y, int y_dtype, int64_t n, void
  *   MMDIT_EPI_GATED_RES y = res + gate[b] * (acc + bias), b = row / rows_per_batch;
  *                       res [M, N] res_dtype F32 | BF16; gate f32, item b at
  *                       gate + b * gate_stride (gate_stride a multiple of 4).
- * y  [M, N] y_dtype F32 | BF16 | F16.  K must be a multiple of 64, N a multiple of 4,
- * M, N >= 0; x and w are addressed with 32-bit offsets: (M + 256) * K and (N + 256) * K
+ * y  [M, N] y_dtype F32 | BF16 | F16; an f16 y saturates at +-65504 (NaN stays NaN).
+ * K must be a multiple of 64, N a multiple of 4, M, N >= 0; x and w are addressed with 32-bit offsets: (M + 256) * K and (N + 256) * K
  * elements must stay below 2^30.  Pointers 16-byte aligned.
  * ------------------------------------------------------------------------------- */
 enum mmdit_epilogue { MMDIT_EPI_NONE = 0, MMDIT_EPI_GELU = 1, MMDIT_EPI_GATED_RES = 2 };
@@ -390,8 +390,11 @@ int mmdit_lite_unpatchify(const void* x, int x_dtype, const void* w, const void*
  *   h2    = LN(x1) (1 + scale_f) + shift_f
  *   out_s = x1 + gate_f (GELU(h2 W_fc1^T + b_fc1) W_fc2^T + b_fc2)   (out_dtype)
  *
- * dims: C = H*D, D = 128, F and C multiples of 256, Dt a multiple of 8, w_dtype BF16.
- * Weights (per stream, nn.Linear layout, all w_dtype): w_mod [6C, Dt], b_mod [6C],
+ * dims: C = H*D, D = 128, F and C multiples of 256, Dt a multiple of 8.
+ * w_dtype: MMDIT_BF16 (every weight bf16), or MMDIT_F16 with act_dtype F16: the four GEMM
+ * matrices w_qkv, w_o, w_fc1, w_fc2 are given in f16 (converted once, e.g. with mmdit_cast,
+ * as a deployment stores them) and every other weight stays bf16.
+ * Weights (per stream, nn.Linear layout): w_mod [6C, Dt], b_mod [6C],
  * w_qkv [3C, C], b_qkv [3C] (rows: q, then k, then v), q_norm, k_norm [D] (or [H, D] with
  * qk_scale_head_stride = D), w_o [C, C], b_o [C], w_fc1 [F, C], b_fc1 [F], w_fc2 [C, F],
  * b_fc2 [C].  Bias pointers may be NULL (no bias).
@@ -399,9 +402,10 @@ int mmdit_lite_unpatchify(const void* x, int x_dtype, const void* w, const void*
  * BF16 | F32; rope describes the visual grid (n_vis = T*H*W); out_vis, out_cond
  * [B, n_s, C] out_dtype F32 | BF16.
  * act_dtype selects the type of every 16-bit intermediate (h, q|k|v, O, h2, GELU output)
- * and hence of every MFMA operand: MMDIT_BF16 (weights used as given) or MMDIT_F16 (the
- * four weight matrices of each stream are converted to f16 in the workspace on every call;
- * f16 keeps 3 more mantissa bits, which the block's range-bounded intermediates can use).
+ * and hence of every MFMA operand: MMDIT_BF16 (weights used as given) or MMDIT_F16 (with
+ * bf16 matrices, the four weight matrices of each stream are converted to f16 in the
+ * workspace on every call; f16 keeps 3 more mantissa bits, which the block's range-bounded
+ * intermediates can use).
  * The modulation vectors, LayerNorm statistics, softmax state and the residual stream x1
  * are f32 in both cases.
  * workspace: >= mmdit_block_workspace_bytes(dims, B, n_vis, n_cond), 256-byte aligned;
@@ -428,7 +432,7 @@ typedef struct {
  *   MMDIT_WS_X1     f32 [B*n, C]  residual after the attention branch
  *   MMDIT_WS_G      act [B*n, F]  GELU(h2 W_fc1^T + b_fc1)
  *   MMDIT_WS_WQKV, MMDIT_WS_WO, MMDIT_WS_W1, MMDIT_WS_W2: f16 copies of w_qkv, w_o, w_fc1,
- *                   w_fc2 (act_dtype F16 only).
+ *                   w_fc2 (act_dtype F16 with w_dtype BF16 only).
  *   MMDIT_WS_SPLIT  f32 64 MiB, stream 0 only: partial sums of the GEMM tiles of a launch's
  *                   last, partial round, each computed over K ranges by several workgroups,
  *                   and likewise the attention's last-round query tiles computed over key

@@ -147,6 +147,10 @@ def test_block_workspace_and_validation(L):
     d16 = mm.BlockDims.make(3072, 24, 12288, 1536, act_dtype=torch.float16)
     per_stream = (3 * 3072 * 3072 + 3072 * 3072 + 2 * 12288 * 3072) * 2
     assert mm.block_workspace_bytes(d16, 1, 32760, 512) == n + 2 * per_stream
+    d16w = mm.BlockDims.make(3072, 24, 12288, 1536, act_dtype=torch.float16, matrix_dtype=torch.float16)
+    assert mm.block_workspace_bytes(d16w, 1, 32760, 512) == n      # f16 matrices given: no copies
+    mixed = mm.BlockDims.make(3072, 24, 12288, 1536, act_dtype=torch.bfloat16, matrix_dtype=torch.float16)
+    assert mm.block_workspace_bytes(mixed, 1, 100, 5) == 0          # f16 matrices need f16 operands
     bad = mm.BlockDims.make(3000, 24, 12288, 1536)
     assert mm.block_workspace_bytes(bad, 1, 100, 5) == 0
     rope = mm.Rope3D.make((21, 30, 52))

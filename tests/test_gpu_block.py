@@ -99,6 +99,27 @@ def test_block_all_bf16_intermediates_runs_and_stays_near_oracle():
     assert_close("out_cond (bf16 act)", to_host64(out_c), ref["out_cond"], 5e-2)
 
 
+def test_block_preconverted_f16_matrices_match_per_call_conversion():
+    """The four GEMM matrices converted to f16 once (mmdit_cast) and passed with w_dtype f16
+    give exactly the output of the per-call conversion, and the workspace holds no copies."""
+    cfg = wl.BLOCK_SMALL
+    raw = wl.block_inputs(cfg)
+    dev, wv, wc = _dev_block(cfg, raw)
+    _, out_v, out_c, _ = _run_block(cfg, dev, wv, wc, torch.float16)
+    conv = lambda w: {k: (mm.cast(t, torch.float16) if k in ("w_qkv", "w_o", "w_fc1", "w_fc2") else t)  # noqa: E731
+                      for k, t in w.items()}
+    dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, cfg.ln_eps, cfg.qk_eps,
+                             act_dtype=torch.float16, matrix_dtype=torch.float16)
+    rope = mm.Rope3D.make(cfg.grid, cfg.rope_split, cfg.rope_base)
+    o2v, o2c, _ = mm.block_fwd(dims, conv(wv), conv(wc), dev["x_vis"], dev["x_cond"], dev["tvec"], rope)
+    torch.cuda.synchronize()
+    assert torch.equal(out_v, o2v) and torch.equal(out_c, o2c)
+    off = mm.block_workspace_offsets(dims, cfg.batch, cfg.n_vis, cfg.n_cond)
+    assert all(off[s][r] == 2 ** 64 - 1 for s in (0, 1) for r in (mm.WS_WQKV, mm.WS_WO, mm.WS_W1, mm.WS_W2))
+    with pytest.raises(mm.MmditError, match="float16"):
+        mm.block_fwd(dims, wv, wc, dev["x_vis"], dev["x_cond"], dev["tvec"], rope)   # bf16 matrices
+
+
 def test_block_zero_modulation_is_exact_identity():
     cfg = wl.BLOCK_TINY
     raw = wl.block_inputs(cfg)

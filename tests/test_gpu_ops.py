@@ -135,3 +135,31 @@ def test_cast_in_place_bf16_to_f16():
     mm.cast(d, torch.float16, out=d.view(torch.float16))
     torch.cuda.synchronize()
     assert torch.equal(d.view(torch.float16).cpu(), x.to(torch.float16))
+
+
+def test_f16_outputs_saturate_instead_of_overflowing():
+    """f16 GEMM and LN-modulate outputs beyond the f16 range saturate at +-65504 (an
+    infinity there would become NaN in the next LayerNorm or softmax); NaN stays NaN."""
+    M, N, K = 64, 256, 64
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    x[:, 0] = 300.0
+    x[1, 0] = -300.0
+    x[2, 0] = float("nan")
+    w = torch.zeros((N, K), dtype=torch.bfloat16)
+    w[:, 0] = 1000.0                                   # products 3e5, beyond 65504
+    w[0, 0] = 1.0                                      # column 0 stays in range: 300
+    y = mm.linear(x.cuda(), w.cuda(), None, y_dtype=torch.float16)
+    torch.cuda.synchronize()
+    y = y.float().cpu()
+    assert torch.all(y[0, 1:] == 65504.0) and torch.all(y[1, 1:] == -65504.0)
+    assert y[0, 0] == 300.0 and torch.isnan(y[2]).all()
+    assert torch.all(y[3:, 1:] == 65504.0)
+    # LN-modulate: shift 1e6 pushes every output past the f16 range
+    B, Nt, C = 1, 4, 256
+    xs = torch.randn((B, Nt, C)).to(torch.bfloat16).cuda()
+    mod = torch.zeros((B, 6 * C), dtype=torch.float32)
+    mod[:, :C] = 1e6
+    mod = mod.cuda()
+    h = mm.modulate_ln(xs, mod[:, :C], mod[:, C:2 * C], y_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert torch.all(h.float().cpu() == 65504.0)

@@ -58,8 +58,10 @@ class BlockDims(ctypes.Structure):
 
     @classmethod
     def make(cls, C, H, F, Dt, ln_eps=1e-6, qk_eps=1e-6, qk_scale_head_stride=0,
-             act_dtype=torch.float16):
-        return cls(C, H, C // H, F, Dt, ln_eps, qk_eps, qk_scale_head_stride, BF16,
+             act_dtype=torch.float16, matrix_dtype=torch.bfloat16):
+        """matrix_dtype: dtype of the four GEMM weight matrices (w_qkv, w_o, w_fc1, w_fc2);
+        float16 (with act_dtype float16) means they were converted once by the caller."""
+        return cls(C, H, C // H, F, Dt, ln_eps, qk_eps, qk_scale_head_stride, _TORCH_DT[matrix_dtype],
                    _TORCH_DT[act_dtype])
 
 
@@ -590,12 +592,16 @@ STREAM_KEYS = ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm", "w_o", "b
                "w_fc2", "b_fc2")
 
 
-def _stream_weights(w: Dict[str, torch.Tensor], device: torch.device) -> StreamWeights:
+MATRIX_KEYS = ("w_qkv", "w_o", "w_fc1", "w_fc2")
+
+
+def _stream_weights(w: Dict[str, torch.Tensor], device: torch.device, matrix_dt: int = BF16) -> StreamWeights:
     sw = StreamWeights()
     for k in STREAM_KEYS:
         t = w.get(k)
-        if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
-            raise MmditError(f"weight {k} must be contiguous bf16")
+        want = torch.float16 if (k in MATRIX_KEYS and matrix_dt == F16) else torch.bfloat16
+        if t is not None and (not t.is_contiguous() or t.dtype != want):
+            raise MmditError(f"weight {k} must be contiguous {want}")
         _on_device(device, **{f"weight {k}": t})
         setattr(sw, k, None if t is None else t.data_ptr())
     return sw
@@ -633,7 +639,8 @@ def block_fwd(dims: BlockDims, w_vis: Dict[str, torch.Tensor], w_cond: Dict[str,
         out_vis = torch.empty((B, n_vis, C), dtype=out_dtype, device=x_vis.device)
     if out_cond is None and n_cond > 0:
         out_cond = torch.empty((B, n_cond, C), dtype=out_dtype, device=x_vis.device)
-    swv, swc = _stream_weights(w_vis, x_vis.device), _stream_weights(w_cond, x_vis.device)
+    swv = _stream_weights(w_vis, x_vis.device, dims.w_dtype)
+    swc = _stream_weights(w_cond, x_vis.device, dims.w_dtype)
     args = (ctypes.byref(dims), ctypes.byref(swv), ctypes.byref(swc), x_vis.data_ptr(),
             _ptr(x_cond) if n_cond else None, _dt(x_vis), tvec.data_ptr(), _dt(tvec),
             ctypes.byref(rope), n_cond, out_vis.data_ptr(), _ptr(out_cond) if n_cond else None,

@@ -29,7 +29,8 @@ static int validate_dims(const mmdit_block_dims* d, int64_t B, int64_t n_vis, in
   if (d->qk_scale_head_stride != 0 && d->qk_scale_head_stride != d->D)
     return fail(MMDIT_ERR_SHAPE, "block: qk_scale_head_stride must be 0 or D");
   if (!(d->ln_eps >= 0.f) || !(d->qk_eps >= 0.f)) return fail(MMDIT_ERR_SHAPE, "block: eps must be >= 0");
-  if (d->w_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "block: weights must be bf16");
+  if (d->w_dtype != MMDIT_BF16 && !(d->w_dtype == MMDIT_F16 && d->act_dtype == MMDIT_F16))
+    return fail(MMDIT_ERR_DTYPE, "block: w_dtype must be bf16, or f16 with act_dtype f16");
   if (d->act_dtype != MMDIT_BF16 && d->act_dtype != MMDIT_F16) return fail(MMDIT_ERR_DTYPE, "block: act_dtype must be bf16 or f16");
   return MMDIT_OK;
 }
@@ -44,7 +45,7 @@ static void layout(const mmdit_block_dims* d, int64_t B, int64_t n_vis, int64_t 
   const int64_t ns[2] = {n_vis, n_cond};
   for (int s = 0; s < 2; ++s) {
     const size_t n = (size_t)(B * ns[s]);
-    const bool cvt = d->act_dtype != d->w_dtype;   // bf16 weights, f16 operands
+    const bool cvt = d->act_dtype != d->w_dtype;   // bf16 matrices, f16 operands: per-call copies
     const size_t sz[MMDIT_WS_COUNT] = {(size_t)B * 6 * C * 4, n * C * 2, n * 3 * C * 2, n * C * 4, n * F * 2,
                                        cvt ? 3 * C * C * 2 : 0, cvt ? C * C * 2 : 0,
                                        cvt ? F * C * 2 : 0, cvt ? C * F * 2 : 0,

@@ -35,6 +35,10 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return f32_to_f16_bits(a) | (f32_to_f16_bits(b) << 16);
 }
+// Range guard for the f16 intermediates (GEMM outputs, LN-modulated activations): a value
+// beyond the f16 range saturates at +-65504 instead of rounding to infinity, which would turn
+// into NaN downstream (LayerNorm, attention); NaN stays NaN.
+__device__ __forceinline__ float sat_f16(float v) { return fabsf(v) > 65504.0f ? copysignf(65504.0f, v) : v; }
 __device__ __forceinline__ float lo_f16(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
 }

@@ -133,9 +133,9 @@ __device__ __forceinline__ void store4(void* base, int64_t idx, const float (&v)
   } else if constexpr (DT == MMDIT_BF16) {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
         make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  } else {
+  } else {   // f16 outputs are intermediates of the block: range-guarded
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
-        make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
+        make_uint2(pack_f16x2(sat_f16(v[0]), sat_f16(v[1])), pack_f16x2(sat_f16(v[2]), sat_f16(v[3])));
   }
 }
 

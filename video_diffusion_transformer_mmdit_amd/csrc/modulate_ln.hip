@@ -73,7 +73,10 @@ __global__ __launch_bounds__(MLN_THREADS) void modulate_ln_kernel(
       load8<MMDIT_F32>(sh, ch * 8, s8);
       load8<MMDIT_F32>(sc, ch * 8, c8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = fmaf((v[i][e] - mean) * rstd, 1.0f + c8[e], s8[e]);
+      for (int e = 0; e < 8; ++e) {
+        o[e] = fmaf((v[i][e] - mean) * rstd, 1.0f + c8[e], s8[e]);
+        if constexpr (YDT == MMDIT_F16) o[e] = sat_f16(o[e]);
+      }
       store8<YDT>(y, base + ch * 8, o);
     }
   }
