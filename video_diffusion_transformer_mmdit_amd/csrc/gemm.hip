@@ -4,18 +4,17 @@
 // kernel runs the Lite model's 2x2 hidden-space merge and unpatchify (section 2.4), with the
 // neighbour gather folded into the x loads and the scatter back to the grid into the stores.
 //
-// gfx950 design (two kernels share the tile, fragment layout and tile order: gemm_k64_kernel
-// for 16-bit operands in every layout, gemm_fp8_kernel for FP8 operands):
-//   - 256 x 256 output tile per workgroup.  16-bit: 8 wave64s, two per SIMD, arranged 2 (M)
-//     x 4 (N), each owning 128 x 64 outputs = 4 x 2 tiles of 32 x 32 MFMAs (128 accumulator
-//     registers).  FP8: 4 wave64s, one per SIMD, 2 x 2, each 128 x 128 outputs (256
-//     accumulator registers in AGPRs).  The MFMA computes C^T (A operand = W rows, B operand
-//     = x rows), so every lane ends up holding four consecutive output columns of one row, 32
-//     rows apart from its neighbours'.
+// gfx950 design (two kernels share the tile, fragment layout, tile order and epilogue:
+// gemm_k64_kernel for 16-bit operands in every layout, gemm_fp8_kernel for FP8 operands):
+//   - 256 x 256 output tile per workgroup of 8 wave64s, two per SIMD, arranged 2 (M) x 4
+//     (N), each owning 128 x 64 outputs = 4 x 2 tiles of 32 x 32 MFMAs (128 accumulator
+//     registers, so two waves fit a SIMD and cover each other's fragment-read waits).  The
+//     MFMA computes C^T (A operand = W rows, B operand = x rows), so every lane ends up
+//     holding four consecutive output columns of one row, 32 rows apart from its neighbours'.
 //   - x and W tiles are K-contiguous in LDS, so both MFMA operands are plain 16-byte LDS
 //     reads, and move by LDS-DMA (buffer loads straight into LDS) issued between the MFMAs.
 //     16-bit: two stages of K = 64 (rows of 128 bytes), one barrier per stage, the next
-//     stage's loads in four fenced groups.  FP8: four stages of 64 bytes per row, the DMA
+//     stage's loads in two fenced groups.  FP8: four stages of 64 bytes per row, the DMA
 //     three stages ahead.  Stage buffers are distinct LDS objects addressed with compile-time
 //     indices, and the DMA destinations pass through an opaque register copy, so the
 //     compiler's wait-count pass leaves every wait to the explicit per-stage ones.
@@ -197,22 +196,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, int nk, int& pi,
   }
 }
 
-// Partial sums of one split workgroup: wave w's accumulator (j, i), element e, lane l at
-// part[((idx * 4 + w) * 16 + 4 j + i) * 16 + e) * 64 + l]: 64 consecutive floats per store
+// Partial sums of one split workgroup: wave w's accumulator (j, i) (j < 2), element e, lane l
+// at part[((idx * 8 + w) * 8 + 4 j + i) * 16 + e) * 64 + l]: 64 consecutive floats per store
 // (stores straight from the accumulator registers; a float4 layout costs register spills).
-__device__ __forceinline__ void gemm_store_part(const GemmArgs& args, int64_t idx, int wave, int lane,
-                                                const f32x16 (&acc)[4][4]) {
-  float* base = args.part + ((idx * 4 + wave) * 16) * 16 * 64 + lane;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) base[((4 * j + i) * 16 + e) * 64] = acc[j][i][e];
-}
-
-// The same for the 8-wave kernel: wave w's accumulator (j, i) (j < 2), element e, lane l at
-// part[((idx * 8 + w) * 8 + 4 j + i) * 16 + e) * 64 + l].
 __device__ __forceinline__ void gemm_store_part8(const GemmArgs& args, int64_t idx, int wave, int lane,
                                                  const f32x16 (&acc)[2][4]) {
   float* base = args.part + ((idx * 8 + wave) * 8) * 16 * 64 + lane;
@@ -260,44 +246,44 @@ __device__ __forceinline__ void res_unpack(const ResRaw<RES_DT>& r, float (&v)[4
 }
 
 // Epilogue of a 256 x 256 tile through LDS, so that the residual loads and the output stores
-// run along rows: wave w restages its 128 x 128 block a quarter (32 rows, accumulators i = q)
-// at a time as f32 in its own LDS region, rows 132 floats apart (the 4-float pad spreads the
-// rows one 16-lane group touches over distinct bank groups), then reads it back two rows per
-// instruction, 32 lanes x 4 columns per row, and applies the FP8 scales, bias, GELU or the
+// run along rows: wave w restages its 128 x 64 block a quarter (32 rows, accumulators i = q)
+// at a time as f32 in its own LDS region, rows 68 floats apart (the 4-float pad spreads the
+// rows one 16-lane group touches over distinct bank groups), then reads it back four rows per
+// instruction, 16 lanes x 4 columns per row, and applies the FP8 scales, bias, GELU or the
 // gated residual to four consecutive outputs per lane.  GEMM_SCATTER_Y: logical output row
 // m, column n goes to column n % C of the full-grid token merged_row0(m) + (s / 2) W + s % 2,
-// s = n / C (a 128-wide block lies inside one s, as C is a multiple of 256).  `region` holds
-// 32 x 132 floats; the caller has made every wave's reads of the K stages complete.
+// s = n / C (a 64-wide block lies inside one s, as C is a multiple of 256).  `region` holds
+// 32 x 68 floats; the caller has made every wave's reads of the K stages complete.
 // Gated residual: the residual of a group of four rows is loaded while the previous group is
 // computed (the quarter's first group before its restaging), so the loads of consecutive
 // groups overlap instead of each group waiting a full memory round trip (all CUs finish their
 // K loops together, and the row-by-row epilogue was bound by the load latency of that burst).
-constexpr int G_EPI_STRIDE = 132;                        // floats per restaged row
-constexpr int G_EPI_BYTES = 32 * G_EPI_STRIDE * 4;       // one wave's quarter block: 16.5 KiB
-template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
-__device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const GemmProblem& Pk,
-                                                   const f32x16 (&acc)[4][4], int m0, int n0, int wm, int wn,
-                                                   int lane, float* region) {
-  constexpr bool FP8 = IN_DT == MMDIT_FP8_E4M3;
+constexpr int G8_THREADS = 512;                         // the 8-wave kernels' workgroup
+constexpr int G8_EPI_STRIDE = 68;                       // floats per restaged row
+constexpr int G8_EPI_BYTES = 32 * G8_EPI_STRIDE * 4;    // one wave's quarter block: 8.5 KiB
+template <int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT, bool FP8 = false>
+__device__ __forceinline__ void gemm_epilogue_rows8(const GemmArgs& args, const GemmProblem& Pk,
+                                                    const f32x16 (&acc)[2][4], int m0, int n0, int wm, int wn,
+                                                    int lane, float* region) {
   // a private copy of the problem: read through the reference, its pointers were reloaded
   // from the kernel arguments after every output store (one scalar load and wait per row)
   const GemmProblem P = Pk;
   const int64_t M = P.M, N = args.N;
   const int l32 = lane & 31, g = lane >> 5;
-  // this lane's four columns in the read phase, their bias
-  const int64_t n = n0 + wn * 128 + 4 * l32;
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const int64_t n = n0 + wn * 64 + 4 * c16;
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
   if (P.bias && n < N) load4<BIAS_DT>(P.bias, n, bias);
   float sw = 1.f;
   if constexpr (FP8) sw = *P.w_scale;
   int sg = 0;
-  if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 128) / args.c;
+  if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 64) / args.c;
   constexpr bool GRES = EPI == MMDIT_EPI_GATED_RES;
-  // residual of rows r0 + 2 k + g (k = 0..3) of quarter q
+  // residual of rows r0 + 4 k + r4 (k = 0..3) of quarter q
   auto res_group = [&](int q, int r0, ResRaw<RES_DT> (&rr)[4]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int64_t m = m0 + wm * 128 + q * 32 + r0 + 2 * k + g;
+      const int64_t m = m0 + wm * 128 + q * 32 + r0 + 4 * k + r4;
       if (m < M && n < N) res_load<RES_DT>(P.res, m * N + n, rr[k]);
     }
   };
@@ -305,28 +291,24 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
   for (int q = 0; q < 4; ++q) {
     ResRaw<RES_DT> rc[4], rn[4];
     if constexpr (GRES) res_group(q, 0, rc);
-    // accumulator (j, q) element e: row l32, column j * 32 + 8 (e / 4) + 4 g + e % 4 (written
-    // element by element, which the compiler merges into 16-byte writes; spelled as float4
-    // writes, it copied the accumulators out first and spilled)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) region[l32 * G_EPI_STRIDE + j * 32 + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[j][q][e];
+      for (int e = 0; e < 16; ++e) region[l32 * G8_EPI_STRIDE + j * 32 + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[j][q][e];
     __syncthreads();
 #pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += 8) {
+    for (int r0 = 0; r0 < 32; r0 += 16) {
       if constexpr (GRES) {
-        if (r0 + 8 < 32) res_group(q, r0 + 8, rn);
+        if (r0 + 16 < 32) res_group(q, r0 + 16, rn);
       }
-      // four rows' reads in flight before the first store
       float4 a4[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        a4[k] = *reinterpret_cast<const float4*>(region + (r0 + 2 * k + g) * G_EPI_STRIDE + 4 * l32);
+        a4[k] = *reinterpret_cast<const float4*>(region + (r0 + 4 * k + r4) * G8_EPI_STRIDE + 4 * c16);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float4 a = a4[k];
-        const int64_t m = m0 + wm * 128 + q * 32 + r0 + 2 * k + g;
+        const int64_t m = m0 + wm * 128 + q * 32 + r0 + 4 * k + r4;
         if (m >= M || n >= N) continue;
         float v[4];
         if constexpr (FP8) {
@@ -362,89 +344,10 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs& args, const G
   }
 }
 
-// Epilogue of the 8-wave kernel (16-bit operands): wave w restages its 128 x 64 block a quarter
-// (32 rows, accumulators i = q) at a time as f32 in its own LDS region (rows 68 floats apart),
-// reads it back four rows per instruction, 16 lanes x 4 columns per row, and applies bias, GELU
-// or the gated residual (residual rows loaded one group ahead, as above).  GEMM_SCATTER_Y: as
-// above (a 64-wide block lies inside one s).  `region` holds 32 x 68 floats.
-constexpr int G8_EPI_STRIDE = 68;                       // floats per restaged row
-constexpr int G8_EPI_BYTES = 32 * G8_EPI_STRIDE * 4;    // one wave's quarter block: 8.5 KiB
-template <int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT>
-__device__ __forceinline__ void gemm_epilogue_rows8(const GemmArgs& args, const GemmProblem& Pk,
-                                                    const f32x16 (&acc)[2][4], int m0, int n0, int wm, int wn,
-                                                    int lane, float* region) {
-  const GemmProblem P = Pk;   // a private copy (see gemm_epilogue_rows)
-  const int64_t M = P.M, N = args.N;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int c16 = lane & 15, r4 = lane >> 4;
-  const int64_t n = n0 + wn * 64 + 4 * c16;
-  float bias[4] = {0.f, 0.f, 0.f, 0.f};
-  if (P.bias && n < N) load4<BIAS_DT>(P.bias, n, bias);
-  int sg = 0;
-  if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 64) / args.c;
-  constexpr bool GRES = EPI == MMDIT_EPI_GATED_RES;
-  // residual of rows r0 + 4 k + r4 (k = 0..3) of quarter q
-  auto res_group = [&](int q, int r0, ResRaw<RES_DT> (&rr)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t m = m0 + wm * 128 + q * 32 + r0 + 4 * k + r4;
-      if (m < M && n < N) res_load<RES_DT>(P.res, m * N + n, rr[k]);
-    }
-  };
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ResRaw<RES_DT> rc[4], rn[4];
-    if constexpr (GRES) res_group(q, 0, rc);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) region[l32 * G8_EPI_STRIDE + j * 32 + 8 * (e >> 2) + 4 * g + (e & 3)] = acc[j][q][e];
-    __syncthreads();
-#pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += 16) {
-      if constexpr (GRES) {
-        if (r0 + 16 < 32) res_group(q, r0 + 16, rn);
-      }
-      float4 a4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        a4[k] = *reinterpret_cast<const float4*>(region + (r0 + 4 * k + r4) * G8_EPI_STRIDE + 4 * c16);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 a = a4[k];
-        const int64_t m = m0 + wm * 128 + q * 32 + r0 + 4 * k + r4;
-        if (m >= M || n >= N) continue;
-        float v[4] = {a.x + bias[0], a.y + bias[1], a.z + bias[2], a.w + bias[3]};
-        if constexpr (GRES) {
-          const int64_t b = (uint32_t)m / (uint32_t)P.rows_per_batch;
-          float r[4], gt[4];
-          res_unpack<RES_DT>(rc[k], r);
-          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = fmaf(gt[c], v[c], r[c]);
-        } else {
-          gemm_epi_tail<EPI, RES_DT>(P, N, m, n, v);
-        }
-        if constexpr (LAYOUT == GEMM_SCATTER_Y) {
-          const int64_t yr = (int64_t)merged_row0((int)m, args) + (sg >> 1) * args.w + (sg & 1);
-          store4<Y_DT>(P.y, yr * args.c + (n - (int64_t)sg * args.c), v);
-        } else {
-          store4<Y_DT>(P.y, m * N + n, v);
-        }
-      }
-      if constexpr (GRES) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) rc[k] = rn[k];
-      }
-    }
-    __syncthreads();
-  }
-}
-
 // FP8 operands (E4M3 codes, one byte per element): four LDS stages of K = 64, rows of 64
 // bytes; each 32 x 32 output tile takes one 32 x 32 x 64 MFMA per stage.
 template <int BIAS_DT, int Y_DT, int EPI, int RES_DT>
-__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(G8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_kernel(GemmArgs args) {
   constexpr int KSTEP = 64;   // K values per stage (64 bytes per row)
   // one LDS object per stage: x tile, then W tile
@@ -462,35 +365,31 @@ void gemm_fp8_kernel(GemmArgs args) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // ---- LDS-DMA: wave w fills rows 64w .. 64w+63 of the x tile and of the W tile with four
-  // 1 KiB loads each (lane l -> row 64w + 16i + l/4, physical chunk l % 4).  The immediate
+  // ---- LDS-DMA: wave w fills rows 32w .. 32w+31 of the x tile and of the W tile with two
+  // 1 KiB loads each (lane l -> row 32w + 16i + l/4, physical chunk l % 4).  The immediate
   // offset i * 1024 moves the LDS destination and the source alike and is taken back out of
-  // the per-lane offset, so all loads of a tile share one LDS base; the K position goes in
+  // the per-lane offset, so both loads of a tile share one LDS base; the K position goes in
   // the scalar offset, which the range check ignores.  Rows past M or N load zeros.
   const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(P.x, M * K);
   const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(P.w, N * K);
-  int xo[4], wo[4];
+  int xo[2], wo[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 64 * wave + 16 * i + (lane >> 2);
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * wave + 16 * i + (lane >> 2);
     const int lc = (lane & 3) ^ swz(row);
     xo[i] = (m0 + row) * (int)K + lc * 16 - i * 1024;
     wo[i] = (n0 + row) * (int)K + lc * 16 - i * 1024;
   }
   auto dma = [&](uint8_t* xs, uint8_t* ws, int k0) {
     const int so = k0 + kb * KSTEP;
-    auto* lx = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 4096));
-    auto* lw = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 4096));
+    auto* lx = opaque_lds((__attribute__((address_space(3))) void*)(xs + wave * 2048));
+    auto* lw = opaque_lds((__attribute__((address_space(3))) void*)(ws + wave * 2048));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[0], so, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lx, 16, xo[3], so, 3072, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[0], so, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[1], so, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[2], so, 2048, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lw, 16, wo[3], so, 3072, 0);
   };
   auto xbuf = [&](auto s) -> uint8_t* {
     constexpr int v = decltype(s)::value;
@@ -509,9 +408,9 @@ void gemm_fp8_kernel(GemmArgs args) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) cofs[h] = l32 * 64 + (((2 * h + g) ^ swz(l32)) << 4);
 
-  f32x16 acc[4][4];   // [n tile][m tile] of C^T
+  f32x16 acc[2][4];   // [n tile][m tile] of C^T
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -524,15 +423,15 @@ void gemm_fp8_kernel(GemmArgs args) {
     asm volatile("" ::: "memory");
   };
   // The whole 32-byte fragments of a stage (both 16-byte halves) are read one stage ahead into
-  // one of two register sets (stage parity), while the 16 MFMAs of the current stage run on
+  // one of two register sets (stage parity), while the 8 MFMAs of the current stage run on
   // the other.
-  uint4 fw8[2][4][2], fx8[2][4][2];
+  uint4 fw8[2][2][2], fx8[2][4][2];
   auto read8 = [&](const uint8_t* xs, const uint8_t* ws, auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fw8[BUF][j][h] = *reinterpret_cast<const uint4*>(ws + (wn * 128 + j * 32) * 64 + cofs[h]);
+      for (int j = 0; j < 2; ++j) fw8[BUF][j][h] = *reinterpret_cast<const uint4*>(ws + (wn * 64 + j * 32) * 64 + cofs[h]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) fx8[BUF][i][h] = *reinterpret_cast<const uint4*>(xs + (wm * 128 + i * 32) * 64 + cofs[h]);
     }
@@ -551,23 +450,27 @@ void gemm_fp8_kernel(GemmArgs args) {
     if (MAIN || kt + 3 < nk) dma(xbuf(ahead), wbuf(ahead), (kt + 3) * KSTEP);
     if (MAIN || kt + 1 < nk) read8(xbuf(next), wbuf(next), nbuf);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[j][i] = mfma_fp8(fw8[buf][j][0], fw8[buf][j][1], fx8[buf][i][0], fx8[buf][i][1], acc[j][i]);
-    // one fragment read after each MFMA, the eight DMA loads among MFMAs 2-9 (fencing the DMA
-    // in two groups as in the 16-bit kernel measured ~1 % slower here)
+    // the twelve fragment reads among the eight MFMAs, the four DMA loads among MFMAs 1-4
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+      if (MAIN) __builtin_amdgcn_sched_group_barrier(0x010, 1, 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-      if (MAIN && i >= 2 && i < 10) __builtin_amdgcn_sched_group_barrier(0x010, 1, 2);
     }
     // the MFMAs only touch registers: keep the scheduler from moving them past the barrier
     __builtin_amdgcn_sched_barrier(0);
-    // this wave's loads of stage kt+2 have landed once at most the eight loads of stage kt+3
+    // this wave's loads of stage kt+2 have landed once at most the four loads of stage kt+3
     // are outstanding; after the barrier stage kt+2 is in LDS for everyone
-    if (MAIN || kt + 3 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    if (MAIN || kt + 3 < nk) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
     gbarrier();
   };
@@ -578,7 +481,7 @@ void gemm_fp8_kernel(GemmArgs args) {
   if (1 < nk) dma(xbuf(S1), wbuf(S1), KSTEP);
   if (2 < nk) dma(xbuf(S2), wbuf(S2), 2 * KSTEP);
   // stages 0 and 1 must be in LDS; stage 2 may still be in flight
-  if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+  if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
   else __builtin_amdgcn_s_waitcnt(0x0F70);
   gbarrier();
   read8(xbuf(S0), wbuf(S0), std::integral_constant<int, 0>{});
@@ -598,14 +501,14 @@ void gemm_fp8_kernel(GemmArgs args) {
   if (kt + 5 < nk) step(S1, TAIL, kt + 5);
 
   if (part_idx >= 0) {
-    gemm_store_part(args, part_idx, wave, lane, acc);
+    gemm_store_part8(args, part_idx, wave, lane, acc);
   } else {
-    // every wave's fragment reads of the last stage are done after this barrier; wave w
-    // restages in stage buffer w
+    // every wave's fragment reads of the last stage are done after this barrier; waves
+    // 3s .. 3s+2 restage in stage buffer s (three 8.5 KiB regions per 32 KiB buffer)
     __syncthreads();
-    uint8_t* rb = wave == 0 ? lds_s0 : wave == 1 ? lds_s1 : wave == 2 ? lds_s2 : lds_s3;
-    gemm_epilogue_rows<MMDIT_FP8_E4M3, BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN>(args, P, acc, m0, n0, wm, wn, lane,
-                                                                             reinterpret_cast<float*>(rb));
+    uint8_t* rb = wave < 3 ? lds_s0 : wave < 6 ? lds_s1 : lds_s2;
+    gemm_epilogue_rows8<BIAS_DT, Y_DT, EPI, RES_DT, GEMM_PLAIN, true>(
+        args, P, acc, m0, n0, wm, wn, lane, reinterpret_cast<float*>(rb + (wave % 3) * G8_EPI_BYTES));
   }
 }
 
@@ -623,7 +526,6 @@ void gemm_fp8_kernel(GemmArgs args) {
 // merged_row0(m) + (s / 2) W + s % 2, s = k / C (a 64-wide K stage never straddles two
 // neighbours, as C is a multiple of 256): the per-row part is per lane, the neighbour part
 // scalar.  GEMM_SCATTER_Y is the epilogue's.
-constexpr int G8_THREADS = 512;
 template <int IN_DT, int BIAS_DT, int Y_DT, int EPI, int RES_DT, int LAYOUT = GEMM_PLAIN>
 __global__ __launch_bounds__(G8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_k64_kernel(GemmArgs args) {
@@ -835,7 +737,7 @@ static void gemm_go(const GemmArgs& a, hipStream_t st) {
     gemm_k64_kernel<IN_DT, BIAS_DT, Y_DT, EPI, RES_DT, LAYOUT><<<dim3((unsigned)a.tiles), G8_THREADS, 0, st>>>(a);
   } else {
     static_assert(LAYOUT == GEMM_PLAIN, "FP8 operands use the plain layout");
-    gemm_fp8_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), GTHREADS, 0, st>>>(a);
+    gemm_fp8_kernel<BIAS_DT, Y_DT, EPI, RES_DT><<<dim3((unsigned)a.tiles), G8_THREADS, 0, st>>>(a);
   }
 }
 
