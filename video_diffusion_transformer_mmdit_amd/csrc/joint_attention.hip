@@ -17,13 +17,16 @@
 //   - P^T comes straight from those accumulators (rounded to f16) as the B operand of
 //     O^T = V^T P^T; O^T accumulates 128 dims x 32 queries per wave in registers.  The V^T
 //     operand is read from row-major V tiles with ds_read_b64_tr_b16.
-//   - K and V tiles of 64 keys reach LDS by LDS-DMA (buffer loads straight into LDS, two
-//     stages each, XOR-swizzled chunks for conflict-free reads).
+//   - K and V tiles of 128 keys reach LDS by LDS-DMA (buffer loads straight into LDS, two
+//     stages each, 128 KiB in all, XOR-swizzled chunks for conflict-free reads).
 //   - Two wave groups ping-pong: a wave alternates an MFMA-only phase (S of the next tile,
-//     P V of this one) and a VALU-only phase (max, lazy rescale, exp2), one group a phase
-//     behind the other, so on every SIMD the matrix pipe and the VALU work concurrently.
-//   - exp2 with log2(e) * softmax_scale folded into one FMA per score; the running max is
-//     only raised when a score exceeds it by more than 2^8 (lazy rescale).
+//     P V of this one: 64 MFMAs) and a VALU-only phase (max, lazy rescale, exp2), one group
+//     a phase behind the other, so on every SIMD the matrix pipe and the VALU work
+//     concurrently; each phase ends with a workgroup barrier, whose pipeline fill and drain
+//     a 128-key tile pays half as often as a 64-key one.
+//   - exp2 with log2(e) * softmax_scale folded into Q; the S^T accumulators start from minus
+//     the running max (a constant C operand of each chain's first MFMA), and the running max
+//     is only raised when a score exceeds it by more than 2^8 (lazy rescale).
 //   - Precision: S = Q K^T runs on the operand type of Q and K (f16 or bf16); P is rounded
 //     to f16 (P lies in [0, 2^8], where f16 keeps 3 more mantissa bits than bf16) and PV runs
 //     on f16 MFMA, so a bf16 V is converted to f16 after it is read from LDS.
@@ -38,9 +41,9 @@ namespace mmdit {
 
 constexpr int ATT_D = 128;
 constexpr int ATT_BM = 256;                       // queries per workgroup (8 waves x 32)
-constexpr int ATT_BN = 64;                        // keys per tile
+constexpr int ATT_BN = 128;                       // keys per tile
 constexpr int ATT_THREADS = 512;
-constexpr int ATT_K_BYTES = ATT_BN * ATT_D * 2;   // 16 KiB
+constexpr int ATT_K_BYTES = ATT_BN * ATT_D * 2;   // 32 KiB
 constexpr float ATT_RESCALE_LOG2 = 8.0f;          // lazy rescale threshold: P <= 2^8
 #ifndef ATT_LDS_AHEAD
 #define ATT_LDS_AHEAD 4                           // MFMAs between an LDS operand read and its use
@@ -142,11 +145,38 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int& bh, int
   }
 }
 
+// Offset of an LDS object in the LDS aperture.  A DS instruction reaches 64 KiB past its
+// address register through its immediate offset; the kernel's four 32 KiB stage buffers
+// span 128 KiB, so reads of a buffer above the first 64 KiB take lane offsets biased by
+// 64 KiB (kept opaque, so that the compiler folds only the buffer's remainder and the
+// compile-time part of each read into the immediate).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Instruction order of an MFMA phase: 32 MFMAs of S^T (one K fragment read each), then 32 of
+// O^T (two V^T fragment reads each), every LDS operand read ATT_LDS_AHEAD MFMAs ahead of its
+// use; with DMA, the phase's eight LDS-DMA loads follow its first eight MFMAs.
+constexpr int att_reads(int n) { return n < 32 ? 1 : n < 64 ? 2 : 0; }
+constexpr int att_first_reads(int n = 0) { return n < ATT_LDS_AHEAD ? att_reads(n) + att_first_reads(n + 1) : 0; }
+
+template <bool DMA, int I = 0>
+__device__ __forceinline__ void m_phase_schedule() {
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, att_first_reads(), 1);
+  if constexpr (I < 64) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    if constexpr (att_reads(I + ATT_LDS_AHEAD) > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, att_reads(I + ATT_LDS_AHEAD), 1);
+    if constexpr (DMA && I < 8) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
+    m_phase_schedule<DMA, I + 1>();
+  }
+}
+
 template <int QK_DT, int V_DT, int OUT_DT, bool LSE>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void joint_attn_mfma_kernel(AttnArgs a) {
-  // LDS: two K stages and two V stages, 16 KiB each, rows of 256 bytes (one key, 128 dims).
-  // Four distinct objects, always addressed with a compile-time stage index, so the wait-count
+  // LDS: two K stages and two V stages, 32 KiB each (128 keys of 256-byte rows).  Four
+  // distinct objects, always addressed with a compile-time stage index, so the wait-count
   // pass can tell an LDS-DMA into one stage from reads of another and does not stall the
   // reads on the prefetch in flight.
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[ATT_K_BYTES];
@@ -222,7 +252,7 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   constexpr std::integral_constant<int, 0> S0{};
   constexpr std::integral_constant<int, 1> S1{};
 
-  // ---- per-lane LDS read offsets
+  // ---- per-lane LDS read offsets (each biased by 64 KiB for a stage buffer above 64 KiB)
   // S^T A operand: key = 32*st + l32, logical chunk 2*ks + g, physical chunk ^ (key % 16)
   int k_rd[8];
 #pragma unroll
@@ -241,34 +271,43 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       v_rd[dt] = (4 * gg + (j >> 2)) * 256 + chunk * 16 + (j & 1) * 8;
     }
   }
+  // (the same bias serves both stages of K and of V: a stage placed elsewhere still reads the
+  // right bytes, its reads just do not fold the whole offset into the immediate)
+  const uint32_t khi = lds_offset(lds_k0) & 0xFFFF0000u, vhi = lds_offset(lds_v0) & 0xFFFF0000u;
+  if (khi) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) { k_rd[ks] += (int)khi; asm volatile("" : "+v"(k_rd[ks])); }
+  }
+  if (vhi) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) { v_rd[dt] += (int)vhi; asm volatile("" : "+v"(v_rd[dt])); }
+  }
 
-  // S^T of one tile, accumulated onto s (set beforehand to minus the running max, so the
-  // product comes out relative to it); the two 32-key halves are independent accumulator
-  // chains, interleaved so that consecutive MFMAs never wait on each other's result
-  auto init_s = [&](f32x16 (&s)[2], float v) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[st][e] = v;
-  };
-  auto compute_s = [&](const uint8_t* kb, f32x16 (&s)[2]) {
+  // S^T of one tile: four independent 32-key accumulator chains, interleaved so that
+  // consecutive MFMAs never wait on each other's result; the first MFMA of each chain takes
+  // `base` (minus the running max in accumulator units, in every element) as its C operand,
+  // so the product comes out relative to the running max with no per-tile initialisation
+  auto compute_s = [&](const uint8_t* kb, f32x16 (&s)[4], const f32x16& base) {
+    kb -= khi;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) s[st] = mfma16<QK_DT>(lds_read16(kb + st * 8192 + k_rd[ks]), qf[ks], s[st]);
+      for (int st = 0; st < 4; ++st)
+        s[st] = mfma16<QK_DT>(lds_read16(kb + st * 8192 + k_rd[ks]), qf[ks], ks == 0 ? base : s[st]);
   };
-  auto row_max = [&](const f32x16 (&s)[2]) {   // max over this query's 64 keys (both half-waves)
+  auto row_max = [&](const f32x16 (&s)[4]) {   // max over this query's 128 keys (both half-waves)
     float m4[4];                                 // four independent chains, then a short tree
 #pragma unroll
-    for (int k = 0; k < 4; ++k) m4[k] = fmaxf(s[0][k], s[1][k]);
+    for (int k = 0; k < 4; ++k) m4[k] = fmaxf(fmaxf(s[0][k], s[1][k]), fmaxf(s[2][k], s[3][k]));
 #pragma unroll
     for (int e = 4; e < 16; e += 4)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) m4[k] = fmaxf(m4[k], fmaxf(s[0][e + k], s[1][e + k]));
+      for (int k = 0; k < 4; ++k)
+        m4[k] = fmaxf(fmaxf(m4[k], fmaxf(s[0][e + k], s[1][e + k])), fmaxf(s[2][e + k], s[3][e + k]));
     return xhalf_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
   };
   auto v_frag = [&](const uint8_t* vb, int dt, int ks) {
-    const uint8_t* p = vb + v_rd[dt] + ks * 4096;
+    const uint8_t* p = vb - vhi + v_rd[dt] + ks * 4096;
     const uint2 lo = lds_read_tr(p), hi = lds_read_tr(p + 2048);
     uint4 f = make_uint4(lo.x, lo.y, hi.x, hi.y);
     if constexpr (V_DT == MMDIT_BF16) {
@@ -286,11 +325,14 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   };
 
   // ---- Ping-pong of two wave groups.  Waves 0-3 (group 0) and 4-7 (group 1) each hold one
-  // wave on every SIMD.  Each wave alternates two phases per 64-key tile:
+  // wave on every SIMD.  Each wave alternates two phases per 128-key tile:
   //   M(j): S_{j+1} = K_{j+1} Q^T and O^T += V_j^T P_j^T -- MFMA and LDS reads only;
   //   V(j): mask, row max, lazy rescale and P_j = exp2(S_j - m) -- VALU only.
+  // One S accumulator set serves every tile: V(j) consumes S_j before M(j) writes S_{j+1}.
   // Group 1 runs one phase behind group 0 and every phase ends with a workgroup barrier, so
-  // on each SIMD one wave keeps the matrix pipe busy while the other runs the softmax.
+  // on each SIMD one wave keeps the matrix pipe busy while the other runs the softmax.  A
+  // tile of 128 keys gives each barrier 64 MFMAs: the pipeline fill and drain around a
+  // barrier is paid once per 128 keys.
   // Tiles move by LDS-DMA, issued between the MFMAs of M(j): group 0 loads V_{j+1} and waits
   // for it at the end of its V(j+1); group 1 loads K_{j+2} and waits at the end of its M(j).
   auto run = [&](auto grp_c) {
@@ -305,21 +347,24 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       seg_base[sg] = base ? base + (b * a.n_seg[sg]) * a.in_stride + h * ATT_D : (GRP ? a.k[0] : a.v[0]);
       seg_bytes[sg] = a.n_seg[sg] > 0 ? ((a.n_seg[sg] - 1) * a.in_stride + ATT_D) * 2 : 0;
     }
-    // DMA i of this wave fills tile rows 4*(4*wg+i) .. +3 in lane order (lane l -> row +
-    // l/16, physical 16-byte chunk l % 16).  K chunks are XOR-swizzled by (row % 16) for the
-    // column reads of S^T, V chunks by 4*(row % 4) for the transposed reads of O^T; each lane
-    // loads the logical chunk that belongs at its physical slot.  The descriptor starts at
-    // the tile and ends with the segment, so rows past the segment's end fail its range check
-    // and arrive as zeros.  All four loads share one LDS base (M0): the immediate offset
-    // i * 1024 moves both the LDS destination and the source, and is taken back out of the
-    // per-lane offset, which is therefore fixed for the whole loop.
+    // DMA i of this wave fills tile rows 32*wg + 4*i .. +3 and, 16 rows further on (scalar
+    // offset 16 rows, LDS 4 KiB further), 32*wg + 16 + 4*i .. +3, in lane order (lane l -> row
+    // + l/16, physical 16-byte chunk l % 16).  K chunks are XOR-swizzled by (row % 16) for the
+    // column reads of S^T, V chunks by 4*(row % 4) for the transposed reads of O^T (rows 16
+    // apart share the swizzle); each lane loads the logical chunk that belongs at its
+    // physical slot.  The descriptor starts at the tile and ends with the segment, so rows
+    // past the segment's end fail its range check and arrive as zeros.  Each half's four
+    // loads share one LDS base (M0): the immediate offset i * 1024 moves both the LDS
+    // destination and the source, and is taken back out of the per-lane offset, which is
+    // therefore fixed for the whole loop.
     int off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 4 * (4 * wg + i) + (lane >> 4);
+      const int row = 32 * wg + 4 * i + (lane >> 4);
       const int chunk = GRP ? ((lane & 15) ^ (row & 15)) : ((lane & 15) ^ ((row & 3) << 2));
       off[i] = row * stride * 2 + chunk * 16 - i * 1024;
     }
+    const int half_soff = 16 * stride * 2;
     auto dma_tile = [&](int jt, uint8_t* dst) {
       int sg, t;
       tile_seg(jt, sg, t);
@@ -327,11 +372,16 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>((sg ? seg_base[1] : seg_base[0]) + tile_elems), (short)0,
           (int)((sg ? seg_bytes[1] : seg_bytes[0]) - tile_elems * 2), 0x00020000);
-      auto* l = (__attribute__((address_space(3))) void*)(dst + wg * 4096);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[0], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[1], 0, 1024, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[2], 0, 2048, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, off[3], 0, 3072, 0);
+      auto* l0 = (__attribute__((address_space(3))) void*)(dst + wg * 8192);
+      auto* l1 = (__attribute__((address_space(3))) void*)(dst + wg * 8192 + 4096);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l0, 16, off[0], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l0, 16, off[1], 0, 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l0, 16, off[2], 0, 2048, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l0, 16, off[3], 0, 3072, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l1, 16, off[0], half_soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l1, 16, off[1], half_soff, 1024, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l1, 16, off[2], half_soff, 2048, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l1, 16, off[3], half_soff, 3072, 0);
     };
 
     f32x16 o[4];
@@ -342,10 +392,14 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     float m_run = 0.f;         // running max of the logits (log2 units), possibly stale by < 2^8;
                                // S accumulators hold logit - m_run in accumulator units
     float l_run = 0.f;         // this lane's partial sum of the probabilities
-    uint4 pf[4];               // P_j rounded to f16, the B operand of O^T
+    uint4 pf[8];               // P_j rounded to f16, the B operand of O^T
+    f32x16 mneg;               // -m_run in accumulator units: the C operand that starts S^T
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mneg[e] = 0.f;
+    asm volatile("" : "+v"(mneg));   // kept in registers, not rematerialised at each use
 
     // M(j): S_{j+1} (past the last tile from a stale stage; never used) and O^T += V_j^T P_j^T
-    auto phase_m = [&](auto cur_c, int jt, f32x16 (&sn)[2]) {
+    auto phase_m = [&](auto cur_c, int jt, f32x16 (&s)[4]) {
       constexpr int CUR = decltype(cur_c)::value;   // jt % 2
       constexpr std::integral_constant<int, CUR> cur{};
       constexpr std::integral_constant<int, CUR ^ 1> oth{};
@@ -354,40 +408,38 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       // last one into a stage nobody reads again.
       if constexpr (GRP == 0) dma_tile(jt + 1 < jend ? jt + 1 : jend - 1, vbuf(oth));
       else dma_tile(jt + 2 < jend ? jt + 2 : jend - 1, kbuf(cur));
-      compute_s(kbuf(oth), sn);
+      compute_s(kbuf(oth), s, mneg);
       const uint8_t* vb = vbuf(cur);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt] = mfma16<MMDIT_F16>(v_frag(vb, dt, ks), pf[ks], o[dt]);
-      // LDS operands are read ATT_LDS_AHEAD MFMAs ahead (K fragments: one read, V^T fragments: two)
-      __builtin_amdgcn_sched_group_barrier(0x100, ATT_LDS_AHEAD, 1);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (i + ATT_LDS_AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        else if (i + ATT_LDS_AHEAD < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        if (i < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
-      }
+      m_phase_schedule<true>();
       // the products must issue in this phase: pin their results ahead of the barrier (the
       // compiler would otherwise sink MFMAs into the softmax phase that first reads them)
-      asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
+      asm volatile("" ::"v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]));
       asm volatile("" ::"v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]));
       if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's K loads have landed
       phase_barrier();
     };
     // V(j): softmax of S_j into P_j
-    auto phase_v = [&](auto cur_c, int jt, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+    auto phase_v = [&](int jt, f32x16 (&s)[4]) {
       {  // keys past the end of their segment (a segment's partial last tile)
         int sg, t;
         tile_seg(jt, sg, t);
         const int valid = tile_rows(sg, t);
         if (valid < ATT_BN) {
+          // element e of chain st holds key 32 st + 8 (e / 4) + 4 g + e % 4: an arithmetic
+          // shift turns (valid - 1 - key) into an all-ones mask for keys past the end, and a
+          // bitfield insert puts -inf there (no per-element compare results to hold)
+          const int vl = valid - 1 - 4 * g;
 #pragma unroll
-          for (int st = 0; st < 2; ++st)
+          for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (st * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= valid) s[st][e] = -INFINITY;
+            for (int e = 0; e < 16; ++e) {
+              const uint32_t m = (uint32_t)((vl - (st * 32 + 8 * (e >> 2) + (e & 3))) >> 31);
+              s[st][e] = __uint_as_float((0xFF800000u & m) | (__float_as_uint(s[st][e]) & ~m));
+            }
         }
       }
       const float mx = row_max(s);
@@ -407,13 +459,17 @@ void joint_attn_mfma_kernel(AttnArgs a) {
         m_run += delta;
         const float d = delta * inv_ce;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 4; ++st)
 #pragma unroll
           for (int e = 0; e < 16; ++e) s[st][e] -= d;
+        const float mb = -m_run * inv_ce;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mneg[e] = mb;
+        asm volatile("" : "+v"(mneg));
       }
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 4; ++st) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           uint32_t w[4];
@@ -431,13 +487,10 @@ void joint_attn_mfma_kernel(AttnArgs a) {
         }
       }
       l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      // the next M phase accumulates S_{j+1} onto minus the running max
-      init_s(sn, -m_run * inv_ce);
-      // likewise pin P, l, m and the initialised accumulators: this VALU work belongs to this
-      // phase, not the next M phase
+      // pin P, l and m: this VALU work belongs to this phase, not the next M phase
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w));
-      asm volatile("" ::"v"(l_run), "v"(m_run), "v"(sn[0]), "v"(sn[1]));
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w));
+      asm volatile("" ::"v"(l_run), "v"(m_run), "v"(mneg));
       if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's V loads have landed
       phase_barrier();
     };
@@ -452,21 +505,20 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     __syncthreads();
     if constexpr (GRP == 1) phase_barrier();   // group 1 runs one phase behind
     if constexpr (GRP == 0) dma_tile(jbeg, lds_v0);
-    f32x16 sa[2], sb[2];
-    init_s(sa, 0.f);
-    compute_s(lds_k0, sa);
-    asm volatile("" ::"v"(sa[0]), "v"(sa[1]));
+    f32x16 s[4];
+    compute_s(lds_k0, s, mneg);
+    asm volatile("" ::"v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]));
     phase_barrier();
     int jt = jbeg;
     for (; jt + 1 < jend; jt += 2) {
-      phase_v(S0, jt, sa, sb);
-      phase_m(S0, jt, sb);
-      phase_v(S1, jt + 1, sb, sa);
-      phase_m(S1, jt + 1, sa);
+      phase_v(jt, s);
+      phase_m(S0, jt, s);
+      phase_v(jt + 1, s);
+      phase_m(S1, jt + 1, s);
     }
     if (jt < jend) {
-      phase_v(S0, jt, sa, sb);
-      phase_m(S0, jt, sb);
+      phase_v(jt, s);
+      phase_m(S0, jt, s);
     }
     if constexpr (GRP == 0) {   // drain the last (unused) V reload, then match group 1's extra barrier
       __builtin_amdgcn_s_waitcnt(0xF70);
