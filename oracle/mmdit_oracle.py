@@ -524,10 +524,11 @@ def quantize_fp8_groups(x: np.ndarray, axes) -> Tuple[np.ndarray, np.ndarray]:
 def attn8_quantize_stream(q: np.ndarray, k: np.ndarray):
     """INT8 codes and scales of one stream's Q^ and K^ (r26).  q, k [B, n, H, D].
     Returns q8 [B, n, H, D], sq [B, n, H], k8 [B, n, H, D], sk [B, H, ceil(n/64)]."""
-    b, n, h, d = q.shape
+    b, _, h, d = q.shape
+    n = k.shape[1]
     q8, sq = quantize_int8(q, axes=3)
     nb = -(-n // ATT8_KEY_BLOCK)
-    k8 = np.empty_like(q8)
+    k8 = np.empty(k.shape, dtype=np.float64)
     sk = np.empty((b, h, nb), dtype=np.float32)
     for j in range(nb):
         blk = k[:, j * ATT8_KEY_BLOCK:(j + 1) * ATT8_KEY_BLOCK]            # [B, <=64, H, D]
@@ -600,6 +601,101 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
         res = res + (np.concatenate([lse_c, lse_v], axis=2),)
     if return_row_sums:
         res = res + (sum_v, sum_c)
+    return res
+
+
+# ------------------------------------------------------- 8-bit block  [Wan-zh 4.4.3]
+#
+# The Wan report (section 4.4.3) serves the DiT with FP8 GEMMs (per-tensor weight scales,
+# per-token activation scales) and the 8-bit attention.  The 8-bit block is the block of
+# [Vimoo 2.2] (block_forward) with (reading r28):
+#   - each of its four Linears (QKV, output, FFN up, FFN down) the FP8 Linear of r24 / r25,
+#     the weight matrix quantized as one tensor (one scale for all of W_qkv's q, k and v
+#     rows), the activation per token;
+#   - the joint attention the 8-bit attention of r26 / r27;
+#   - the quantizers' inputs the block's stored 16-bit intermediates h, O, h2, GELU output
+#     and q^ | k^ | v, i.e. those tensors rounded to f16 (nearest even); the modulation, the
+#     LayerNorm statistics, the residual x1 and the outputs are not rounded.
+
+
+def f16_round(x: np.ndarray) -> np.ndarray:
+    """x rounded to IEEE binary16 (nearest even), back in float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def fp8_weight(w: np.ndarray) -> Tuple[np.ndarray, float]:
+    """A weight matrix quantized per tensor (r25): (E4M3 values, scale)."""
+    qw, sw = quantize_fp8(w, per_row=False)
+    return qw, float(sw[0])
+
+
+def fp8_linear_prequantized(x: np.ndarray, qw: np.ndarray, sw: float, b: Optional[np.ndarray]) -> np.ndarray:
+    """The FP8 Linear with an already quantized weight: x [..., K] quantized per token (r25),
+    the product of the quantized values exact, y = (q_x q_w^T) s_x s_w + b."""
+    qx, sx = quantize_fp8(x, per_row=True)
+    y = (qx @ qw.T) * sx.astype(np.float64)[..., None] * sw
+    return y if b is None else y + b
+
+
+def block_forward_8bit(x_vis: np.ndarray, x_cond: np.ndarray, tvec: np.ndarray,
+                       w_vis: Dict[str, np.ndarray], w_cond: Dict[str, np.ndarray],
+                       grid: Tuple[int, int, int], heads: int,
+                       ln_eps: float = 1e-6, qk_eps: float = 1e-6,
+                       split=(16, 56, 56), base: float = 10000.0,
+                       vis_rows: Optional[np.ndarray] = None,
+                       cond_rows: Optional[np.ndarray] = None,
+                       keep: bool = True) -> Dict[str, np.ndarray]:
+    """The 8-bit dual-stream block (r28): block_forward's steps with FP8 Linears and the
+    8-bit joint attention, each quantizer fed the f16 rounding of its input.  Arguments and
+    result as for block_forward (``*_rows`` restrict the query-side work to those rows)."""
+    c = x_vis.shape[-1]
+    d = c // heads
+    res: Dict[str, np.ndarray] = {}
+    mods, qkv, wq = {}, {}, {}
+    for s, x, w, rows in (("vis", x_vis, w_vis, vis_rows), ("cond", x_cond, w_cond, cond_rows)):
+        wq[s] = {k: fp8_weight(w[k]) for k in ("w_qkv", "w_o", "w_fc1", "w_fc2")}
+        mods[s] = modulation(w["w_mod"], w["b_mod"], tvec)
+        m = mods[s]
+        h = f16_round(modulate(layer_norm(x, ln_eps), m["shift_a"], m["scale_a"]))
+        b_, n_ = x.shape[:2]
+        qw, sw = wq[s]["w_qkv"]
+        qw_q, qw_k, qw_v = np.split(qw, 3, axis=0)
+        b_q, b_k, b_v = np.split(w["b_qkv"], 3)
+        hq = h if rows is None else h[:, rows]
+        # the stored projections are f16; q^ and k^ are normalised and rotated from them
+        q = f16_round(fp8_linear_prequantized(hq, qw_q, sw, b_q)).reshape(b_, hq.shape[1], heads, d)
+        k = f16_round(fp8_linear_prequantized(h, qw_k, sw, b_k)).reshape(b_, n_, heads, d)
+        v = f16_round(fp8_linear_prequantized(h, qw_v, sw, b_v)).reshape(b_, n_, heads, d)
+        qkv[s] = (q, k, v)
+        if keep:
+            res[f"h_{s}"] = hq
+            res[f"mod_{s}"] = np.concatenate([m[nm] for nm in MOD_ORDER], axis=-1)
+    q_v, k_v, v_v = qkv["vis"]
+    q_c, k_c, v_c = qkv["cond"]
+    ang = rope_angles(grid, split, base)
+    k_v = f16_round(rope_rotate(rms_norm_heads(k_v, w_vis["k_norm"], qk_eps), ang))
+    q_v = f16_round(rope_rotate(rms_norm_heads(q_v, w_vis["q_norm"], qk_eps),
+                                ang if vis_rows is None else ang[vis_rows]))
+    k_c = f16_round(rms_norm_heads(k_c, w_cond["k_norm"], qk_eps))
+    q_c = f16_round(rms_norm_heads(q_c, w_cond["q_norm"], qk_eps))
+    o_v, o_c = joint_attention_8bit(q_v, k_v, v_v, q_c, k_c, v_c)
+    if keep:
+        res["qh_vis"], res["qh_cond"] = q_v, q_c
+    for s, x, w, rows, o in (("vis", x_vis, w_vis, vis_rows, o_v),
+                             ("cond", x_cond, w_cond, cond_rows, o_c)):
+        m = mods[s]
+        xs = x if rows is None else x[:, rows]
+        o = f16_round(o.reshape(o.shape[0], o.shape[1], c))
+        a = fp8_linear_prequantized(o, *wq[s]["w_o"], w["b_o"])
+        x1 = xs + m["gate_a"][:, None, :] * a
+        h2 = f16_round(modulate(layer_norm(x1, ln_eps), m["shift_f"], m["scale_f"]))
+        g = f16_round(gelu(fp8_linear_prequantized(h2, *wq[s]["w_fc1"], w["b_fc1"])))
+        out = x1 + m["gate_f"][:, None, :] * fp8_linear_prequantized(g, *wq[s]["w_fc2"], w["b_fc2"])
+        res[f"out_{s}"] = out
+        if keep:
+            res[f"o_{s}"] = o
+            res[f"x1_{s}"] = x1
+            res[f"h2_{s}"] = h2
     return res
 
 

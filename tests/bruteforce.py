@@ -268,3 +268,60 @@ def attention_8bit(q_rows, k_rows, v_rows, seg_of_key, scale, round_fp8):
         ell = sum(p)
         outs.append([sum(p[j] * v8[j][c] for j in range(len(p))) * float(sv[c]) / ell for c in range(d)])
     return outs
+
+
+# ------------------------------------------------------------------ 8-bit block
+def f16_scalar(v):
+    """v rounded to IEEE binary16 through the struct module's half-precision packing."""
+    import struct
+    return struct.unpack("<e", struct.pack("<e", v))[0]
+
+
+def block_forward_8bit(x_vis, x_cond, tvec, w_vis, w_cond, grid, heads, ln_eps, qk_eps, round_fp8,
+                       split=(16, 56, 56), base=10000.0):
+    """The 8-bit block with loops: the block's steps with every Linear the FP8 Linear above
+    (weights quantized once per matrix, activations per row) and the attention the 8-bit
+    attention above, per head; h, q^ / k^ / v, O, h2 and the GELU output rounded to binary16
+    before they are quantized.  Same arguments as block_forward plus ``round_fp8``."""
+    c = len(x_vis[0]) if x_vis else len(x_cond[0])
+    d = c // heads
+    h16 = lambda rows: [[f16_scalar(v) for v in r] for r in rows]  # noqa: E731
+    streams = {"vis": (x_vis, w_vis), "cond": (x_cond, w_cond)}
+    mod, heads_qkv = {}, {}
+    for s, (x, w) in streams.items():
+        m = matvec(w["w_mod"], tvec, w["b_mod"])
+        mod[s] = [m[i * c:(i + 1) * c] for i in range(6)]
+        shift_a, scale_a = mod[s][0], mod[s][1]
+        hrows = [[v * (1.0 + sc) + sh for v, sc, sh in zip(layernorm_vec(xt, ln_eps), scale_a, shift_a)] for xt in x]
+        qkv = h16(fp8_linear(h16(hrows), w["w_qkv"], w["b_qkv"], round_fp8)) if x else []
+        heads_qkv[s] = qkv
+    per_head = {}
+    for hd in range(heads):
+        qs, keys, vals, seg = [], [], [], []
+        for s, gq, gk in (("vis", w_vis["q_norm"], w_vis["k_norm"]), ("cond", w_cond["q_norm"], w_cond["k_norm"])):
+            for n, r in enumerate(heads_qkv[s]):
+                q = rmsnorm_vec(r[hd * d:(hd + 1) * d], gq, qk_eps)
+                k = rmsnorm_vec(r[c + hd * d:c + (hd + 1) * d], gk, qk_eps)
+                if s == "vis":
+                    pos = decode_position(n, grid)
+                    q, k = rope_vec(q, pos, split, base), rope_vec(k, pos, split, base)
+                qs.append(([f16_scalar(v) for v in q], 0 if s == "vis" else 1))
+                keys.append([f16_scalar(v) for v in k])
+                vals.append(r[2 * c + hd * d:2 * c + (hd + 1) * d])
+                seg.append((0 if s == "vis" else 1, n))
+        per_head[hd] = attention_8bit(qs, keys, vals, seg, 1.0 / math.sqrt(d), round_fp8)
+    outs = {}
+    base_row = {"vis": 0, "cond": len(x_vis)}
+    for s, (x, w) in streams.items():
+        _, _, gate_a, shift_f, scale_f, gate_f = mod[s]
+        if not x:
+            outs[s] = []
+            continue
+        o_rows = h16([[v for hd in range(heads) for v in per_head[hd][base_row[s] + n]] for n in range(len(x))])
+        a = fp8_linear(o_rows, w["w_o"], w["b_o"], round_fp8)
+        x1 = [[xv + g * av for xv, g, av in zip(xt, gate_a, ar)] for xt, ar in zip(x, a)]
+        h2 = h16([[v * (1.0 + sc) + sh for v, sc, sh in zip(layernorm_vec(r, ln_eps), scale_f, shift_f)] for r in x1])
+        g = h16([[gelu(v) for v in r] for r in fp8_linear(h2, w["w_fc1"], w["b_fc1"], round_fp8)])
+        y = fp8_linear(g, w["w_fc2"], w["b_fc2"], round_fp8)
+        outs[s] = [[xv + gg * yv for xv, gg, yv in zip(r, gate_f, yr)] for r, yr in zip(x1, y)]
+    return outs["vis"], outs["cond"]

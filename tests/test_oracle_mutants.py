@@ -19,7 +19,8 @@ ORIG = {name: getattr(om, name) for name in
          "modulate", "layer_norm", "linear", "gelu", "modulation", "joint_attention",
          "timestep_sinusoid", "silu", "timestep_path", "lite_merge_gather", "lite_unpatchify",
          "fp8_e4m3_round", "quantize_fp8", "fp8_linear", "quant_scale",
-         "attn8_quantize_stream", "attn8_quantize_v", "quantize_int8", "joint_attention_8bit")}
+         "attn8_quantize_stream", "attn8_quantize_v", "quantize_int8", "joint_attention_8bit",
+         "f16_round", "fp8_weight", "fp8_linear_prequantized")}
 
 
 def _rope_sign(x, angles):
@@ -257,6 +258,20 @@ def _att8_variant(floor=False, shift=8.0, exact_sum=False):
     return f
 
 
+def _f16_not_rounded(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _fp8_weight_per_row(w):
+    qw, sw = om.quantize_fp8(w, per_row=True)
+    return qw * sw.astype(np.float64)[:, None], 1.0
+
+
+def _fp8_linear_requantize_slices(x, qw, sw, b):
+    # the weight slice handed in gets its own per-tensor scale (W_qkv's q, k, v separately)
+    return ORIG["fp8_linear_prequantized"](x, *ORIG["fp8_weight"](qw * sw), b)
+
+
 MUTANTS = {
     "rope_sign": ("rope_rotate", _rope_sign),
     "rope_band_order": ("rope_angles", _band_order),
@@ -295,6 +310,9 @@ MUTANTS = {
     "att8_floor_reference": ("joint_attention_8bit", _att8_variant(floor=True)),
     "att8_no_shift": ("joint_attention_8bit", _att8_variant(shift=0.0)),
     "att8_unquantized_row_sum": ("joint_attention_8bit", _att8_variant(exact_sum=True)),
+    "block8_no_f16_storage": ("f16_round", _f16_not_rounded),
+    "block8_weights_per_row": ("fp8_weight", _fp8_weight_per_row),
+    "block8_qkv_slice_scales": ("fp8_linear_prequantized", _fp8_linear_requantize_slices),
 }
 
 PIN_TESTS = [f for name, f in inspect.getmembers(pins, inspect.isfunction) if name.startswith("test_")]

@@ -671,3 +671,73 @@ def test_attention_8bit_stays_near_exact_attention():
     for x, y in zip(a, e):
         rms_err = np.sqrt(np.mean((x - y) ** 2)) / np.sqrt(np.mean(y ** 2))
         assert 0.005 < rms_err < 0.06, rms_err
+
+
+# ------------------------------------------------------------------ 8-bit block
+
+
+def _e4m3_nearest():
+    """Scalar E4M3 rounding (nearest, ties to the even code) by bisection over every finite
+    positive E4M3 value, the values decoded by torch's float8_e4m3fn."""
+    import bisect
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).tolist()
+
+    def rnd(v):
+        a = min(abs(v), 448.0)
+        i = bisect.bisect_left(vals, a)
+        if i == 0:
+            r = vals[0]
+        elif i == len(vals):
+            r = vals[-1]
+        else:
+            lo, hi = vals[i - 1], vals[i]
+            r = lo if (a - lo < hi - a or (a - lo == hi - a and (i - 1) % 2 == 0)) else hi
+        return math.copysign(r, v)
+    return rnd
+
+
+def _tiny_block8(seed=0):
+    # one head (C = 128) keeps the loops of the brute force short
+    return _tiny_block(seed=seed, c=128, heads=1, f=32, grid=(1, 2, 3), n_cond=3)
+
+
+def test_block_8bit_against_bruteforce_loops():
+    x_vis, x_cond, tvec, ws, grid, heads = _tiny_block8()
+    res = oracle.block_forward_8bit(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads)
+    lw = {s: {k: v.tolist() for k, v in ws[s].items()} for s in ws}
+    bv, bc = bf.block_forward_8bit(x_vis[0].tolist(), x_cond[0].tolist(), tvec[0].tolist(),
+                                   lw["vis"], lw["cond"], grid, heads, 1e-6, 1e-6, _e4m3_nearest())
+    np.testing.assert_allclose(res["out_vis"][0], np.array(bv), rtol=0, atol=1e-9)
+    np.testing.assert_allclose(res["out_cond"][0], np.array(bc), rtol=0, atol=1e-9)
+
+
+def test_block_8bit_zero_modulation_is_identity_and_rows():
+    """Zero gates leave x untouched whatever the branches compute; the requested rows of a
+    sampled call equal those rows of the full call (per-token quantization is row-local)."""
+    x_vis, x_cond, tvec, ws, grid, heads = _tiny_block8(seed=3)
+    z = {s: dict(ws[s], w_mod=0 * ws[s]["w_mod"], b_mod=0 * ws[s]["b_mod"]) for s in ws}
+    res = oracle.block_forward_8bit(x_vis, x_cond, tvec, z["vis"], z["cond"], grid, heads)
+    np.testing.assert_array_equal(res["out_vis"], x_vis)
+    np.testing.assert_array_equal(res["out_cond"], x_cond)
+    full = oracle.block_forward_8bit(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads)
+    rv, rc = np.array([0, 4, 5]), np.array([1])
+    part = oracle.block_forward_8bit(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads,
+                                     vis_rows=rv, cond_rows=rc)
+    for nm in ("out", "x1", "h2", "o", "qh"):
+        np.testing.assert_allclose(part[f"{nm}_vis"], full[f"{nm}_vis"][:, rv], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(part[f"{nm}_cond"], full[f"{nm}_cond"][:, rc], rtol=1e-12, atol=1e-13)
+
+
+def test_block_8bit_stays_near_the_16bit_block():
+    """Quantization moves each branch by a few percent (E4M3 keeps 3 mantissa bits, INT8 7)
+    -- a wrong formula misses by order one; the identical steps elsewhere keep the residual
+    stream x1 - x and the FFN branch within that distance of the 16-bit block's."""
+    x_vis, x_cond, tvec, ws, grid, heads = _tiny_block(seed=8, grid=(1, 3, 4), n_cond=5)
+    a = oracle.block_forward_8bit(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads)
+    e = oracle.block_forward(x_vis, x_cond, tvec, ws["vis"], ws["cond"], grid, heads)
+    for s, x in (("vis", x_vis), ("cond", x_cond)):
+        for nm, base in (("x1", x), ("out", e[f"x1_{s}"])):
+            ref = e[f"{nm}_{s}"] - base
+            got = a[f"{nm}_{s}"] - (x if nm == "x1" else a[f"x1_{s}"])
+            rel = np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
+            assert 0.003 < rel < 0.15, (s, nm, rel)
