@@ -312,6 +312,48 @@ def attention_8bit(dev):
     return res
 
 
+def block_8bit(cfg, wv, wc, t, rope, hip):
+    """The 480p block in the Wan report's 8-bit inference setup (section 4.4.3): the four GEMM
+    matrices quantized to E4M3 per tensor once, at load; every GEMM on FP8 operands (its f16
+    input quantized per token inside the step) and the 8-bit joint attention (its operands
+    quantized inside the step).  Same inputs as the 16-bit step; stages from hipEvents."""
+    import torch
+    import video_diffusion_transformer_mmdit_amd as mm
+    dev = t["x_vis"].device
+    w8v, w8c = mm.fp8_block_weights(wv), mm.fp8_block_weights(wc)
+    dims = mm.BlockDims.make(cfg.width, cfg.heads, cfg.ffn, cfg.t_dim, cfg.ln_eps, cfg.qk_eps,
+                             act_dtype=torch.float16, matrix_dtype=torch.float8_e4m3fn)
+    ws = torch.empty(mm.block_workspace_bytes(dims, 1, cfg.n_vis, cfg.n_cond), dtype=torch.uint8, device=dev)
+    ov = torch.empty((1, cfg.n_vis, cfg.width), dtype=torch.float32, device=dev)
+    oc = torch.empty((1, cfg.n_cond, cfg.width), dtype=torch.float32, device=dev)
+    steps = 10
+    events = [[hip.event() for _ in range(2 * mm.STAGE_COUNT)] for _ in range(steps)]
+
+    def step(evs=None):
+        mm.block_fwd(dims, w8v, w8c, t["x_vis"], t["x_cond"], t["tvec"], rope, workspace=ws, out_vis=ov,
+                     out_cond=oc, stage_events=evs)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stage = {name: float(np.mean([hip.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in events]))
+             for i, name in enumerate(mm.STAGES)}
+    for e in events:
+        for x in e:
+            hip.destroy(x)
+    att = stage["attention"]
+    return {"ms_per_step": round(ms, 4), "tokens": cfg.n_tokens, "tokens_per_s": round(cfg.n_tokens / (ms * 1e-3), 1),
+            "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+            "attention_tflops": round(cfg.attn_flops / (att * 1e-3) / 1e12, 1),
+            "attention_frac_8bit_peak": round(cfg.attn_flops / (att * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "note": "GEMM stages include the per-token FP8 quantization of their input, the attention stage "
+                    "the quantization of its operands; weights quantized once at load"}
+
+
 def lite_block(dev):
     """One block of the Lite backbone at 480p: the 2x2-merged 21x15x26 = 8190 visual tokens +
     512 conditioning tokens, the 16-wide timestep bottleneck, otherwise the block above."""
@@ -510,6 +552,9 @@ def main():
     if not args.no_next:
         log("timestep path and Lite merge / unpatchify")
         res["next_rows"] = next_rows(dev)
+        log("8-bit block at 480p")
+        del ws
+        res["next_rows"]["block_8bit_480p"] = block_8bit(cfg, wv_bf, wc_bf, t, rope, hip)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on this host)")
         res["cpu_baseline"] = cpu_baseline(cfg, raw)

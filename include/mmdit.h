@@ -394,6 +394,13 @@ int mmdit_lite_unpatchify(const void* x, int x_dtype, const void* w, const void*
  * w_dtype: MMDIT_BF16 (every weight bf16), or MMDIT_F16 with act_dtype F16: the four GEMM
  * matrices w_qkv, w_o, w_fc1, w_fc2 are given in f16 (converted once, e.g. with mmdit_cast,
  * as a deployment stores them) and every other weight stays bf16.
+ * w_dtype MMDIT_FP8_E4M3 with act_dtype F16 selects the 8-bit block of the Wan report's
+ * inference setup (section 4.4.3): the four GEMM matrices are E4M3 codes with one f32 scale
+ * each (s_qkv, s_o, s_fc1, s_fc2, device pointers; mmdit_quantize_fp8 per tensor makes
+ * them), every GEMM quantizes its f16 input per token (mmdit_quantize_fp8's rule) and runs
+ * as mmdit_linear_fp8, and the attention quantizes the f16 q^ | k^ | v rows as
+ * mmdit_attn8_quantize and runs mmdit_joint_attention_8bit; everything else is as in the
+ * 16-bit block.  The scale pointers are ignored for the other w_dtypes.
  * Weights (per stream, nn.Linear layout): w_mod [6C, Dt], b_mod [6C],
  * w_qkv [3C, C], b_qkv [3C] (rows: q, then k, then v), q_norm, k_norm [D] (or [H, D] with
  * qk_scale_head_stride = D), w_o [C, C], b_o [C], w_fc1 [F, C], b_fc1 [F], w_fc2 [C, F],
@@ -414,6 +421,7 @@ int mmdit_lite_unpatchify(const void* x, int x_dtype, const void* w, const void*
 typedef struct {
   const void *w_mod, *b_mod, *w_qkv, *b_qkv, *q_norm, *k_norm,
              *w_o, *b_o, *w_fc1, *b_fc1, *w_fc2, *b_fc2;
+  const float *s_qkv, *s_o, *s_fc1, *s_fc2;   /* E4M3 matrices only: [1] f32 scale each */
 } mmdit_stream_weights;
 
 typedef struct {
@@ -436,10 +444,18 @@ typedef struct {
  *   MMDIT_WS_SPLIT  f32 64 MiB, stream 0 only: partial sums of the GEMM tiles of a launch's
  *                   last, partial round, each computed over K ranges by several workgroups,
  *                   and likewise the attention's last-round query tiles computed over key
- *                   ranges (its contents after the call are scratch). */
+ *                   ranges (its contents after the call are scratch).
+ *   8-bit block (w_dtype MMDIT_FP8_E4M3) only:
+ *   MMDIT_WS_XQ     E4M3 [B*n, max(C, F)] codes of the current GEMM input (after the call:
+ *                   those of the GELU output g, [B*n, F])
+ *   MMDIT_WS_XS     f32 [B*n] their per-token scales
+ *   MMDIT_WS_Q8, MMDIT_WS_QS, MMDIT_WS_K8, MMDIT_WS_KS, MMDIT_WS_V8T: the stream's
+ *                   mmdit_attn8_stream operands (q8, q_scale, k8, k_scale, v8t)
+ *   MMDIT_WS_VS     f32 [B, H, D], stream 0 only: the V scales of both streams */
 enum { MMDIT_WS_MOD = 0, MMDIT_WS_H = 1, MMDIT_WS_QKV = 2, MMDIT_WS_X1 = 3, MMDIT_WS_G = 4,
        MMDIT_WS_WQKV = 5, MMDIT_WS_WO = 6, MMDIT_WS_W1 = 7, MMDIT_WS_W2 = 8, MMDIT_WS_SPLIT = 9,
-       MMDIT_WS_COUNT = 10 };
+       MMDIT_WS_XQ = 10, MMDIT_WS_XS = 11, MMDIT_WS_Q8 = 12, MMDIT_WS_QS = 13, MMDIT_WS_K8 = 14,
+       MMDIT_WS_KS = 15, MMDIT_WS_V8T = 16, MMDIT_WS_VS = 17, MMDIT_WS_COUNT = 18 };
 
 size_t mmdit_block_workspace_bytes(const mmdit_block_dims* dims, int64_t B, int64_t n_vis,
                                    int64_t n_cond);
@@ -462,14 +478,15 @@ int mmdit_block_fwd(const mmdit_block_dims* dims,
  * events: array of 2 * MMDIT_STAGE_COUNT hipEvent_t handles (passed as void*), entry
  * 2*i before stage i and 2*i+1 after it; the array or any entry may be NULL (not
  * recorded).  Everything else is exactly mmdit_block_fwd. */
-enum { MMDIT_STAGE_MOD_LN1 = 0,       /* modulation GEMV, LN-modulate (+ f16 FFN weight copy) */
-       MMDIT_STAGE_QKV = 1,           /* QKV GEMM                                            */
+enum { MMDIT_STAGE_MOD_LN1 = 0,       /* modulation GEMV, LN-modulate (+ f16 weight copies)  */
+       MMDIT_STAGE_QKV = 1,           /* QKV GEMM (8-bit block: with the quantization of h)  */
        MMDIT_STAGE_QK_NORM_ROPE = 2,  /* QK RMSNorm + 3D RoPE                                */
-       MMDIT_STAGE_ATTENTION = 3,     /* joint attention                                     */
-       MMDIT_STAGE_OUT_PROJ = 4,      /* output projection + gated residual                  */
+       MMDIT_STAGE_ATTENTION = 3,     /* joint attention (8-bit block: with its operands'    */
+                                      /* quantization)                                       */
+       MMDIT_STAGE_OUT_PROJ = 4,      /* output projection + gated residual (8-bit: with O's) */
        MMDIT_STAGE_LN2 = 5,           /* LN-modulate of the FFN branch                       */
-       MMDIT_STAGE_FFN_UP = 6,        /* FFN up + GELU                                       */
-       MMDIT_STAGE_FFN_DOWN = 7,      /* FFN down + gated residual                           */
+       MMDIT_STAGE_FFN_UP = 6,        /* FFN up + GELU (8-bit: with h2's quantization)       */
+       MMDIT_STAGE_FFN_DOWN = 7,      /* FFN down + gated residual (8-bit: with g's)         */
        MMDIT_STAGE_COUNT = 8 };
 
 int mmdit_block_fwd_events(const mmdit_block_dims* dims,

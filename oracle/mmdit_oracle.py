@@ -558,18 +558,31 @@ def joint_attention_8bit(q_vis, k_vis, v_vis, q_cond, k_cond, v_cond,
     i.e. ln(sum_j P'_j) + (M - 8) ln 2, laid out [B, H, n_cond + n_vis] ([cond | vis]); with
     ``return_row_sums``, the sums sum_j P'_j themselves ([B, H, rows] per stream, in the
     order of the returned rows)."""
-    b, _, h, d = q_vis.shape
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    kc = float(scale) * LOG2E
     qa, sqa, ka, ska = attn8_quantize_stream(q_vis, k_vis)
     qc, sqc, kcd, skc = attn8_quantize_stream(q_cond, k_cond)
     v8v, v8c, sv = attn8_quantize_v(v_vis, v_cond)
+    return attention_8bit_from_codes(qa, sqa, ka, ska, qc, sqc, kcd, skc, v8v, v8c, sv, scale,
+                                     vis_rows, cond_rows, chunk, return_lse, return_row_sums)
+
+
+def attention_8bit_from_codes(qa, sqa, ka, ska, qc, sqc, kcd, skc, v8v, v8c, sv,
+                              scale: Optional[float] = None,
+                              vis_rows: Optional[np.ndarray] = None,
+                              cond_rows: Optional[np.ndarray] = None, chunk: int = 1024,
+                              return_lse: bool = False, return_row_sums: bool = False):
+    """The steps of joint_attention_8bit after the quantization (r27), from the codes and
+    scales of attn8_quantize_stream (per stream: Q codes [B, n, H, D], their scales [B, n, H],
+    K codes, K block scales [B, H, ceil(n/64)]) and attn8_quantize_v (V values of the codes
+    per stream, V scales [B, H, D]).  Options and result as for joint_attention_8bit."""
+    b, _, h, d = qa.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kc = float(scale) * LOG2E
     # keys in [vis | cond] order (any order gives the same result), each with its block scale
     k8 = np.concatenate([ka, kcd], axis=1)                                  # [B, N, H, D]
     v8 = np.concatenate([v8v, v8c], axis=1)
     blk = lambda s_, n: np.repeat(s_, ATT8_KEY_BLOCK, axis=2)[:, :, :n]    # noqa: E731
-    skj = np.concatenate([blk(ska, k_vis.shape[1]), blk(skc, k_cond.shape[1])], axis=2)   # [B, H, N]
+    skj = np.concatenate([blk(ska, ka.shape[1]), blk(skc, kcd.shape[1])], axis=2)   # [B, H, N]
     skcj = skj.astype(np.float64) * kc
 
     def run(q8, sq, rows):

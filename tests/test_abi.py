@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    assert mm.abi_version() == 7
+    assert mm.abi_version() == 8
     assert L.mmdit_status_str(0) == b"MMDIT_OK"
     assert L.mmdit_status_str(ERR_ALIAS) == b"MMDIT_ERR_ALIAS"
     assert L.mmdit_status_str(99) == b"MMDIT_ERR_UNKNOWN"

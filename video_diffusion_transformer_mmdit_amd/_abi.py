@@ -16,8 +16,9 @@ import torch
 
 F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 EPI_NONE, EPI_GELU, EPI_GATED_RES = 0, 1, 2
-WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_WQKV, WS_WO, WS_W1, WS_W2, WS_SPLIT = range(10)
-WS_COUNT = 10
+(WS_MOD, WS_H, WS_QKV, WS_X1, WS_G, WS_WQKV, WS_WO, WS_W1, WS_W2, WS_SPLIT,
+ WS_XQ, WS_XS, WS_Q8, WS_QS, WS_K8, WS_KS, WS_V8T, WS_VS) = range(18)
+WS_COUNT = 18
 STAGES = ("mod_ln1", "qkv", "qk_norm_rope", "attention", "out_proj", "ln2", "ffn_up", "ffn_down")
 STAGE_COUNT = len(STAGES)
 
@@ -48,7 +49,8 @@ class Attn8Stream(ctypes.Structure):
 
 class StreamWeights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm",
-                                         "w_o", "b_o", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+                                         "w_o", "b_o", "w_fc1", "b_fc1", "w_fc2", "b_fc2",
+                                         "s_qkv", "s_o", "s_fc1", "s_fc2")]
 
 
 class BlockDims(ctypes.Structure):
@@ -60,9 +62,11 @@ class BlockDims(ctypes.Structure):
     def make(cls, C, H, F, Dt, ln_eps=1e-6, qk_eps=1e-6, qk_scale_head_stride=0,
              act_dtype=torch.float16, matrix_dtype=torch.bfloat16):
         """matrix_dtype: dtype of the four GEMM weight matrices (w_qkv, w_o, w_fc1, w_fc2);
-        float16 (with act_dtype float16) means they were converted once by the caller."""
-        return cls(C, H, C // H, F, Dt, ln_eps, qk_eps, qk_scale_head_stride, _TORCH_DT[matrix_dtype],
-                   _TORCH_DT[act_dtype])
+        float16 (with act_dtype float16) means they were converted once by the caller;
+        torch.float8_e4m3fn (with act_dtype float16) selects the 8-bit block, its matrices
+        given as E4M3 codes (uint8) with their scales (see fp8_block_weights)."""
+        mdt = FP8_E4M3 if matrix_dtype == torch.float8_e4m3fn else _TORCH_DT[matrix_dtype]
+        return cls(C, H, C // H, F, Dt, ln_eps, qk_eps, qk_scale_head_stride, mdt, _TORCH_DT[act_dtype])
 
 
 def library_path() -> str:
@@ -593,17 +597,36 @@ STREAM_KEYS = ("w_mod", "b_mod", "w_qkv", "b_qkv", "q_norm", "k_norm", "w_o", "b
 
 
 MATRIX_KEYS = ("w_qkv", "w_o", "w_fc1", "w_fc2")
+SCALE_KEYS = ("s_qkv", "s_o", "s_fc1", "s_fc2")   # E4M3 matrices: their per-tensor scales
+
+
+def fp8_block_weights(w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+    """The weights of one stream for the 8-bit block: the four GEMM matrices as E4M3 codes
+    (uint8) quantized per tensor by mmdit_quantize_fp8, with their f32 scales under s_qkv,
+    s_o, s_fc1, s_fc2; every other weight unchanged.  Done once, at load."""
+    out = dict(w)
+    for k, sk in zip(MATRIX_KEYS, SCALE_KEYS):
+        out[k], out[sk] = quantize_fp8(w[k].contiguous(), per_row=False)
+    return out
 
 
 def _stream_weights(w: Dict[str, torch.Tensor], device: torch.device, matrix_dt: int = BF16) -> StreamWeights:
     sw = StreamWeights()
+    mat_want = {F16: torch.float16, FP8_E4M3: torch.uint8}.get(matrix_dt, torch.bfloat16)
     for k in STREAM_KEYS:
         t = w.get(k)
-        want = torch.float16 if (k in MATRIX_KEYS and matrix_dt == F16) else torch.bfloat16
+        want = mat_want if k in MATRIX_KEYS else torch.bfloat16
         if t is not None and (not t.is_contiguous() or t.dtype != want):
             raise MmditError(f"weight {k} must be contiguous {want}")
         _on_device(device, **{f"weight {k}": t})
         setattr(sw, k, None if t is None else t.data_ptr())
+    if matrix_dt == FP8_E4M3:
+        for k in SCALE_KEYS:
+            t = w.get(k)
+            if t is None or t.dtype != torch.float32 or t.numel() != 1:
+                raise MmditError(f"the 8-bit block needs {k}, a one-element f32 tensor")
+            _on_device(device, **{f"weight {k}": t})
+            setattr(sw, k, t.data_ptr())
     return sw
 
 

@@ -120,7 +120,7 @@ const char* mmdit_status_str(int s) {
 
 const char* mmdit_last_error(void) { return g_last_error.c_str(); }
 
-int mmdit_abi_version(void) { return 7; }
+int mmdit_abi_version(void) { return 8; }
 
 int mmdit_modulate_ln(const void* x, int x_dtype, const void* branch, int branch_dtype,
                       const float* gate, float* x_out, const float* shift, const float* scale,
