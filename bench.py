@@ -36,8 +36,8 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only
 # for the kernel source they were taken on: a different joint_attention.hip reports null.
-ATTN_COUNTERS = {"source_sha256": "a185da4d81ba65ed",
-                 "fetch_kib": 1167653.5 + 15813.8, "write_kib": 227854.4 + 3056.0,
+ATTN_COUNTERS = {"source_sha256": "1e0b9e4d5f8a456f",
+                 "fetch_kib": 1104412.2 + 15816.3, "write_kib": 227865.3 + 3056.0,
                  "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -413,6 +413,8 @@ def main():
                     help="type of the 16-bit intermediates and MFMA operands")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the timing of the timestep path and Lite merge")
+    ap.add_argument("--next", choices=("all", "block_8bit"), default="all",
+                    help="which next rows to time (block_8bit: only the 8-bit block, e.g. for a profile)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload attention records and the memory-bound kernels alone")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -551,7 +553,7 @@ def main():
         res["memory_bound_kernels"] = memory_bound_kernels(dev)
     if not args.no_next:
         log("timestep path and Lite merge / unpatchify")
-        res["next_rows"] = next_rows(dev)
+        res["next_rows"] = next_rows(dev) if args.next == "all" else {}
         log("8-bit block at 480p")
         del ws
         res["next_rows"]["block_8bit_480p"] = block_8bit(cfg, wv_bf, wc_bf, t, rope, hip)
