@@ -24,6 +24,8 @@
 //     raised (powers of two commute with it above the subnormal range).
 //   - Ping-pong of two wave groups (MFMA-only phases against VALU-only phases), LDS-DMA of
 //     K and V tiles (8 KiB each) two stages deep, heads kept per XCD: as in the 16-bit kernel.
+//     Each phase covers a pair of 64-key tiles (each with its own K scale), so the pipeline
+//     fill and drain around a phase's barrier is paid once per 128 keys.
 #include <type_traits>
 
 #include "common.h"
@@ -110,11 +112,12 @@ __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_c
 template <int OUT_DT, bool LSE>
 __global__ __launch_bounds__(A8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void joint_attn_8bit_kernel(Attn8Args a) {
-  // two K stages (rows = keys, 128 bytes) and two V^T stages (rows = channels, 64 bytes)
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[A8_TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[A8_TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[A8_TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[A8_TILE_BYTES];
+  // two K stages (rows = keys, 128 bytes) and two V^T stages (rows = channels, 64 bytes), each
+  // stage a pair of 64-key tiles
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[2 * A8_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[2 * A8_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[2 * A8_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[2 * A8_TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -155,12 +158,13 @@ void joint_attn_8bit_kernel(Attn8Args a) {
   const int t_vis = (int)((n_vis + A8_BN - 1) / A8_BN);
   const int t_cond = (int)((n_cond + A8_BN - 1) / A8_BN);
   const int ntiles = t_vis + t_cond;
-  // this workgroup's key tiles [jbeg, jend): all of them, or one range of a split-tail item
-  int jbeg = 0, jend = ntiles;
+  const int npairs = (ntiles + 1) / 2;   // pair p: tiles 2p and 2p + 1 (the latter may not exist)
+  // this workgroup's pairs [jbeg, jend): all of them, or one range of a split-tail item
+  int jbeg = 0, jend = npairs;
   if (slot >= 0) {
     const int sp = slot % a.split;
-    jbeg = (int)((int64_t)ntiles * sp / a.split);
-    jend = (int)((int64_t)ntiles * (sp + 1) / a.split);
+    jbeg = (int)((int64_t)npairs * sp / a.split);
+    jend = (int)((int64_t)npairs * (sp + 1) / a.split);
   }
   auto tile_seg = [&](int jt, int& sg, int& t) { sg = jt < t_vis ? 0 : 1; t = sg ? jt - t_vis : jt; };
   auto kbuf = [&](auto stage) -> uint8_t* { if constexpr (decltype(stage)::value == 0) return lds_k0; else return lds_k1; };
@@ -181,11 +185,13 @@ void joint_attn_8bit_kernel(Attn8Args a) {
   for (int hh = 0; hh < 2; ++hh) v_rd[hh] = l32 * 64 + (((2 * hh + g) ^ ((l32 >> 2) & 3)) << 4);
 
   const i32x16 izero = {};
-  auto compute_s = [&](const uint8_t* kb, i32x16 (&s)[2]) {
+  // S^T of a pair: chains st = 0, 1 (the 32-key halves of the first tile) and 2, 3 (second)
+  auto compute_s = [&](const uint8_t* kb, i32x16 (&s)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) s[st] = mfma_i8(lds16(kb + st * 4096 + k_rd[c]), qf[c], c == 0 ? izero : s[st]);
+      for (int st = 0; st < 4; ++st)
+        s[st] = mfma_i8(lds16(kb + (st >> 1) * A8_TILE_BYTES + (st & 1) * 4096 + k_rd[c]), qf[c], c == 0 ? izero : s[st]);
   };
   auto phase_barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -239,7 +245,14 @@ void joint_attn_8bit_kernel(Attn8Args a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, vrow[1] * (int)np + off[1], 0, 1024, 0);
       }
     };
+    // both tiles of pair jp (a second tile past the last one is not loaded: its keys are
+    // masked and its stale stage contents never reach a weight)
+    auto dma_pair = [&](int jp, uint8_t* dst) {
+      dma_tile(2 * jp, dst);
+      if (2 * jp + 1 < ntiles) dma_tile(2 * jp + 1, dst + A8_TILE_BYTES);
+    };
     auto k_scale = [&](int jt) {
+      if (jt >= ntiles) jt = ntiles - 1;   // the missing second tile of the last pair
       int sg, t;
       tile_seg(jt, sg, t);
       const int nb = sg ? t_cond : t_vis;
@@ -254,63 +267,85 @@ void joint_attn_8bit_kernel(Attn8Args a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) ol[e] = 0.f;
     float m_run = 0.f;     // integer-valued reference (log2 units)
-    uint4 pf[2];           // P'_j as E4M3 codes: bytes 16 hh + 4 i + c = key 32 hh + 8 i + 4 g + c
+    uint4 pf[4];           // P'_j as E4M3 codes: tile u's bytes 16 hh + 4 i + c in pf[2 u + hh] = its
+                           // key 32 hh + 8 i + 4 g + c
     const uint4 ones = make_uint4(0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u);   // E4M3 1.0
 
-    // M(j): S_{j+1} and O^T += V_j^T P_j'^T (with the row sums) -- MFMA and LDS reads only
-    auto phase_m = [&](auto cur_c, int jt, i32x16 (&sn)[2]) {
+    // M(j): S of pair j+1 and O^T += V_j^T P_j'^T (with the row sums) -- MFMA and LDS reads only
+    auto phase_m = [&](auto cur_c, int jp, i32x16 (&s)[4]) {
       constexpr int CUR = decltype(cur_c)::value;
       constexpr std::integral_constant<int, CUR> cur{};
       constexpr std::integral_constant<int, CUR ^ 1> oth{};
-      if constexpr (GRP == 0) dma_tile(jt + 1 < jend ? jt + 1 : jend - 1, vbuf(oth));
-      else dma_tile(jt + 2 < jend ? jt + 2 : jend - 1, kbuf(cur));
-      compute_s(kbuf(oth), sn);
+      if constexpr (GRP == 0) dma_pair(jp + 1 < jend ? jp + 1 : jend - 1, vbuf(oth));
+      else dma_pair(jp + 2 < jend ? jp + 2 : jend - 1, kbuf(cur));
+      compute_s(kbuf(oth), s);
       const uint8_t* vb = vbuf(cur);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        o[dt] = mfma_f8(lds16(vb + dt * 2048 + v_rd[0]), lds16(vb + dt * 2048 + v_rd[1]), pf[0], pf[1], o[dt]);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          o[dt] = mfma_f8(lds16(vb + u * A8_TILE_BYTES + dt * 2048 + v_rd[0]),
+                          lds16(vb + u * A8_TILE_BYTES + dt * 2048 + v_rd[1]), pf[2 * u], pf[2 * u + 1], o[dt]);
       ol = mfma_f8(ones, ones, pf[0], pf[1], ol);
+      ol = mfma_f8(ones, ones, pf[2], pf[3], ol);
+      // 16 S MFMAs (one K read each), 8 P V MFMAs (two V reads each), 2 row-sum MFMAs; the
+      // reads four ahead of their use, the phase's four DMA loads after its first four MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-      for (int i = 0; i < 13; ++i) {
+      for (int i = 0; i < 26; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        if (i < 2) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
+        if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        if (i < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
       }
-      asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
+      asm volatile("" ::"v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]));
       asm volatile("" ::"v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(ol));
       if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's K loads have landed
       phase_barrier();
     };
-    // the K scale of the tile the next V phase works on, loaded one phase ahead
-    float sk_next = k_scale(jbeg);
-    // V(j): integer row max, integer reference, P'_j = E4M3(2^(acc c + 8 - m))
-    auto phase_v = [&](auto cur_c, int jt, i32x16 (&s)[2]) {
-      const float skt = sk_next;
-      sk_next = k_scale(jt + 1 < jend ? jt + 1 : jt);
-      int sg, t;
-      tile_seg(jt, sg, t);
-      const int64_t rows = a.n_seg[sg] - (int64_t)t * A8_BN;
-      if (rows < A8_BN) {   // keys past the end of their stream
+    // the K scales of the pair the next V phase works on, loaded one phase ahead
+    float sk_next[2] = {k_scale(2 * jbeg), k_scale(2 * jbeg + 1)};
+    // V(j): integer row maxima, integer reference, P'_j = E4M3(2^(acc c + 8 - m))
+    auto phase_v = [&](int jp, i32x16 (&s)[4]) {
+      const float skt[2] = {sk_next[0], sk_next[1]};
+      const int jn = jp + 1 < jend ? jp + 1 : jp;
+      sk_next[0] = k_scale(2 * jn);
+      sk_next[1] = k_scale(2 * jn + 1);
+      int mxu[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int u = 0; u < 2; ++u) {
+        const int jt = 2 * jp + u;
+        int64_t rows = 0;   // valid keys of tile u (none for a second tile past the last one)
+        if (jt < ntiles) {
+          int sg, t;
+          tile_seg(jt, sg, t);
+          rows = a.n_seg[sg] - (int64_t)t * A8_BN;
+        }
+        if (rows < A8_BN) {   // keys past the end of their stream
+          // element e of chain st holds key 32 st + 8 (e / 4) + 4 g + e % 4 of the tile: an
+          // arithmetic shift turns (rows - 1 - key) into an all-ones mask for keys past the end
+          const int vl = (int)rows - 1 - 4 * g;
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (st * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= rows) s[st][e] = INT32_MIN;
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int m = (vl - (st * 32 + 8 * (e >> 2) + (e & 3))) >> 31;
+              s[2 * u + st][e] = (INT32_MIN & m) | (s[2 * u + st][e] & ~m);
+            }
+        }
+        int m4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m4[k] = max(s[2 * u][k], s[2 * u + 1][k]);
+#pragma unroll
+        for (int e = 4; e < 16; e += 4)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) m4[k] = max(m4[k], max(s[2 * u][e + k], s[2 * u + 1][e + k]));
+        mxu[u] = xhalf_max_i(max(max(m4[0], m4[1]), max(m4[2], m4[3])));
       }
-      int m4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) m4[k] = max(s[0][k], s[1][k]);
-#pragma unroll
-      for (int e = 4; e < 16; e += 4)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) m4[k] = max(m4[k], max(s[0][e + k], s[1][e + k]));
-      const int mx = xhalf_max_i(max(max(m4[0], m4[1]), max(m4[2], m4[3])));
-      const float ci = sq * (skt * kc);
-      const float mt = ceilf((float)mx * ci);
-      if (jt == jbeg || __any(mt > m_run)) {
-        const float mnew = jt == jbeg ? mt : fmaxf(m_run, mt);
-        if (jt != jbeg) {
+      const float ci[2] = {sq * (skt[0] * kc), sq * (skt[1] * kc)};
+      const float mt = fmaxf(ceilf((float)mxu[0] * ci[0]), ceilf((float)mxu[1] * ci[1]));
+      if (jp == jbeg || __any(mt > m_run)) {
+        const float mnew = jp == jbeg ? mt : fmaxf(m_run, mt);
+        if (jp != jbeg) {
           const int sh = (int)(m_run - mnew);   // <= 0: an exact power-of-two rescale
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt)
@@ -323,48 +358,50 @@ void joint_attn_8bit_kernel(Attn8Args a) {
       }
       const float bias = 8.f - m_run;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 4; ++st) {
+        const float c = ci[st >> 1];
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 0], ci, bias));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 1], ci, bias));
-          const float p2 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 2], ci, bias));
-          const float p3 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 3], ci, bias));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 0], c, bias));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 1], c, bias));
+          const float p2 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 2], c, bias));
+          const float p3 = __builtin_amdgcn_exp2f(fmaf((float)s[st][4 * i + 3], c, bias));
           int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
           x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
           w[i] = (uint32_t)x;
         }
         pf[st] = make_uint4(w[0], w[1], w[2], w[3]);
       }
-      asm volatile("" ::"v"(pf[0].x), "v"(pf[0].y), "v"(pf[0].z), "v"(pf[0].w));
-      asm volatile("" ::"v"(pf[1].x), "v"(pf[1].y), "v"(pf[1].z), "v"(pf[1].w), "v"(m_run));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w));
+      asm volatile("" ::"v"(m_run));
       if constexpr (GRP == 0) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's V loads have landed
       phase_barrier();
     };
 
     if constexpr (GRP == 1) {
-      dma_tile(jbeg, lds_k0);
-      if (jbeg + 1 < jend) dma_tile(jbeg + 1, lds_k1);
+      dma_pair(jbeg, lds_k0);
+      if (jbeg + 1 < jend) dma_pair(jbeg + 1, lds_k1);
       __builtin_amdgcn_s_waitcnt(0xF70);
     }
     __syncthreads();
     if constexpr (GRP == 1) phase_barrier();
-    if constexpr (GRP == 0) dma_tile(jbeg, lds_v0);
-    i32x16 sa[2], sb[2];
-    compute_s(lds_k0, sa);
-    asm volatile("" ::"v"(sa[0]), "v"(sa[1]));
+    if constexpr (GRP == 0) dma_pair(jbeg, lds_v0);
+    i32x16 s[4];
+    compute_s(lds_k0, s);
+    asm volatile("" ::"v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]));
     phase_barrier();
-    int jt = jbeg;
-    for (; jt + 1 < jend; jt += 2) {
-      phase_v(S0, jt, sa);
-      phase_m(S0, jt, sb);
-      phase_v(S1, jt + 1, sb);
-      phase_m(S1, jt + 1, sa);
+    int jp = jbeg;
+    for (; jp + 1 < jend; jp += 2) {
+      phase_v(jp, s);
+      phase_m(S0, jp, s);
+      phase_v(jp + 1, s);
+      phase_m(S1, jp + 1, s);
     }
-    if (jt < jend) {
-      phase_v(S0, jt, sa);
-      phase_m(S0, jt, sb);
+    if (jp < jend) {
+      phase_v(jp, s);
+      phase_m(S0, jp, s);
     }
     if constexpr (GRP == 0) {
       __builtin_amdgcn_s_waitcnt(0xF70);
@@ -498,12 +535,13 @@ int launch_joint_attention_8bit(const mmdit_attn8_stream* const* seg, const int6
   // Split tail (with a workspace and no LSE): when the items fill R < P workgroup slots of
   // the last round (P = the CU count, one workgroup per CU), cut each of those R items into
   // S = P / R key ranges (at most one per key tile), merged afterwards
-  const int64_t ntiles = (n[0] + A8_BN - 1) / A8_BN + (n[1] + A8_BN - 1) / A8_BN;
+  // key ranges are whole pairs of 64-key tiles (the kernel's phase)
+  const int64_t npairs = ((n[0] + A8_BN - 1) / A8_BN + (n[1] + A8_BN - 1) / A8_BN + 1) / 2;
   const int64_t round = device_cu_count();
   if (split_ws && !L && items > round) {
     const int64_t R = items % round;
     int64_t S = R ? round / R : 0;
-    if (S > ntiles) S = ntiles;
+    if (S > npairs) S = npairs;
     if (R > 0 && S > (int64_t)(split_ws_bytes / ((size_t)R * A8_PART_FLOATS * 4))) S = (int64_t)(split_ws_bytes / ((size_t)R * A8_PART_FLOATS * 4));
     if (R > 0 && S >= 2 && (size_t)(R * S * A8_PART_FLOATS) * 4 <= split_ws_bytes) {
       a.full = (int)(items - R);
