@@ -245,11 +245,13 @@ void joint_attn_8bit_kernel(Attn8Args a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, vrow[1] * (int)np + off[1], 0, 1024, 0);
       }
     };
-    // both tiles of pair jp (a second tile past the last one is not loaded: its keys are
-    // masked and its stale stage contents never reach a weight)
+    // both tiles of pair jp.  A second tile past the last one takes the first tile's codes
+    // again: its keys are masked to a zero weight, but the FP8 product of a zero weight with a
+    // stale NaN code left in LDS by an earlier kernel would still be NaN, so that half must hold
+    // finite codes.
     auto dma_pair = [&](int jp, uint8_t* dst) {
       dma_tile(2 * jp, dst);
-      if (2 * jp + 1 < ntiles) dma_tile(2 * jp + 1, dst + A8_TILE_BYTES);
+      dma_tile(2 * jp + 1 < ntiles ? 2 * jp + 1 : 2 * jp, dst + A8_TILE_BYTES);
     };
     auto k_scale = [&](int jt) {
       if (jt >= ntiles) jt = ntiles - 1;   // the missing second tile of the last pair
