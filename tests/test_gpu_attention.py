@@ -261,6 +261,39 @@ def test_attention_split_tail_with_workspace():
         assert_close(f"o_cond[b={b}]", to_host64(o_c[b:b + 1]), r_c, 2e-2)
 
 
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("split", [False, True], ids=["one_pass", "split_tail"])
+def test_logits_far_above_the_running_max(dt, split):
+    """Keys in later tiles whose logits lie far above everything before them: about 10 log2
+    units (weights up to ~2^8 above the first tile's max, kept without raising it), then about
+    20, 40 and 69 (in a middle visual tile, the partial last visual tile and the conditioning
+    segment), each of which passes the f16-safe bound of its tile.  A tile
+    whose weights would pass that bound raises the running max and is weighed again;
+    the output stays finite and matches the oracle, for f16 Q (scaled before the product)
+    and bf16 Q (scaled at the exponential), in one pass and with the split tail's key ranges
+    (B = 2, 24 heads, 1400 + 77 tokens: 32 items of the last round in 8 ranges each)."""
+    B, nv, nc, H, D = 2, 1400, 77, 24, 128
+    g = torch.Generator().manual_seed(71)
+    u = torch.randn((H, D), generator=g)
+    q = lambda n: u + 0.5 * torch.randn((B, n, H, D), generator=g)  # noqa: E731
+    k = lambda n: 0.5 * torch.randn((B, n, H, D), generator=g)  # noqa: E731
+    qv, qc, kv, kc = q(nv), q(nc), k(nv), k(nc)
+    unit = u / math.sqrt(D)   # q . (lam * unit) / sqrt(D) is about lam nats
+    for rows, at, lam in ((kv, 150, 7.0), (kv, 300, 14.0), (kv, 1395, 28.0), (kc, 40, 48.0)):
+        rows[:, at] = lam * unit
+    vv = torch.randn((B, nv, H, D), generator=g)
+    vc = torch.randn((B, nc, H, D), generator=g)
+    qv, kv, vv, qc, kc, vc = (t.to(dt).cuda() for t in (qv, kv, vv, qc, kc, vc))
+    ws = torch.empty(mm.ATTN_SPLIT_BYTES, dtype=torch.uint8, device="cuda") if split else None
+    o_v, o_c = mm.joint_attention(qv, kv, vv, qc, kc, vc, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o_v).all() and torch.isfinite(o_c).all()
+    for b in range(B):
+        r_v, r_c = _oracle_attn(*(t[b:b + 1].contiguous() for t in (qv, kv, vv, qc, kc, vc)))
+        assert_close(f"o_vis[b={b}]", to_host64(o_v[b:b + 1]), r_v, 2e-2)
+        assert_close(f"o_cond[b={b}]", to_host64(o_c[b:b + 1]), r_c, 2e-2)
+
+
 def test_host_workspace_or_output_raises_before_launch():
     """GPU inputs with a host workspace (or a host output) are refused by the binding."""
     q = _rand((1, 300, 2, 128), 51)

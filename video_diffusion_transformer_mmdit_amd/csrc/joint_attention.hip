@@ -12,24 +12,28 @@
 //   - The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16} (A = 32 keys x 16 dims
 //     from LDS, B = the wave's Q held in registers for the whole kernel).  In the S^T
 //     accumulator layout every lane holds one query (lane % 32) and 16 keys, so the online
-//     softmax statistics are per-lane scalars and only the row max needs one exchange
-//     between the two half-waves per tile; the row sum is combined once at the end.
+//     softmax statistics are per-lane scalars and only a row max needs an exchange between
+//     the two half-waves; the row sum is combined once at the end.
 //   - P^T comes straight from those accumulators (rounded to f16) as the B operand of
 //     O^T = V^T P^T; O^T accumulates 128 dims x 32 queries per wave in registers.  The V^T
 //     operand is read from row-major V tiles with ds_read_b64_tr_b16.
 //   - K and V tiles of 128 keys reach LDS by LDS-DMA (buffer loads straight into LDS, two
 //     stages each, 128 KiB in all, XOR-swizzled chunks for conflict-free reads).
 //   - Two wave groups ping-pong: a wave alternates an MFMA-only phase (S of the next tile,
-//     P V of this one: 64 MFMAs) and a VALU-only phase (max, lazy rescale, exp2), one group
+//     P V of this one: 64 MFMAs) and a VALU-only phase (exp2, row sums), one group
 //     a phase behind the other, so on every SIMD the matrix pipe and the VALU work
 //     concurrently; each phase ends with a workgroup barrier, whose pipeline fill and drain
 //     a 128-key tile pays half as often as a 64-key one.
 //   - exp2 with log2(e) * softmax_scale folded into Q; the S^T accumulators start from minus
-//     the running max (a constant C operand of each chain's first MFMA), and the running max
-//     is only raised when a score exceeds it by more than 2^8 (lazy rescale).
+//     the running max (a constant C operand of each chain's first MFMA).  The first tile of
+//     a key range sets the running max exactly; after that a tile is weighed against the max
+//     as it stands, and only when a lane's sum of the tile's weights passes 2^14 (which
+//     bounds each weight) is the max raised to the tile's row max and the tile weighed again
+//     (its S recomputed from the K tile still in LDS).  No row max is taken per tile: the
+//     softmax phase is exponentials, packing and sums.
 //   - Precision: S = Q K^T runs on the operand type of Q and K (f16 or bf16); P is rounded
-//     to f16 (P lies in [0, 2^8], where f16 keeps 3 more mantissa bits than bf16) and PV runs
-//     on f16 MFMA, so a bf16 V is converted to f16 after it is read from LDS.
+//     to f16 (P lies in [0, 2^14], where f16 keeps 3 more mantissa bits than bf16) and PV
+//     runs on f16 MFMA, so a bf16 V is converted to f16 after it is read from LDS.
 //
 // fp32 path: a plain wave-per-query VALU kernel with the same online softmax, used for the
 // fp32 workload (small sizes).
@@ -44,7 +48,11 @@ constexpr int ATT_BM = 256;                       // queries per workgroup (8 wa
 constexpr int ATT_BN = 128;                       // keys per tile
 constexpr int ATT_THREADS = 512;
 constexpr int ATT_K_BYTES = ATT_BN * ATT_D * 2;   // 32 KiB
-constexpr float ATT_RESCALE_LOG2 = 8.0f;          // lazy rescale threshold: P <= 2^8
+// A tile's weights are taken against the running max as it stands; only when one lane's sum
+// of its weights in the tile (which bounds each of them, all being >= 0) passes this limit is
+// the max raised to the tile's and the tile's weights taken again, so every f16 weight that
+// reaches the P V product is at most 2^14.
+constexpr float ATT_WEIGHT_SUM_LIMIT = 16384.0f;
 #ifndef ATT_LDS_AHEAD
 #define ATT_LDS_AHEAD 4                           // MFMAs between an LDS operand read and its use
 #endif
@@ -327,7 +335,8 @@ void joint_attn_mfma_kernel(AttnArgs a) {
   // ---- Ping-pong of two wave groups.  Waves 0-3 (group 0) and 4-7 (group 1) each hold one
   // wave on every SIMD.  Each wave alternates two phases per 128-key tile:
   //   M(j): S_{j+1} = K_{j+1} Q^T and O^T += V_j^T P_j^T -- MFMA and LDS reads only;
-  //   V(j): mask, row max, lazy rescale and P_j = exp2(S_j - m) -- VALU only.
+  //   V(j): mask and P_j = exp2(S_j - m), with the running max raised only when a weight
+  //         would pass 2^14 -- VALU only.
   // One S accumulator set serves every tile: V(j) consumes S_j before M(j) writes S_{j+1}.
   // Group 1 runs one phase behind group 0 and every phase ends with a workgroup barrier, so
   // on each SIMD one wave keeps the matrix pipe busy while the other runs the softmax.  A
@@ -389,7 +398,7 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-    float m_run = 0.f;         // running max of the logits (log2 units), possibly stale by < 2^8;
+    float m_run = 0.f;         // running max of the logits (log2 units), possibly stale by < 14;
                                // S accumulators hold logit - m_run in accumulator units
     float l_run = 0.f;         // this lane's partial sum of the probabilities
     uint4 pf[8];               // P_j rounded to f16, the B operand of O^T
@@ -422,9 +431,11 @@ void joint_attn_mfma_kernel(AttnArgs a) {
       if constexpr (GRP == 1) __builtin_amdgcn_s_waitcnt(0xF70);   // this wave's K loads have landed
       phase_barrier();
     };
-    // V(j): softmax of S_j into P_j
-    auto phase_v = [&](int jt, f32x16 (&s)[4]) {
-      {  // keys past the end of their segment (a segment's partial last tile)
+    // V(j): softmax of S_j into P_j.  K_j is still in its stage here (group 1 refills that stage
+    // with K_{j+2} only in its M(j), behind both groups' V(j)).
+    auto phase_v = [&](auto cur_c, int jt, f32x16 (&s)[4]) {
+      constexpr std::integral_constant<int, decltype(cur_c)::value> cur{};
+      auto mask_tail = [&]() {  // keys past the end of their segment (a segment's partial last tile)
         int sg, t;
         tile_seg(jt, sg, t);
         const int valid = tile_rows(sg, t);
@@ -441,14 +452,14 @@ void joint_attn_mfma_kernel(AttnArgs a) {
               s[st][e] = __uint_as_float((0xFF800000u & m) | (__float_as_uint(s[st][e]) & ~m));
             }
         }
-      }
-      const float mx = row_max(s);
-      // S and mx hold logit - m_run.  The first tile sets the running max exactly; later the
-      // max is only raised when a logit exceeds it by more than 2^8 (lazy rescale)
-      const float dl = mx * ce;
-      if (jt == jbeg || __any(dl > ATT_RESCALE_LOG2)) {
-        const float delta = jt == jbeg ? dl : fmaxf(dl, 0.f);
-        if (jt != jbeg) {
+      };
+      mask_tail();
+      // S holds logit - m_run.  raise_max moves the running max up to this tile's row max (the
+      // first tile of a range sets it exactly), rescaling O and l by an exact 2^-delta.
+      auto raise_max = [&](bool first) {
+        const float dl = row_max(s) * ce;
+        const float delta = first ? dl : fmaxf(dl, 0.f);
+        if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-delta);
           l_run *= alpha;
 #pragma unroll
@@ -466,27 +477,41 @@ void joint_attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) mneg[e] = mb;
         asm volatile("" : "+v"(mneg));
-      }
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      };
+      // P = 2^S into the f16 B operands of the P V product; returns this lane's sum of P
+      auto weights = [&]() {
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < 4; ++st) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t w[4];
+          for (int hh = 0; hh < 2; ++hh) {
+            uint32_t w[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(PRESCALE ? s[st][8 * hh + 2 * i] : s[st][8 * hh + 2 * i] * ce);
-            const float p1 = __builtin_amdgcn_exp2f(PRESCALE ? s[st][8 * hh + 2 * i + 1] : s[st][8 * hh + 2 * i + 1] * ce);
-            w[i] = cvt_pk_f16(p0, p1);
-            // plain f32 adds in four chains: the dot-product path (v_dot2) shares the matrix
-            // pipe and stalls behind the other wave's MFMAs
-            ls[(i & 1) * 2] += p0;
-            ls[(i & 1) * 2 + 1] += p1;
+            for (int i = 0; i < 4; ++i) {
+              const float p0 = __builtin_amdgcn_exp2f(PRESCALE ? s[st][8 * hh + 2 * i] : s[st][8 * hh + 2 * i] * ce);
+              const float p1 = __builtin_amdgcn_exp2f(PRESCALE ? s[st][8 * hh + 2 * i + 1] : s[st][8 * hh + 2 * i + 1] * ce);
+              w[i] = cvt_pk_f16(p0, p1);
+              // plain f32 adds in four chains: the dot-product path (v_dot2) shares the matrix
+              // pipe and stalls behind the other wave's MFMAs
+              ls[(i & 1) * 2] += p0;
+              ls[(i & 1) * 2 + 1] += p1;
+            }
+            pf[st * 2 + hh] = make_uint4(w[0], w[1], w[2], w[3]);
           }
-          pf[st * 2 + hh] = make_uint4(w[0], w[1], w[2], w[3]);
         }
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      };
+      if (jt == jbeg) raise_max(true);
+      float lt = weights();
+      if (jt != jbeg && __any(lt > ATT_WEIGHT_SUM_LIMIT)) {
+        // rare (a logit far above the running max): S_j again from K_j with the same C operand,
+        // so bit-identical, rather than holding S beside P through the exponentials
+        compute_s(kbuf(cur), s, mneg);
+        mask_tail();
+        raise_max(false);
+        lt = weights();
       }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      l_run += lt;
       // pin P, l and m: this VALU work belongs to this phase, not the next M phase
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w));
@@ -511,13 +536,13 @@ void joint_attn_mfma_kernel(AttnArgs a) {
     phase_barrier();
     int jt = jbeg;
     for (; jt + 1 < jend; jt += 2) {
-      phase_v(jt, s);
+      phase_v(S0, jt, s);
       phase_m(S0, jt, s);
-      phase_v(jt + 1, s);
+      phase_v(S1, jt + 1, s);
       phase_m(S1, jt + 1, s);
     }
     if (jt < jend) {
-      phase_v(jt, s);
+      phase_v(S0, jt, s);
       phase_m(S0, jt, s);
     }
     if constexpr (GRP == 0) {   // drain the last (unused) V reload, then match group 1's extra barrier
