@@ -24,8 +24,8 @@
 //     Rows past the end of x or W fail the buffer descriptor's range check and arrive as
 //     zeros.
 //   - Tiles are renumbered so that each XCD (workgroups go round-robin over the 8 XCDs) owns
-//     a contiguous run of tiles, and runs are rastered in bands of 4 M-tiles, keeping the
-//     x and W panels that concurrent workgroups of one XCD share inside its L2.
+//     a contiguous run of tiles, and runs are rastered in bands of 4 M-tiles (2 at K >= 8192),
+//     keeping the x and W panels that concurrent workgroups of one XCD share inside its L2.
 //   - The epilogue restages each wave's block through LDS (free after the last stage) and
 //     applies the FP8 scales, bias, GELU or the gated residual along rows, before the only
 //     store of y.
@@ -39,7 +39,6 @@ namespace mmdit {
 
 constexpr int GBM = 256, GBN = 256, GBK = 32;
 constexpr int GTHREADS = 256;
-constexpr int GROUP_M = 4;   // M-tiles per raster band (4 measured ~1 % faster than 2, 8 or 16)
 constexpr int G_TILE_BYTES = 256 * GBK * 2;   // one operand tile of one stage: 16 KiB
 constexpr size_t G_PART_BYTES = 256 * 256 * 4;   // f32 partial sums of one tile
 
@@ -54,6 +53,9 @@ struct GemmArgs {
   int split;
   float* part;
   int64_t N, K;
+  // M-tiles per raster band: 4 (measured ~1 % faster than 2, 8 or 16 at K = 3072), 2 for the
+  // 16-bit kernel at K >= 8192 (FFN down 1.7 % faster than with 4)
+  int group_m;
   // 2x2 spatial regrouping (GEMM_GATHER_X / GEMM_SCATTER_Y): hidden width C, full grid
   // width W, merged grid width W/2 and merged tokens per frame (H/2)(W/2)
   int c, w, w2, hw2;
@@ -164,18 +166,18 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* opaque_lds(__
 }
 
 // Tile of virtual index t: tiles are renumbered so that each XCD (workgroups go round-robin
-// over the 8 XCDs) owns a contiguous run of the whole-tile range, and rastered in groups of 8
-// M-tiles inside a problem.
+// over the 8 XCDs) owns a contiguous run of the whole-tile range, and rastered in bands of
+// args.group_m M-tiles inside a problem.
 __device__ __forceinline__ void gemm_tile_of(const GemmArgs& args, int64_t t, int& pi, int& m0, int& n0) {
   if (t < args.full && (args.full & 7) == 0) t = (t & 7) * (args.full >> 3) + (t >> 3);
   pi = t < args.tiles0 ? 0 : 1;
   if (pi) t -= args.tiles0;
   const int64_t M = args.p[pi].M, N = args.N;
   const int64_t nTm = (M + GBM - 1) / GBM, nTn = (N + GBN - 1) / GBN;
-  const int64_t per_group = (int64_t)GROUP_M * nTn;
+  const int64_t per_group = (int64_t)args.group_m * nTn;
   const int64_t grp = t / per_group;
-  const int64_t first_m = grp * GROUP_M;
-  const int64_t gm = (nTm - first_m) < GROUP_M ? (nTm - first_m) : GROUP_M;
+  const int64_t first_m = grp * args.group_m;
+  const int64_t gm = (nTm - first_m) < args.group_m ? (nTm - first_m) : args.group_m;
   const int64_t in_grp = t - grp * per_group;
   m0 = (int)((first_m + in_grp % gm) * GBM);
   n0 = (int)((in_grp / gm) * GBN);
@@ -302,6 +304,23 @@ __device__ __forceinline__ void gemm_epilogue_rows8(const GemmArgs& args, const 
   int sg = 0;
   if constexpr (LAYOUT == GEMM_SCATTER_Y) sg = (n0 + wn * 64) / args.c;
   constexpr bool GRES = EPI == MMDIT_EPI_GATED_RES;
+  // Gates of the batch items this wave's 128 rows belong to: with at least 128 rows per item
+  // they span at most two (b0 below row `bnd`, b0 + 1 from it on), loaded once here instead of
+  // a division and a gate load per row; shorter items take the per-row form.
+  float g0[4] = {0.f, 0.f, 0.f, 0.f}, g1[4] = {0.f, 0.f, 0.f, 0.f};
+  int64_t bnd = 0;
+  bool gate_rows = false;
+  if constexpr (GRES) {
+    const uint32_t rpb = (uint32_t)P.rows_per_batch;
+    const int64_t mw = m0 + wm * 128;
+    gate_rows = rpb < 128;
+    if (!gate_rows && mw < M && n < N) {
+      const uint32_t b0 = (uint32_t)mw / rpb;
+      bnd = (int64_t)(b0 + 1) * rpb;
+      load4<MMDIT_F32>(P.gate, (int64_t)b0 * P.gate_stride + n, g0);
+      if (bnd < M && bnd < mw + 128) load4<MMDIT_F32>(P.gate, (int64_t)(b0 + 1) * P.gate_stride + n, g1);
+    }
+  }
   // residual of rows r0 + 4 k + r4 (k = 0..3) of quarter q
   auto res_group = [&](int q, int r0, ResRaw<RES_DT> (&rr)[4]) {
 #pragma unroll
@@ -342,10 +361,15 @@ __device__ __forceinline__ void gemm_epilogue_rows8(const GemmArgs& args, const 
           v[0] = a.x + bias[0]; v[1] = a.y + bias[1]; v[2] = a.z + bias[2]; v[3] = a.w + bias[3];
         }
         if constexpr (GRES) {
-          const int64_t b = (uint32_t)m / (uint32_t)P.rows_per_batch;
           float r[4], gt[4];
           res_unpack<RES_DT>(rc[k], r);
-          load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
+          if (gate_rows) {
+            const int64_t b = (uint32_t)m / (uint32_t)P.rows_per_batch;
+            load4<MMDIT_F32>(P.gate, b * P.gate_stride + n, gt);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) gt[c] = m < bnd ? g0[c] : g1[c];
+          }
 #pragma unroll
           for (int c = 0; c < 4; ++c) v[c] = fmaf(gt[c], v[c], r[c]);
         } else {
@@ -779,6 +803,7 @@ int launch_lite_regroup(int layout, const void* x, const void* w, const void* bi
   a.tiles0 = a.tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   a.full = a.tiles;
   a.split = 1;
+  a.group_m = 4;
   a.N = N; a.K = K;
   a.c = (int)C; a.w = (int)W; a.w2 = (int)(W / 2); a.hw2 = (int)((H / 2) * (W / 2));
   if (a.tiles == 0) return MMDIT_OK;
@@ -819,6 +844,7 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   a.K = K;
   a.full = a.tiles;
   a.split = 1;
+  a.group_m = x_dtype != MMDIT_FP8_E4M3 && K >= 8192 ? 2 : 4;
   if (a.tiles == 0) return MMDIT_OK;
   // Split tail: when the tiles fill R < P workgroup slots of the last round (P = the CU
   // count, one workgroup per CU), cut each of those R tiles into S = P / R K ranges (at
