@@ -203,7 +203,9 @@ def memory_bound_kernels(dev):
     """The block's memory-bound kernels at the 480p visual stream's shapes, alone: the
     modulation GEMV (one stream's W_mod 18432 x 1536 bf16), LN-modulate before attention (x
     bf16 -> h f16) and before the FFN (x1 f32 -> h2 f16), and QK-RMSNorm + 3D RoPE in place on
-    the packed q|k|v rows (f16).  Algorithmic bytes: each tensor read or written once."""
+    the packed q|k|v rows (f16).  Algorithmic bytes: each tensor read or written once.  A
+    device-to-device copy of the LN's x (201 MB read, 201 MB written) is timed beside them as
+    the rate a plain stream reaches on this machine (`frac_copy`)."""
     import torch
     import video_diffusion_transformer_mmdit_amd as mm
     import workloads as wl
@@ -228,7 +230,13 @@ def memory_bound_kernels(dev):
         nb = N * C * (el + 2)
         out[name] = {"ms": round(ms, 4), "bytes": nb, "GB_per_s": round(nb / ms / 1e6, 1),
                      "frac_hbm": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
-    del x, x1, h
+    xc = torch.empty_like(x)
+    ms = time_calls(lambda: xc.copy_(x), reps=20)
+    nb = 2 * x.numel() * 2
+    copy_gbs = nb / ms / 1e6
+    out["device_copy"] = {"ms": round(ms, 4), "bytes": nb, "GB_per_s": round(copy_gbs, 1),
+                          "frac_hbm": round(copy_gbs / PEAK_HBM_GBS, 4)}
+    del x, x1, h, xc
     qkv = torch.randn((1, N, 3, cfg.heads, 128), generator=g, device=dev).to(torch.float16)
     gq = (1 + 0.1 * torch.randn((128,), generator=g, device=dev)).to(torch.bfloat16)
     gk = (1 + 0.1 * torch.randn((128,), generator=g, device=dev)).to(torch.bfloat16)
@@ -238,6 +246,9 @@ def memory_bound_kernels(dev):
     nb = 4 * N * C * 2
     out["qk_norm_rope"] = {"ms": round(ms, 4), "bytes": nb, "GB_per_s": round(nb / ms / 1e6, 1),
                            "frac_hbm": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    for k, v in out.items():
+        if k != "device_copy":
+            v["frac_copy"] = round(v["GB_per_s"] / copy_gbs, 4)
     return out
 
 
