@@ -53,8 +53,9 @@ struct GemmArgs {
   int split;
   float* part;
   int64_t N, K;
-  // M-tiles per raster band: 4 (measured ~1 % faster than 2, 8 or 16 at K = 3072), 2 for the
-  // 16-bit kernel at K >= 8192 (FFN down 1.7 % faster than with 4)
+  // M-tiles per raster band: 4 (measured ~1 % faster than 2, 8 or 16 at K = 3072), 2 at
+  // K >= 8192 (FFN down 1.7 %, its FP8 form in the 8-bit block 3 %, the Lite merge 3 % faster
+  // than with 4)
   int group_m;
   // 2x2 spatial regrouping (GEMM_GATHER_X / GEMM_SCATTER_Y): hidden width C, full grid
   // width W, merged grid width W/2 and merged tokens per frame (H/2)(W/2)
@@ -803,7 +804,7 @@ int launch_lite_regroup(int layout, const void* x, const void* w, const void* bi
   a.tiles0 = a.tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   a.full = a.tiles;
   a.split = 1;
-  a.group_m = 4;
+  a.group_m = K >= 8192 ? 2 : 4;
   a.N = N; a.K = K;
   a.c = (int)C; a.w = (int)W; a.w2 = (int)(W / 2); a.hw2 = (int)((H / 2) * (W / 2));
   if (a.tiles == 0) return MMDIT_OK;
@@ -844,7 +845,7 @@ int launch_linear(const GemmProblem* probs, int nprobs, int x_dtype, int bias_dt
   a.K = K;
   a.full = a.tiles;
   a.split = 1;
-  a.group_m = x_dtype != MMDIT_FP8_E4M3 && K >= 8192 ? 2 : 4;
+  a.group_m = K >= 8192 ? 2 : 4;
   if (a.tiles == 0) return MMDIT_OK;
   // Split tail: when the tiles fill R < P workgroup slots of the last round (P = the CU
   // count, one workgroup per CU), cut each of those R tiles into S = P / R K ranges (at
