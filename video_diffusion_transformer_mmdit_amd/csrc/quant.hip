@@ -4,8 +4,9 @@
 //   s = amax / 448 (f32; an all-zero group takes s = 1),  code = E4M3(clamp(x * (1/s), +-448))
 //
 // with round-to-nearest-even in the hardware conversion (v_cvt_pk_fp8_f32).  Bound by HBM:
-// per row one read of x (a second pass re-reads the row from cache) and one write of the
-// codes.  Rows go to one wave each, 8 elements per lane per step.
+// per row one read of x and one write of the codes.  Rows go to one wave each, 8 elements
+// per lane per step; rows of 3072 or 12288 16-bit values stay in registers between the amax
+// and the coding pass, other rows are read a second time (from cache when still there).
 #include "common.h"
 
 namespace mmdit {
@@ -23,13 +24,65 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 __device__ __forceinline__ float clamp_fp8(float v) { return fminf(fmaxf(v, -FP8_MAX), FP8_MAX); }
 
+// codes of eight values at q[idx .. idx + 7]
+__device__ __forceinline__ void store_codes8(float (&v)[8], float inv, uint8_t* q, int64_t idx) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = clamp_fp8(v[e] * inv);
+  *reinterpret_cast<uint2*>(q + idx) = make_uint2(pack_fp8x4(v[0], v[1], v[2], v[3]), pack_fp8x4(v[4], v[5], v[6], v[7]));
+}
+
 template <int DT>
 __device__ __forceinline__ void quant8(const void* x, int64_t idx, float inv, uint8_t* q) {
   float v[8];
   load8<DT>(x, idx, v);
+  store_codes8(v, inv, q, idx);
+}
+
+// Eight 16-bit values of one 16-byte chunk as floats (as load8 widens them).
+template <int DT>
+__device__ __forceinline__ void widen8(const uint4& w, float (&v)[8]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = clamp_fp8(v[e] * inv);
-  *reinterpret_cast<uint2*>(q + idx) = make_uint2(pack_fp8x4(v[0], v[1], v[2], v[3]), pack_fp8x4(v[4], v[5], v[6], v[7]));
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == MMDIT_BF16) { v[2 * i] = lo_bf16(ws[i]); v[2 * i + 1] = hi_bf16(ws[i]); }
+    else { v[2 * i] = lo_f16(ws[i]); v[2 * i + 1] = hi_f16(ws[i]); }
+  }
+}
+
+// Per-row quantization of 16-bit rows of 512 * CPL values: each lane keeps its CPL chunks in
+// registers between the amax and the coding pass, so the row crosses HBM once (the generic
+// kernel below re-reads it, from cache when it is still there).
+template <int DT, int CPL>
+__global__ __launch_bounds__(256) void quant_rows_reg_kernel(const void* __restrict__ x, int64_t rows,
+                                                             uint8_t* __restrict__ q, float* __restrict__ scales) {
+  constexpr int COLS = 512 * CPL;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t base = row * COLS;
+  uint4 raw[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+    raw[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base + (lane + 64 * i) * 8);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    float v[8];
+    widen8<DT>(raw[i], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float s = fp8_scale(amax);
+  const float inv = 1.f / s;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    float v[8];
+    widen8<DT>(raw[i], v);
+    store_codes8(v, inv, q, base + (lane + 64 * i) * 8);
+  }
+  if (lane == 0) scales[row] = s;
 }
 
 template <int DT>
@@ -92,7 +145,18 @@ template <int DT>
 static int quant_go(const void* x, int64_t rows, int64_t cols, int per_row, uint8_t* q, float* scales,
                     hipStream_t stream) {
   if (per_row) {
-    quant_rows_kernel<DT><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(x, rows, (int)cols, q, scales);
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if constexpr (DT != MMDIT_F32) {
+      if (cols == 512 * 6) {
+        quant_rows_reg_kernel<DT, 6><<<grid, 256, 0, stream>>>(x, rows, q, scales);
+        return check_launch("quantize_fp8 rows");
+      }
+      if (cols == 512 * 24) {
+        quant_rows_reg_kernel<DT, 24><<<grid, 256, 0, stream>>>(x, rows, q, scales);
+        return check_launch("quantize_fp8 rows");
+      }
+    }
+    quant_rows_kernel<DT><<<grid, 256, 0, stream>>>(x, rows, (int)cols, q, scales);
     return check_launch("quantize_fp8 rows");
   }
   const int64_t n8 = rows * cols / 8;
