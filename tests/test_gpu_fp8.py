@@ -25,6 +25,7 @@ def _rand(shape, seed, std=1.0, dtype=torch.bfloat16):
 
 
 @pytest.mark.parametrize("dtype,rows,cols", [(torch.bfloat16, 300, 3072), (torch.float16, 77, 12288),
+                                             (torch.float16, 6, 3072), (torch.bfloat16, 3, 12288),
                                              (torch.float32, 5, 136), (torch.bfloat16, 1, 8)])
 @pytest.mark.parametrize("per_row", [True, False])
 def test_quantize_fp8_codes_bit_exact(dtype, rows, cols, per_row):

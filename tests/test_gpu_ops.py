@@ -83,8 +83,12 @@ def test_linear(M, N, K, dt, epi, ydt):
 
 @pytest.mark.parametrize("resdt,ydt", [(torch.bfloat16, torch.float32), (torch.float32, torch.float32),
                                        (torch.float32, torch.bfloat16)])
-def test_linear_gated_residual(resdt, ydt):
-    B, n, C, K = 2, 150, 512, 1024
+@pytest.mark.parametrize("B,n", [(2, 150), (3, 128), (3, 127), (2, 300)])
+def test_linear_gated_residual(resdt, ydt, B, n):
+    """Batch items of 150 rows start inside a wave's 128 rows, of 128 rows on a wave's first
+    row, of 300 rows inside the second 256-row tile; items shorter than 128 rows take the
+    epilogue's per-row gate lookup."""
+    C, K = 512, 1024
     x = _rand((B * n, K), 10, 1.0)
     w = _rand((C, K), 11, 0.02)
     b = _rand((C,), 12, 0.02)
