@@ -36,8 +36,8 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only
 # for the kernel source they were taken on: a different joint_attention.hip reports null.
-ATTN_COUNTERS = {"source_sha256": "5b9c0b9202801d1b",
-                 "fetch_kib": 1104369.4 + 15814.0, "write_kib": 227867.8 + 3056.0,
+ATTN_COUNTERS = {"source_sha256": "39024d9182be8c82",
+                 "fetch_kib": 1104356.0 + 15815.9, "write_kib": 227870.6 + 3056.0,
                  "fetch_scale": 2.0, "write_scale": 1.0}
 
 
