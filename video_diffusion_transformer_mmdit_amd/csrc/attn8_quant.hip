@@ -33,6 +33,21 @@ __device__ __forceinline__ uint32_t pack_i8x4(const float (&v)[8], int o, float 
   return w;
 }
 
+// The four 8-value chunks of a thread's 32 dims of one token row, every load issued before
+// any use (a load under a branch waited for its data before the branch closed); a row past
+// the stream's end reads its last row and is zeroed.
+template <int DT>
+__device__ __forceinline__ void load_dims32(const void* p, int64_t elem, bool valid, float (&x)[4][8]) {
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) load8<DT>(p, elem + 8 * ch, x[ch]);
+  if (!valid) {
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[ch][e] = 0.f;
+  }
+}
+
 // One workgroup per (64-token block, head, batch item) of one stream.  Thread t owns token
 // t / 4 of the block and dims [32 (t % 4), +32).
 template <int DT>
@@ -46,18 +61,13 @@ __global__ __launch_bounds__(256) void attn8_qk_quant_kernel(const void* __restr
   const int tok = threadIdx.x >> 2, qtr = threadIdx.x & 3;
   const int64_t row = (int64_t)blk * A8_TILE + tok;
   const bool valid = row < n;
-  const int64_t src = (b * n + row) * stride + h * A8_D + 32 * qtr;
+  const int64_t src = (b * n + (valid ? row : n - 1)) * stride + h * A8_D + 32 * qtr;
   float qv[4][8], kv[4][8];
   float qa = 0.f, ka = 0.f;
+  load_dims32<DT>(q, src, valid, qv);
+  load_dims32<DT>(k, src, valid, kv);
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch) {
-    if (valid) {
-      load8<DT>(q, src + 8 * ch, qv[ch]);
-      load8<DT>(k, src + 8 * ch, kv[ch]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[ch][e] = kv[ch][e] = 0.f;
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qa = fmaxf(qa, fabsf(qv[ch][e]));
@@ -109,16 +119,13 @@ __global__ __launch_bounds__(256) void attn8_v_amax_kernel(const void* __restric
   const int tok = threadIdx.x >> 2, qtr = threadIdx.x & 3;
   const int64_t row = (int64_t)blk * A8_TILE + tok;
   float m[32];
+  {
+    float x[4][8];
+    load_dims32<DT>(v, (b * n + (row < n ? row : n - 1)) * stride + h * A8_D + 32 * qtr, row < n, x);
 #pragma unroll
-  for (int ch = 0; ch < 4; ++ch) {
-    float x[8];
-    if (row < n) load8<DT>(v, (b * n + row) * stride + h * A8_D + 32 * qtr + 8 * ch, x);
-    else {
+    for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m[8 * ch + e] = fabsf(x[e]);
+      for (int e = 0; e < 8; ++e) m[8 * ch + e] = fabsf(x[ch][e]);
   }
   // lanes 4 apart hold the same dims of other tokens
 #pragma unroll
@@ -149,14 +156,11 @@ __global__ __launch_bounds__(256) void attn8_v_quant_kernel(const void* __restri
   const int64_t row = (int64_t)blk * A8_TILE + tok;
   const float* am = amax + ((int64_t)b * H + h) * A8_D + 32 * qtr;
   const int pos = a8_vpos(tok);
+  float xv[4][8];
+  load_dims32<DT>(v, (b * n + (row < n ? row : n - 1)) * stride + h * A8_D + 32 * qtr, row < n, xv);
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch) {
-    float x[8];
-    if (row < n) load8<DT>(v, (b * n + row) * stride + h * A8_D + 32 * qtr + 8 * ch, x);
-    else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
+    const float (&x)[8] = xv[ch];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const float a0 = am[8 * ch + e], a1 = am[8 * ch + e + 1];
