@@ -30,13 +30,20 @@ __global__ __launch_bounds__(MLN_THREADS) void modulate_ln_kernel(
   const float* sh = shift + b * mod_stride;
   const float* sc = scale + b * mod_stride;
 
+  // Every chunk load is issued before any is used: a load under a bounds branch waited for its
+  // data before the branch closed, so the row's loads went out one at a time.  Chunks past the
+  // row's end load its last chunk and are then zeroed.
   float v[CPL][8];
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int ch = lane + 64 * i;
+    load8<XDT>(x, base + (ch < nchunks ? ch : nchunks - 1) * 8, v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int ch = lane + 64 * i;
     if (ch < nchunks) {
-      load8<XDT>(x, base + ch * 8, v[i]);
       if constexpr (BRANCH) {
         float br[8], gt[8];
         load8<BDT>(branch, base + ch * 8, br);
@@ -65,13 +72,23 @@ __global__ __launch_bounds__(MLN_THREADS) void modulate_ln_kernel(
     }
   }
   const float rstd = rsqrtf(wave_sum<64>(sq) / (float)C + eps);
+  // shift and scale of chunk i + 1 are loaded while chunk i is finished and stored
+  auto mod_load = [&](int i, float (&s8)[8], float (&c8)[8]) {
+    const int ch = lane + 64 * i;
+    const int chc = ch < nchunks ? ch : nchunks - 1;
+    load8<MMDIT_F32>(sh, chc * 8, s8);
+    load8<MMDIT_F32>(sc, chc * 8, c8);
+  };
+  float s8n[8], c8n[8];
+  mod_load(0, s8n, c8n);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int ch = lane + 64 * i;
+    float s8[8], c8[8], o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { s8[e] = s8n[e]; c8[e] = c8n[e]; }
+    if (i + 1 < CPL) mod_load(i + 1, s8n, c8n);
     if (ch < nchunks) {
-      float s8[8], c8[8], o[8];
-      load8<MMDIT_F32>(sh, ch * 8, s8);
-      load8<MMDIT_F32>(sc, ch * 8, c8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         o[e] = fmaf((v[i][e] - mean) * rstd, 1.0f + c8[e], s8[e]);
